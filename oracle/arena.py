@@ -1,0 +1,73 @@
+"""Block arena: where each token's K and V live (oracle; test infrastructure only).
+
+[K3] section 1 "Block-Arena KV Cache": KV memory is reserved once as an arena
+of fixed-size blocks; a sequence's block table maps its logical block i
+(positions 16i .. 16i+15) to a physical block id.  [K3] section 4 reads the
+blocks in place through that table.
+
+Layout (the pages fix none; this is the layout the library documents):
+  K arena  [num_blocks][Hkv][16][D]   token-major inside a (block, head) tile
+  V arena  [num_blocks][Hkv][D][16]   head-dim-major inside a (block, head) tile
+Position ``pos`` of a sequence with table ``bt`` lives in block ``bt[pos // 16]``,
+slot ``pos % 16``.
+
+Two forms:
+  Arena          the values themselves (storage dtype), unwritten slots = NaN
+  SymbolicArena  for each (block, slot) *which* append wrote it (source id,
+                 token index); values are drawn and rotated on demand.  Used for
+                 workloads too large to materialise on the host.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 16
+
+
+def slots(table_row, start: int, n: int):
+    """Physical (block, slot) of positions start .. start+n-1."""
+    pos = start + np.arange(n, dtype=np.int64)
+    row = np.asarray(table_row, dtype=np.int64)
+    return row[pos // BLOCK], pos % BLOCK
+
+
+class Arena:
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype):
+        self.k = np.full((num_blocks, num_kv_heads, BLOCK, head_dim), np.nan, dtype=dtype)
+        self.v = np.full((num_blocks, num_kv_heads, head_dim, BLOCK), np.nan, dtype=dtype)
+
+    def write(self, table_row, start: int, k_store: np.ndarray, v_store: np.ndarray) -> None:
+        """k_store, v_store [n][Hkv][D] (already in the storage dtype)."""
+        blk, slot = slots(table_row, start, k_store.shape[0])
+        self.k[blk, :, slot, :] = k_store
+        self.v[blk, :, :, slot] = v_store
+
+    def copy_block(self, src: int, dst: int) -> None:
+        self.k[dst] = self.k[src]
+        self.v[dst] = self.v[src]
+
+    def gather(self, table_row, length: int):
+        """Dense K, V [length][Hkv][D] of one sequence (the copy the method avoids)."""
+        blk, slot = slots(table_row, 0, length)
+        return self.k[blk, :, slot, :], self.v[blk, :, :, slot]
+
+
+class SymbolicArena:
+    """Per (block, slot): the source that wrote it and the token index inside it."""
+
+    def __init__(self, num_blocks: int):
+        self.src = np.full((num_blocks, BLOCK), -1, dtype=np.int64)
+        self.tok = np.full((num_blocks, BLOCK), -1, dtype=np.int64)
+
+    def write(self, table_row, start: int, n: int, source: int) -> None:
+        blk, slot = slots(table_row, start, n)
+        self.src[blk, slot] = source
+        self.tok[blk, slot] = np.arange(n, dtype=np.int64)
+
+    def copy_block(self, src: int, dst: int) -> None:
+        self.src[dst] = self.src[src]
+        self.tok[dst] = self.tok[src]
+
+    def provenance(self, table_row, length: int):
+        blk, slot = slots(table_row, 0, length)
+        return self.src[blk, slot], self.tok[blk, slot]

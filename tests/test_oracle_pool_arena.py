@@ -1,0 +1,131 @@
+"""Pins for oracle.pool and oracle.arena (CPU only).
+
+  * the LIFO free list against the worked example in tests/golden/lifo_pool.txt
+    (Kshipra part 3, section 1: pop() returns the highest id first, a freed
+    block is the next one handed out);
+  * reference counts and copy-on-write rules (part 3, section 3), and
+    conservation of blocks over random operation sequences;
+  * KV sizing against the figures the pages print (tests/golden/kv_sizing.txt);
+  * arena slot placement against a brute-force per-element loop.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import arena, pool
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_lifo_worked_example():
+    p = pool.Pool(8)
+    for line in open(os.path.join(GOLDEN, "lifo_pool.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        op, arg = line[0], int(line[1])
+        if op == "alloc":
+            assert p.alloc() == arg
+        elif op == "free":
+            p.decref(arg)
+        elif op == "free_count":
+            assert p.num_free == arg
+
+
+def test_fresh_pool_pops_highest_first():
+    p = pool.Pool(32)
+    assert [p.alloc() for _ in range(5)] == [31, 30, 29, 28, 27]
+
+
+def test_out_of_blocks():
+    p = pool.Pool(2)
+    p.alloc(), p.alloc()
+    with pytest.raises(pool.OutOfBlocks):
+        p.alloc()
+
+
+def test_refcount_and_cow():
+    p = pool.Pool(4)
+    b = p.alloc()                      # 3
+    p.incref(b)                        # shared by two owners
+    nb, copied = p.cow(b)
+    assert copied and nb == 2 and p.refcount[b] == 1 and p.refcount[nb] == 1
+    same, copied = p.cow(b)            # sole owner now: written in place
+    assert not copied and same == b
+    p.decref(b)
+    assert p.alloc() == b              # freed block reused next
+    with pytest.raises(pool.RefcountError):
+        p.decref(1)                    # never allocated
+    with pytest.raises(pool.RefcountError):
+        p.incref(0)
+
+
+def test_random_ops_conserve_blocks():
+    rng = np.random.default_rng(0)
+    p = pool.Pool(50)
+    held = []                          # one entry per reference
+    for _ in range(5000):
+        r = rng.random()
+        if r < 0.4 and p.num_free:
+            held.append(p.alloc())
+        elif r < 0.55 and held:
+            b = held[rng.integers(len(held))]
+            p.incref(b)
+            held.append(b)
+        elif r < 0.7 and held:
+            i = rng.integers(len(held))
+            nb, copied = p.cow(held[i]) if p.num_free or held.count(held[i]) == 1 else (held[i], False)
+            held[i] = nb
+        elif held:
+            i = rng.integers(len(held))
+            p.decref(held.pop(i))
+        live = set(held)
+        assert p.num_free + len(live) == 50
+        for b in live:
+            assert p.refcount[b] == held.count(b)
+        assert len(set(p.free)) == len(p.free) and not (set(p.free) & live)
+
+
+def test_kv_sizing_golden():
+    for line in open(os.path.join(GOLDEN, "kv_sizing.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        layers, hkv, d, nbytes, tokens, expected = map(int, line)
+        per_layer = arena.Arena(1, hkv, d, np.float16 if nbytes == 2 else np.float32)
+        block_bytes = per_layer.k[0].nbytes + per_layer.v[0].nbytes   # one 16-token block
+        assert layers * tokens * block_bytes // arena.BLOCK == expected
+
+
+def test_arena_slots_brute_force():
+    rng = np.random.default_rng(2)
+    N, H, D = 12, 3, 8
+    a = arena.Arena(N, H, D, np.float16)
+    table = rng.permutation(N)[:5]
+    start, n = 7, 60
+    k = rng.standard_normal((n, H, D)).astype(np.float16)
+    v = rng.standard_normal((n, H, D)).astype(np.float16)
+    a.write(table, start, k, v)
+    exp_k = np.full((N, H, 16, D), np.nan, np.float16)
+    exp_v = np.full((N, H, D, 16), np.nan, np.float16)
+    for t in range(n):
+        pos = start + t
+        blk, slot = table[pos // 16], pos % 16
+        for h in range(H):
+            for d in range(D):
+                exp_k[blk, h, slot, d] = k[t, h, d]
+                exp_v[blk, h, d, slot] = v[t, h, d]
+    assert np.array_equal(a.k.view(np.uint16), exp_k.view(np.uint16))
+    assert np.array_equal(a.v.view(np.uint16), exp_v.view(np.uint16))
+    K, V = a.gather(table, start + n)
+    assert np.array_equal(K[start:], k) and np.array_equal(V[start:], v)
+    assert np.isnan(K[:start].astype(np.float32)).all()
+
+
+def test_symbolic_arena_tracks_copies():
+    s = arena.SymbolicArena(6)
+    s.write([5, 4], 0, 20, source=3)
+    s.copy_block(4, 1)
+    src, tok = s.provenance([5, 1], 20)
+    assert (src == 3).all() and (tok == np.arange(20)).all()
