@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Paged-KV attention benchmark on one MI355X.
+
+Default run (N = 1):
+  * decode: 64 decode tokens, contexts U[512, 4096], one Llama-3-8B-shaped layer
+    (Hq 32 / Hkv 8, head dim 128, fp16, 16-token blocks, shuffled arena).  A
+    step = restore the un-rotated queries + kv_append_rope for the 64 new
+    tokens + paged_attention_decode (split kernel + log-sum-exp combine).
+    `value` is the algorithmic decode bytes of one step / step time.
+  * chunk prefill (reported under "chunk_prefill"): 8 sequences with cached
+    prefixes 16*U{0..224} and a 512-token chunk each; a step = restore q +
+    kv_append_rope + paged_attention_chunk; TFLOP/s over visible pairs.
+Inputs are synthetic and resident in HBM before timing.  Each timed step
+rotates over --layers copies of the arena (a layer's worth each) so repeated
+steps cannot be served from the 256 MB Infinity Cache.
+
+`roofline` refers to the dominant kernel call (paged_attention_decode), timed
+with HIP events on the stream it is launched on.  `cpu_baseline` times the CPU
+oracle on the same decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_F16_TFLOPS = 2516.6     # MI355X dense fp16 MFMA
+METRIC = "paged-attn decode HBM GB/s + chunk-prefill TFLOP/s, % of MI355X roofline"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_steps(torch, run_step, kernel_events, steps, warmup):
+    for i in range(warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    kernel_events.clear()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ker_ms = [a.elapsed_time(b) for a, b in kernel_events]
+    return (t1 - t0) * 1e3 / steps, sum(ker_ms) / len(ker_ms)
+
+
+def make_layers(torch, dw, n):
+    layers = [(dw.k_arena, dw.v_arena)]
+    for _ in range(n - 1):
+        layers.append((dw.k_arena.clone(), dw.v_arena.clone()))
+    return layers
+
+
+def bench_decode(torch, args):
+    from paged_kv_chunked_amd import harness, workloads
+    w = workloads.decode_batch()
+    log(f"decode set-up: {w.num_blocks} blocks")
+    dw = harness.DeviceWorkload(w)
+    layers = make_layers(torch, dw, args.layers)
+    events = []
+
+    def run(i):
+        k, v = layers[i % len(layers)]
+        dw.reset_q()
+        dw.append(k_arena=k, v_arena=v)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dw.decode(k_arena=k, v_arena=v)
+        b.record()
+        events.append((a, b))
+
+    ms_step, ms_kernel = time_steps(torch, run, events, args.steps, args.warmup)
+    nbytes = dw.decode_bytes()
+    return w, dw, ms_step, ms_kernel, nbytes
+
+
+def bench_chunk(torch, args):
+    from paged_kv_chunked_amd import harness, workloads
+    w = workloads.chunk_batch()
+    log(f"chunk set-up: {w.num_blocks} blocks")
+    dw = harness.DeviceWorkload(w)
+    layers = make_layers(torch, dw, args.layers)
+    events = []
+
+    def run(i):
+        k, v = layers[i % len(layers)]
+        dw.reset_q()
+        dw.append(k_arena=k, v_arena=v)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dw.chunk(k_arena=k, v_arena=v)
+        b.record()
+        events.append((a, b))
+
+    ms_step, ms_kernel = time_steps(torch, run, events, args.steps, args.warmup)
+    return w, dw, ms_step, ms_kernel, dw.chunk_flops()
+
+
+def cpu_baseline(w, target_s):
+    """The oracle (numpy fp64) on the decode workload: append + attention for
+    every decode row, repeated until about target_s seconds have passed."""
+    from oracle import script as oscript
+    from paged_kv_chunked_amd import harness
+    try:
+        import threadpoolctl
+        blas = threadpoolctl.threadpool_info()
+        threads = max((p.get("num_threads", 1) for p in blas), default=1)
+    except Exception:  # pragma: no cover - reporting only
+        threads = len(os.sched_getaffinity(0))
+    st = oscript.run_script(w)
+    cu = [0]
+    for s in w.step:
+        cu.append(cu[-1] + s.count)
+    scale = harness.default_scale(w.head_dim)
+    rows_done = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        q_rot = oscript.append_step(w, st)
+        for r in range(len(w.step)):
+            oscript.attend_row(w, st, r, q_rot[cu[r]:cu[r + 1]], scale)
+            rows_done += 1
+        passes += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    return time.perf_counter() - t0, passes, threads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=4,
+                    help="arena copies rotated over (Infinity Cache guard)")
+    ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the hot path is a "
+              "single-GPU kernel library; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_chunked_amd as pkv
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pkv.lib()
+
+    w, dw, ms_step, ms_dec, nbytes = bench_decode(torch, args)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = nbytes / (ms_dec * 1e-3) / 1e9
+    log(f"decode: step {ms_step:.4f} ms, kernel {ms_dec:.4f} ms, {nbytes / 1e6:.1f} MB "
+        f"-> {achieved:.0f} GB/s kernel, {value:.0f} GB/s step")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_llama3_8b: 64 sequences x 1 query token, contexts U[512,4096], "
+                        "Hq 32 / Hkv 8, head_dim 128, fp16 K/V/Q ~ N(0,1), block 16, "
+                        "shuffled arena (total + 10%), step = kv_append_rope + decode",
+            "num_seqs": len(w.step),
+            "context_tokens": int(sum(dw.dec_lens_host)),
+            "arena_blocks": w.num_blocks,
+            "layers_rotated": args.layers,
+        },
+        "roofline": {
+            "kernel": "paged_attention_decode (decode_split_kernel + decode_combine_kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": nbytes,
+            "avg_launch_ms": round(ms_dec, 5),
+        },
+    }
+    if not args.no_chunk:
+        wc, dwc, ms_cstep, ms_chunk, flops = bench_chunk(torch, args)
+        tf_kernel = flops / (ms_chunk * 1e-3) / 1e12
+        tf_step = flops / (ms_cstep * 1e-3) / 1e12
+        log(f"chunk: step {ms_cstep:.4f} ms, kernel {ms_chunk:.4f} ms, {flops / 1e9:.1f} GFLOP "
+            f"-> {tf_kernel:.1f} TFLOP/s kernel")
+        out["chunk_prefill"] = {
+            "workload": "chunk_llama3_8b: 8 sequences, prefix 16*U{0..224}, 512-token chunk, "
+                        "Hq 32 / Hkv 8, head_dim 128, fp16, RoPE theta 5e5",
+            "value": round(tf_step, 2),
+            "unit": "TFLOP/s",
+            "ms_per_step": round(ms_cstep, 5),
+            "roofline": {
+                "kernel": "paged_attention_chunk (chunk_mfma_kernel)",
+                "bound": "mfma",
+                "achieved": round(tf_kernel, 2),
+                "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(tf_kernel / PEAK_F16_TFLOPS, 4),
+                "traffic": None,
+                "algorithmic_flops_per_launch": flops,
+                "avg_launch_ms": round(ms_chunk, 5),
+            },
+        }
+        del dwc
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        secs, passes, threads = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = {
+            "value": round(nbytes * passes / secs / 1e9, 4),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole decode step (append + attention, {len(w.step)} sequences) "
+                      f"x {passes} passes, {secs:.1f} s, numpy fp64",
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * pkv.h — C ABI of libpkv: attention over a block-arena ("paged") KV cache with
+ * grouped-query heads, for AMD MI355X (gfx950).
+ *
+ * Method: the Kshipra blog series, part 3 (blog/kshipra-3).  Section 1
+ * "Block-Arena KV Cache": KV memory is reserved once as an arena of
+ * fixed-size blocks handed out by a LIFO free list; no allocation per token.
+ * Section 3 "Radix-Tree Prefix Cache": shared blocks are kept alive by
+ * reference counts and a block that diverges is copied before it is written.
+ * Section 4 "Chunked Prefill": attention over a chunk runs an online softmax
+ * across KV blocks read in place from the arena; RoPE uses absolute positions
+ * (a chunk after P cached tokens is rotated at P, P+1, ...); the causal mask
+ * covers the chunk; the result equals dense masked attention.  Part 2
+ * (blog/kshipra-2) section 1 "KV-Caching": a decode step appends the new token's
+ * K/V and attends over the whole cache, the new token included.
+ *
+ * Conventions (every entry point):
+ *   - Return value: PKV_OK, or an error code after host-side validation of
+ *     pointers, geometry, dtypes, sizes and workspace.  Nothing is launched
+ *     when an error is returned.  A failed kernel launch returns PKV_ERR_HIP.
+ *   - Device pointers are owned by the caller.  The library never allocates or
+ *     frees device memory, never synchronises the device, and launches only on
+ *     `stream` (a hipStream_t; NULL = the default stream).  Calls are
+ *     asynchronous with respect to the host unless stated otherwise.
+ *   - Device-resident tables (block ids, lengths, positions) are the caller's
+ *     contract and are not read by the host.  Kernels clamp every index they
+ *     derive from them so that a bad table cannot address memory outside the
+ *     buffers described here; the results for such rows are then unspecified.
+ *     pkv_validate_tables() checks host copies of the tables.
+ *   - Layouts (row-major, innermost index last):
+ *       K arena  [num_blocks][num_kv_heads][16][head_dim]   token-major tile
+ *       V arena  [num_blocks][num_kv_heads][head_dim][16]   head-dim-major tile
+ *     Position `pos` of a sequence whose block-table row is `bt` lives in
+ *     physical block bt[pos / 16], slot pos % 16.  Query head h reads KV head
+ *     h / (num_q_heads / num_kv_heads).
+ *   - Positions are absolute and start at 0 for each sequence's first token
+ *     (part 2, section 2 "Static Batching & the Left-Padding Position Bug").
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+#define PKV_BLOCK_SIZE 16
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,       /* a required pointer is NULL */
+  PKV_ERR_SHAPE = 2,      /* geometry or size not supported / inconsistent */
+  PKV_ERR_DTYPE = 3,      /* unsupported storage or output dtype */
+  PKV_ERR_RANGE = 4,      /* an id, count or position out of range */
+  PKV_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required */
+  PKV_ERR_NOMEM = 6,      /* block pool exhausted */
+  PKV_ERR_REFCOUNT = 7,   /* reference count misuse (block not allocated) */
+  PKV_ERR_HIP = 8         /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_F16 = 0, PKV_F32 = 1 } pkv_dtype;
+
+/* Geometry of one layer's arena.  block_size must be 16; head_dim even and
+ * <= 256; num_q_heads a multiple of num_kv_heads; dtype is the storage dtype of
+ * q, k, v and both arenas (IEEE binary16 or binary32). */
+typedef struct pkv_geom {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pkv_dtype */
+} pkv_geom;
+
+const char* pkv_status_string(pkv_status s);
+int32_t pkv_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * RoPE table (part 3, section 4: RoPE at absolute positions).
+ * Rotate-half RoPE: element i pairs with i + D/2, angle pos * theta^(-2i/D).
+ * Table layout: fp64 [max_pos][head_dim/2][2] = (cos, sin), computed on the host
+ * in fp64 with the C library's pow/cos/sin.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_rope_table_bytes(int32_t head_dim, int32_t max_pos, size_t* bytes);
+/* Fills a host buffer of pkv_rope_table_bytes() bytes. */
+pkv_status pkv_rope_table_host(double* cos_sin, double theta, int32_t head_dim,
+                               int32_t max_pos);
+/* Fills a device buffer: builds the table on the host and copies it with a
+ * synchronous copy on `stream` (set-up call, blocks the host until done). */
+pkv_status pkv_rope_table_init(void* d_cos_sin, double theta, int32_t head_dim,
+                               int32_t max_pos, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_append_rope — append new tokens to the arena (part 3 sections 1 and 4).
+ * For every new token t of sequence b at absolute position
+ *   pos = chunk_start[b] + (t - cu_q_lens[b]):
+ *   q[t][h][:] (all query heads) and k (all KV heads) are rotated by RoPE at
+ *   pos in fp64 (products and sums, no fused multiply-add) and rounded once,
+ *   round-to-nearest-even, to the storage dtype; q is overwritten in place;
+ *   rotated k goes to K arena[bt[b][pos/16]][g][pos%16][:], and v, unchanged, to
+ *   V arena[bt[b][pos/16]][g][:][pos%16].
+ * q            device [num_tokens][Hq][D], rotated in place; may be NULL
+ *              (cache fill without queries).
+ * k, v         device [num_tokens][Hkv][D], read only.
+ * block_table  device int32 [num_seqs][max_blocks_per_seq].
+ * cu_q_lens    device int32 [num_seqs+1], cu_q_lens[0] = 0, nondecreasing,
+ *              cu_q_lens[num_seqs] = num_tokens (empty sequences allowed).
+ * chunk_start  device int32 [num_seqs], first new position P_b of each sequence.
+ * rope_table   device table of pkv_rope_table_init() for >= rope_max_pos
+ *              positions.  Tokens whose position is >= rope_max_pos or past the
+ *              block table are skipped (caller contract violation).
+ * num_tokens == 0 or num_seqs == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+pkv_status kv_append_rope(const pkv_geom* geom, void* q, const void* k, const void* v,
+                          void* k_arena, void* v_arena, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                          const int32_t* chunk_start, int32_t num_seqs, int32_t num_tokens,
+                          const void* rope_table, int32_t rope_max_pos, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * paged_attention_decode — one query token per sequence (part 2 section 1;
+ * part 3 section 4's online-softmax merge over blocks read in place).
+ * For sequence b with context length L = context_lens[b] (the new token,
+ * already appended at position L-1, included) and each query head h:
+ *   out[b][h][:] = softmax_j((q[b][h] . k_j) * scale) @ V,  j = 0 .. L-1.
+ * Split-KV: each sequence's keys are cut into fixed 256-token splits processed
+ * in parallel; splits are merged by their log-sum-exp.  The split size never
+ * depends on the batch, so a sequence's result does not either.
+ * out          device fp32 [num_seqs][Hq][D]  (out_dtype must be PKV_F32).
+ * q            device [num_seqs][Hq][D], already rotated (kv_append_rope).
+ * context_lens device int32 [num_seqs], 1 <= L <= max_context_len
+ *              (rows with L <= 0 are written as zeros).
+ * max_context_len  host upper bound of context_lens (sizes the grid and the
+ *              workspace); must be <= max_blocks_per_seq * 16.
+ * workspace    device scratch of paged_attention_decode_workspace_bytes()
+ *              bytes (split partials); may be NULL when that size is 0.
+ * scale        softmax scale, normally 1/sqrt(head_dim).
+ * ------------------------------------------------------------------------- */
+pkv_status paged_attention_decode_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
+                                                  int32_t max_context_len, size_t* bytes);
+pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                  const void* q, const void* k_arena, const void* v_arena,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, float scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * paged_attention_chunk — prefill chunks (part 3 section 4).
+ * Sequence b has C_b = cu_q_lens[b+1] - cu_q_lens[b] new rows at absolute
+ * positions P_b .. P_b + C_b - 1 (P_b = chunk_start[b]); its cached prefix and
+ * the chunk itself are already in the arena (kv_append_rope).  Row i sees keys
+ * j <= P_b + i: the whole prefix and the chunk up to and including itself.
+ *   out[t][h][:] = softmax_j((q[t][h] . k_j) * scale) @ V over those keys.
+ * out          device fp32 [num_tokens][Hq][D]  (out_dtype must be PKV_F32).
+ * q            device [num_tokens][Hq][D], already rotated.
+ * max_q_len    host upper bound of C_b; max_context_len host upper bound of
+ *              P_b + C_b, <= max_blocks_per_seq * 16.
+ * workspace    as for decode (current kernels need 0 bytes).
+ * ------------------------------------------------------------------------- */
+pkv_status paged_attention_chunk_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
+                                                 int32_t num_tokens, int32_t max_context_len,
+                                                 size_t* bytes);
+pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                 const void* q, const void* k_arena, const void* v_arena,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* cu_q_lens, const int32_t* chunk_start,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                                 int32_t max_context_len, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pkv_copy_blocks — the copy of copy-on-write (part 3 section 3): for each
+ * pair i, block src_dst[2i] is copied bit for bit onto block src_dst[2i+1] in
+ * both arenas (all KV heads, all 16 slots).  src_dst: device int32 [n][2];
+ * pairs whose ids are out of range are skipped.  Destinations must be distinct
+ * and must not be sources of other pairs in the same call.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_copy_blocks(const pkv_geom* geom, void* k_arena, void* v_arena,
+                           const int32_t* src_dst, int32_t n, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block pool (part 3 sections 1 and 3).  The free list starts as
+ * [0, 1, ..., N-1]; allocation pops from its end (highest id first); a block
+ * whose count drops to 0 is pushed on the end and is the next one allocated.
+ * Not thread-safe; owned by the caller.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_pool pkv_pool;
+pkv_pool* pkv_pool_create(int32_t num_blocks);          /* NULL if num_blocks < 1 */
+void pkv_pool_destroy(pkv_pool* pool);
+pkv_status pkv_pool_alloc(pkv_pool* pool, int32_t* id); /* count := 1; NOMEM if empty */
+/* n allocations in a row; all-or-nothing (NOMEM leaves the pool unchanged). */
+pkv_status pkv_pool_alloc_n(pkv_pool* pool, int32_t n, int32_t* ids);
+pkv_status pkv_pool_incref(pkv_pool* pool, int32_t id); /* share one more time */
+pkv_status pkv_pool_decref(pkv_pool* pool, int32_t id); /* at 0: back on the free list */
+/* Copy-on-write decision: if id is shared (count > 1) a fresh block is popped
+ * (*out_id), one reference to id is dropped and *copied = 1 — the caller then
+ * copies the data (pkv_copy_blocks); otherwise *out_id = id, *copied = 0. */
+pkv_status pkv_pool_cow(pkv_pool* pool, int32_t id, int32_t* out_id, int32_t* copied);
+int32_t pkv_pool_num_free(const pkv_pool* pool);
+int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t id); /* -1 if out of range */
+/* Copies the free list, bottom first, into out[0..cap); *n = its length. */
+pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* Host check of table copies: every row with length L > 0 needs
+ * ceil(L/16) <= max_blocks_per_seq entries, each in [0, num_blocks). */
+pkv_status pkv_validate_tables(const pkv_geom* geom, const int32_t* h_block_table,
+                               int32_t max_blocks_per_seq, const int32_t* h_lens,
+                               int32_t num_seqs);
+
+/* The library's fp64 -> fp16 rounding (round-to-nearest-even, subnormals,
+ * overflow to infinity), the same routine kv_append_rope uses on the device,
+ * run on the host: n values from x to out (IEEE binary16 bit patterns). */
+pkv_status pkv_f64_to_f16_host(const double* x, uint16_t* out, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,122 @@
+// C ABI entry points of libpkv: host-side validation, then kernel launches on
+// the caller's stream.  See include/pkv.h for the contracts.
+#include "pkv_internal.h"
+
+namespace {
+
+pkv_status check_geom(const pkv_geom* g) {
+  if (!g) return PKV_ERR_NULL;
+  if (g->block_size != PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
+  if (g->num_blocks < 1 || g->num_kv_heads < 1 || g->num_q_heads < 1) return PKV_ERR_SHAPE;
+  if (g->num_q_heads % g->num_kv_heads) return PKV_ERR_SHAPE;
+  if (g->head_dim < 2 || g->head_dim % 2 || g->head_dim > 256) return PKV_ERR_SHAPE;
+  if (g->dtype != PKV_F16 && g->dtype != PKV_F32) return PKV_ERR_DTYPE;
+  return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+pkv_status kv_append_rope(const pkv_geom* geom, void* q, const void* k, const void* v,
+                          void* k_arena, void* v_arena, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                          const int32_t* chunk_start, int32_t num_seqs, int32_t num_tokens,
+                          const void* rope_table, int32_t rope_max_pos, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0) return PKV_ERR_RANGE;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_arena || !v_arena || !block_table || !cu_q_lens || !chunk_start ||
+      !rope_table)
+    return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || rope_max_pos < 1) return PKV_ERR_RANGE;
+  return hip_status(pkv::launch_append_rope(*geom, q, k, v, k_arena, v_arena, block_table,
+                                            max_blocks_per_seq, cu_q_lens, chunk_start,
+                                            num_seqs, num_tokens, rope_table, rope_max_pos,
+                                            (hipStream_t)stream));
+}
+
+pkv_status paged_attention_decode_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
+                                                  int32_t max_context_len, size_t* bytes) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (!bytes) return PKV_ERR_NULL;
+  if (num_seqs < 0 || max_context_len < 0) return PKV_ERR_RANGE;
+  *bytes = pkv::decode_workspace_bytes(*geom, num_seqs, max_context_len);
+  return PKV_OK;
+}
+
+pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                  const void* q, const void* k_arena, const void* v_arena,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, float scale, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  if (num_seqs < 0) return PKV_ERR_RANGE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_arena || !v_arena || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || max_context_len < 1 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return PKV_ERR_RANGE;
+  const size_t need = pkv::decode_workspace_bytes(*geom, num_seqs, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  return hip_status(pkv::launch_decode(*geom, (float*)out, q, k_arena, v_arena, block_table,
+                                       max_blocks_per_seq, context_lens, num_seqs,
+                                       max_context_len, scale, workspace,
+                                       (hipStream_t)stream));
+}
+
+pkv_status paged_attention_chunk_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
+                                                 int32_t num_tokens, int32_t max_context_len,
+                                                 size_t* bytes) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (!bytes) return PKV_ERR_NULL;
+  if (num_seqs < 0 || num_tokens < 0 || max_context_len < 0) return PKV_ERR_RANGE;
+  *bytes = 0;
+  return PKV_OK;
+}
+
+pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                 const void* q, const void* k_arena, const void* v_arena,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* cu_q_lens, const int32_t* chunk_start,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                                 int32_t max_context_len, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0) return PKV_ERR_RANGE;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_arena || !v_arena || !block_table || !cu_q_lens || !chunk_start)
+    return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || max_q_len < 1 || max_context_len < max_q_len ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return PKV_ERR_RANGE;
+  return hip_status(pkv::launch_chunk(*geom, (float*)out, q, k_arena, v_arena, block_table,
+                                      max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs,
+                                      num_tokens, max_q_len, max_context_len, scale,
+                                      (hipStream_t)stream));
+}
+
+pkv_status pkv_copy_blocks(const pkv_geom* geom, void* k_arena, void* v_arena,
+                           const int32_t* src_dst, int32_t n, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (n < 0) return PKV_ERR_RANGE;
+  if (n == 0) return PKV_OK;
+  if (!k_arena || !v_arena || !src_dst) return PKV_ERR_NULL;
+  return hip_status(pkv::launch_copy_blocks(*geom, k_arena, v_arena, src_dst, n,
+                                            (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal declarations shared by the libpkv translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// Decode split size in tokens (16 arena blocks).  Fixed, never derived from the
+// batch, so a sequence's decode result is independent of the other sequences.
+constexpr int kDecodeSplit = 256;
+constexpr int kBlock = PKV_BLOCK_SIZE;
+
+// fp64 -> IEEE binary16 bits, round to nearest, ties to even, written from the
+// IEEE 754 definition: the exact value sig * 2^(e-52) is expressed in units of
+// the destination ulp 2^(max(e,-14)-10); the dropped bits decide the rounding.
+// Handles fp16 subnormals, overflow to infinity, infinities and NaN.
+__host__ __device__ inline uint16_t f64_to_f16_bits(double x) {
+  uint64_t u;
+  __builtin_memcpy(&u, &x, 8);
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  const int bexp = (int)((u >> 52) & 0x7FF);
+  const uint64_t man = u & ((1ull << 52) - 1);
+  if (bexp == 0x7FF) return (uint16_t)(sign | 0x7C00u | (man ? 0x0200u : 0u));
+  if (bexp == 0) return sign;                     // |x| < 2^-1022: rounds to zero
+  const int e = bexp - 1023;
+  if (e > 15) return (uint16_t)(sign | 0x7C00u);  // >= 2^16: infinity
+  const uint64_t sig = (1ull << 52) | man;
+  const int te = e < -14 ? -14 : e;
+  const int shift = 42 + (te - e);               // 52 - 10 + (te - e)
+  if (shift >= 54) return sign;                   // below half the smallest subnormal
+  uint64_t qv = sig >> shift;
+  const uint64_t rem = sig & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (qv & 1))) ++qv;
+  if (te == -14 && qv < 1024) return (uint16_t)(sign | qv);          // subnormal
+  const uint32_t bits = ((uint32_t)(te + 15) << 10) + (uint32_t)(qv - 1024);  // carry ok
+  if (bits >= 0x7C00u) return (uint16_t)(sign | 0x7C00u);
+  return (uint16_t)(sign | bits);
+}
+
+// ---- launchers (defined in the kernel translation units) -------------------
+hipError_t launch_append_rope(const pkv_geom& g, void* q, const void* k, const void* v,
+                              void* k_arena, void* v_arena, const int32_t* block_table,
+                              int max_blocks, const int32_t* cu_q_lens,
+                              const int32_t* chunk_start, int num_seqs, int num_tokens,
+                              const void* rope_table, int rope_max_pos, hipStream_t stream);
+
+bool decode_fast_path(const pkv_geom& g);
+size_t decode_workspace_bytes(const pkv_geom& g, int num_seqs, int max_context_len);
+hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const void* k_arena,
+                         const void* v_arena, const int32_t* block_table, int max_blocks,
+                         const int32_t* context_lens, int num_seqs, int max_context_len,
+                         float scale, void* workspace, hipStream_t stream);
+
+bool chunk_fast_path(const pkv_geom& g);
+hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
+                        const void* v_arena, const int32_t* block_table, int max_blocks,
+                        const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
+                        int num_tokens, int max_q_len, int max_context_len, float scale,
+                        hipStream_t stream);
+
+// Generic (any dtype / head_dim / group) attention, one workgroup per
+// (row, query head).  Decode rows when cu_q_lens == nullptr.
+hipError_t launch_attend_generic(const pkv_geom& g, float* out, const void* q,
+                                 const void* k_arena, const void* v_arena,
+                                 const int32_t* block_table, int max_blocks,
+                                 const int32_t* context_lens, const int32_t* cu_q_lens,
+                                 const int32_t* chunk_start, int num_seqs, int num_rows,
+                                 float scale, hipStream_t stream);
+
+hipError_t launch_copy_blocks(const pkv_geom& g, void* k_arena, void* v_arena,
+                              const int32_t* src_dst, int n, hipStream_t stream);
+
+}  // namespace pkv

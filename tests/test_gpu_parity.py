@@ -1,0 +1,303 @@
+"""GPU parity: the HIP library against the CPU oracle (needs an MI355X).
+
+Every case runs a seeded workload through libpkv (pool script on the library
+pool, cache fills and the step's append through kv_append_rope, copy-on-write
+through pkv_copy_blocks, then paged_attention_chunk / paged_attention_decode)
+and through the oracle, and compares:
+  * block tables, rotated queries and arena contents: bit for bit;
+  * attention outputs: max |gpu - oracle| <= 2e-3 and mean <= 2e-4 (fp16
+    inputs, fp32 accumulation; fp32 workloads share the bound).
+Small workloads are compared element by element everywhere; the full-size
+decode and chunk workloads are compared in full; the mixed and long-context
+workloads on sampled sequences and rows (their K/V regenerated and rotated by
+the oracle for just those sequences).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_chunked_amd as pkv  # noqa: E402
+from oracle import rope as orope  # noqa: E402
+from oracle import script as oscript  # noqa: E402
+from paged_kv_chunked_amd import harness, workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-3
+MEAN_ABS = 2e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.fail("libpkv.so is not built")
+    pkv.lib()
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint16 if a.dtype == np.float16 else np.uint32)
+
+
+class Errors:
+    def __init__(self):
+        self.max = 0.0
+        self.sum = 0.0
+        self.n = 0
+
+    def add(self, got, exp):
+        d = np.abs(np.asarray(got, np.float64) - exp)
+        assert np.isfinite(d).all(), "non-finite output"
+        self.max = max(self.max, float(d.max()))
+        self.sum += float(d.sum())
+        self.n += d.size
+
+    def check(self, name):
+        mean = self.sum / max(self.n, 1)
+        say(f"{name}: {self.n} outputs, max abs {self.max:.3e}, mean abs {mean:.3e}")
+        assert self.max <= MAX_ABS, (name, self.max)
+        assert mean <= MEAN_ABS, (name, mean)
+
+
+def run_case(w, full_arena=True, dec_sample=None, chunk_sample=None):
+    """Runs workload w on the GPU and checks it against the oracle."""
+    say(f"{w.name}: set-up (blocks={w.num_blocks}, step rows={len(w.step)})")
+    dw = harness.DeviceWorkload(w)
+    dw.reset_q()
+    say(f"{w.name}: step")
+    dw.step()
+    torch.cuda.synchronize()
+    say(f"{w.name}: oracle")
+    st = oscript.run_script(w, materialize=full_arena)
+    assert dw.copies == st.copies
+    assert np.array_equal(dw.bt_host, oscript.block_table(w, st))
+    q_rot = oscript.append_step(w, st)
+    assert np.array_equal(bits(dw.q.cpu().numpy()), bits(q_rot)), "rotated q differs"
+    if full_arena:
+        assert np.array_equal(bits(dw.k_arena.cpu().numpy()), bits(st.arena.k)), "K arena differs"
+        assert np.array_equal(bits(dw.v_arena.cpu().numpy()), bits(st.arena.v)), "V arena differs"
+    errs = Errors()
+    cu = dw.cu_host
+    dec_rows = dw.dec_rows if dec_sample is None else dec_sample
+    for r in dec_rows:
+        s = w.step[r]
+        if not full_arena:  # the sampled sequence's arena blocks, bit for bit
+            K, V = oscript.sequence_kv(w, st, r)
+            L = s.start + 1
+            tab = torch.tensor(dw.tables[s.seq][:-(-L // 16)], device=dw.device)
+            kg = dw.k_arena.index_select(0, tab).cpu().numpy()
+            vg = dw.v_arena.index_select(0, tab).cpu().numpy()
+            kg = kg.transpose(0, 2, 1, 3).reshape(-1, w.num_kv_heads, w.head_dim)[:L]
+            vg = vg.transpose(0, 3, 1, 2).reshape(-1, w.num_kv_heads, w.head_dim)[:L]
+            assert np.array_equal(bits(kg), bits(K)) and np.array_equal(bits(vg), bits(V))
+        exp = oscript.attend_row(w, st, r, q_rot[cu[r]:cu[r + 1]], dw.scale)[0]
+        errs.add(dw.dec_out[r - dw.dec_rows[0]].cpu().numpy(), exp)
+    chunk_rows = dw.chunk_rows if chunk_sample is None else list(chunk_sample)
+    for r in chunk_rows:
+        s = w.step[r]
+        rows = None
+        if chunk_sample is not None:
+            rng = np.random.default_rng(r)
+            rows = np.unique(np.concatenate([[0, s.count - 1],
+                                             rng.integers(0, s.count, size=chunk_sample[r])]))
+        exp = oscript.attend_row(w, st, r, q_rot[cu[r]:cu[r + 1]], dw.scale, rows=rows)
+        t0 = cu[r] - dw.chunk_tok0
+        got = dw.chunk_out[t0:t0 + s.count].cpu().numpy()
+        errs.add(got if rows is None else got[rows], exp)
+    errs.check(w.name)
+    return dw, st, q_rot
+
+
+# ---------------------------------------------------------------------------
+# small workloads: every element
+# ---------------------------------------------------------------------------
+
+def small_decode():
+    lens = [1, 2, 15, 16, 17, 100, 255, 256, 257, 258, 511, 512, 513, 1000, 1600, 2049]
+    return workloads.build("small_decode", 11, "f16", 32, 8, 128, 5.0e5,
+                           [(L - 1, 1) for L in lens], max_blocks_per_seq=130)
+
+
+def small_chunk():
+    seqs = [(0, 1), (0, 33), (48, 16), (5, 70), (100, 129), (0, 200), (300, 64), (17, 5),
+            (1000, 31), (64, 64)]
+    return workloads.build("small_chunk", 12, "f16", 32, 8, 128, 5.0e5, seqs,
+                           max_blocks_per_seq=80)
+
+
+def small_mixed():
+    return workloads.mixed_step(num_chunks=2, chunk=96, num_decodes=40, lo=1, hi=1200,
+                                num_sharers=5, shared_prefix=256, parent_tokens=264)
+
+
+def generic_shape(name, dtype, hq, hkv, d):
+    seqs = [(0, 1), (40, 1), (299, 1), (0, 20), (37, 45)]
+    return workloads.build(name, 13, dtype, hq, hkv, d, 1.0e4, seqs, max_blocks_per_seq=24)
+
+
+SMALL = {
+    "tiny_f32": workloads.tiny,
+    "small_decode": small_decode,
+    "small_chunk": small_chunk,
+    "small_mixed": small_mixed,
+    "generic_f16_d64": lambda: generic_shape("generic_f16_d64", "f16", 8, 2, 64),
+    "generic_f16_g2": lambda: generic_shape("generic_f16_g2", "f16", 8, 4, 128),
+    "generic_f16_g8": lambda: generic_shape("generic_f16_g8", "f16", 16, 2, 128),
+    "generic_f32_d128": lambda: generic_shape("generic_f32_d128", "f32", 8, 2, 128),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small(name):
+    run_case(SMALL[name]())
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+
+def test_decode_full():
+    run_case(workloads.decode_batch())
+
+
+def test_chunk_full():
+    run_case(workloads.chunk_batch())
+
+
+def test_mixed_full_sampled():
+    w = workloads.mixed_step()
+    sharers = [op[1] for op in w.script if op[0] == "fork"]
+    rng = np.random.default_rng(0)
+    others = rng.choice(w.decode_rows(), size=6, replace=False).tolist()
+    run_case(w, full_arena=False, dec_sample=sorted(set(sharers[:4] + others)),
+             chunk_sample={r: 24 for r in w.chunk_rows()})
+
+
+def test_long_full_sampled():
+    w = workloads.long_context()
+    run_case(w, full_arena=False, dec_sample=[1, 17, 32], chunk_sample={0: 40})
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU path
+# ---------------------------------------------------------------------------
+
+def _same_data_other_blocks(seed_perm):
+    seqs = [(L - 1, 1) for L in (300, 1000, 17, 2500)] + [(77, 150), (0, 64)]
+    return workloads.build("perm", 21, "f16", 32, 8, 128, 5.0e5, seqs, slack=1.5,
+                           max_blocks_per_seq=160,
+                           shuffle_rng=np.random.default_rng(seed_perm))
+
+
+def test_block_permutation_invariance_bitwise():
+    outs = []
+    for sp in (1, 2):
+        w = _same_data_other_blocks(sp)
+        say(f"permutation {sp}")
+        dw = harness.DeviceWorkload(w)
+        dw.reset_q()
+        dw.step()
+        torch.cuda.synchronize()
+        outs.append((dw.bt_host.copy(), dw.dec_out.cpu().numpy(), dw.chunk_out.cpu().numpy()))
+    assert not np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(bits(outs[0][1]), bits(outs[1][1]))
+    assert np.array_equal(bits(outs[0][2]), bits(outs[1][2]))
+
+
+def test_batch_invariance_bitwise():
+    w = workloads.decode_batch(num_seqs=16, lo=1, hi=3000)
+    say("batch invariance")
+    dw = harness.DeviceWorkload(w)
+    dw.reset_q()
+    dw.step()
+    torch.cuda.synchronize()
+    full = dw.dec_out.cpu().numpy()
+    for r in (0, 5, 15):
+        out = torch.empty((1, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dw.device)
+        L = int(dw.dec_lens_host[r])
+        ws_n = pkv.paged_attention_decode_workspace_bytes(dw.g, 1, L)
+        ws = torch.empty(max(ws_n, 4) // 4, dtype=torch.float32, device=dw.device) if ws_n else None
+        pkv.paged_attention_decode(dw.g, out, dw.dec_q[r:r + 1], dw.k_arena, dw.v_arena,
+                                   dw.dec_bt[r:r + 1], dw.dec_lens[r:r + 1], L, dw.scale, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out.cpu().numpy()[0]), bits(full[r]))
+
+
+def test_single_key_returns_v_exactly():
+    w = workloads.build("one_key", 31, "f16", 32, 8, 128, 5.0e5, [(0, 1), (0, 1)],
+                        max_blocks_per_seq=2)
+    dw = harness.DeviceWorkload(w)
+    dw.reset_q()
+    dw.step()
+    torch.cuda.synchronize()
+    _, _, v = w.draw_step_packed()
+    out = dw.dec_out.cpu().numpy()
+    for b in range(2):
+        for h in range(32):
+            assert np.array_equal(out[b, h], v[b, h // 4].astype(np.float32))
+
+
+def test_decode_matches_last_chunk_row():
+    w = workloads.build("last_row", 41, "f16", 32, 8, 128, 5.0e5, [(700, 100)],
+                        max_blocks_per_seq=60)
+    dw = harness.DeviceWorkload(w)
+    dw.reset_q()
+    dw.step()
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device=dw.device)
+    lens = torch.tensor([800], dtype=torch.int32, device=dw.device)
+    ws_n = pkv.paged_attention_decode_workspace_bytes(dw.g, 1, 800)
+    ws = torch.empty(ws_n // 4, dtype=torch.float32, device=dw.device)
+    pkv.paged_attention_decode(dw.g, out, dw.chunk_q[99:100], dw.k_arena, dw.v_arena,
+                               dw.chunk_bt, lens, 800, dw.scale, ws)
+    torch.cuda.synchronize()
+    d = np.abs(out.cpu().numpy()[0] - dw.chunk_out[99].cpu().numpy())
+    assert d.max() <= MAX_ABS
+
+
+def test_copy_blocks_bitwise_and_skips_bad_pairs():
+    g = pkv.geom(8, 2, 8, 64)
+    k = torch.randn(8, 2, 16, 64, device="cuda").half()
+    v = torch.randn(8, 2, 64, 16, device="cuda").half()
+    k0, v0 = k.clone(), v.clone()
+    pairs = torch.tensor([[1, 5], [2, 6], [3, 99], [-1, 0]], dtype=torch.int32, device="cuda")
+    pkv.pkv_copy_blocks(g, k, v, pairs)
+    torch.cuda.synchronize()
+    exp_k, exp_v = k0.clone(), v0.clone()
+    exp_k[5], exp_v[5] = k0[1], v0[1]
+    exp_k[6], exp_v[6] = k0[2], v0[2]
+    assert torch.equal(k.view(torch.int16), exp_k.view(torch.int16))
+    assert torch.equal(v.view(torch.int16), exp_v.view(torch.int16))
+
+
+def test_empty_and_degenerate_batches():
+    g = pkv.geom(4, 8, 32, 128)
+    dev = "cuda"
+    k_ar = torch.zeros(4, 8, 16, 128, dtype=torch.float16, device=dev)
+    v_ar = torch.zeros(4, 8, 128, 16, dtype=torch.float16, device=dev)
+    bt = torch.tensor([[0, 1], [2, 3]], dtype=torch.int32, device=dev)
+    # a chunk batch with an empty sequence in the middle
+    cu = torch.tensor([0, 3, 3, 5], dtype=torch.int32, device=dev)
+    starts = torch.tensor([0, 7, 20], dtype=torch.int32, device=dev)
+    bt3 = torch.tensor([[0, 1], [2, 3], [1, 0]], dtype=torch.int32, device=dev)
+    q = torch.randn(5, 32, 128, device=dev).half()
+    out = torch.full((5, 32, 128), float("nan"), device=dev)
+    pkv.paged_attention_chunk(g, out, q, k_ar, v_ar, bt3, cu, starts, 3, 25, 0.1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    # decode rows of length 0 give zeros
+    lens = torch.tensor([0, 5], dtype=torch.int32, device=dev)
+    outd = torch.full((2, 32, 128), float("nan"), device=dev)
+    pkv.paged_attention_decode(g, outd, q[:2].contiguous(), k_ar, v_ar, bt, lens, 32, 0.1, None)
+    torch.cuda.synchronize()
+    assert torch.equal(outd[0], torch.zeros_like(outd[0])) and torch.isfinite(outd[1]).all()
+    del math

@@ -1,0 +1,248 @@
+"""Host-side tests of libpkv (CPU only, no GPU calls).
+
+  * the library loads and exports every function include/pkv.h declares;
+  * the library pool equals the oracle pool bit for bit (ids handed out,
+    copy-on-write decisions, free-list order) on random operation sequences
+    and on every workload's pool script;
+  * the library's RoPE table equals the oracle's bit for bit;
+  * the library's fp64 -> fp16 rounding equals numpy's (itself pinned to exact
+    rational rounding in test_oracle_rope.py);
+  * argument validation of every entry point (errors return before anything
+    is launched, so these calls are safe without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_chunked_amd as pkv
+from oracle import pool as opool
+from oracle import rope as orope
+from oracle import script as oscript
+from paged_kv_chunked_amd import harness, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.skip("libpkv.so not built")
+    return pkv.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert pkv.pkv_abi_version() == 1
+
+
+def test_rope_table_bitwise_equals_oracle(lib):
+    for theta, D, max_pos in [(1.0e4, 64, 700), (5.0e5, 128, 9000)]:
+        ours = np.empty((max_pos, D // 2, 2), np.float64)
+        pkv.pkv_rope_table_host(ours, theta, D, max_pos)
+        cos, sin = orope.cos_sin_table(theta, D, max_pos)
+        assert np.array_equal(ours[..., 0].view(np.uint64), cos.view(np.uint64))
+        assert np.array_equal(ours[..., 1].view(np.uint64), sin.view(np.uint64))
+    assert pkv.pkv_rope_table_bytes(128, 10) == 10 * 64 * 16
+
+
+def test_f64_to_f16_matches_numpy(lib):
+    rng = np.random.default_rng(0)
+    special = np.array([0.0, -0.0, 1.0, 65504.0, 65519.99, 65520.0, 1e6, -1e6, np.inf, -np.inf,
+                        2.0 ** -24, 2.0 ** -25, 2.0 ** -25 + 2.0 ** -50, 3 * 2.0 ** -25,
+                        2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 2.0 ** -1030, 5e-324,
+                        1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -40])
+    mant = rng.integers(0, 2 ** 11, size=20000)
+    ties = (1.0 + (2 * mant + 1) * 2.0 ** -12) * 2.0 ** rng.integers(-26, 16, size=20000)
+    near = ties * (1 + rng.choice([-1, 1], size=20000) * 2.0 ** -45)
+    bits = rng.integers(0, 2 ** 64 - 1, size=20000, dtype=np.uint64).view(np.float64)
+    bits = bits[np.isfinite(bits)]
+    x = np.concatenate([special, -special, ties, -ties, near, bits,
+                        rng.standard_normal(100000) * 4, rng.standard_normal(20000) * 1e-5])
+    ours = np.empty(x.size, np.uint16)
+    pkv.pkv_f64_to_f16_host(x, ours)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+    nan = np.array([np.nan])
+    o = np.empty(1, np.uint16)
+    pkv.pkv_f64_to_f16_host(nan, o)
+    assert (o[0] & 0x7C00) == 0x7C00 and (o[0] & 0x3FF) != 0
+
+
+# ---------------------------------------------------------------------------
+# pool
+# ---------------------------------------------------------------------------
+
+def test_pool_random_ops_match_oracle(lib):
+    rng = np.random.default_rng(3)
+    for trial in range(5):
+        N = int(rng.integers(1, 40))
+        a, b = pkv.Pool(N), opool.Pool(N)
+        held = []
+        for _ in range(3000):
+            r = rng.random()
+            if r < 0.35:
+                if b.num_free:
+                    x = b.alloc()
+                    assert a.alloc() == x
+                    held.append(x)
+                else:
+                    with pytest.raises(pkv.PkvError) as e:
+                        a.alloc()
+                    assert e.value.code == 6
+            elif r < 0.5 and held:
+                x = held[int(rng.integers(len(held)))]
+                a.incref(x)
+                b.incref(x)
+                held.append(x)
+            elif r < 0.65 and held:
+                i = int(rng.integers(len(held)))
+                x = held[i]
+                if b.refcount[x] > 1 and not b.num_free:
+                    continue
+                nb, cb = b.cow(x)
+                na, ca = a.cow(x)
+                assert (na, ca) == (nb, cb)
+                held[i] = nb
+            elif held:
+                x = held.pop(int(rng.integers(len(held))))
+                a.decref(x)
+                b.decref(x)
+            assert a.num_free == b.num_free
+            assert list(a.free_list()) == b.free
+        for x in range(N):
+            assert a.refcount(x) == b.refcount.get(x, 0)
+
+
+def test_pool_errors(lib):
+    p = pkv.Pool(2)
+    with pytest.raises(pkv.PkvError) as e:
+        p.decref(0)
+    assert e.value.code == 7
+    with pytest.raises(pkv.PkvError) as e:
+        p.incref(5)
+    assert e.value.code == 4
+    with pytest.raises(pkv.PkvError) as e:
+        p.alloc_n(3)
+    assert e.value.code == 6 and p.num_free == 2      # all or nothing
+    x = p.alloc()
+    assert p.cow(x) == (x, False)
+    assert lib.pkv_pool_create(0) is None
+
+
+@pytest.mark.parametrize("make", [
+    workloads.tiny,
+    lambda: workloads.decode_batch(num_seqs=9, lo=1, hi=700),
+    lambda: workloads.chunk_batch(num_seqs=3, chunk=100, max_prefix_blocks=20),
+    lambda: workloads.mixed_step(num_chunks=2, chunk=40, num_decodes=30, lo=20, hi=600,
+                                 num_sharers=4, shared_prefix=64, parent_tokens=72),
+    workloads.decode_batch, workloads.chunk_batch, workloads.mixed_step,
+])
+def test_workload_tables_match_oracle(lib, make):
+    w = make()
+    tables = {s: [] for s in range(w.num_pool_seqs)}
+    p = pkv.Pool(w.num_blocks)
+    copies = harness.run_pool_script(w, p, tables)
+    st = oscript.run_script(w, materialize=False)
+    assert tables == st.tables
+    assert copies == st.copies
+    assert list(p.free_list()) == st.pool.free
+
+
+def test_validate_tables(lib):
+    g = pkv.geom(10, 2, 4, 64)
+    bt = np.array([[3, 4, -1], [9, -1, -1]], np.int32)
+    pkv.pkv_validate_tables(g, bt, np.array([20, 16], np.int32))
+    for lens in ([20, 17], [49, 1], [-1, 1]):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_validate_tables(g, bt, np.array(lens, np.int32))
+        assert e.value.code == 4
+    bad = bt.copy()
+    bad[1, 0] = 10
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_validate_tables(g, bad, np.array([20, 16], np.int32))
+
+
+# ---------------------------------------------------------------------------
+# argument validation of the device entry points (nothing is launched)
+# ---------------------------------------------------------------------------
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _geom(**kw):
+    g = dict(num_blocks=64, block_size=16, num_kv_heads=8, num_q_heads=32, head_dim=128, dtype=0)
+    g.update(kw)
+    return pkv.Geom(**g)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_size=32), 2), (dict(num_q_heads=30), 2), (dict(head_dim=130 * 2), 2),
+    (dict(head_dim=3), 2), (dict(num_blocks=0), 2), (dict(dtype=7), 3), (dict(num_kv_heads=0), 2),
+])
+def test_bad_geometry_rejected(lib, kw, code):
+    g = _geom(**kw)
+    r = lib.kv_append_rope(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE,
+                           1, 1, FAKE, 100, None)
+    assert r == code
+    r = lib.paged_attention_decode(ctypes.byref(g), FAKE, 1, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1,
+                                   64, 0.1, FAKE, 1 << 20, None)
+    assert r == code
+    r = lib.paged_attention_chunk(ctypes.byref(g), FAKE, 1, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE,
+                                  1, 16, 16, 64, 0.1, None, 0, None)
+    assert r == code
+    assert lib.pkv_copy_blocks(ctypes.byref(g), FAKE, FAKE, FAKE, 1, None) == code
+
+
+def test_entry_point_errors(lib):
+    g = _geom()
+    gp = ctypes.byref(g)
+    # nulls
+    assert lib.kv_append_rope(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1,
+                              FAKE, 100, None) == 1
+    assert lib.kv_append_rope(gp, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1,
+                              FAKE, 100, None) == 1
+    assert lib.paged_attention_decode(gp, None, 1, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 64, 0.1,
+                                      FAKE, 1 << 20, None) == 1
+    # empty batches are a no-op (no launch)
+    assert lib.kv_append_rope(gp, None, None, None, None, None, None, 4, None, None, 0, 0, None,
+                              100, None) == 0
+    assert lib.paged_attention_decode(gp, None, 1, None, None, None, None, 4, None, 0, 64, 0.1,
+                                      None, 0, None) == 0
+    assert lib.paged_attention_chunk(gp, None, 1, None, None, None, None, 4, None, None, 0, 0,
+                                     16, 64, 0.1, None, 0, None) == 0
+    assert lib.pkv_copy_blocks(gp, None, None, None, 0, None) == 0
+    # dtype of the output
+    assert lib.paged_attention_decode(gp, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 64, 0.1,
+                                      FAKE, 1 << 20, None) == 3
+    # context longer than the block table can hold
+    assert lib.paged_attention_decode(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 65, 0.1,
+                                      FAKE, 1 << 20, None) == 4
+    assert lib.paged_attention_chunk(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 16,
+                                     16, 65, 0.1, None, 0, None) == 4
+    assert lib.paged_attention_chunk(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 16,
+                                     32, 16, 0.1, None, 0, None) == 4
+    # workspace
+    need = pkv.paged_attention_decode_workspace_bytes(g, 3, 1000)
+    assert need == 3 * 32 * 4 * 130 * 4
+    assert pkv.paged_attention_decode_workspace_bytes(g, 3, 256) == 0
+    assert lib.paged_attention_decode(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000,
+                                      0.1, FAKE, need - 1, None) == 5
+    assert lib.paged_attention_decode(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000,
+                                      0.1, None, need, None) == 5
+    assert pkv.paged_attention_chunk_workspace_bytes(g, 2, 100, 500) == 0
+    assert lib.pkv_status_string(5) == b"workspace missing or too small"
