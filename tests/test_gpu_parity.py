@@ -12,7 +12,6 @@ decode and chunk workloads are compared in full; the mixed and long-context
 workloads on sampled sequences and rows (their K/V regenerated and rotated by
 the oracle for just those sequences).
 """
-import math
 import os
 
 import numpy as np
@@ -300,4 +299,3 @@ def test_empty_and_degenerate_batches():
     pkv.paged_attention_decode(g, outd, q[:2].contiguous(), k_ar, v_ar, bt, lens, 32, 0.1, None)
     torch.cuda.synchronize()
     assert torch.equal(outd[0], torch.zeros_like(outd[0])) and torch.isfinite(outd[1]).all()
-    del math
