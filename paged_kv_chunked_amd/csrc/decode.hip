@@ -8,15 +8,20 @@
 //   * split-KV: the keys of each sequence are cut into fixed 256-token splits
 //     (16 arena blocks); one 64-lane wavefront per (sequence, KV head, split)
 //     serves all 4 query heads of the group, so each K/V byte is read once;
-//   * each 16-token block is one 4 KiB K tile and one 4 KiB V tile, fetched
-//     with 16-byte fully coalesced loads into registers one block ahead, then
-//     staged in LDS (XOR-swizzled: conflict-free 16-byte reads);
-//   * QK: lane (h, j) = (query head, token) dots q_h with k_j using packed
-//     fp16 dot products accumulating in fp32; the per-head block max is a
-//     16-lane reduction; p = 2^(s - m) in fp32 (scores carry log2(e));
-//   * PV: lane (h, c) accumulates 8 head dims (c, c+16, ...) over the block's
-//     16 tokens with mixed fp16 x fp32 fused multiply-adds, rescaled by
-//     2^(m_old - m_new) when the running max moves;
+//   * per pair of blocks (32 tokens) the two small contractions, S = q . K^T
+//     ([4 heads x 128] . [128 x 32]) and o += P . V, run on the fp16 matrix
+//     cores (v_mfma_f32_16x16x32_f16, fp32 accumulation).  This is not to
+//     reach matrix-core throughput (4 of the 16 MFMA columns carry heads): it
+//     takes the multiply-adds, fp16 conversions and cross-lane traffic off the
+//     vector ALUs and LDS, which otherwise sit at ~50% busy at full HBM rate;
+//   * K and V tiles go from HBM straight into operand registers: each lane
+//     issues 16-byte loads (64 B contiguous per token row for K; 512 B
+//     contiguous per block for the head-dim-major V tile), the next pair is in
+//     flight while the current one is computed, and the split's block-table
+//     entries are fetched once into a register up front;
+//   * online softmax in fp32 on scores in log2 units; accumulators are
+//     rescaled only when some head's running max moved; P is rounded to fp16
+//     for the second product and the denominator sums those rounded values;
 //   * a split writes its unnormalised (o, m, l); a second kernel merges the
 //     splits of each (sequence, head) by their log-sum-exp.  A sequence that
 //     fits one split is normalised and written by the split kernel directly.
@@ -26,47 +31,64 @@
 namespace pkv {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kG = 4;
 
-__device__ inline half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-__device__ inline float lo_f(uint32_t x) { return (float)__builtin_bit_cast(half2_t, x).x; }
-__device__ inline float hi_f(uint32_t x) { return (float)__builtin_bit_cast(half2_t, x).y; }
+// Blocks per split: kDecodeSplit tokens.
+constexpr int kSB = kDecodeSplit / kBlock;
+static_assert(kSB % 2 == 0, "splits are walked in pairs of blocks");
 
-__device__ inline uint32_t mask_pair(uint32_t x, int key0, int valid) {
-  // zero the fp16 halves whose key index (key0, key0 + 1) is >= valid
-  if (key0 >= valid) return 0u;
-  if (key0 + 1 >= valid) return x & 0xFFFFu;
-  return x;
-}
-
-// One block's K tile and V tile of one KV head: 4 x 16 B per lane, each
-// 64-lane load covering 1 KiB contiguously.
-struct Tile {
-  u32x4 k[4], v[4];
+// The K and V tiles of a pair of arena blocks (32 tokens), already in the MFMA
+// operand layouts (see decode_split_kernel).
+struct Pair {
+  half8_t k[2][4];  // [u][kd]: A operand of S^T = K . Q^T
+  half8_t v[8];     // [db]:    A operand of O^T += V^T . P^T
 };
 
-__device__ inline Tile load_tile(const _Float16* __restrict__ k_arena,
-                                 const _Float16* __restrict__ v_arena, int blk, int num_blocks,
-                                 int Hkv, int g, int lane) {
-  if (blk < 0 || blk >= num_blocks) blk = 0;
-  const size_t tile = ((size_t)blk * Hkv + g) * (kBlock * kD / 8);  // in u32x4
-  const u32x4* kb = (const u32x4*)k_arena + tile;
-  const u32x4* vb = (const u32x4*)v_arena + tile;
-  Tile t;
+__device__ inline Pair load_pair(const _Float16* __restrict__ k_arena,
+                                 const _Float16* __restrict__ v_arena, int blk_a, int blk_b,
+                                 int Hkv, int g, int ln, int lq) {
+  Pair pr;
+  const size_t tile_elems = (size_t)kBlock * kD;
+  // K: this lane is MFMA row ln -> block ln/8, token 8*((ln>>2)&1) + 4u + (ln&3);
+  // it supplies head dims 32kd + 8lq .. +8 of that token.
+  {
+    const int blk = (ln >> 3) ? blk_b : blk_a;
+    const _Float16* kt = k_arena + ((size_t)blk * Hkv + g) * tile_elems;
+    const int tok = 8 * ((ln >> 2) & 1) + (ln & 3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    t.k[i] = kb[i * 64 + lane];
-    t.v[i] = vb[i * 64 + lane];
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd)
+        pr.k[u][kd] = *(const half8_t*)(kt + (tok + 4 * u) * kD + 32 * kd + 8 * lq);
   }
-  return t;
+  // V^T: this lane is MFMA row ln -> head dim 16db + ln; it supplies the 8
+  // tokens 8*(lq&1) .. +8 of block lq/2 (16 contiguous bytes of the V tile).
+  {
+    const int blk = (lq >> 1) ? blk_b : blk_a;
+    const _Float16* vt = v_arena + ((size_t)blk * Hkv + g) * tile_elems;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      pr.v[db] = *(const half8_t*)(vt + (16 * db + ln) * kBlock + 8 * (lq & 1));
+  }
+  return pr;
 }
 
+// One 64-lane wavefront per (sequence b, KV head g, split of kSB blocks).
+// Per pair of blocks (32 tokens):
+//   S^T[token][head] = K . Q^T on 2 x 4 MFMAs 16x16x32 (only columns 0..3 are
+//     real heads; the query group is 4), keys permuted so that afterwards
+//     lane (ln, lq) holds 8 consecutive tokens 8*(lq&1).. of block lq/2 for
+//     head ln;
+//   online softmax on those values (row max: 2 cross-lane steps);
+//   O^T[dim][head] += V^T . P^T on 8 MFMAs, P rounded to fp16 and the
+//     denominator summed from the rounded values.
+// K/V go from HBM straight into operand registers; the next pair is loaded
+// while the current one is computed.
 __global__ __launch_bounds__(64) void decode_split_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
@@ -75,147 +97,135 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     int nsplit_max, int num_blocks) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
+  const int ln = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
-  const int h = lane >> 4;  // query head within the group
-  const int j = lane & 15;  // token (QK) / head-dim lane (PV)
   // clamp to what the grid and workspace cover (a caller contract violation
   // then gives unspecified values, never an out-of-bounds access)
   const int L = min(min(context_lens[b], max_blocks * kBlock), nsplit_max * kDecodeSplit);
-  const int tok0 = split * kDecodeSplit;
   if (L <= 0) {
-    if (split == 0) {
-      float* o = out + ((size_t)b * Hq + g * kG + h) * kD;
+    if (split == 0 && ln < kG) {
+      float* o = out + ((size_t)b * Hq + g * kG + ln) * kD + 4 * lq;
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) o[j + 16 * dd] = 0.f;
+      for (int db = 0; db < 8; ++db) *(f32x4*)(o + 16 * db) = (f32x4)0.f;
     }
     return;
   }
-  if (tok0 >= L) return;
-  const int tok1 = min(L, tok0 + kDecodeSplit);
-  const int nblk = (tok1 - tok0 + kBlock - 1) / kBlock;
-  const int nsplit = (L + kDecodeSplit - 1) / kDecodeSplit;
+  const int nb_seq = (L + kBlock - 1) / kBlock;
+  const int blk0 = split * kSB;
+  if (blk0 >= nb_seq) return;
+  const int nb = min(kSB, nb_seq - blk0);
+  const int nsplit = (nb_seq + kSB - 1) / kSB;
+  const int npairs = (nb + 1) >> 1;
 
-  // q of head g*4+h, all 128 dims, as 64 packed fp16 pairs
-  uint32_t qv[64];
-  {
-    const u32x4* qp = (const u32x4*)(q + ((size_t)b * Hq + g * kG + h) * kD);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const u32x4 x = qp[c];
-      qv[4 * c] = x.x; qv[4 * c + 1] = x.y; qv[4 * c + 2] = x.z; qv[4 * c + 3] = x.w;
-    }
+  // physical ids of this split's blocks: lane i holds entry i
+  int my_blk = 0;
+  if (lane < nb) {
+    my_blk = block_table[(size_t)b * max_blocks + blk0 + lane];
+    if (my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
   }
+  // Q^T (B operand): column ln = head g*4+ln, dims 32kd + 8lq .. +8
+  half8_t qb[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd)
+    qb[kd] = ln < kG ? *(const half8_t*)(q + ((size_t)b * Hq + g * kG + ln) * kD + 32 * kd + 8 * lq)
+                     : (half8_t)(_Float16)0.f;
 
-  __shared__ u32x4 k_lds[16 * 16];   // [token][16 B chunk ^ token]
-  __shared__ u32x4 v_lds[kD * 2];    // [dim][8-key half ^ ((dim >> 3) & 1)]
-  __shared__ float p_lds[64];        // [head][token]
-
-  const int32_t* bt = block_table + (size_t)b * max_blocks + (tok0 >> 4);
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = (f32x4)0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  float o[8];
-#pragma unroll
-  for (int dd = 0; dd < 8; ++dd) o[dd] = 0.f;
-  const int vsw = (j >> 3) & 1;
 
-  Tile nxt = load_tile(k_arena, v_arena, bt[0], num_blocks, Hkv, g, lane);
-  for (int n = 0; n < nblk; ++n) {
-    const Tile cur = nxt;
-    const int valid = min(kBlock, tok1 - (tok0 + n * kBlock));
-    __syncthreads();  // the previous block's LDS reads are done
+  auto pair_ids = [&](int p, int& a, int& c) {
+    a = __builtin_amdgcn_readlane(my_blk, 2 * p);
+    c = 2 * p + 1 < nb ? __builtin_amdgcn_readlane(my_blk, 2 * p + 1) : a;
+  };
+  auto compute = [&](const Pair& pr, int p) {
+    f32x4 s[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = i * 4 + (lane >> 4), c = lane & 15;
-      k_lds[row * 16 + (c ^ row)] = cur.k[i];
-      const int d = i * 32 + (lane >> 1), hh = lane & 1;
-      u32x4 x = cur.v[i];
-      if (valid < kBlock) {  // keys past the context: zero V (their p is 0, 0*NaN is not)
-        const int k0 = hh * 8;
-        x.x = mask_pair(x.x, k0, valid);
-        x.y = mask_pair(x.y, k0 + 2, valid);
-        x.z = mask_pair(x.z, k0 + 4, valid);
-        x.w = mask_pair(x.w, k0 + 6, valid);
-      }
-      v_lds[d * 2 + (hh ^ ((d >> 3) & 1))] = x;
-    }
-    __syncthreads();
-    if (n + 1 < nblk) nxt = load_tile(k_arena, v_arena, bt[n + 1], num_blocks, Hkv, g, lane);
-
-    // scores of the block: lane (h, j)
-    float a0 = 0.f, a1 = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      s[u] = (f32x4)0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const u32x4 kk = k_lds[j * 16 + (c ^ j)];
-      a0 = __builtin_amdgcn_fdot2(as_h2(qv[4 * c]), as_h2(kk.x), a0, false);
-      a1 = __builtin_amdgcn_fdot2(as_h2(qv[4 * c + 1]), as_h2(kk.y), a1, false);
-      a0 = __builtin_amdgcn_fdot2(as_h2(qv[4 * c + 2]), as_h2(kk.z), a0, false);
-      a1 = __builtin_amdgcn_fdot2(as_h2(qv[4 * c + 3]), as_h2(kk.w), a1, false);
+      for (int kd = 0; kd < 4; ++kd)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr.k[u][kd], qb[kd], s[u], 0, 0, 0);
     }
-    const float s = j < valid ? (a0 + a1) * scale_log2 : -INFINITY;
-    float mb = s;
-    mb = fmaxf(mb, __shfl_xor(mb, 1, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 2, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 4, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 8, 16));
-    const float m_new = fmaxf(m_run, mb);  // finite: every block has a valid token
-    const float alpha = exp2f(m_run - m_new);
-    const float p = exp2f(s - m_new);
-    l_run = l_run * alpha + p;
+    // absolute token of element e = 4u + i of this lane
+    const int tok0 = (blk0 + 2 * p + (lq >> 1)) * kBlock + 8 * (lq & 1);
+    const int nvalid = L - tok0;  // elements e < nvalid are real keys
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = s[e >> 2][e & 3] * scale_log2;
+      if (e >= nvalid) x = -INFINITY;
+      sv[e] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: the first key of a split is real
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    }
     m_run = m_new;
-    p_lds[lane] = p;
-    __syncthreads();
-
-    float pj[16];
-    {
-      const f32x4* pp = (const f32x4*)(p_lds + h * 16);
+    half8_t pb;
+    float lsum = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 x = pp[c];
-        pj[4 * c] = x.x; pj[4 * c + 1] = x.y; pj[4 * c + 2] = x.z; pj[4 * c + 3] = x.w;
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
+      pb[e] = ph;
+      lsum += (float)ph;
+    }
+    l_run += lsum;
+    const bool tail = nvalid < 8;  // keys past the context: zero V (0 * NaN is NaN)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      half8_t va = pr.v[db];
+      if (tail) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) va[e] = (_Float16)0.f;
       }
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[db], 0, 0, 0);
     }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int d = j + 16 * dd;
-      const u32x4 v0 = v_lds[d * 2 + vsw];        // keys 0..7
-      const u32x4 v1 = v_lds[d * 2 + (vsw ^ 1)];  // keys 8..15
-      float acc = o[dd] * alpha;
-      acc = __builtin_fmaf(pj[0], lo_f(v0.x), acc);
-      acc = __builtin_fmaf(pj[1], hi_f(v0.x), acc);
-      acc = __builtin_fmaf(pj[2], lo_f(v0.y), acc);
-      acc = __builtin_fmaf(pj[3], hi_f(v0.y), acc);
-      acc = __builtin_fmaf(pj[4], lo_f(v0.z), acc);
-      acc = __builtin_fmaf(pj[5], hi_f(v0.z), acc);
-      acc = __builtin_fmaf(pj[6], lo_f(v0.w), acc);
-      acc = __builtin_fmaf(pj[7], hi_f(v0.w), acc);
-      acc = __builtin_fmaf(pj[8], lo_f(v1.x), acc);
-      acc = __builtin_fmaf(pj[9], hi_f(v1.x), acc);
-      acc = __builtin_fmaf(pj[10], lo_f(v1.y), acc);
-      acc = __builtin_fmaf(pj[11], hi_f(v1.y), acc);
-      acc = __builtin_fmaf(pj[12], lo_f(v1.z), acc);
-      acc = __builtin_fmaf(pj[13], hi_f(v1.z), acc);
-      acc = __builtin_fmaf(pj[14], lo_f(v1.w), acc);
-      acc = __builtin_fmaf(pj[15], hi_f(v1.w), acc);
-      o[dd] = acc;
+  };
+
+  int ba, bb;
+  pair_ids(0, ba, bb);
+  Pair cur = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+  for (int p = 0; p < npairs; p += 2) {
+    Pair nxt;
+    if (p + 1 < npairs) {
+      pair_ids(p + 1, ba, bb);
+      nxt = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
     }
+    compute(cur, p);
+    if (p + 1 >= npairs) break;
+    if (p + 2 < npairs) {
+      pair_ids(p + 2, ba, bb);
+      cur = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+    }
+    compute(nxt, p + 1);
   }
 
   float l_row = l_run;
-  l_row += __shfl_xor(l_row, 1, 16);
-  l_row += __shfl_xor(l_row, 2, 16);
-  l_row += __shfl_xor(l_row, 4, 16);
-  l_row += __shfl_xor(l_row, 8, 16);
-  const int hq = g * kG + h;
+  l_row += __shfl_xor(l_row, 16);
+  l_row += __shfl_xor(l_row, 32);
+  if (ln >= kG) return;
+  const int hq = g * kG + ln;
   if (nsplit == 1) {
     const float inv = 1.f / l_row;
-    float* dst = out + ((size_t)b * Hq + hq) * kD;
+    float* dst = out + ((size_t)b * Hq + hq) * kD + 4 * lq;
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) dst[j + 16 * dd] = o[dd] * inv;
+    for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * inv;
   } else {
     const size_t part = ((size_t)b * Hq + hq) * nsplit_max + split;
-    float* dst = ws_o + part * kD;
+    float* dst = ws_o + part * kD + 4 * lq;
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) dst[j + 16 * dd] = o[dd];
-    if (j == 0) {
+    for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db];
+    if (lq == 0) {
       ws_ml[2 * part] = m_run;
       ws_ml[2 * part + 1] = l_row;
     }
