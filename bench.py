@@ -70,7 +70,6 @@ def bench_decode(torch, args):
 
     def run(i):
         k, v = layers[i % len(layers)]
-        dw.reset_q()
         dw.append(k_arena=k, v_arena=v)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
@@ -94,7 +93,6 @@ def bench_chunk(torch, args):
 
     def run(i):
         k, v = layers[i % len(layers)]
-        dw.reset_q()
         dw.append(k_arena=k, v_arena=v)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
@@ -145,6 +143,11 @@ def main():
     ap.add_argument("--layers", type=int, default=4,
                     help="arena copies rotated over (Infinity Cache guard)")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode leg (profiling the chunk kernel alone)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before timing, copy this many MiB once (a device copy of "
+                         "known size to scale HBM counters against)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -160,6 +163,19 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     pkv.lib()
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.no_decode:
+        args.no_cpu_baseline = True
+        wc, dwc, ms_cstep, ms_chunk, flops = bench_chunk(torch, args)
+        log(f"chunk: step {ms_cstep:.4f} ms, kernel {ms_chunk:.4f} ms, "
+            f"{flops / (ms_chunk * 1e-3) / 1e12:.1f} TFLOP/s kernel")
+        return
 
     w, dw, ms_step, ms_dec, nbytes = bench_decode(torch, args)
     value = nbytes / (ms_step * 1e-3) / 1e9

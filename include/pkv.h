@@ -27,9 +27,12 @@
  *     derive from them so that a bad table cannot address memory outside the
  *     buffers described here; the results for such rows are then unspecified.
  *     pkv_validate_tables() checks host copies of the tables.
- *   - Layouts (row-major, innermost index last):
- *       K arena  [num_blocks][num_kv_heads][16][head_dim]   token-major tile
- *       V arena  [num_blocks][num_kv_heads][head_dim][16]   head-dim-major tile
+ *   - Layouts (row-major, innermost index last), x = 16 / sizeof(element)
+ *     (8 for fp16, 4 for fp32):
+ *       K arena  [num_blocks][num_kv_heads][head_dim/x][16][x]  element d of the
+ *                key in slot s at [d/x][s][d%x]: the 16 keys' 16-byte pieces of
+ *                one head-dim range are contiguous
+ *       V arena  [num_blocks][num_kv_heads][head_dim][16]       head-dim-major
  *     Position `pos` of a sequence whose block-table row is `bt` lives in
  *     physical block bt[pos / 16], slot pos % 16.  Query head h reads KV head
  *     h / (num_q_heads / num_kv_heads).
@@ -63,9 +66,10 @@ typedef enum pkv_status {
 
 typedef enum pkv_dtype { PKV_F16 = 0, PKV_F32 = 1 } pkv_dtype;
 
-/* Geometry of one layer's arena.  block_size must be 16; head_dim even and
- * <= 256; num_q_heads a multiple of num_kv_heads; dtype is the storage dtype of
- * q, k, v and both arenas (IEEE binary16 or binary32). */
+/* Geometry of one layer's arena.  block_size must be 16; head_dim a multiple of
+ * x (8 for fp16, 4 for fp32) and <= 256; num_q_heads a multiple of
+ * num_kv_heads; dtype is the storage dtype of q, k, v and both arenas (IEEE
+ * binary16 or binary32). */
 typedef struct pkv_geom {
   int32_t num_blocks;
   int32_t block_size;
@@ -99,11 +103,13 @@ pkv_status pkv_rope_table_init(void* d_cos_sin, double theta, int32_t head_dim,
  *   pos = chunk_start[b] + (t - cu_q_lens[b]):
  *   q[t][h][:] (all query heads) and k (all KV heads) are rotated by RoPE at
  *   pos in fp64 (products and sums, no fused multiply-add) and rounded once,
- *   round-to-nearest-even, to the storage dtype; q is overwritten in place;
- *   rotated k goes to K arena[bt[b][pos/16]][g][pos%16][:], and v, unchanged, to
- *   V arena[bt[b][pos/16]][g][:][pos%16].
- * q            device [num_tokens][Hq][D], rotated in place; may be NULL
- *              (cache fill without queries).
+ *   round-to-nearest-even, to the storage dtype; the rotated q goes to q_out;
+ *   rotated k goes to the K arena, block bt[b][pos/16], slot pos%16, and v,
+ *   unchanged, to the V arena, same block and slot.
+ * q            device [num_tokens][Hq][D], read; may be NULL (cache fill
+ *              without queries).
+ * q_out        device [num_tokens][Hq][D] for the rotated queries; NULL or
+ *              equal to q rotates q in place (no other overlap allowed).
  * k, v         device [num_tokens][Hkv][D], read only.
  * block_table  device int32 [num_seqs][max_blocks_per_seq].
  * cu_q_lens    device int32 [num_seqs+1], cu_q_lens[0] = 0, nondecreasing,
@@ -114,8 +120,9 @@ pkv_status pkv_rope_table_init(void* d_cos_sin, double theta, int32_t head_dim,
  *              block table are skipped (caller contract violation).
  * num_tokens == 0 or num_seqs == 0 is a no-op.
  * ------------------------------------------------------------------------- */
-pkv_status kv_append_rope(const pkv_geom* geom, void* q, const void* k, const void* v,
-                          void* k_arena, void* v_arena, const int32_t* block_table,
+pkv_status kv_append_rope(const pkv_geom* geom, void* q, void* q_out, const void* k,
+                          const void* v, void* k_arena, void* v_arena,
+                          const int32_t* block_table,
                           int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
                           const int32_t* chunk_start, int32_t num_seqs, int32_t num_tokens,
                           const void* rope_table, int32_t rope_max_pos, void* stream);

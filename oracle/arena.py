@@ -6,8 +6,9 @@ of fixed-size blocks; a sequence's block table maps its logical block i
 blocks in place through that table.
 
 Layout (the pages fix none; this is the layout the library documents):
-  K arena  [num_blocks][Hkv][16][D]   token-major inside a (block, head) tile
-  V arena  [num_blocks][Hkv][D][16]   head-dim-major inside a (block, head) tile
+  K arena  [num_blocks][Hkv][D/x][16][x]   x = 16 bytes of elements (8 for fp16,
+           4 for fp32): element d of the key in slot s sits at [d // x][s][d % x]
+  V arena  [num_blocks][Hkv][D][16]        head-dim-major inside a (block, head) tile
 Position ``pos`` of a sequence with table ``bt`` lives in block ``bt[pos // 16]``,
 slot ``pos % 16``.
 
@@ -31,15 +32,23 @@ def slots(table_row, start: int, n: int):
     return row[pos // BLOCK], pos % BLOCK
 
 
+def piece(dtype) -> int:
+    """Elements per 16-byte piece of the K layout."""
+    return 16 // np.dtype(dtype).itemsize
+
+
 class Arena:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype):
-        self.k = np.full((num_blocks, num_kv_heads, BLOCK, head_dim), np.nan, dtype=dtype)
+        x = piece(dtype)
+        self.x = x
+        self.k = np.full((num_blocks, num_kv_heads, head_dim // x, BLOCK, x), np.nan, dtype=dtype)
         self.v = np.full((num_blocks, num_kv_heads, head_dim, BLOCK), np.nan, dtype=dtype)
 
     def write(self, table_row, start: int, k_store: np.ndarray, v_store: np.ndarray) -> None:
         """k_store, v_store [n][Hkv][D] (already in the storage dtype)."""
-        blk, slot = slots(table_row, start, k_store.shape[0])
-        self.k[blk, :, slot, :] = k_store
+        n, H, D = k_store.shape
+        blk, slot = slots(table_row, start, n)
+        self.k[blk, :, :, slot, :] = k_store.reshape(n, H, D // self.x, self.x)
         self.v[blk, :, :, slot] = v_store
 
     def copy_block(self, src: int, dst: int) -> None:
@@ -49,7 +58,8 @@ class Arena:
     def gather(self, table_row, length: int):
         """Dense K, V [length][Hkv][D] of one sequence (the copy the method avoids)."""
         blk, slot = slots(table_row, 0, length)
-        return self.k[blk, :, slot, :], self.v[blk, :, :, slot]
+        K = self.k[blk, :, :, slot, :]                       # [L][Hkv][D/x][x]
+        return K.reshape(length, K.shape[1], -1), self.v[blk, :, :, slot]
 
 
 class SymbolicArena:

@@ -52,8 +52,8 @@ _SIGS = {
     "pkv_rope_table_bytes": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_rope_table_host": (ctypes.c_int, [_P, ctypes.c_double, _I32, _I32]),
     "pkv_rope_table_init": (ctypes.c_int, [_P, ctypes.c_double, _I32, _I32, _P]),
-    "kv_append_rope": (ctypes.c_int, [_PG, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32,
-                                      _P, _I32, _P]),
+    "kv_append_rope": (ctypes.c_int, [_PG, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32,
+                                      _I32, _P, _I32, _P]),
     "paged_attention_decode_workspace_bytes": (ctypes.c_int, [_PG, _I32, _I32,
                                                               ctypes.POINTER(ctypes.c_size_t)]),
     "paged_attention_decode": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _I32,
@@ -149,11 +149,13 @@ def pkv_rope_table_init(table, theta: float, head_dim: int, max_pos: int, stream
 
 def kv_append_rope(g: Geom, q, k, v, k_arena, v_arena, block_table, cu_q_lens, chunk_start,
                    rope_table, rope_max_pos: int, num_tokens: Optional[int] = None,
-                   stream=None) -> None:
+                   q_out=None, stream=None) -> None:
+    """q_out=None rotates q in place."""
     num_seqs = chunk_start.shape[0]
     if num_tokens is None:
         num_tokens = k.shape[0]
-    _check(lib().kv_append_rope(ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v), _ptr(k_arena),
+    _check(lib().kv_append_rope(ctypes.byref(g), _ptr(q), _ptr(q_out), _ptr(k), _ptr(v),
+                                _ptr(k_arena),
                                 _ptr(v_arena), _ptr(block_table), block_table.shape[1],
                                 _ptr(cu_q_lens), _ptr(chunk_start), num_seqs, num_tokens,
                                 _ptr(rope_table), rope_max_pos, _stream(stream)),

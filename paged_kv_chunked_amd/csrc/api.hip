@@ -9,8 +9,10 @@ pkv_status check_geom(const pkv_geom* g) {
   if (g->block_size != PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
   if (g->num_blocks < 1 || g->num_kv_heads < 1 || g->num_q_heads < 1) return PKV_ERR_SHAPE;
   if (g->num_q_heads % g->num_kv_heads) return PKV_ERR_SHAPE;
-  if (g->head_dim < 2 || g->head_dim % 2 || g->head_dim > 256) return PKV_ERR_SHAPE;
   if (g->dtype != PKV_F16 && g->dtype != PKV_F32) return PKV_ERR_DTYPE;
+  // head_dim: a whole number of 16-byte pieces (the K tile layout), <= 256
+  const int piece = g->dtype == PKV_F16 ? 8 : 4;
+  if (g->head_dim < piece || g->head_dim % piece || g->head_dim > 256) return PKV_ERR_SHAPE;
   return PKV_OK;
 }
 
@@ -20,7 +22,8 @@ pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_
 
 extern "C" {
 
-pkv_status kv_append_rope(const pkv_geom* geom, void* q, const void* k, const void* v,
+pkv_status kv_append_rope(const pkv_geom* geom, void* q, void* q_out, const void* k,
+                          const void* v,
                           void* k_arena, void* v_arena, const int32_t* block_table,
                           int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
                           const int32_t* chunk_start, int32_t num_seqs, int32_t num_tokens,
@@ -33,10 +36,10 @@ pkv_status kv_append_rope(const pkv_geom* geom, void* q, const void* k, const vo
       !rope_table)
     return PKV_ERR_NULL;
   if (max_blocks_per_seq < 1 || rope_max_pos < 1) return PKV_ERR_RANGE;
-  return hip_status(pkv::launch_append_rope(*geom, q, k, v, k_arena, v_arena, block_table,
-                                            max_blocks_per_seq, cu_q_lens, chunk_start,
-                                            num_seqs, num_tokens, rope_table, rope_max_pos,
-                                            (hipStream_t)stream));
+  return hip_status(pkv::launch_append_rope(*geom, q, q_out ? q_out : q, k, v, k_arena,
+                                            v_arena, block_table, max_blocks_per_seq,
+                                            cu_q_lens, chunk_start, num_seqs, num_tokens,
+                                            rope_table, rope_max_pos, (hipStream_t)stream));
 }
 
 pkv_status paged_attention_decode_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,

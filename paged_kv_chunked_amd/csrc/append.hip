@@ -2,15 +2,19 @@
 // into the block arena (Kshipra part 3, section 1 "Block-Arena KV Cache" and
 // section 4 "Chunked Prefill": RoPE at absolute positions P onward).
 //
-// One workgroup per new token.  Each thread owns whole rotation pairs
-// (i, i + D/2), so q is rotated in place without races.  The rotation runs in
-// fp64 with fused multiply-add disabled and is rounded once to the storage
-// dtype (fp16: f64_to_f16_bits; fp32: the hardware's round-to-nearest-even
-// convert), so the stored values are exactly determined by the inputs.
+// Arena layouts: K [block][head][D/x][16][x] with x = 16 bytes of elements,
+// V [block][head][D][16].  One 256-thread workgroup per new token; each thread
+// owns whole rotation pairs (i, i + D/2), so an in-place q rotation is
+// race-free.  The rotation runs in fp64 with fused multiply-add disabled and is
+// rounded once to the storage dtype (fp16: f64_to_f16_bits; fp32: the
+// hardware's round-to-nearest-even convert), so the stored values are exactly
+// determined by the inputs.
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
+
+constexpr int kThreads = 256;
 
 template <typename T> __device__ inline T store_f64(double x);
 template <> __device__ inline _Float16 store_f64<_Float16>(double x) {
@@ -26,20 +30,15 @@ __device__ inline void rope_pair(double x0, double x1, double c, double s, doubl
 }
 
 template <typename T>
-__global__ __launch_bounds__(128) void append_rope_kernel(
-    T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    T* __restrict__ k_arena, T* __restrict__ v_arena, const int32_t* __restrict__ block_table,
-    int max_blocks, const int32_t* __restrict__ cu_q_lens,
-    const int32_t* __restrict__ chunk_start, int num_seqs, const double2* __restrict__ cs,
-    int rope_max_pos, int num_blocks, int Hq, int Hkv, int D) {
+__global__ __launch_bounds__(kThreads) void append_rope_kernel(
+    const T* q, T* q_out, const T* __restrict__ k,
+    const T* __restrict__ v, T* __restrict__ k_arena, T* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
+    int num_seqs, const double2* __restrict__ cs, int rope_max_pos, int num_blocks, int Hq,
+    int Hkv, int D) {
   const int t = blockIdx.x;
-  // sequence of token t: the last b with cu_q_lens[b] <= t
-  int lo = 0, hi = num_seqs;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu_q_lens[mid] <= t) lo = mid; else hi = mid;
-  }
-  const int b = lo;
+  const int b = find_seq(cu_q_lens, num_seqs, t);
   const int pos = chunk_start[b] + (t - cu_q_lens[b]);
   if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
   const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];
@@ -48,28 +47,32 @@ __global__ __launch_bounds__(128) void append_rope_kernel(
   const double2* row = cs + (size_t)pos * half;
 
   if (q != nullptr) {
-    for (int idx = threadIdx.x; idx < Hq * half; idx += blockDim.x) {
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < Hq * half; idx += kThreads) {
       const int h = idx / half, i = idx - h * half;
-      T* qp = q + ((size_t)t * Hq + h) * D;
+      const size_t base = ((size_t)t * Hq + h) * D;
       const double2 c = row[i];
       double o0, o1;
-      rope_pair((double)qp[i], (double)qp[i + half], c.x, c.y, o0, o1);
-      qp[i] = store_f64<T>(o0);
-      qp[i + half] = store_f64<T>(o1);
+      rope_pair((double)q[base + i], (double)q[base + i + half], c.x, c.y, o0, o1);
+      q_out[base + i] = store_f64<T>(o0);
+      q_out[base + i + half] = store_f64<T>(o1);
     }
   }
   if (blk < 0 || blk >= num_blocks) return;
-  for (int idx = threadIdx.x; idx < Hkv * half; idx += blockDim.x) {
+  constexpr int x = 16 / sizeof(T);  // K tile layout [D/x][16][x]
+#pragma unroll 2
+  for (int idx = threadIdx.x; idx < Hkv * half; idx += kThreads) {
     const int h = idx / half, i = idx - h * half;
     const T* kp = k + ((size_t)t * Hkv + h) * D;
     const double2 c = row[i];
     double o0, o1;
     rope_pair((double)kp[i], (double)kp[i + half], c.x, c.y, o0, o1);
-    T* dst = k_arena + (((size_t)blk * Hkv + h) * kBlock + slot) * D;
-    dst[i] = store_f64<T>(o0);
-    dst[i + half] = store_f64<T>(o1);
+    T* tile = k_arena + ((size_t)blk * Hkv + h) * kBlock * D;
+    tile[((i / x) * kBlock + slot) * x + i % x] = store_f64<T>(o0);
+    tile[(((i + half) / x) * kBlock + slot) * x + (i + half) % x] = store_f64<T>(o1);
   }
-  for (int idx = threadIdx.x; idx < Hkv * D; idx += blockDim.x) {
+#pragma unroll 4
+  for (int idx = threadIdx.x; idx < Hkv * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
     v_arena[(((size_t)blk * Hkv + h) * D + d) * kBlock + slot] = v[((size_t)t * Hkv + h) * D + d];
   }
@@ -77,24 +80,25 @@ __global__ __launch_bounds__(128) void append_rope_kernel(
 
 }  // namespace
 
-hipError_t launch_append_rope(const pkv_geom& g, void* q, const void* k, const void* v,
-                              void* k_arena, void* v_arena, const int32_t* block_table,
-                              int max_blocks, const int32_t* cu_q_lens,
-                              const int32_t* chunk_start, int num_seqs, int num_tokens,
-                              const void* rope_table, int rope_max_pos, hipStream_t stream) {
-  const dim3 grid(num_tokens), block(128);
+hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, const void* k,
+                              const void* v, void* k_arena, void* v_arena,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* cu_q_lens, const int32_t* chunk_start,
+                              int num_seqs, int num_tokens, const void* rope_table,
+                              int rope_max_pos, hipStream_t stream) {
+  const dim3 grid(num_tokens), block(kThreads);
   if (g.dtype == PKV_F16) {
-    hipLaunchKernelGGL(append_rope_kernel<_Float16>, grid, block, 0, stream, (_Float16*)q,
-                       (const _Float16*)k, (const _Float16*)v, (_Float16*)k_arena,
-                       (_Float16*)v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
+    hipLaunchKernelGGL(append_rope_kernel<_Float16>, grid, block, 0, stream,
+                       (const _Float16*)q, (_Float16*)q_out, (const _Float16*)k,
+                       (const _Float16*)v, (_Float16*)k_arena, (_Float16*)v_arena, block_table,
+                       max_blocks, cu_q_lens, chunk_start, num_seqs, (const double2*)rope_table,
+                       rope_max_pos, g.num_blocks, g.num_q_heads, g.num_kv_heads, g.head_dim);
+  } else {
+    hipLaunchKernelGGL(append_rope_kernel<float>, grid, block, 0, stream, (const float*)q,
+                       (float*)q_out, (const float*)k, (const float*)v, (float*)k_arena,
+                       (float*)v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
                        num_seqs, (const double2*)rope_table, rope_max_pos, g.num_blocks,
                        g.num_q_heads, g.num_kv_heads, g.head_dim);
-  } else {
-    hipLaunchKernelGGL(append_rope_kernel<float>, grid, block, 0, stream, (float*)q,
-                       (const float*)k, (const float*)v, (float*)k_arena, (float*)v_arena,
-                       block_table, max_blocks, cu_q_lens, chunk_start, num_seqs,
-                       (const double2*)rope_table, rope_max_pos, g.num_blocks, g.num_q_heads,
-                       g.num_kv_heads, g.head_dim);
   }
   return hipGetLastError();
 }

@@ -10,14 +10,15 @@
 //     are the 4 query heads of the group, so every K/V tile is fetched from
 //     memory once for all of them;
 //   * keys are walked in tiles of 64 = 4 arena blocks looked up in the block
-//     table; a tile is loaded into registers one step ahead and staged in LDS:
-//     K token-major, V head-dim-major (the arena's own layouts), XOR-swizzled
-//     so the MFMA operand reads are bank-conflict free;
+//     table; a tile is loaded into registers one step ahead and staged in LDS
+//     in the arena's own tile layouts (K in 16-byte pieces grouped by piece,
+//     V head-dim-major, the latter XOR-swizzled), so every MFMA operand read
+//     is bank-conflict free;
 //   * S^T = K Q^T is computed with keys along the MFMA M dimension, so each
 //     lane ends up holding 16 keys of one query row: the row max and sum are
 //     lane-local plus two cross-lane steps, and the probabilities are already
-//     in the B-operand layout of O^T += V^T P^T (keys are permuted
-//     consistently in both products, which a contraction allows);
+//     in the B-operand layout of O^T += V^T P^T (the V^T operand takes the
+//     same keys, 4 from each of two blocks, in the same order);
 //   * online softmax in fp32 (scores in log2 units), P rounded to fp16 for the
 //     second product, and the denominator summed from those rounded values so
 //     the weights still add up to one;
@@ -33,24 +34,15 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kG = 4;
 constexpr int kBM = 32;  // chunk rows per workgroup (per wave: 32 rows of one head)
 constexpr int kBN = 64;  // keys per tile (4 arena blocks)
 
-// K LDS swizzle: the 16 keys one MFMA reads together differ in key bits
-// {0,1,3,4}; mapping them to 4 distinct bits spreads the 16 lanes over 16
-// different 16-byte chunks.
-__device__ inline int k_swz(int key) { return (key & 3) | ((key >> 1) & 12); }
-
-// Physical key (0..63 in the tile) behind row m of the 16-key S^T block kb.
-// Chosen so that, after the first product, lane group q holds keys
-// 32u + 8q .. 32u + 8q + 7 (u = kb / 2): 8 consecutive keys of one arena
-// block — exactly one 16-byte V^T read in the second product.
-__device__ inline int key_of(int kb, int m) {
-  return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
-}
+// fp16 elements per 16-byte piece of the K layout [block][head][D/8][16][8].
+constexpr int kX = 8;
 
 __device__ inline uint32_t mask_pair(uint32_t x, int key0, int limit) {
   if (key0 >= limit) return 0u;
@@ -105,8 +97,13 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
   const int nblk_seq = (Lc + kBlock - 1) / kBlock;
   const int32_t* bt = block_table + (size_t)b * max_blocks;
 
-  __shared__ u32x4 k_lds[kBN * 16];      // [key][16 B chunk ^ k_swz(key)]   16 KiB
-  __shared__ u32x4 v_lds[4 * kD * 2];    // [block][dim][half ^ sw(dim)]      16 KiB
+  // K: 4 blocks in the arena's own tile layout [block][piece][key][16 B], so
+  //    the operand reads (16 keys x one piece per 16 lanes) are contiguous.
+  // V: 4 blocks [block][dim][4 pieces of 4 keys]; the 8-byte piece index is
+  //    XOR-ed with 2 * bit 3 of the dim so the 32 lanes of one ds_read_b64
+  //    (16 dims x 2 pieces) hit 32 different bank pairs.
+  __shared__ u32x4 k_lds[4 * 256];       // 16 KiB
+  __shared__ u32x2 v_lds[4 * kD * 4];    // 16 KiB
 
   u32x4 kst[4], vst[4];
   auto load_tile = [&](int t) {
@@ -128,18 +125,19 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
   auto store_tile = [&](int t) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int key = 16 * a + (tid >> 4), c = tid & 15;
-      k_lds[key * 16 + (c ^ k_swz(key))] = kst[a];
-      const int d = tid >> 1, hh = tid & 1;
+      k_lds[a * 256 + tid] = kst[a];
+      const int d = tid >> 1, hh = tid & 1;  // V tile 16-byte unit tid: dim d, keys 8hh..
       u32x4 x = vst[a];
-      const int k0 = t * kBN + 16 * a + 8 * hh;  // absolute key of the first half
+      const int k0 = t * kBN + 16 * a + 8 * hh;  // absolute key of its first half
       if (k0 + 8 > Lc) {
         x.x = mask_pair(x.x, k0, Lc);
         x.y = mask_pair(x.y, k0 + 2, Lc);
         x.z = mask_pair(x.z, k0 + 4, Lc);
         x.w = mask_pair(x.w, k0 + 6, Lc);
       }
-      v_lds[(a * kD + d) * 2 + (hh ^ ((d >> 3) & 1))] = x;
+      const int sw = 2 * ((d >> 3) & 1);
+      v_lds[(a * kD + d) * 4 + ((2 * hh) ^ sw)] = u32x2{x.x, x.y};
+      v_lds[(a * kD + d) * 4 + ((2 * hh + 1) ^ sw)] = u32x2{x.z, x.w};
     }
   };
 
@@ -157,23 +155,21 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
     __syncthreads();
     if (t + 1 < ntiles) load_tile(t + 1);
 
-    // S^T[key][row] = K . Q^T
+    // S^T[key][row] = K . Q^T; block kb of the tile = MFMA rows (keys) 0..15
     f32x4 sacc[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       sacc[kb][0] = (f32x4)0.f;
       sacc[kb][1] = (f32x4)0.f;
-      const int key = key_of(kb, lr);
-      const int sw = k_swz(key);
 #pragma unroll
       for (int kd = 0; kd < 4; ++kd) {
-        const half8_t ka = __builtin_bit_cast(half8_t, k_lds[key * 16 + ((4 * kd + lq) ^ sw)]);
+        const half8_t ka = __builtin_bit_cast(half8_t, k_lds[kb * 256 + (4 * kd + lq) * 16 + lr]);
         sacc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[0][kd], sacc[kb][0], 0, 0, 0);
         sacc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[1][kd], sacc[kb][1], 0, 0, 0);
       }
     }
 
-    // online softmax per row (this lane: rows 16rb + lr, keys key_of(kb, 4lq + i))
+    // online softmax per row (this lane: rows 16rb + lr, keys 16kb + 4lq + i)
     const bool need_mask = t * kBN + kBN - 1 > first_pos;
     half8_t pb[2][2];  // [u][rb]: B operand of the second product
     float alpha[2];
@@ -185,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float s = sacc[kb][rb][i] * scale_log2;
-          if (need_mask && t * kBN + key_of(kb, 4 * lq + i) > prow[rb]) s = -INFINITY;
+          if (need_mask && t * kBN + 16 * kb + 4 * lq + i > prow[rb]) s = -INFINITY;
           sacc[kb][rb][i] = s;
           mx = fmaxf(mx, s);
         }
@@ -210,15 +206,17 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) oacc[db][rb] *= alpha[rb];
 
-    // O^T[dim][row] += V^T[dim][key] . P^T[key][row]
+    // O^T[dim][row] += V^T[dim][key] . P^T[key][row]; MFMA u contracts keys
+    // 4lq..4lq+3 of blocks 2u and 2u+1 in this lane (the order of pb)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int a = 2 * u + (lq >> 1), hh = lq & 1;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const int d = 16 * db + lr;
-        const half8_t va =
-            __builtin_bit_cast(half8_t, v_lds[(a * kD + d) * 2 + (hh ^ ((d >> 3) & 1))]);
+        const int pj = lq ^ (2 * ((d >> 3) & 1));
+        const u32x2 lo = v_lds[((2 * u) * kD + d) * 4 + pj];
+        const u32x2 hi = v_lds[((2 * u + 1) * kD + d) * 4 + pj];
+        const half8_t va = __builtin_bit_cast(half8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
         oacc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[u][0], oacc[db][0], 0, 0, 0);
         oacc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[u][1], oacc[db][1], 0, 0, 0);
       }

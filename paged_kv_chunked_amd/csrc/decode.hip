@@ -8,6 +8,7 @@
 //   * split-KV: the keys of each sequence are cut into fixed 256-token splits
 //     (16 arena blocks); one 64-lane wavefront per (sequence, KV head, split)
 //     serves all 4 query heads of the group, so each K/V byte is read once;
+//     the waves of all KV heads of one (sequence, split) form one workgroup;
 //   * per pair of blocks (32 tokens) the two small contractions, S = q . K^T
 //     ([4 heads x 128] . [128 x 32]) and o += P . V, run on the fp16 matrix
 //     cores (v_mfma_f32_16x16x32_f16, fp32 accumulation).  This is not to
@@ -36,69 +37,113 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kG = 4;
 
+// Minimum resident waves per SIMD the split kernel is compiled for (register
+// budget 512 / this).
+#ifndef PKV_DECODE_WAVES_PER_SIMD
+#define PKV_DECODE_WAVES_PER_SIMD 2
+#endif
+
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-// Blocks per split: kDecodeSplit tokens.
+// Blocks per split: kDecodeSplit tokens (at most 64: one table entry per lane).
 constexpr int kSB = kDecodeSplit / kBlock;
+static_assert(kSB <= 64, "one block-table entry per lane");
 static_assert(kSB % 2 == 0, "splits are walked in pairs of blocks");
 
-// The K and V tiles of a pair of arena blocks (32 tokens), already in the MFMA
-// operand layouts (see decode_split_kernel).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// fp16 elements per 16-byte piece of the K layout [block][head][D/8][16][8].
+constexpr int kX = 8;
+
+// Streaming loads: every K/V byte is read once per call.
+__device__ inline half8_t ld16(const _Float16* p) {
+  return __builtin_bit_cast(half8_t, __builtin_nontemporal_load((const u32x4*)p));
+}
+__device__ inline u32x2 ld8(const _Float16* p) {
+  return __builtin_nontemporal_load((const u32x2*)p);
+}
+
+// The K and V tiles of a pair of arena blocks A, B (32 tokens), already in the
+// MFMA operand layouts.
 struct Pair {
-  half8_t k[2][4];  // [u][kd]: A operand of S^T = K . Q^T
-  half8_t v[8];     // [db]:    A operand of O^T += V^T . P^T
+  half8_t k[2][4];  // [block][kd]: A operand of S^T = K . Q^T
+  half8_t v[8];     // [db]:        A operand of O^T += V^T . P^T
 };
 
 __device__ inline Pair load_pair(const _Float16* __restrict__ k_arena,
                                  const _Float16* __restrict__ v_arena, int blk_a, int blk_b,
                                  int Hkv, int g, int ln, int lq) {
   Pair pr;
-  const size_t tile_elems = (size_t)kBlock * kD;
-  // K: this lane is MFMA row ln -> block ln/8, token 8*((ln>>2)&1) + 4u + (ln&3);
-  // it supplies head dims 32kd + 8lq .. +8 of that token.
-  {
-    const int blk = (ln >> 3) ? blk_b : blk_a;
-    const _Float16* kt = k_arena + ((size_t)blk * Hkv + g) * tile_elems;
-    const int tok = 8 * ((ln >> 2) & 1) + (ln & 3);
+  const size_t tile = (size_t)kBlock * kD;
+  const _Float16* ka = k_arena + ((size_t)blk_a * Hkv + g) * tile;
+  const _Float16* kb = k_arena + ((size_t)blk_b * Hkv + g) * tile;
+  // K: MFMA row ln = token ln of the block; the lane supplies head dims
+  // 8 * (4kd + lq) .. +8, i.e. piece 4kd + lq.  Per instruction the wave reads
+  // pieces 4kd .. 4kd+3 of all 16 tokens: 1 KiB contiguous.
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int kd = 0; kd < 4; ++kd)
-        pr.k[u][kd] = *(const half8_t*)(kt + (tok + 4 * u) * kD + 32 * kd + 8 * lq);
+  for (int kd = 0; kd < 4; ++kd) {
+    pr.k[0][kd] = ld16(ka + ((4 * kd + lq) * kBlock + ln) * kX);
+    pr.k[1][kd] = ld16(kb + ((4 * kd + lq) * kBlock + ln) * kX);
   }
-  // V^T: this lane is MFMA row ln -> head dim 16db + ln; it supplies the 8
-  // tokens 8*(lq&1) .. +8 of block lq/2 (16 contiguous bytes of the V tile).
-  {
-    const int blk = (lq >> 1) ? blk_b : blk_a;
-    const _Float16* vt = v_arena + ((size_t)blk * Hkv + g) * tile_elems;
+  // V^T: MFMA row ln = head dim 16db + ln; the lane supplies keys 4lq .. 4lq+3
+  // of block A then of block B (the order the probabilities come out of the
+  // first product in).  Per instruction: 512 contiguous bytes of a V tile.
+  const _Float16* va = v_arena + ((size_t)blk_a * Hkv + g) * tile;
+  const _Float16* vb = v_arena + ((size_t)blk_b * Hkv + g) * tile;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      pr.v[db] = *(const half8_t*)(vt + (16 * db + ln) * kBlock + 8 * (lq & 1));
+  for (int db = 0; db < 8; ++db) {
+    const u32x2 lo = ld8(va + (16 * db + ln) * kBlock + 4 * lq);
+    const u32x2 hi = ld8(vb + (16 * db + ln) * kBlock + 4 * lq);
+    pr.v[db] = __builtin_bit_cast(half8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
   }
   return pr;
 }
 
 // One 64-lane wavefront per (sequence b, KV head g, split of kSB blocks).
-// Per pair of blocks (32 tokens):
+// Per pair of blocks A, B (32 tokens):
 //   S^T[token][head] = K . Q^T on 2 x 4 MFMAs 16x16x32 (only columns 0..3 are
-//     real heads; the query group is 4), keys permuted so that afterwards
-//     lane (ln, lq) holds 8 consecutive tokens 8*(lq&1).. of block lq/2 for
-//     head ln;
+//     real heads; the query group is 4); lane (ln, lq) then holds tokens
+//     4lq .. 4lq+3 of A and of B for head ln;
 //   online softmax on those values (row max: 2 cross-lane steps);
 //   O^T[dim][head] += V^T . P^T on 8 MFMAs, P rounded to fp16 and the
 //     denominator summed from the rounded values.
 // K/V go from HBM straight into operand registers; the next pair is loaded
 // while the current one is computed.
-__global__ __launch_bounds__(64) void decode_split_kernel(
+// Waves per workgroup: the KV heads of one (sequence, split) run side by side,
+// so a block's heads (contiguous in the arena) are fetched together and the
+// block-table entries are shared through the cache.
+#ifndef PKV_DECODE_WAVES_PER_WG
+#define PKV_DECODE_WAVES_PER_WG 8
+#endif
+constexpr int kDecodeWavesPerWG = PKV_DECODE_WAVES_PER_WG;
+
+__global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_split_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
     const _Float16* __restrict__ v_arena, const int32_t* __restrict__ block_table,
     int max_blocks, const int32_t* __restrict__ context_lens, float scale_log2, int Hkv,
     int nsplit_max, int num_blocks) {
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.z * kDecodeWavesPerWG + (threadIdx.x >> 6);
+  if (g >= Hkv) return;
+  const int lane = threadIdx.x & 63;
   const int ln = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
+  const int blk0 = split * kSB;
+  // Everything that does not depend on the context length is requested first,
+  // so the three loads below overlap instead of forming a dependent chain:
+  // this split's block-table entries (lane i: entry i; entries past the
+  // sequence are never used), the group's queries, and the length itself.
+  int my_blk = 0;
+  if (lane < kSB && blk0 + lane < max_blocks)
+    my_blk = block_table[(size_t)b * max_blocks + blk0 + lane];
+  // Q^T (B operand): column ln = head g*4+ln, dims 32kd + 8lq .. +8
+  half8_t qb[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd)
+    qb[kd] = ln < kG ? *(const half8_t*)(q + ((size_t)b * Hq + g * kG + ln) * kD + 32 * kd + 8 * lq)
+                     : (half8_t)(_Float16)0.f;
   // clamp to what the grid and workspace cover (a caller contract violation
   // then gives unspecified values, never an out-of-bounds access)
   const int L = min(min(context_lens[b], max_blocks * kBlock), nsplit_max * kDecodeSplit);
@@ -111,24 +156,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     return;
   }
   const int nb_seq = (L + kBlock - 1) / kBlock;
-  const int blk0 = split * kSB;
   if (blk0 >= nb_seq) return;
   const int nb = min(kSB, nb_seq - blk0);
   const int nsplit = (nb_seq + kSB - 1) / kSB;
   const int npairs = (nb + 1) >> 1;
-
-  // physical ids of this split's blocks: lane i holds entry i
-  int my_blk = 0;
-  if (lane < nb) {
-    my_blk = block_table[(size_t)b * max_blocks + blk0 + lane];
-    if (my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
-  }
-  // Q^T (B operand): column ln = head g*4+ln, dims 32kd + 8lq .. +8
-  half8_t qb[4];
-#pragma unroll
-  for (int kd = 0; kd < 4; ++kd)
-    qb[kd] = ln < kG ? *(const half8_t*)(q + ((size_t)b * Hq + g * kG + ln) * kD + 32 * kd + 8 * lq)
-                     : (half8_t)(_Float16)0.f;
+  if (lane >= nb || my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
 
   f32x4 o[8];
 #pragma unroll
@@ -148,15 +180,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
       for (int kd = 0; kd < 4; ++kd)
         s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr.k[u][kd], qb[kd], s[u], 0, 0, 0);
     }
-    // absolute token of element e = 4u + i of this lane
-    const int tok0 = (blk0 + 2 * p + (lq >> 1)) * kBlock + 8 * (lq & 1);
-    const int nvalid = L - tok0;  // elements e < nvalid are real keys
+    // element e of this lane: token 4lq + (e & 3) of block A (e < 4) or B
+    const int tok_a = (blk0 + 2 * p) * kBlock + 4 * lq;
+    const int nva = L - tok_a, nvb = nva - kBlock;  // valid elements of A / B
     float sv[8];
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x = s[e >> 2][e & 3] * scale_log2;
-      if (e >= nvalid) x = -INFINITY;
+      const bool ok = e < 4 ? e < nva : e - 4 < nvb;
+      const float x = ok ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
       sv[e] = x;
       mx = fmaxf(mx, x);
     }
@@ -179,35 +211,41 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
       lsum += (float)ph;
     }
     l_run += lsum;
-    const bool tail = nvalid < 8;  // keys past the context: zero V (0 * NaN is NaN)
+    // keys past the context (only in the sequence's last pair): zero V, since
+    // their p is 0 but 0 * NaN is not
+    const bool tail_pair = (blk0 + 2 * p + 2) * kBlock > L;  // wave-uniform
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       half8_t va = pr.v[db];
-      if (tail) {
+      if (tail_pair) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (e >= nvalid) va[e] = (_Float16)0.f;
+          va[e] = (e < 4 ? e < nva : e - 4 < nvb) ? va[e] : (_Float16)0.f;
       }
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[db], 0, 0, 0);
     }
   };
 
-  int ba, bb;
-  pair_ids(0, ba, bb);
-  Pair cur = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
-  for (int p = 0; p < npairs; p += 2) {
-    Pair nxt;
-    if (p + 1 < npairs) {
-      pair_ids(p + 1, ba, bb);
-      nxt = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+  // Two pair buffers in flight, loop fully unrolled (a split is at most
+  // kSB / 2 pairs).  The prefetch is issued unconditionally (past the last
+  // pair it re-requests the last pair, a cache hit), so the loads outstanding
+  // at each wait are the same on every path and the wait before a pair's MFMAs
+  // covers that pair only, never the prefetch behind it.
+  Pair buf[2];
+  {
+    int ba, bb;
+    pair_ids(0, ba, bb);
+    buf[0] = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+  }
+#pragma unroll
+  for (int p = 0; p < kSB / 2; ++p) {
+    if (p + 1 < kSB / 2) {
+      int ba, bb;
+      pair_ids(min(p + 1, npairs - 1), ba, bb);
+      buf[(p + 1) & 1] = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the compute
     }
-    compute(cur, p);
-    if (p + 1 >= npairs) break;
-    if (p + 2 < npairs) {
-      pair_ids(p + 2, ba, bb);
-      cur = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
-    }
-    compute(nxt, p + 1);
+    if (p < npairs) compute(buf[p & 1], p);
   }
 
   float l_row = l_run;
@@ -279,8 +317,9 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
   float* ws_o = (float*)workspace;
   float* ws_ml = ws_o ? ws_o + (size_t)num_seqs * g.num_q_heads * nsplit * kD : nullptr;
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(nsplit, g.num_kv_heads, num_seqs), dim3(64), 0,
-                     stream, out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
+  const int wpg = g.num_kv_heads < kDecodeWavesPerWG ? g.num_kv_heads : kDecodeWavesPerWG;
+  const int zg = (g.num_kv_heads + kDecodeWavesPerWG - 1) / kDecodeWavesPerWG;
+  hipLaunchKernelGGL(decode_split_kernel, dim3(nsplit, num_seqs, zg), dim3(64 * wpg), 0, stream, out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
                      (const _Float16*)v_arena, block_table, max_blocks, context_lens,
                      scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
   hipError_t e = hipGetLastError();

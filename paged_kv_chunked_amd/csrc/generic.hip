@@ -27,12 +27,7 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(
     b = row;
     L = context_lens[b];
   } else {
-    int lo = 0, hi = num_seqs;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (cu_q_lens[mid] <= row) lo = mid; else hi = mid;
-    }
-    b = lo;
+    b = find_seq(cu_q_lens, num_seqs, row);
     L = chunk_start[b] + (row - cu_q_lens[b]) + 1;  // keys j <= own position
   }
   L = min(L, max_blocks * kBlock);
@@ -59,8 +54,9 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(
     const T* vt = v_arena + ((size_t)blk * Hkv + g) * D * kBlock;
     const int tok = n * kBlock + jl;
     float part = 0.f;
+    constexpr int x = 16 / sizeof(T);  // K tile layout [D/x][16][x]
     if (tok < L)
-      for (int d = sub; d < D; d += 8) part += qs[d] * (float)kt[jl * D + d];
+      for (int d = sub; d < D; d += 8) part += qs[d] * (float)kt[((d / x) * kBlock + jl) * x + d % x];
     part += __shfl_xor(part, 1, 8);
     part += __shfl_xor(part, 2, 8);
     part += __shfl_xor(part, 4, 8);

@@ -8,9 +8,13 @@
 
 namespace pkv {
 
-// Decode split size in tokens (16 arena blocks).  Fixed, never derived from the
-// batch, so a sequence's decode result is independent of the other sequences.
-constexpr int kDecodeSplit = 256;
+// Decode split size in tokens (a multiple of 32).  Fixed at build time, never
+// derived from the batch, so a sequence's decode result is independent of the
+// other sequences.
+#ifndef PKV_DECODE_SPLIT
+#define PKV_DECODE_SPLIT 256
+#endif
+constexpr int kDecodeSplit = PKV_DECODE_SPLIT;
 constexpr int kBlock = PKV_BLOCK_SIZE;
 
 // fp64 -> IEEE binary16 bits, round to nearest, ties to even, written from the
@@ -41,12 +45,32 @@ __host__ __device__ inline uint16_t f64_to_f16_bits(double x) {
   return (uint16_t)(sign | bits);
 }
 
+// Sequence of packed row t: the last b in [0, num_seqs) with cu[b] <= t
+// (cu nondecreasing, cu[0] = 0).  Wave-parallel search: each round the 64
+// lanes test 64 evenly spaced candidates and the range shrinks 64-fold, so up
+// to 4096 sequences cost two dependent loads.  Every lane of the wave must
+// call it with the same t.
+__device__ inline int find_seq(const int32_t* __restrict__ cu, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs;  // the answer lies in [lo, hi); cu[lo] <= t
+  const int lane = threadIdx.x & 63;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const unsigned long long m = __ballot(idx < hi && cu[idx] <= t);
+    if (m == 0) break;  // only if cu[0] > t (caller contract violation)
+    lo += (63 - __clzll(m)) * step;  // true lanes form a prefix: cu is sorted
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
 // ---- launchers (defined in the kernel translation units) -------------------
-hipError_t launch_append_rope(const pkv_geom& g, void* q, const void* k, const void* v,
-                              void* k_arena, void* v_arena, const int32_t* block_table,
-                              int max_blocks, const int32_t* cu_q_lens,
-                              const int32_t* chunk_start, int num_seqs, int num_tokens,
-                              const void* rope_table, int rope_max_pos, hipStream_t stream);
+hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, const void* k,
+                              const void* v, void* k_arena, void* v_arena,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* cu_q_lens, const int32_t* chunk_start,
+                              int num_seqs, int num_tokens, const void* rope_table,
+                              int rope_max_pos, hipStream_t stream);
 
 bool decode_fast_path(const pkv_geom& g);
 size_t decode_workspace_bytes(const pkv_geom& g, int num_seqs, int max_context_len);

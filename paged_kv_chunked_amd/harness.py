@@ -88,7 +88,8 @@ class DeviceWorkload:
         self.threads = threads
         self.scale = default_scale(w.head_dim)
         N, H, D = w.num_blocks, w.num_kv_heads, w.head_dim
-        self.k_arena = torch.full((N, H, BLOCK_SIZE, D), float("nan"), dtype=self.tdtype,
+        x = 16 // (2 if w.dtype == "f16" else 4)   # elements per 16-byte piece of K
+        self.k_arena = torch.full((N, H, D // x, BLOCK_SIZE, x), float("nan"), dtype=self.tdtype,
                                   device=self.device)
         self.v_arena = torch.full((N, H, D, BLOCK_SIZE), float("nan"), dtype=self.tdtype,
                                   device=self.device)
@@ -159,8 +160,8 @@ class DeviceWorkload:
         torch = _torch()
         w, dev = self.w, self.device
         q, k, v = w.draw_step_packed(threads=self.threads)
-        self.q_raw = torch.from_numpy(q).to(dev)
-        self.q = self.q_raw.clone()
+        self.q_raw = torch.from_numpy(q).to(dev)          # as drawn (read by the append)
+        self.q = torch.empty_like(self.q_raw)               # rotated queries (append output)
         self.k_new = torch.from_numpy(k).to(dev)
         self.v_new = torch.from_numpy(v).to(dev)
         counts = np.array([s.count for s in w.step], np.int64)
@@ -207,16 +208,12 @@ class DeviceWorkload:
             self.chunk_max_ctx = int((self.starts_host[r0:r1] + counts_c).max())
             self.chunk_out = torch.empty((t1 - t0, Hq, D), dtype=torch.float32, device=dev)
 
-    def reset_q(self):
-        """Restores the un-rotated step queries (append rotates q in place)."""
-        self.q.copy_(self.q_raw)
-
     def append(self, stream=None, k_arena=None, v_arena=None):
-        kv_append_rope(self.g, self.q, self.k_new, self.v_new,
+        kv_append_rope(self.g, self.q_raw, self.k_new, self.v_new,
                        self.k_arena if k_arena is None else k_arena,
                        self.v_arena if v_arena is None else v_arena,
                        self.bt, self.cu, self.starts, self.rope, self.rope_max_pos,
-                       stream=stream)
+                       q_out=self.q, stream=stream)
 
     def decode(self, stream=None, k_arena=None, v_arena=None):
         if self.dec_rows:
@@ -236,7 +233,7 @@ class DeviceWorkload:
                                   stream=stream)
 
     def step(self, stream=None, k_arena=None, v_arena=None):
-        """One pass of the hot path over the step batch (q must be un-rotated)."""
+        """One pass of the hot path over the step batch."""
         self.append(stream, k_arena, v_arena)
         self.chunk(stream, k_arena, v_arena)
         self.decode(stream, k_arena, v_arena)

@@ -72,7 +72,6 @@ def run_case(w, full_arena=True, dec_sample=None, chunk_sample=None):
     """Runs workload w on the GPU and checks it against the oracle."""
     say(f"{w.name}: set-up (blocks={w.num_blocks}, step rows={len(w.step)})")
     dw = harness.DeviceWorkload(w)
-    dw.reset_q()
     say(f"{w.name}: step")
     dw.step()
     torch.cuda.synchronize()
@@ -96,7 +95,7 @@ def run_case(w, full_arena=True, dec_sample=None, chunk_sample=None):
             tab = torch.tensor(dw.tables[s.seq][:-(-L // 16)], device=dw.device)
             kg = dw.k_arena.index_select(0, tab).cpu().numpy()
             vg = dw.v_arena.index_select(0, tab).cpu().numpy()
-            kg = kg.transpose(0, 2, 1, 3).reshape(-1, w.num_kv_heads, w.head_dim)[:L]
+            kg = kg.transpose(0, 3, 1, 2, 4).reshape(-1, w.num_kv_heads, w.head_dim)[:L]
             vg = vg.transpose(0, 3, 1, 2).reshape(-1, w.num_kv_heads, w.head_dim)[:L]
             assert np.array_equal(bits(kg), bits(K)) and np.array_equal(bits(vg), bits(V))
         exp = oscript.attend_row(w, st, r, q_rot[cu[r]:cu[r + 1]], dw.scale)[0]
@@ -204,7 +203,6 @@ def test_block_permutation_invariance_bitwise():
         w = _same_data_other_blocks(sp)
         say(f"permutation {sp}")
         dw = harness.DeviceWorkload(w)
-        dw.reset_q()
         dw.step()
         torch.cuda.synchronize()
         outs.append((dw.bt_host.copy(), dw.dec_out.cpu().numpy(), dw.chunk_out.cpu().numpy()))
@@ -217,7 +215,6 @@ def test_batch_invariance_bitwise():
     w = workloads.decode_batch(num_seqs=16, lo=1, hi=3000)
     say("batch invariance")
     dw = harness.DeviceWorkload(w)
-    dw.reset_q()
     dw.step()
     torch.cuda.synchronize()
     full = dw.dec_out.cpu().numpy()
@@ -236,7 +233,6 @@ def test_single_key_returns_v_exactly():
     w = workloads.build("one_key", 31, "f16", 32, 8, 128, 5.0e5, [(0, 1), (0, 1)],
                         max_blocks_per_seq=2)
     dw = harness.DeviceWorkload(w)
-    dw.reset_q()
     dw.step()
     torch.cuda.synchronize()
     _, _, v = w.draw_step_packed()
@@ -250,7 +246,6 @@ def test_decode_matches_last_chunk_row():
     w = workloads.build("last_row", 41, "f16", 32, 8, 128, 5.0e5, [(700, 100)],
                         max_blocks_per_seq=60)
     dw = harness.DeviceWorkload(w)
-    dw.reset_q()
     dw.step()
     out = torch.empty((1, 32, 128), dtype=torch.float32, device=dw.device)
     lens = torch.tensor([800], dtype=torch.int32, device=dw.device)
@@ -265,7 +260,7 @@ def test_decode_matches_last_chunk_row():
 
 def test_copy_blocks_bitwise_and_skips_bad_pairs():
     g = pkv.geom(8, 2, 8, 64)
-    k = torch.randn(8, 2, 16, 64, device="cuda").half()
+    k = torch.randn(8, 2, 8, 16, 8, device="cuda").half()
     v = torch.randn(8, 2, 64, 16, device="cuda").half()
     k0, v0 = k.clone(), v.clone()
     pairs = torch.tensor([[1, 5], [2, 6], [3, 99], [-1, 0]], dtype=torch.int32, device="cuda")
@@ -281,7 +276,7 @@ def test_copy_blocks_bitwise_and_skips_bad_pairs():
 def test_empty_and_degenerate_batches():
     g = pkv.geom(4, 8, 32, 128)
     dev = "cuda"
-    k_ar = torch.zeros(4, 8, 16, 128, dtype=torch.float16, device=dev)
+    k_ar = torch.zeros(4, 8, 16, 16, 8, dtype=torch.float16, device=dev)
     v_ar = torch.zeros(4, 8, 128, 16, dtype=torch.float16, device=dev)
     bt = torch.tensor([[0, 1], [2, 3]], dtype=torch.int32, device=dev)
     # a chunk batch with an empty sequence in the middle

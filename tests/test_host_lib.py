@@ -192,12 +192,13 @@ def _geom(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(block_size=32), 2), (dict(num_q_heads=30), 2), (dict(head_dim=130 * 2), 2),
-    (dict(head_dim=3), 2), (dict(num_blocks=0), 2), (dict(dtype=7), 3), (dict(num_kv_heads=0), 2),
+    (dict(head_dim=3), 2), (dict(head_dim=12), 2), (dict(head_dim=6, dtype=1), 2),
+    (dict(num_blocks=0), 2), (dict(dtype=7), 3), (dict(num_kv_heads=0), 2),
 ])
 def test_bad_geometry_rejected(lib, kw, code):
     g = _geom(**kw)
-    r = lib.kv_append_rope(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE,
-                           1, 1, FAKE, 100, None)
+    r = lib.kv_append_rope(ctypes.byref(g), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                           FAKE, 1, 1, FAKE, 100, None)
     assert r == code
     r = lib.paged_attention_decode(ctypes.byref(g), FAKE, 1, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1,
                                    64, 0.1, FAKE, 1 << 20, None)
@@ -212,15 +213,15 @@ def test_entry_point_errors(lib):
     g = _geom()
     gp = ctypes.byref(g)
     # nulls
-    assert lib.kv_append_rope(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1,
-                              FAKE, 100, None) == 1
-    assert lib.kv_append_rope(gp, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1,
+    assert lib.kv_append_rope(None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1,
+                              1, FAKE, 100, None) == 1
+    assert lib.kv_append_rope(gp, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 1,
                               FAKE, 100, None) == 1
     assert lib.paged_attention_decode(gp, None, 1, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 64, 0.1,
                                       FAKE, 1 << 20, None) == 1
     # empty batches are a no-op (no launch)
-    assert lib.kv_append_rope(gp, None, None, None, None, None, None, 4, None, None, 0, 0, None,
-                              100, None) == 0
+    assert lib.kv_append_rope(gp, None, None, None, None, None, None, None, 4, None, None, 0, 0,
+                              None, 100, None) == 0
     assert lib.paged_attention_decode(gp, None, 1, None, None, None, None, 4, None, 0, 64, 0.1,
                                       None, 0, None) == 0
     assert lib.paged_attention_chunk(gp, None, 1, None, None, None, None, 4, None, None, 0, 0,

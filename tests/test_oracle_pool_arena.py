@@ -100,21 +100,22 @@ def test_kv_sizing_golden():
 
 def test_arena_slots_brute_force():
     rng = np.random.default_rng(2)
-    N, H, D = 12, 3, 8
+    N, H, D = 12, 3, 32
     a = arena.Arena(N, H, D, np.float16)
     table = rng.permutation(N)[:5]
     start, n = 7, 60
     k = rng.standard_normal((n, H, D)).astype(np.float16)
     v = rng.standard_normal((n, H, D)).astype(np.float16)
     a.write(table, start, k, v)
-    exp_k = np.full((N, H, 16, D), np.nan, np.float16)
+    x = 8                                   # fp16: 8 elements per 16-byte piece
+    exp_k = np.full((N, H, D // x, 16, x), np.nan, np.float16)
     exp_v = np.full((N, H, D, 16), np.nan, np.float16)
     for t in range(n):
         pos = start + t
         blk, slot = table[pos // 16], pos % 16
         for h in range(H):
             for d in range(D):
-                exp_k[blk, h, slot, d] = k[t, h, d]
+                exp_k[blk, h, d // x, slot, d % x] = k[t, h, d]
                 exp_v[blk, h, d, slot] = v[t, h, d]
     assert np.array_equal(a.k.view(np.uint16), exp_k.view(np.uint16))
     assert np.array_equal(a.v.view(np.uint16), exp_v.view(np.uint16))
