@@ -133,7 +133,7 @@ pkv_status kv_append_rope(const pkv_geom* geom, void* q, void* q_out, const void
  * For sequence b with context length L = context_lens[b] (the new token,
  * already appended at position L-1, included) and each query head h:
  *   out[b][h][:] = softmax_j((q[b][h] . k_j) * scale) @ V,  j = 0 .. L-1.
- * Split-KV: each sequence's keys are cut into fixed 256-token splits processed
+ * Split-KV: each sequence's keys are cut into fixed 384-token splits processed
  * in parallel; splits are merged by their log-sum-exp.  The split size never
  * depends on the batch, so a sequence's result does not either.
  * out          device fp32 [num_seqs][Hq][D]  (out_dtype must be PKV_F32).

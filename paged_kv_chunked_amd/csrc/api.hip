@@ -71,7 +71,7 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   return hip_status(pkv::launch_decode(*geom, (float*)out, q, k_arena, v_arena, block_table,
                                        max_blocks_per_seq, context_lens, num_seqs,
-                                       max_context_len, scale, workspace,
+                                       max_context_len, scale, workspace, workspace_bytes,
                                        (hipStream_t)stream));
 }
 

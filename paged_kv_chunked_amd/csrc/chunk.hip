@@ -55,9 +55,20 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
     const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
-    float scale_log2, int Hkv, int n_qtiles, int num_blocks, int num_tokens) {
-  const int qt = n_qtiles - 1 - (int)blockIdx.x;  // later (longer) row tiles first
-  const int g = blockIdx.y, b = blockIdx.z;
+    float scale_log2, int Hkv, int num_seqs, int n_qtiles, int num_blocks, int num_tokens) {
+  // XCD-aware order.  Linear workgroup id i runs on XCD i % 8.  The pairs
+  // p = b * Hkv + g are dealt to XCDs round-robin (p % 8) and all row tiles of
+  // a pair stay on its XCD, so the pair's K/V tiles are fetched into one L2
+  // and reused by its row tiles; within an XCD, later (longer) row tiles of a
+  // pair are issued first.
+  const int npairs = num_seqs * Hkv;
+  const int i = blockIdx.x;
+  const int xcd = i & 7, j = i >> 3;
+  const int lp = j / n_qtiles;                  // pair index among this XCD's pairs
+  const int qt = n_qtiles - 1 - (j - lp * n_qtiles);
+  const int p = lp * 8 + xcd;
+  if (p >= npairs) return;
+  const int b = p / Hkv, g = p - b * Hkv;
   const int row0 = cu_q_lens[b];
   const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
   if (qt * kBM >= C) return;
@@ -258,10 +269,12 @@ hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void
                                  cu_q_lens, chunk_start, num_seqs, num_tokens, scale, stream);
   const int n_qtiles = (max_q_len + kBM - 1) / kBM;
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(chunk_mfma_kernel, dim3(n_qtiles, g.num_kv_heads, num_seqs), dim3(256), 0,
-                     stream, out, (const _Float16*)q, (const _Float16*)k_arena,
-                     (const _Float16*)v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
-                     scale_log2, g.num_kv_heads, n_qtiles, g.num_blocks, num_tokens);
+  const long npairs = (long)num_seqs * g.num_kv_heads;
+  const long nwg = 8 * ((npairs + 7) / 8) * n_qtiles;
+  hipLaunchKernelGGL(chunk_mfma_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, out,
+                     (const _Float16*)q, (const _Float16*)k_arena, (const _Float16*)v_arena,
+                     block_table, max_blocks, cu_q_lens, chunk_start, scale_log2,
+                     g.num_kv_heads, num_seqs, n_qtiles, g.num_blocks, num_tokens);
   return hipGetLastError();
 }
 

@@ -5,8 +5,8 @@
 //
 // Tuned path (fp16 storage, head_dim 128, 4 query heads per KV head — the
 // Llama-3-8B layer shape):
-//   * split-KV: the keys of each sequence are cut into fixed 256-token splits
-//     (16 arena blocks); one 64-lane wavefront per (sequence, KV head, split)
+//   * split-KV: the keys of each sequence are cut into fixed 384-token splits
+//     (24 arena blocks); one 64-lane wavefront per (sequence, KV head, split)
 //     serves all 4 query heads of the group, so each K/V byte is read once;
 //     the waves of all KV heads of one (sequence, split) form one workgroup;
 //   * per pair of blocks (32 tokens) the two small contractions, S = q . K^T
@@ -15,17 +15,26 @@
 //     reach matrix-core throughput (4 of the 16 MFMA columns carry heads): it
 //     takes the multiply-adds, fp16 conversions and cross-lane traffic off the
 //     vector ALUs and LDS, which otherwise sit at ~50% busy at full HBM rate;
-//   * K and V tiles go from HBM straight into operand registers: each lane
-//     issues 16-byte loads (64 B contiguous per token row for K; 512 B
-//     contiguous per block for the head-dim-major V tile), the next pair is in
-//     flight while the current one is computed, and the split's block-table
-//     entries are fetched once into a register up front;
+//   * K and V tiles go from HBM straight into operand registers with
+//     non-temporal loads: per instruction the wave reads 1 KiB contiguous of a
+//     K tile (the arena keeps K in 16-byte pieces grouped by piece) and 512 B
+//     contiguous of a head-dim-major V tile; the next pair is in flight while
+//     the current one is computed, and the split's block-table entries are
+//     fetched once into a register up front;
+//   * the grid's split dimension is padded to an odd width so that a given
+//     split index is not pinned to the same XCDs (workgroups are dealt to the
+//     8 XCDs round-robin by linear id): otherwise the XCDs that always draw
+//     split 0 carry far more work than those drawing high split indices;
 //   * online softmax in fp32 on scores in log2 units; accumulators are
 //     rescaled only when some head's running max moved; P is rounded to fp16
 //     for the second product and the denominator sums those rounded values;
 //   * a split writes its unnormalised (o, m, l); a second kernel merges the
 //     splits of each (sequence, head) by their log-sum-exp.  A sequence that
 //     fits one split is normalised and written by the split kernel directly.
+//     (Merging inside the split kernel — the last split to finish, found with
+//     an atomic counter — needs device-scope release/acquire fences, which on
+//     this multi-XCD part write back and invalidate the L2 per wave; measured
+//     4x slower than the second launch.)
 // Other shapes run the generic kernel.
 #include "pkv_internal.h"
 
@@ -120,10 +129,11 @@ constexpr int kDecodeWavesPerWG = PKV_DECODE_WAVES_PER_WG;
 
 __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_split_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
-    const _Float16* __restrict__ v_arena, const int32_t* __restrict__ block_table,
-    int max_blocks, const int32_t* __restrict__ context_lens, float scale_log2, int Hkv,
-    int nsplit_max, int num_blocks) {
+    const _Float16* __restrict__ q,
+    const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks) {
   const int split = blockIdx.x, b = blockIdx.y;
   const int g = blockIdx.z * kDecodeWavesPerWG + (threadIdx.x >> 6);
   if (g >= Hkv) return;
@@ -251,15 +261,18 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
   float l_row = l_run;
   l_row += __shfl_xor(l_row, 16);
   l_row += __shfl_xor(l_row, 32);
-  if (ln >= kG) return;
   const int hq = g * kG + ln;
   if (nsplit == 1) {
-    const float inv = 1.f / l_row;
-    float* dst = out + ((size_t)b * Hq + hq) * kD + 4 * lq;
+    if (ln < kG) {
+      const float inv = 1.f / l_row;
+      float* dst = out + ((size_t)b * Hq + hq) * kD + 4 * lq;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * inv;
-  } else {
-    const size_t part = ((size_t)b * Hq + hq) * nsplit_max + split;
+      for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * inv;
+    }
+    return;
+  }
+  if (ln < kG) {
+    const size_t part = ((size_t)b * nsplit_max + split) * Hq + hq;
     float* dst = ws_o + part * kD + 4 * lq;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db];
@@ -270,26 +283,65 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
   }
 }
 
-// Merge the splits of one (sequence, query head): weights 2^(m_s - M).
-__global__ __launch_bounds__(128) void decode_combine_kernel(
+// Log-sum-exp merge of the splits of the 4 query heads of one (sequence b, KV
+// head g): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s.  The split weights are computed once into LDS; then each
+// thread accumulates 2 head dims of one head over the splits with independent
+// 8-byte loads.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineMaxSplits = 512;  // LDS capacity; longer rows loop
+
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     float* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ context_lens, int max_blocks, int Hq, int nsplit_max) {
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.x, b = blockIdx.y;
   const int L = min(min(context_lens[b], max_blocks * kBlock), nsplit_max * kDecodeSplit);
   const int nsplit = (L + kDecodeSplit - 1) / kDecodeSplit;
   if (nsplit <= 1) return;
-  const size_t part0 = ((size_t)b * Hq + h) * nsplit_max;
+  __shared__ float w_lds[kG][kCombineMaxSplits];
+  __shared__ float inv_den[kG];
+  const int tid = threadIdx.x;
+  const int hh = tid >> 6, d = 2 * (tid & 63);  // head within the group, 2 dims
+  // partial (b, split s, head h) sits at ((b * nsplit_max + s) * Hq + h)
+  const size_t part0 = (size_t)b * nsplit_max * Hq + g * kG + hh;
+  const size_t pstride = Hq;  // between consecutive splits of one head
   const float* ml = ws_ml + 2 * part0;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-  float den = 0.f, acc = 0.f;
-  const float* po = ws_o + part0 * kD + threadIdx.x;
-  for (int s = 0; s < nsplit; ++s) {
-    const float w = exp2f(ml[2 * s] - M);
-    den += w * ml[2 * s + 1];
-    acc += w * po[(size_t)s * kD];
+  const float* po = ws_o + part0 * kD + d;
+  float a0 = 0.f, a1 = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineMaxSplits) {
+    const int ns = min(kCombineMaxSplits, nsplit - s0);
+    // wave hh: running max and denominator of head hh over this range
+    float M = -INFINITY;
+    for (int s = tid & 63; s < nsplit; s += 64) M = fmaxf(M, ml[2 * s * pstride]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float den = 0.f;
+    for (int s = tid & 63; s < ns; s += 64) {
+      const float w = exp2f(ml[2 * (s0 + s) * pstride] - M);
+      w_lds[hh][s] = w;
+      den += w * ml[2 * (s0 + s) * pstride + 1];
+    }
+    if (s0 == 0) {
+      for (int s = ns + (tid & 63); s < nsplit; s += 64)
+        den += exp2f(ml[2 * s * pstride] - M) * ml[2 * s * pstride + 1];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+      if ((tid & 63) == 0) inv_den[hh] = 1.f / den;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) {
+      const float w = w_lds[hh][s];
+      const float2 o2 = *(const float2*)(po + (size_t)(s0 + s) * pstride * kD);
+      a0 += w * o2.x;
+      a1 += w * o2.y;
+    }
+    __syncthreads();
   }
-  out[((size_t)b * Hq + h) * kD + threadIdx.x] = acc / den;
+  float* dst = out + ((size_t)b * Hq + g * kG + hh) * kD + d;
+  const float inv = inv_den[hh];
+  dst[0] = a0 * inv;
+  dst[1] = a1 * inv;
 }
 
 }  // namespace
@@ -298,34 +350,55 @@ bool decode_fast_path(const pkv_geom& g) {
   return g.dtype == PKV_F16 && g.head_dim == kD && g.num_q_heads == kG * g.num_kv_heads;
 }
 
+// Workspace: [partial o: S x nsplit x Hq x D floats][partial (m, l): S x nsplit x
+// Hq x 2 floats], nsplit = ceil(max_context_len / kDecodeSplit); split-major,
+// so the waves of one workgroup write one contiguous range.
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 size_t decode_workspace_bytes(const pkv_geom& g, int num_seqs, int max_context_len) {
   if (!decode_fast_path(g)) return 0;
   const size_t nsplit = (size_t)(max_context_len + kDecodeSplit - 1) / kDecodeSplit;
   if (nsplit <= 1) return 0;
-  return (size_t)num_seqs * g.num_q_heads * nsplit * (kD + 2) * sizeof(float);
+  const size_t parts = (size_t)num_seqs * g.num_q_heads * nsplit;
+  return align256(parts * kD * sizeof(float)) + parts * 2 * sizeof(float);
 }
 
 hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const void* k_arena,
                          const void* v_arena, const int32_t* block_table, int max_blocks,
                          const int32_t* context_lens, int num_seqs, int max_context_len,
-                         float scale, void* workspace, hipStream_t stream) {
+                         float scale, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
   if (!decode_fast_path(g))
     return launch_attend_generic(g, out, q, k_arena, v_arena, block_table, max_blocks,
                                  context_lens, nullptr, nullptr, num_seqs, num_seqs, scale,
                                  stream);
   const int nsplit = (max_context_len + kDecodeSplit - 1) / kDecodeSplit;
-  float* ws_o = (float*)workspace;
-  float* ws_ml = ws_o ? ws_o + (size_t)num_seqs * g.num_q_heads * nsplit * kD : nullptr;
+  (void)workspace_bytes;
+  float* ws_o = nullptr;
+  float* ws_ml = nullptr;
+  if (nsplit > 1) {
+    const size_t parts = (size_t)num_seqs * g.num_q_heads * nsplit;
+    ws_o = (float*)workspace;
+    ws_ml = (float*)((char*)workspace + align256(parts * kD * sizeof(float)));
+  }
   const float scale_log2 = scale * 1.4426950408889634f;
   const int wpg = g.num_kv_heads < kDecodeWavesPerWG ? g.num_kv_heads : kDecodeWavesPerWG;
   const int zg = (g.num_kv_heads + kDecodeWavesPerWG - 1) / kDecodeWavesPerWG;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(nsplit, num_seqs, zg), dim3(64 * wpg), 0, stream, out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id, and the id
+  // is split + gx * sequence.  With an even gx a split index would always land
+  // on the same XCDs — the low splits (present in every sequence) on some, the
+  // high ones (long sequences only) on others.  An odd gx rotates each split
+  // index across all XCDs; the extra column of workgroups exits at once.
+  const int gx = nsplit | 1;
+  const dim3 grid(gx, num_seqs, zg);
+  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64 * wpg), 0, stream,
+                     out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
                      (const _Float16*)v_arena, block_table, max_blocks, context_lens,
                      scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit <= 1) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(g.num_q_heads, num_seqs), dim3(kD), 0, stream,
-                     out, ws_o, ws_ml, context_lens, max_blocks, g.num_q_heads, nsplit);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(g.num_kv_heads, num_seqs), dim3(kCombineThreads),
+                     0, stream, out, ws_o, ws_ml, context_lens, max_blocks, g.num_q_heads, nsplit);
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ namespace pkv {
 // derived from the batch, so a sequence's decode result is independent of the
 // other sequences.
 #ifndef PKV_DECODE_SPLIT
-#define PKV_DECODE_SPLIT 256
+#define PKV_DECODE_SPLIT 384
 #endif
 constexpr int kDecodeSplit = PKV_DECODE_SPLIT;
 constexpr int kBlock = PKV_BLOCK_SIZE;
@@ -77,7 +77,8 @@ size_t decode_workspace_bytes(const pkv_geom& g, int num_seqs, int max_context_l
 hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const void* k_arena,
                          const void* v_arena, const int32_t* block_table, int max_blocks,
                          const int32_t* context_lens, int num_seqs, int max_context_len,
-                         float scale, void* workspace, hipStream_t stream);
+                         float scale, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 bool chunk_fast_path(const pkv_geom& g);
 hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,

@@ -192,7 +192,8 @@ class DeviceWorkload:
             self.dec_lens = torch.from_numpy(lens).to(dev)
             self.dec_max_len = int(lens.max())
             ws = paged_attention_decode_workspace_bytes(self.g, len(dec), self.dec_max_len)
-            self.dec_ws = (torch.empty(max(ws, 4) // 4, dtype=torch.float32, device=dev)
+            # zero-filled once: the decode merge counters must start at zero
+            self.dec_ws = (torch.zeros(max(ws, 4) // 4, dtype=torch.float32, device=dev)
                            if ws else None)
             self.dec_out = torch.empty((len(dec), Hq, D), dtype=torch.float32, device=dev)
         if chk:

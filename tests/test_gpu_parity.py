@@ -222,7 +222,7 @@ def test_batch_invariance_bitwise():
         out = torch.empty((1, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dw.device)
         L = int(dw.dec_lens_host[r])
         ws_n = pkv.paged_attention_decode_workspace_bytes(dw.g, 1, L)
-        ws = torch.empty(max(ws_n, 4) // 4, dtype=torch.float32, device=dw.device) if ws_n else None
+        ws = torch.zeros(max(ws_n, 4) // 4, dtype=torch.float32, device=dw.device) if ws_n else None
         pkv.paged_attention_decode(dw.g, out, dw.dec_q[r:r + 1], dw.k_arena, dw.v_arena,
                                    dw.dec_bt[r:r + 1], dw.dec_lens[r:r + 1], L, dw.scale, ws)
         torch.cuda.synchronize()
@@ -250,7 +250,7 @@ def test_decode_matches_last_chunk_row():
     out = torch.empty((1, 32, 128), dtype=torch.float32, device=dw.device)
     lens = torch.tensor([800], dtype=torch.int32, device=dw.device)
     ws_n = pkv.paged_attention_decode_workspace_bytes(dw.g, 1, 800)
-    ws = torch.empty(ws_n // 4, dtype=torch.float32, device=dw.device)
+    ws = torch.zeros(ws_n // 4, dtype=torch.float32, device=dw.device)
     pkv.paged_attention_decode(dw.g, out, dw.chunk_q[99:100], dw.k_arena, dw.v_arena,
                                dw.chunk_bt, lens, 800, dw.scale, ws)
     torch.cuda.synchronize()

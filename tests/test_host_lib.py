@@ -239,8 +239,9 @@ def test_entry_point_errors(lib):
                                      32, 16, 0.1, None, 0, None) == 4
     # workspace
     need = pkv.paged_attention_decode_workspace_bytes(g, 3, 1000)
-    assert need == 3 * 32 * 4 * 130 * 4
-    assert pkv.paged_attention_decode_workspace_bytes(g, 3, 256) == 0
+    parts = 3 * 32 * -(-1000 // 384)                 # sequences x heads x 384-token splits
+    assert need == -(-parts * 128 * 4 // 256) * 256 + parts * 2 * 4
+    assert pkv.paged_attention_decode_workspace_bytes(g, 3, 384) == 0   # one split: no partials
     assert lib.paged_attention_decode(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000,
                                       0.1, FAKE, need - 1, None) == 5
     assert lib.paged_attention_decode(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000,
