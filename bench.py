@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_F16_TFLOPS = 2516.6     # MI355X dense fp16 MFMA
 METRIC = "paged-attn decode HBM GB/s + chunk-prefill TFLOP/s, % of MI355X roofline"
@@ -177,6 +178,7 @@ def main():
             f"{flops / (ms_chunk * 1e-3) / 1e12:.1f} TFLOP/s kernel")
         return
 
+    from paged_kv_chunked_amd.rocprof_summary import load_traffic
     w, dw, ms_step, ms_dec, nbytes = bench_decode(torch, args)
     value = nbytes / (ms_step * 1e-3) / 1e9
     achieved = nbytes / (ms_dec * 1e-3) / 1e9
@@ -211,7 +213,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": load_traffic(TRAFFIC, "paged_attention_decode"),
             "algorithmic_bytes_per_launch": nbytes,
             "avg_launch_ms": round(ms_dec, 5),
         },
@@ -235,7 +237,7 @@ def main():
                 "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": round(tf_kernel / PEAK_F16_TFLOPS, 4),
-                "traffic": None,
+                "traffic": load_traffic(TRAFFIC, "paged_attention_chunk"),
                 "algorithmic_flops_per_launch": flops,
                 "avg_launch_ms": round(ms_chunk, 5),
             },

@@ -1,0 +1,137 @@
+"""Summaries of rocprofv3 result databases for profiles/.
+
+    python -m paged_kv_chunked_amd.rocprof_summary stats DB OUT.md --command "..."
+        per-kernel dispatch count and average / min / max / total duration
+        (a --kernel-trace --stats run).
+    python -m paged_kv_chunked_amd.rocprof_summary traffic FETCH_DB WRITE_DB OUT.json \
+            --copy-mib N --command "..."
+        HBM bytes per dispatch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE).
+        Each counter is scaled by what it reads for the device copy of N MiB
+        that bench.py --calibrate-copy-mib N performs first (the first
+        __amd_rocclr_copyBuffer dispatch): scale = N MiB / counter value.  The
+        record stores the SHA-256 of the kernel sources, so bench.py only uses
+        it while those sources are unchanged.
+
+rocprofv3 writes one SQLite database per process; its ``kernels`` and
+``pmc_events`` views are read here.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import hashlib
+import json
+import os
+import sqlite3
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+# kernel call -> (kernel symbol substrings, source files whose change invalidates it)
+CALLS = {
+    "paged_attention_decode": (("decode_split_kernel", "decode_combine_kernel"),
+                               ("decode.hip", "pkv_internal.h")),
+    "paged_attention_chunk": (("chunk_mfma_kernel",), ("chunk.hip", "pkv_internal.h")),
+    "kv_append_rope": (("append_rope_kernel",), ("append.hip", "pkv_internal.h")),
+}
+
+
+def sources_sha(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_rows(db):
+    c = sqlite3.connect(db)
+    return c.execute("select name, duration from kernels").fetchall()
+
+
+def stats(db, out, command):
+    agg = collections.defaultdict(list)
+    for name, dur in kernel_rows(db):
+        agg[name].append(dur)
+    lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | total (ms) |",
+             "|---|---|---|---|---|---|"]
+    for name, durs in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) < 110 else name[:107] + "..."
+        lines.append(f"| `{short}` | {len(durs)} | {sum(durs) / len(durs) / 1e3:.2f} | "
+                     f"{min(durs) / 1e3:.2f} | {max(durs) / 1e3:.2f} | {sum(durs) / 1e6:.3f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def _pmc(db, counter):
+    c = sqlite3.connect(db)
+    rows = c.execute("select dispatch_id, name, counter_value from pmc_events "
+                     "where counter_name = ? order by dispatch_id", (counter,)).fetchall()
+    return rows
+
+
+def traffic(fetch_db, write_db, out, copy_mib, command):
+    copy_kib = copy_mib * 1024.0
+    rec = {"command": command, "copy_mib": copy_mib, "calls": {}}
+    for key, db, counter in (("fetch", fetch_db, "FETCH_SIZE"), ("write", write_db, "WRITE_SIZE")):
+        rows = _pmc(db, counter)
+        copy = [v for _, n, v in rows if "copyBuffer" in n]
+        scale = copy_kib / copy[0]
+        rec[f"{key}_scale"] = scale
+        for call, (syms, _) in CALLS.items():
+            per = collections.defaultdict(list)
+            for _, name, v in rows:
+                for sname in syms:
+                    if sname in name:
+                        per[sname].append(v)
+            if not per:
+                continue
+            entry = rec["calls"].setdefault(call, {})
+            kib = sum(sum(v) / len(v) for v in per.values())
+            entry[f"{key}_kib_per_call_raw"] = kib
+            entry[f"{key}_bytes_per_call"] = kib * scale * 1024.0
+            entry["kernels"] = sorted(per)
+    for call, (_, files) in CALLS.items():
+        if call in rec["calls"]:
+            rec["calls"][call]["sources_sha256"] = sources_sha(files)
+            rec["calls"][call]["sources"] = list(files)
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+
+
+def load_traffic(path, call):
+    """Bytes per call (fetch + write) if the record matches the current sources."""
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+        entry = rec["calls"][call]
+        if entry["sources_sha256"] != sources_sha(entry["sources"]):
+            return None
+        return entry["fetch_bytes_per_call"] + entry["write_bytes_per_call"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("db")
+    a.add_argument("out")
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_db")
+    b.add_argument("write_db")
+    b.add_argument("out")
+    b.add_argument("--copy-mib", type=int, required=True)
+    b.add_argument("--command", required=True)
+    args = ap.parse_args()
+    if args.cmd == "stats":
+        stats(args.db, args.out, args.command)
+    else:
+        traffic(args.fetch_db, args.write_db, args.out, args.copy_mib, args.command)
+
+
+if __name__ == "__main__":
+    main()
