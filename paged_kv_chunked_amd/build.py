@@ -23,6 +23,10 @@ LIB = os.path.join(HERE, "libpkv.so")
 ARCH = "gfx950"
 SOURCES = ["host.cpp", "api.hip", "append.hip", "decode.hip", "chunk.hip", "generic.hip",
            "copy.hip"]
+# Per-file device flags.  The chunk kernel never lets a NaN reach a max (masked
+# scores are replaced by -inf with a select, V past the sequence is zeroed as
+# integers), so its device code may drop the quieting of max operands.
+EXTRA_DEVICE_FLAGS = {"chunk.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -43,6 +47,8 @@ def _compile(src: str) -> str:
     cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + common_flags()
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
+    for f in EXTRA_DEVICE_FLAGS.get(src, []):
+        cmd += ["-Xarch_device", f]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -26,15 +26,17 @@
 //     first row position; V slots past the sequence's length are zeroed in LDS
 //     (p = 0 there, but 0 * NaN would not be 0).
 // Other shapes run the generic kernel.
+#include <cmath>
+
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kG = 4;
@@ -49,6 +51,29 @@ __device__ inline uint32_t mask_pair(uint32_t x, int key0, int limit) {
   if (key0 + 1 >= limit) return x & 0xFFFFu;
   return x;
 }
+
+// Reductions over the four lanes {l, l^16, l^32, l^48} that hold one row,
+// through the gfx950 cross-row lane swaps (no LDS round trip).
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// How far (log2 units) a row's running maximum may lag the true maximum before
+// the accumulator is rescaled: probabilities stay <= 2^8, well inside fp16.
+constexpr float kSlack = 8.f;
 
 __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
     float* __restrict__ out, const _Float16* __restrict__ q,
@@ -108,13 +133,15 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
   const int nblk_seq = (Lc + kBlock - 1) / kBlock;
   const int32_t* bt = block_table + (size_t)b * max_blocks;
 
+  // Two LDS buffers (tile t in buffer t & 1), so one barrier per tile suffices.
   // K: 4 blocks in the arena's own tile layout [block][piece][key][16 B], so
   //    the operand reads (16 keys x one piece per 16 lanes) are contiguous.
-  // V: 4 blocks [block][dim][4 pieces of 4 keys]; the 8-byte piece index is
-  //    XOR-ed with 2 * bit 3 of the dim so the 32 lanes of one ds_read_b64
-  //    (16 dims x 2 pieces) hit 32 different bank pairs.
-  __shared__ u32x4 k_lds[4 * 256];       // 16 KiB
-  __shared__ u32x2 v_lds[4 * kD * 4];    // 16 KiB
+  // V: [block pair u][dim][4 units of 16 B]; unit j of (u, d) holds keys
+  //    4j..4j+3 of block 2u followed by the same keys of block 2u+1, exactly
+  //    the A operand of one PV MFMA.  Unit j sits in slot j ^ ((d >> 1) & 3),
+  //    so any 8 consecutive dims of one unit index fill a 128-byte bank line.
+  __shared__ u32x4 k_lds[2][4 * 256];       // 2 x 16 KiB
+  __shared__ u32x4 v_lds[2][2 * kD * 4];    // 2 x 16 KiB
 
   u32x4 kst[4], vst[4];
   auto load_tile = [&](int t) {
@@ -134,21 +161,26 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
     }
   };
   auto store_tile = [&](int t) {
+    u32x4* kl = k_lds[t & 1];
+    u32x4* vl = v_lds[t & 1];
+    const int d = tid >> 1, hh = tid & 1;  // V tile 16-byte unit tid: dim d, keys 8hh..
+    const int sw = (d >> 1) & 3;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      k_lds[a * 256 + tid] = kst[a];
-      const int d = tid >> 1, hh = tid & 1;  // V tile 16-byte unit tid: dim d, keys 8hh..
-      u32x4 x = vst[a];
+      kl[a * 256 + tid] = kst[a];
       const int k0 = t * kBN + 16 * a + 8 * hh;  // absolute key of its first half
-      if (k0 + 8 > Lc) {
-        x.x = mask_pair(x.x, k0, Lc);
-        x.y = mask_pair(x.y, k0 + 2, Lc);
-        x.z = mask_pair(x.z, k0 + 4, Lc);
-        x.w = mask_pair(x.w, k0 + 6, Lc);
+      if (k0 + 8 > Lc) {  // zero V past the sequence: p = 0 there, but 0 * NaN is not 0
+        vst[a].x = mask_pair(vst[a].x, k0, Lc);
+        vst[a].y = mask_pair(vst[a].y, k0 + 2, Lc);
+        vst[a].z = mask_pair(vst[a].z, k0 + 4, Lc);
+        vst[a].w = mask_pair(vst[a].w, k0 + 6, Lc);
       }
-      const int sw = 2 * ((d >> 3) & 1);
-      v_lds[(a * kD + d) * 4 + ((2 * hh) ^ sw)] = u32x2{x.x, x.y};
-      v_lds[(a * kD + d) * 4 + ((2 * hh + 1) ^ sw)] = u32x2{x.z, x.w};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const u32x4 e = vst[2 * u], o = vst[2 * u + 1];
+      vl[(u * kD + d) * 4 + ((2 * hh) ^ sw)] = u32x4{e.x, e.y, o.x, o.y};
+      vl[(u * kD + d) * 4 + ((2 * hh + 1) ^ sw)] = u32x4{e.z, e.w, o.z, o.w};
     }
   };
 
@@ -157,16 +189,22 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = (f32x4)0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // Per row: running maximum of the raw scores, the raw score above which
+  // the accumulator must be rescaled, -max * scale_log2, and the denominator.
+  float m_raw[2] = {-INFINITY, -INFINITY}, m_lim[2] = {-INFINITY, -INFINITY};
+  float m_off[2] = {0.f, 0.f}, l_run[2] = {0.f, 0.f};
+  const float slack_raw = kSlack / scale_log2;
+  const half2_t ones = {(_Float16)1.f, (_Float16)1.f};
 
   load_tile(0);
+  store_tile(0);
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    store_tile(t);
-    __syncthreads();
+    __syncthreads();  // tile t is in LDS; every wave is done with tile t - 1
     if (t + 1 < ntiles) load_tile(t + 1);
+    const u32x4* kl = k_lds[t & 1];
+    const u32x4* vl = v_lds[t & 1];
 
-    // S^T[key][row] = K . Q^T; block kb of the tile = MFMA rows (keys) 0..15
+    // S^T[key][row] = K . Q^T (raw scores); block kb of the tile = MFMA rows 0..15
     f32x4 sacc[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -174,48 +212,71 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
       sacc[kb][1] = (f32x4)0.f;
 #pragma unroll
       for (int kd = 0; kd < 4; ++kd) {
-        const half8_t ka = __builtin_bit_cast(half8_t, k_lds[kb * 256 + (4 * kd + lq) * 16 + lr]);
+        const half8_t ka = __builtin_bit_cast(half8_t, kl[kb * 256 + (4 * kd + lq) * 16 + lr]);
         sacc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[0][kd], sacc[kb][0], 0, 0, 0);
         sacc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[1][kd], sacc[kb][1], 0, 0, 0);
       }
     }
 
-    // online softmax per row (this lane: rows 16rb + lr, keys 16kb + 4lq + i)
-    const bool need_mask = t * kBN + kBN - 1 > first_pos;
-    half8_t pb[2][2];  // [u][rb]: B operand of the second product
-    float alpha[2];
+    // causal mask (and keys past the sequence) only where the tile reaches
+    // past the smallest row position
+    if (t * kBN + kBN - 1 > first_pos || t * kBN + kBN > Lc) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t * kBN + 16 * kb + 4 * lq + i > prow[rb]) sacc[kb][rb][i] = -INFINITY;
+    }
+
+    // online softmax per row (this lane: rows 16rb + lr, keys 16kb + 4lq + i).
+    // The running maximum is only raised when some score exceeds it by more
+    // than kSlack; both the numerator and the denominator use the same
+    // (possibly stale) maximum, so the quotient is unchanged.
+    float mloc[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float mx = -INFINITY;
+      float a0 = fmaxf(sacc[0][rb][0], sacc[0][rb][1]), a1 = fmaxf(sacc[0][rb][2], sacc[0][rb][3]);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 1; kb < 4; ++kb) {
+        a0 = fmaxf(a0, fmaxf(sacc[kb][rb][0], sacc[kb][rb][1]));
+        a1 = fmaxf(a1, fmaxf(sacc[kb][rb][2], sacc[kb][rb][3]));
+      }
+      mloc[rb] = fmaxf(a0, a1);
+    }
+    if (__any(mloc[0] > m_lim[0] || mloc[1] > m_lim[1])) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = sacc[kb][rb][i] * scale_log2;
-          if (need_mask && t * kBN + 16 * kb + 4 * lq + i > prow[rb]) s = -INFINITY;
-          sacc[kb][rb][i] = s;
-          mx = fmaxf(mx, s);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[rb], mx);  // finite: key 0 is in tile 0 for every row
-      alpha[rb] = exp2f(m_run[rb] - m_new);
-      m_run[rb] = m_new;
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mx = max_xor16(max_xor32(mloc[rb]));
+        const float m_new = fmaxf(m_raw[rb], mx);  // finite: key 0 is in tile 0 for every row
+        const float alpha = __builtin_amdgcn_exp2f((m_raw[rb] - m_new) * scale_log2);
+        m_raw[rb] = m_new;
+        m_lim[rb] = m_new + slack_raw;
+        m_off[rb] = -m_new * scale_log2;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[db][rb] *= alpha;
+      }
+    }
+
+    half8_t pb[2][2];  // [u][rb]: B operand of the second product
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const _Float16 ph = (_Float16)exp2f(sacc[kb][rb][i] - m_new);
-          lsum += (float)ph;
-          pb[kb >> 1][rb][4 * (kb & 1) + i] = ph;
+        for (int i = 0; i < 4; i += 2) {
+          const half2_t ph = {
+              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i], scale_log2, m_off[rb])),
+              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i + 1], scale_log2, m_off[rb]))};
+          lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
+          pb[kb >> 1][rb][4 * (kb & 1) + i] = ph[0];
+          pb[kb >> 1][rb][4 * (kb & 1) + i + 1] = ph[1];
         }
-      l_run[rb] = l_run[rb] * alpha[rb] + lsum;
+      l_run[rb] += lsum;
     }
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) oacc[db][rb] *= alpha[rb];
 
     // O^T[dim][row] += V^T[dim][key] . P^T[key][row]; MFMA u contracts keys
     // 4lq..4lq+3 of blocks 2u and 2u+1 in this lane (the order of pb)
@@ -224,21 +285,17 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const int d = 16 * db + lr;
-        const int pj = lq ^ (2 * ((d >> 3) & 1));
-        const u32x2 lo = v_lds[((2 * u) * kD + d) * 4 + pj];
-        const u32x2 hi = v_lds[((2 * u + 1) * kD + d) * 4 + pj];
-        const half8_t va = __builtin_bit_cast(half8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
+        const half8_t va = __builtin_bit_cast(half8_t, vl[(u * kD + d) * 4 + (lq ^ ((d >> 1) & 3))]);
         oacc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[u][0], oacc[db][0], 0, 0, 0);
         oacc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[u][1], oacc[db][1], 0, 0, 0);
       }
     }
+    if (t + 1 < ntiles) store_tile(t + 1);  // other buffer: its readers passed the barrier
   }
 
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    float l = l_run[rb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_xor16(sum_xor32(l_run[rb]));
     const float inv = 1.f / l;
     const int r = qt * kBM + 16 * rb + lr;
     if (r < C) {
@@ -264,7 +321,8 @@ hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void
                         int num_tokens, int max_q_len, int max_context_len, float scale,
                         hipStream_t stream) {
   (void)max_context_len;
-  if (!chunk_fast_path(g))
+  // the fast path tracks maxima of raw scores, which needs scale > 0
+  if (!chunk_fast_path(g) || !(scale > 0.f) || !std::isfinite(scale))
     return launch_attend_generic(g, out, q, k_arena, v_arena, block_table, max_blocks, nullptr,
                                  cu_q_lens, chunk_start, num_seqs, num_tokens, scale, stream);
   const int n_qtiles = (max_q_len + kBM - 1) / kBM;
