@@ -194,6 +194,15 @@ def paged_attention_chunk_workspace_bytes(g: Geom, num_seqs: int, num_tokens: in
 def paged_attention_chunk(g: Geom, out, q, k_arena, v_arena, block_table, cu_q_lens,
                           chunk_start, max_q_len: int, max_context_len: int, scale: float,
                           workspace=None, stream=None) -> None:
+    """``workspace``: a device tensor of at least
+    paged_attention_chunk_workspace_bytes(...) bytes (the schedule of the
+    attention kernel); None makes a fresh one from torch's allocator."""
+    if workspace is None:
+        need = paged_attention_chunk_workspace_bytes(g, chunk_start.shape[0], q.shape[0],
+                                                     max_context_len)
+        if need:
+            import torch
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().paged_attention_chunk(ctypes.byref(g), _ptr(out), F32, _ptr(q), _ptr(k_arena),
                                        _ptr(v_arena), _ptr(block_table), block_table.shape[1],

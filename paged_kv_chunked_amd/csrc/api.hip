@@ -82,7 +82,7 @@ pkv_status paged_attention_chunk_workspace_bytes(const pkv_geom* geom, int32_t n
   if (st != PKV_OK) return st;
   if (!bytes) return PKV_ERR_NULL;
   if (num_seqs < 0 || num_tokens < 0 || max_context_len < 0) return PKV_ERR_RANGE;
-  *bytes = 0;
+  *bytes = pkv::chunk_workspace_bytes(*geom, num_seqs, num_tokens);
   return PKV_OK;
 }
 
@@ -93,8 +93,6 @@ pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dt
                                  int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
                                  int32_t max_context_len, float scale, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   pkv_status st = check_geom(geom);
   if (st != PKV_OK) return st;
   if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
@@ -105,10 +103,12 @@ pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dt
   if (max_blocks_per_seq < 1 || max_q_len < 1 || max_context_len < max_q_len ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
     return PKV_ERR_RANGE;
+  const size_t need = pkv::chunk_workspace_bytes(*geom, num_seqs, num_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   return hip_status(pkv::launch_chunk(*geom, (float*)out, q, k_arena, v_arena, block_table,
                                       max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs,
-                                      num_tokens, max_q_len, max_context_len, scale,
-                                      (hipStream_t)stream));
+                                      num_tokens, max_q_len, max_context_len, scale, workspace,
+                                      workspace_bytes, (hipStream_t)stream));
 }
 
 pkv_status pkv_copy_blocks(const pkv_geom* geom, void* k_arena, void* v_arena,

@@ -6,26 +6,31 @@
 // Tuned path (fp16 storage, head_dim 128, 4 query heads per KV head): a dense
 // contraction, so both products run on gfx950 fp16 matrix cores
 // (v_mfma_f32_16x16x32_f16, fp32 accumulation).
-//   * one workgroup = (sequence, KV head, tile of 32 chunk rows); its 4 waves
-//     are the 4 query heads of the group, so every K/V tile is fetched from
-//     memory once for all of them;
+//   * one workgroup = (sequence, KV head, tile of 64 chunk rows), 8 waves: wave
+//     w serves query head 4g + (w & 3) for rows 32 (w >> 2) .. +31 of the tile,
+//     so every K/V tile is fetched once for 4 heads x 64 rows;
 //   * keys are walked in tiles of 64 = 4 arena blocks looked up in the block
-//     table; a tile is loaded into registers one step ahead and staged in LDS
-//     in the arena's own tile layouts (K in 16-byte pieces grouped by piece,
-//     V head-dim-major, the latter XOR-swizzled), so every MFMA operand read
-//     is bank-conflict free;
-//   * S^T = K Q^T is computed with keys along the MFMA M dimension, so each
-//     lane ends up holding 16 keys of one query row: the row max and sum are
-//     lane-local plus two cross-lane steps, and the probabilities are already
-//     in the B-operand layout of O^T += V^T P^T (the V^T operand takes the
-//     same keys, 4 from each of two blocks, in the same order);
+//     table.  Tiles travel from memory straight into a 4-stage LDS ring
+//     (direct-to-LDS 16-byte loads, up to three tiles in flight) in the
+//     arena's own layouts: K [block][16-byte dim piece][key] and V
+//     [block][dim][two 8-key halves], with 16-byte units swapped on the way
+//     in so the operand reads below are bank-conflict free;
+//   * S^T = K Q^T puts keys on the MFMA M dimension, so each lane ends up
+//     holding 16 keys of one query row: the row max and sum are lane-local
+//     plus two cross-lane steps.  The keys are assigned to MFMA rows so that
+//     a lane's 8 probabilities for the second product are 8 consecutive keys
+//     of one block: the B operand of O^T += V^T P^T is then built in
+//     registers, and the matching V^T operand is one 16-byte piece of the
+//     arena's V row;
 //   * online softmax in fp32 (scores in log2 units), P rounded to fp16 for the
 //     second product, and the denominator summed from those rounded values so
-//     the weights still add up to one;
-//   * the causal mask is applied only on tiles that reach past the tile's
-//     first row position; V slots past the sequence's length are zeroed in LDS
-//     (p = 0 there, but 0 * NaN would not be 0).
-// Other shapes run the generic kernel.
+//     the weights still add up to one; the running maximum is only moved when
+//     a score exceeds it by a margin (quotient unchanged, see kSlack);
+//   * the causal mask is applied only on tiles that reach past a wave's first
+//     row position; V slots past the sequence's length are zeroed in LDS in
+//     the last tile (p = 0 there, but 0 * NaN would not be 0).
+// Work items are dispatched longest first (chunk_order_kernel).  Other shapes
+// run the generic kernel.
 #include <cmath>
 
 #include "pkv_internal.h"
@@ -40,17 +45,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kG = 4;
-constexpr int kBM = 32;  // chunk rows per workgroup (per wave: 32 rows of one head)
-constexpr int kBN = 64;  // keys per tile (4 arena blocks)
-
-// fp16 elements per 16-byte piece of the K layout [block][head][D/8][16][8].
-constexpr int kX = 8;
-
-__device__ inline uint32_t mask_pair(uint32_t x, int key0, int limit) {
-  if (key0 >= limit) return 0u;
-  if (key0 + 1 >= limit) return x & 0xFFFFu;
-  return x;
-}
+constexpr int kBM = 32;            // rows per wave
+constexpr int kRowGroups = 2;      // waves per query head in a workgroup
+constexpr int kRows = kBM * kRowGroups;  // chunk rows per workgroup
+constexpr int kBN = 64;            // keys per tile (4 arena blocks)
+constexpr int kWaves = kG * kRowGroups;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;         // LDS ring depth (tiles)
+constexpr int kUnitsPerBlock = kBlock * kD * 2 / 16;  // 16-byte units in one (block, head) tile
+constexpr int kStageUnits = 2 * 4 * kUnitsPerBlock;    // K and V of 4 blocks
 
 // Reductions over the four lanes {l, l^16, l^32, l^48} that hold one row,
 // through the gfx950 cross-row lane swaps (no LDS round trip).
@@ -71,45 +74,191 @@ __device__ inline float sum_xor16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Three-way maximum as one v_max3_f32.  fmaxf would first quiet each operand
+// (the compiler cannot tell that matrix-core results are never signalling
+// NaNs), doubling the instruction count of the row maximum.
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// One 16-byte direct-to-LDS load per lane: lane i's 16 bytes from `src` land
+// at LDS byte address lds + 16 i.  Issued from asm so that the compiler does
+// not drain the vector-memory counter before every LDS read; the kernel waits
+// for these loads itself (wait_vm) before the barrier that publishes a tile.
+__device__ inline void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // How far (log2 units) a row's running maximum may lag the true maximum before
 // the accumulator is rescaled: probabilities stay <= 2^8, well inside fp16.
 constexpr float kSlack = 8.f;
 
-__global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
+// Work of row tile rt of sequence b, in 64-key tiles (0 if the tile is empty).
+// The same arithmetic decides the tile loop of the attention kernel.
+__device__ inline int chunk_item_cost(const int32_t* __restrict__ cu_q_lens,
+                                      const int32_t* __restrict__ chunk_start, int b, int rt,
+                                      int max_blocks, int num_tokens) {
+  const int row0 = cu_q_lens[b];
+  const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
+  if (rt * kRows >= C) return 0;
+  const int P = chunk_start[b];
+  const int Lc = min(P + C, max_blocks * kBlock);
+  if (Lc <= 0) return 0;
+  const int kend = min(Lc, P + min(C, rt * kRows + kRows));
+  return max(1, (kend + kBN - 1) / kBN);
+}
+
+constexpr int kOrderBuckets = 4096;  // costs at or above the last bucket share it
+
+// Schedule of the attention kernel: the (sequence, row tile) items sorted by
+// decreasing work (counting sort on the tile count; equal costs in any order),
+// so the longest items are dispatched first and the short ones fill the gaps
+// at the end.  One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void chunk_order_kernel(
+    int32_t* __restrict__ order, const int32_t* __restrict__ cu_q_lens,
+    const int32_t* __restrict__ chunk_start, int num_seqs, int n_rtiles, int max_blocks,
+    int num_tokens) {
+  __shared__ int hist[kOrderBuckets];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int n = num_seqs * n_rtiles;
+  for (int c = tid; c < kOrderBuckets; c += 1024) hist[c] = 0;
+  __syncthreads();
+  for (int k = tid; k < n; k += 1024) {
+    const int b = k / n_rtiles, rt = k - b * n_rtiles;
+    const int c = min(chunk_item_cost(cu_q_lens, chunk_start, b, rt, max_blocks, num_tokens),
+                      kOrderBuckets - 1);
+    atomicAdd(&hist[c], 1);
+  }
+  __syncthreads();
+  // exclusive scan in decreasing cost order: thread t owns the 4 buckets
+  // kOrderBuckets - 1 - 4t - {0..3}
+  int own[4], sum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    own[u] = hist[kOrderBuckets - 1 - 4 * tid - u];
+    sum += own[u];
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int x = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  int start = part[tid] - sum;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    hist[kOrderBuckets - 1 - 4 * tid - u] = start;
+    start += own[u];
+  }
+  __syncthreads();
+  for (int k = tid; k < n; k += 1024) {
+    const int b = k / n_rtiles, rt = k - b * n_rtiles;
+    const int c = min(chunk_item_cost(cu_q_lens, chunk_start, b, rt, max_blocks, num_tokens),
+                      kOrderBuckets - 1);
+    order[atomicAdd(&hist[c], 1)] = k;
+  }
+}
+
+// Zero the halves of a 16-byte V unit (8 consecutive keys key0..key0+7) whose
+// key is >= limit.
+__device__ inline u32x4 mask_unit(u32x4 x, int key0, int limit) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int k = key0 + 2 * c;
+    uint32_t w = x[c];
+    if (k >= limit) w = 0u;
+    else if (k + 1 >= limit) w &= 0xFFFFu;
+    x[c] = w;
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
     float* __restrict__ out, const _Float16* __restrict__ q,
     const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
-    float scale_log2, int Hkv, int num_seqs, int n_qtiles, int num_blocks, int num_tokens) {
-  // XCD-aware order.  Linear workgroup id i runs on XCD i % 8.  The pairs
-  // p = b * Hkv + g are dealt to XCDs round-robin (p % 8) and all row tiles of
-  // a pair stay on its XCD, so the pair's K/V tiles are fetched into one L2
-  // and reused by its row tiles; within an XCD, later (longer) row tiles of a
-  // pair are issued first.
-  const int npairs = num_seqs * Hkv;
+    const int32_t* __restrict__ order, float scale_log2, int Hkv, int num_seqs, int n_rtiles,
+    int num_blocks, int num_tokens) {
+  // Workgroup i takes item order[i / Hkv] for KV head i % Hkv.  Linear
+  // workgroup ids are dealt to the 8 XCDs round-robin, so with Hkv a multiple
+  // of 8 every row tile of a (sequence, KV head) pair runs on one XCD and the
+  // pair's K/V tiles are fetched into that XCD's L2 once; the longest items
+  // are issued first.
   const int i = blockIdx.x;
-  const int xcd = i & 7, j = i >> 3;
-  const int lp = j / n_qtiles;                  // pair index among this XCD's pairs
-  const int qt = n_qtiles - 1 - (j - lp * n_qtiles);
-  const int p = lp * 8 + xcd;
-  if (p >= npairs) return;
-  const int b = p / Hkv, g = p - b * Hkv;
+  const int k = i / Hkv, g = i - k * Hkv;
+  if (k >= num_seqs * n_rtiles) return;
+  const int item = order[k];
+  const int b = item / n_rtiles, rt = item - b * n_rtiles;
   const int row0 = cu_q_lens[b];
   const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
-  if (qt * kBM >= C) return;
+  if (rt * kRows >= C) return;
   const int P = chunk_start[b];
   const int Lc = min(P + C, max_blocks * kBlock);  // keys that exist
   if (Lc <= 0) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is made visibly uniform, so block-table reads indexed by
+  // it are scalar loads (they must not add to the vector-memory count)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
-  const int h = g * kG + wave;
+  const int h = g * kG + (wave & 3);
+  const int wrow0 = rt * kRows + kBM * (wave >> 2);  // first chunk row of this wave
 
-  // Q^T as the B operand: qf[rb][kd] = Q[row 16rb + lr][dims 32kd + 8lq .. +8]
+  // 4 stages x (K: 4 blocks x 256 units, then V: 4 blocks x 256 units)
+  __shared__ u32x4 ring[kStages * kStageUnits];  // 128 KiB
+
+  const int row_hi = min(C, rt * kRows + kRows);
+  const int kend = min(Lc, P + row_hi);  // keys [0, kend) are visible to some row
+  const int ntiles = (kend + kBN - 1) / kBN;
+  const int nblk_seq = (Lc + kBlock - 1) / kBlock;
+  const int32_t* bt = block_table + (size_t)b * max_blocks;
+
+  // Tile loads.  Wave w moves quarters 2(w&1) and 2(w&1)+1 of block w >> 1's
+  // K and V tiles (4 x 1 KiB); a lane's unit goes to position pos of the
+  // block's 256 units:
+  //   K: pos = piece * 16 + slot', fetched from slot' ^ 4 in odd blocks, so
+  //      the two blocks an operand read touches use disjoint banks;
+  //   V: pos = dim * 2 + half', fetched from half' ^ (dim >> 3 & 1), so the
+  //      16 dims an operand read touches use disjoint banks.
+  // Past the sequence's last block the id of that last block is used (its
+  // contents never reach the output: scores masked, V zeroed).
+  const int dma_blk = wave >> 1;
+  const uint32_t ring_lds =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)ring;
+  auto issue_tile = [&](int t) {
+    int blk = bt[min(t * 4 + dma_blk, nblk_seq - 1)];
+    blk = (blk < 0 || blk >= num_blocks) ? 0 : blk;
+    const u32x4* kt = (const u32x4*)k_arena + ((size_t)blk * Hkv + g) * kUnitsPerBlock;
+    const u32x4* vt = (const u32x4*)v_arena + ((size_t)blk * Hkv + g) * kUnitsPerBlock;
+    const uint32_t st = ring_lds + (uint32_t)((t % kStages) * kStageUnits * 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int qq = 2 * (wave & 1) + j;
+      const int pos = qq * 64 + lane;
+      const uint32_t off = (uint32_t)((dma_blk * kUnitsPerBlock + qq * 64) * 16);
+      dma16(kt + (pos ^ (4 * (dma_blk & 1))), __builtin_amdgcn_readfirstlane(st + off));
+      dma16(vt + (pos ^ ((pos >> 4) & 1)),
+            __builtin_amdgcn_readfirstlane(st + 4 * kUnitsPerBlock * 16 + off));
+    }
+  };
+
+  // Q^T as the B operand: qf[rb][kd] = Q[row wrow0 + 16rb + lr][dims 32kd + 8lq .. +8]
   half8_t qf[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int r = qt * kBM + 16 * rb + lr;
+    const int r = wrow0 + 16 * rb + lr;
 #pragma unroll
     for (int kd = 0; kd < 4; ++kd) {
       if (r < C) {
@@ -120,69 +269,19 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
       }
     }
   }
+  // every query load is complete before the first tile load is issued, so the
+  // tile waits below count tile loads only
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+  if (ntiles > 2) issue_tile(2);
+
   // absolute positions of this lane's two rows (rows past the chunk borrow the
   // last valid position so they stay finite; they are never stored)
   int prow[2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) prow[rb] = min(P + qt * kBM + 16 * rb + lr, Lc - 1);
-
-  const int row_hi = min(C, qt * kBM + kBM);
-  const int kend = min(Lc, P + row_hi);  // keys [0, kend) are visible to some row
-  const int ntiles = (kend + kBN - 1) / kBN;
-  const int first_pos = P + qt * kBM;    // smallest row position in the tile
-  const int nblk_seq = (Lc + kBlock - 1) / kBlock;
-  const int32_t* bt = block_table + (size_t)b * max_blocks;
-
-  // Two LDS buffers (tile t in buffer t & 1), so one barrier per tile suffices.
-  // K: 4 blocks in the arena's own tile layout [block][piece][key][16 B], so
-  //    the operand reads (16 keys x one piece per 16 lanes) are contiguous.
-  // V: [block pair u][dim][4 units of 16 B]; unit j of (u, d) holds keys
-  //    4j..4j+3 of block 2u followed by the same keys of block 2u+1, exactly
-  //    the A operand of one PV MFMA.  Unit j sits in slot j ^ ((d >> 1) & 3),
-  //    so any 8 consecutive dims of one unit index fill a 128-byte bank line.
-  __shared__ u32x4 k_lds[2][4 * 256];       // 2 x 16 KiB
-  __shared__ u32x4 v_lds[2][2 * kD * 4];    // 2 x 16 KiB
-
-  u32x4 kst[4], vst[4];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int lb = t * 4 + a;
-      if (lb < nblk_seq) {
-        int blk = bt[lb];
-        if (blk < 0 || blk >= num_blocks) blk = 0;
-        const size_t tile = ((size_t)blk * Hkv + g) * (kBlock * kD / 8);
-        kst[a] = ((const u32x4*)k_arena)[tile + tid];
-        vst[a] = ((const u32x4*)v_arena)[tile + tid];
-      } else {
-        kst[a] = (u32x4)0u;
-        vst[a] = (u32x4)0u;
-      }
-    }
-  };
-  auto store_tile = [&](int t) {
-    u32x4* kl = k_lds[t & 1];
-    u32x4* vl = v_lds[t & 1];
-    const int d = tid >> 1, hh = tid & 1;  // V tile 16-byte unit tid: dim d, keys 8hh..
-    const int sw = (d >> 1) & 3;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      kl[a * 256 + tid] = kst[a];
-      const int k0 = t * kBN + 16 * a + 8 * hh;  // absolute key of its first half
-      if (k0 + 8 > Lc) {  // zero V past the sequence: p = 0 there, but 0 * NaN is not 0
-        vst[a].x = mask_pair(vst[a].x, k0, Lc);
-        vst[a].y = mask_pair(vst[a].y, k0 + 2, Lc);
-        vst[a].z = mask_pair(vst[a].z, k0 + 4, Lc);
-        vst[a].w = mask_pair(vst[a].w, k0 + 6, Lc);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const u32x4 e = vst[2 * u], o = vst[2 * u + 1];
-      vl[(u * kD + d) * 4 + ((2 * hh) ^ sw)] = u32x4{e.x, e.y, o.x, o.y};
-      vl[(u * kD + d) * 4 + ((2 * hh + 1) ^ sw)] = u32x4{e.z, e.w, o.z, o.w};
-    }
-  };
+  for (int rb = 0; rb < 2; ++rb) prow[rb] = min(P + wrow0 + 16 * rb + lr, Lc - 1);
+  const int first_pos = P + wrow0;  // smallest row position of this wave
 
   f32x4 oacc[8][2];
 #pragma unroll
@@ -196,54 +295,111 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
   const float slack_raw = kSlack / scale_log2;
   const half2_t ones = {(_Float16)1.f, (_Float16)1.f};
 
-  load_tile(0);
-  store_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // tile t is in LDS; every wave is done with tile t - 1
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const u32x4* kl = k_lds[t & 1];
-    const u32x4* vl = v_lds[t & 1];
+  // Operand addresses (16-byte units within a stage).  K fragment of MFMA kb,
+  // dim piece 4kd + lq: MFMA row m = lr holds key slot
+  // 8((m >> 2) & 1) + 4(kb & 1) + (m & 3) of block 2(kb >> 1) + (m >> 3).
+  const int ka = lr >> 3;  // block offset within the pair of blocks
+  const int kslot0 = 8 * ((lr >> 2) & 1) + (lr & 3);
+  // V fragment of dims block db for the keys of MFMA u: 16-byte unit
+  // (block 2u + (lq >> 1), dim 16db + lr, half (lq & 1) ^ (lr >> 3 & 1))
+  const int vhalf = (lq & 1) ^ ((lr >> 3) & 1);
 
-    // S^T[key][row] = K . Q^T (raw scores); block kb of the tile = MFMA rows 0..15
+  for (int t = 0; t < ntiles; ++t) {
+    // tile t's loads (this wave's) are done; then every wave's, and every
+    // wave has finished tile t - 1, whose stage the next load reuses
+    if (t + 2 < ntiles) wait_vm<8>();
+    else if (t + 1 < ntiles) wait_vm<4>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 3 < ntiles) issue_tile(t + 3);
+    const u32x4* kl = ring + (t % kStages) * kStageUnits;
+    const u32x4* vl = kl + 4 * kUnitsPerBlock;
+    if (t * kBN + kBN > Lc) {
+      // last tile: zero V of keys past the sequence (2 units per thread)
+      u32x4* vw = ring + (t % kStages) * kStageUnits + 4 * kUnitsPerBlock;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int unit = tid + e * kThreads;  // [block][dim][half']
+        const int a = unit >> 8, d = (unit >> 1) & (kD - 1), hs = unit & 1;
+        const int key0 = t * kBN + 16 * a + 8 * (hs ^ ((d >> 3) & 1));
+        if (key0 + 8 > Lc) vw[unit] = mask_unit(vw[unit], key0, Lc);
+      }
+      __syncthreads();
+    }
+
+    // S^T[key][row] = K . Q^T (raw scores).  The K fragments of MFMA kb + 1
+    // are read while kb's products run.
     f32x4 sacc[4][2];
+    half8_t kf[2][4];
+    auto read_k = [&](int kb, half8_t* f) {
+      const int a = 2 * (kb >> 1) + ka;
+      const int s = (kslot0 + 4 * (kb & 1)) ^ (4 * (a & 1));
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd)
+        f[kd] = __builtin_bit_cast(half8_t, kl[a * kUnitsPerBlock + (4 * kd + lq) * 16 + s]);
+    };
+    read_k(0, kf[0]);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      if (kb < 3) read_k(kb + 1, kf[(kb + 1) & 1]);
       sacc[kb][0] = (f32x4)0.f;
       sacc[kb][1] = (f32x4)0.f;
 #pragma unroll
       for (int kd = 0; kd < 4; ++kd) {
-        const half8_t ka = __builtin_bit_cast(half8_t, kl[kb * 256 + (4 * kd + lq) * 16 + lr]);
-        sacc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[0][kd], sacc[kb][0], 0, 0, 0);
-        sacc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[1][kd], sacc[kb][1], 0, 0, 0);
+        sacc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb & 1][kd], qf[0][kd], sacc[kb][0], 0, 0, 0);
+        sacc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb & 1][kd], qf[1][kd], sacc[kb][1], 0, 0, 0);
+      }
+    }
+    // the first two V fragment pairs are read during the softmax
+    half8_t vf[3][2];
+    auto read_v = [&](int db, half8_t* f) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int a = 2 * u + (lq >> 1);
+        f[u] = __builtin_bit_cast(half8_t, vl[a * kUnitsPerBlock + (16 * db + lr) * 2 + vhalf]);
+      }
+    };
+    read_v(0, vf[0]);
+    read_v(1, vf[1]);
+    // Instruction order of this block: each LDS read is issued about two
+    // products ahead of the first product that needs it, so the read latency
+    // hides behind matrix-core work (the scheduler would otherwise place
+    // every read right before its use).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+
+    // Causal mask (and keys past the sequence) only where the tile reaches
+    // past this wave's smallest row position.  Score (kb, i) of this lane is
+    // key 16(2(kb >> 1) + (lq >> 1)) + 8(lq & 1) + 4(kb & 1) + i of the tile.
+    if (t * kBN + kBN - 1 > first_pos || t * kBN + kBN > Lc) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key0 = t * kBN + 16 * (2 * (kb >> 1) + (lq >> 1)) + 8 * (lq & 1) + 4 * (kb & 1);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + i > prow[rb]) sacc[kb][rb][i] = -INFINITY;
       }
     }
 
-    // causal mask (and keys past the sequence) only where the tile reaches
-    // past the smallest row position
-    if (t * kBN + kBN - 1 > first_pos || t * kBN + kBN > Lc) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t * kBN + 16 * kb + 4 * lq + i > prow[rb]) sacc[kb][rb][i] = -INFINITY;
-    }
-
-    // online softmax per row (this lane: rows 16rb + lr, keys 16kb + 4lq + i).
-    // The running maximum is only raised when some score exceeds it by more
-    // than kSlack; both the numerator and the denominator use the same
-    // (possibly stale) maximum, so the quotient is unchanged.
+    // online softmax per row (this lane: rows 16rb + lr, 16 keys each).  The
+    // running maximum is only raised when some score exceeds it by more than
+    // kSlack; both the numerator and the denominator use the same (possibly
+    // stale) maximum, so the quotient is unchanged.
     float mloc[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float a0 = fmaxf(sacc[0][rb][0], sacc[0][rb][1]), a1 = fmaxf(sacc[0][rb][2], sacc[0][rb][3]);
-#pragma unroll
-      for (int kb = 1; kb < 4; ++kb) {
-        a0 = fmaxf(a0, fmaxf(sacc[kb][rb][0], sacc[kb][rb][1]));
-        a1 = fmaxf(a1, fmaxf(sacc[kb][rb][2], sacc[kb][rb][3]));
-      }
-      mloc[rb] = fmaxf(a0, a1);
+      const f32x4 s0 = sacc[0][rb], s1 = sacc[1][rb], s2 = sacc[2][rb], s3 = sacc[3][rb];
+      const float a0 = max3f(s0[0], s0[1], s0[2]), a1 = max3f(s0[3], s1[0], s1[1]);
+      const float a2 = max3f(s1[2], s1[3], s2[0]), a3 = max3f(s2[1], s2[2], s2[3]);
+      const float a4 = max3f(s3[0], s3[1], s3[2]);
+      mloc[rb] = max3f(max3f(a0, a1, a2), max3f(a3, a4, s3[3]), a0);
     }
     if (__any(mloc[0] > m_lim[0] || mloc[1] > m_lim[1])) {
 #pragma unroll
@@ -260,7 +416,9 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
       }
     }
 
-    half8_t pb[2][2];  // [u][rb]: B operand of the second product
+    // pb[u][rb]: B operand of the second product, keys 8(lq & 1) .. +7 of
+    // block 2u + (lq >> 1) = scores (kb = 2u, i = 0..3), (kb = 2u + 1, i = 0..3)
+    half8_t pb[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float lsum = 0.f;
@@ -278,26 +436,27 @@ __global__ __launch_bounds__(256, 2) void chunk_mfma_kernel(
       l_run[rb] += lsum;
     }
 
-    // O^T[dim][row] += V^T[dim][key] . P^T[key][row]; MFMA u contracts keys
-    // 4lq..4lq+3 of blocks 2u and 2u+1 in this lane (the order of pb)
+    // O^T[dim][row] += V^T[dim][key] . P^T[key][row].  The V fragments of dims
+    // block db + 2 are read before block db's four products (scheduling
+    // barriers keep that order).
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int db = 0; db < 8; ++db) {
+      if (db + 2 < 8) read_v(db + 2, vf[(db + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int d = 16 * db + lr;
-        const half8_t va = __builtin_bit_cast(half8_t, vl[(u * kD + d) * 4 + (lq ^ ((d >> 1) & 3))]);
-        oacc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[u][0], oacc[db][0], 0, 0, 0);
-        oacc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[u][1], oacc[db][1], 0, 0, 0);
+      for (int u = 0; u < 2; ++u) {
+        oacc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % 3][u], pb[u][0], oacc[db][0], 0, 0, 0);
+        oacc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % 3][u], pb[u][1], oacc[db][1], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (t + 1 < ntiles) store_tile(t + 1);  // other buffer: its readers passed the barrier
   }
 
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const float l = sum_xor16(sum_xor32(l_run[rb]));
     const float inv = 1.f / l;
-    const int r = qt * kBM + 16 * rb + lr;
+    const int r = wrow0 + 16 * rb + lr;
     if (r < C) {
       float* dst = out + ((size_t)(row0 + r) * Hq + h) * kD + 4 * lq;
 #pragma unroll
@@ -315,24 +474,36 @@ bool chunk_fast_path(const pkv_geom& g) {
   return g.dtype == PKV_F16 && g.head_dim == kD && g.num_q_heads == kG * g.num_kv_heads;
 }
 
+size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens) {
+  if (!chunk_fast_path(g) || num_seqs <= 0 || num_tokens <= 0) return 0;
+  // the schedule: one int32 per (sequence, row tile)
+  return (size_t)num_seqs * (size_t)((num_tokens + kRows - 1) / kRows) * sizeof(int32_t);
+}
+
 hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
                         const void* v_arena, const int32_t* block_table, int max_blocks,
                         const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
                         int num_tokens, int max_q_len, int max_context_len, float scale,
-                        hipStream_t stream) {
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   (void)max_context_len;
   // the fast path tracks maxima of raw scores, which needs scale > 0
   if (!chunk_fast_path(g) || !(scale > 0.f) || !std::isfinite(scale))
     return launch_attend_generic(g, out, q, k_arena, v_arena, block_table, max_blocks, nullptr,
                                  cu_q_lens, chunk_start, num_seqs, num_tokens, scale, stream);
-  const int n_qtiles = (max_q_len + kBM - 1) / kBM;
+  // no sequence has more rows than the batch
+  const int n_rtiles = (min(max_q_len, num_tokens) + kRows - 1) / kRows;
+  const long n_items = (long)num_seqs * n_rtiles;
+  if (!workspace || workspace_bytes < (size_t)n_items * sizeof(int32_t))
+    return hipErrorInvalidValue;
+  int32_t* order = (int32_t*)workspace;
+  hipLaunchKernelGGL(chunk_order_kernel, dim3(1), dim3(1024), 0, stream, order, cu_q_lens,
+                     chunk_start, num_seqs, n_rtiles, max_blocks, num_tokens);
   const float scale_log2 = scale * 1.4426950408889634f;
-  const long npairs = (long)num_seqs * g.num_kv_heads;
-  const long nwg = 8 * ((npairs + 7) / 8) * n_qtiles;
-  hipLaunchKernelGGL(chunk_mfma_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, out,
+  const long nwg = n_items * g.num_kv_heads;
+  hipLaunchKernelGGL(chunk_mfma_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, out,
                      (const _Float16*)q, (const _Float16*)k_arena, (const _Float16*)v_arena,
-                     block_table, max_blocks, cu_q_lens, chunk_start, scale_log2,
-                     g.num_kv_heads, num_seqs, n_qtiles, g.num_blocks, num_tokens);
+                     block_table, max_blocks, cu_q_lens, chunk_start, order, scale_log2,
+                     g.num_kv_heads, num_seqs, n_rtiles, g.num_blocks, num_tokens);
   return hipGetLastError();
 }
 

@@ -81,11 +81,12 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
                          hipStream_t stream);
 
 bool chunk_fast_path(const pkv_geom& g);
+size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens);
 hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
                         const void* v_arena, const int32_t* block_table, int max_blocks,
                         const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
                         int num_tokens, int max_q_len, int max_context_len, float scale,
-                        hipStream_t stream);
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 // Generic (any dtype / head_dim / group) attention, one workgroup per
 // (row, query head).  Decode rows when cu_q_lens == nullptr.

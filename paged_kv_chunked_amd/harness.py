@@ -18,6 +18,7 @@ from typing import Dict, List
 import numpy as np
 
 from . import (BLOCK_SIZE, F16, F32, Pool, geom, kv_append_rope, paged_attention_chunk,
+               paged_attention_chunk_workspace_bytes,
                paged_attention_decode, paged_attention_decode_workspace_bytes, pkv_copy_blocks,
                pkv_rope_table_bytes, pkv_rope_table_init)
 from . import workloads as _wl
@@ -208,6 +209,9 @@ class DeviceWorkload:
             self.chunk_max_q = int(counts_c.max())
             self.chunk_max_ctx = int((self.starts_host[r0:r1] + counts_c).max())
             self.chunk_out = torch.empty((t1 - t0, Hq, D), dtype=torch.float32, device=dev)
+            ws = paged_attention_chunk_workspace_bytes(self.g, r1 - r0, t1 - t0,
+                                                       self.chunk_max_ctx)
+            self.chunk_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
 
     def append(self, stream=None, k_arena=None, v_arena=None):
         kv_append_rope(self.g, self.q_raw, self.k_new, self.v_new,
@@ -231,7 +235,7 @@ class DeviceWorkload:
                                   self.v_arena if v_arena is None else v_arena,
                                   self.chunk_bt, self.chunk_cu, self.chunk_starts,
                                   self.chunk_max_q, self.chunk_max_ctx, self.scale,
-                                  stream=stream)
+                                  self.chunk_ws, stream=stream)
 
     def step(self, stream=None, k_arena=None, v_arena=None):
         """One pass of the hot path over the step batch."""

@@ -246,5 +246,13 @@ def test_entry_point_errors(lib):
                                       0.1, FAKE, need - 1, None) == 5
     assert lib.paged_attention_decode(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000,
                                       0.1, None, need, None) == 5
-    assert pkv.paged_attention_chunk_workspace_bytes(g, 2, 100, 500) == 0
+    # chunk: the schedule, one int32 per (sequence, 64-row tile)
+    need = pkv.paged_attention_chunk_workspace_bytes(g, 2, 100, 500)
+    assert need == 2 * 2 * 4
+    assert lib.paged_attention_chunk(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 2, 100,
+                                     64, 500, 0.1, FAKE, need - 1, None) == 5
+    assert lib.paged_attention_chunk(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 2, 100,
+                                     64, 500, 0.1, None, need, None) == 5
+    g32 = _geom(dtype=1)   # fp32 storage runs the generic kernel: no schedule
+    assert pkv.paged_attention_chunk_workspace_bytes(g32, 2, 100, 500) == 0
     assert lib.pkv_status_string(5) == b"workspace missing or too small"
