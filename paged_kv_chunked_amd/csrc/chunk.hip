@@ -13,7 +13,7 @@
 //     table.  Tiles travel from memory straight into a 4-stage LDS ring
 //     (direct-to-LDS 16-byte loads, up to three tiles in flight) in the
 //     arena's own layouts: K [block][16-byte dim piece][key] and V
-//     [block][dim][two 8-key halves], with 16-byte units swapped on the way
+//     [block][dim][two 8-key halves], with 16-byte units permuted on the way
 //     in so the operand reads below are bank-conflict free;
 //   * S^T = K Q^T puts keys on the MFMA M dimension, so each lane ends up
 //     holding 16 keys of one query row: the row max and sum are lane-local
@@ -45,12 +45,17 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kG = 4;
-constexpr int kBM = 32;            // rows per wave
-constexpr int kRowGroups = 2;      // waves per query head in a workgroup
-constexpr int kRows = kBM * kRowGroups;  // chunk rows per workgroup
+#ifndef PKV_CHUNK_RB
+#define PKV_CHUNK_RB 2
+#endif
+constexpr int kRB = PKV_CHUNK_RB;  // 16-row blocks per wave
+constexpr int kBM = 16 * kRB;      // rows per wave
+constexpr int kRows = 64;          // chunk rows per workgroup
+constexpr int kRowGroups = kRows / kBM;  // waves per query head in a workgroup
 constexpr int kBN = 64;            // keys per tile (4 arena blocks)
 constexpr int kWaves = kG * kRowGroups;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kLoadsPerTile = 2 * 16 / kWaves;  // direct-to-LDS loads per wave per tile
 constexpr int kStages = 4;         // LDS ring depth (tiles)
 constexpr int kUnitsPerBlock = kBlock * kD * 2 / 16;  // 16-byte units in one (block, head) tile
 constexpr int kStageUnits = 2 * 4 * kUnitsPerBlock;    // K and V of 4 blocks
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
   const int lr = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
   const int h = g * kG + (wave & 3);
-  const int wrow0 = rt * kRows + kBM * (wave >> 2);  // first chunk row of this wave
+  const int wrow0 = rt * kRows + kBM * (wave >> 2);  // (kRowGroups waves per head)  // first chunk row of this wave
 
   // 4 stages x (K: 4 blocks x 256 units, then V: 4 blocks x 256 units)
   __shared__ u32x4 ring[kStages * kStageUnits];  // 128 KiB
@@ -225,16 +230,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
   const int nblk_seq = (Lc + kBlock - 1) / kBlock;
   const int32_t* bt = block_table + (size_t)b * max_blocks;
 
-  // Tile loads.  Wave w moves quarters 2(w&1) and 2(w&1)+1 of block w >> 1's
-  // K and V tiles (4 x 1 KiB); a lane's unit goes to position pos of the
-  // block's 256 units:
+  // Tile loads.  Each block's K and V tiles are 4 quarters of 1 KiB; wave w
+  // moves quarters w * kQuarters .. +kQuarters-1 of the 16 (block = index / 4);
+  // a lane's unit goes to position pos of the block's 256 units:
   //   K: pos = piece * 16 + slot', fetched from slot' ^ 4 in odd blocks, so
   //      the two blocks an operand read touches use disjoint banks;
-  //   V: pos = dim * 2 + half', fetched from half' ^ (dim >> 3 & 1), so the
-  //      16 dims an operand read touches use disjoint banks.
+  //   V: pos = (dim * 2 + half + 16 (block & 1)) mod 256: the odd blocks'
+  //      units are rotated by 16, so the two blocks an operand read touches
+  //      use disjoint banks (measured conflict-free on gfx950).
   // Past the sequence's last block the id of that last block is used (its
   // contents never reach the output: scores masked, V zeroed).
-  const int dma_blk = wave >> 1;
+  constexpr int kQuarters = 16 / kWaves;  // 1 KiB quarters of block tiles per wave
+  const int dma_blk = (wave * kQuarters) >> 2;
   const uint32_t ring_lds =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)ring;
   auto issue_tile = [&](int t) {
@@ -244,20 +251,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
     const u32x4* vt = (const u32x4*)v_arena + ((size_t)blk * Hkv + g) * kUnitsPerBlock;
     const uint32_t st = ring_lds + (uint32_t)((t % kStages) * kStageUnits * 16);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int qq = 2 * (wave & 1) + j;
+    for (int j = 0; j < kQuarters; ++j) {
+      const int qq = (wave * kQuarters + j) & 3;
       const int pos = qq * 64 + lane;
       const uint32_t off = (uint32_t)((dma_blk * kUnitsPerBlock + qq * 64) * 16);
       dma16(kt + (pos ^ (4 * (dma_blk & 1))), __builtin_amdgcn_readfirstlane(st + off));
-      dma16(vt + (pos ^ ((pos >> 4) & 1)),
+      dma16(vt + ((pos - 16 * (dma_blk & 1)) & (kUnitsPerBlock - 1)),
             __builtin_amdgcn_readfirstlane(st + 4 * kUnitsPerBlock * 16 + off));
     }
   };
 
   // Q^T as the B operand: qf[rb][kd] = Q[row wrow0 + 16rb + lr][dims 32kd + 8lq .. +8]
-  half8_t qf[2][4];
+  half8_t qf[kRB][4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int r = wrow0 + 16 * rb + lr;
 #pragma unroll
     for (int kd = 0; kd < 4; ++kd) {
@@ -278,20 +285,26 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
 
   // absolute positions of this lane's two rows (rows past the chunk borrow the
   // last valid position so they stay finite; they are never stored)
-  int prow[2];
+  int prow[kRB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) prow[rb] = min(P + wrow0 + 16 * rb + lr, Lc - 1);
+  for (int rb = 0; rb < kRB; ++rb) prow[rb] = min(P + wrow0 + 16 * rb + lr, Lc - 1);
   const int first_pos = P + wrow0;  // smallest row position of this wave
 
-  f32x4 oacc[8][2];
+  f32x4 oacc[8][kRB];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) oacc[db][rb] = (f32x4)0.f;
+    for (int rb = 0; rb < kRB; ++rb) oacc[db][rb] = (f32x4)0.f;
   // Per row: running maximum of the raw scores, the raw score above which
   // the accumulator must be rescaled, -max * scale_log2, and the denominator.
-  float m_raw[2] = {-INFINITY, -INFINITY}, m_lim[2] = {-INFINITY, -INFINITY};
-  float m_off[2] = {0.f, 0.f}, l_run[2] = {0.f, 0.f};
+  float m_raw[kRB], m_lim[kRB], m_off[kRB], l_run[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    m_raw[rb] = -INFINITY;
+    m_lim[rb] = -INFINITY;
+    m_off[rb] = 0.f;
+    l_run[rb] = 0.f;
+  }
   const float slack_raw = kSlack / scale_log2;
   const half2_t ones = {(_Float16)1.f, (_Float16)1.f};
 
@@ -301,14 +314,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
   const int ka = lr >> 3;  // block offset within the pair of blocks
   const int kslot0 = 8 * ((lr >> 2) & 1) + (lr & 3);
   // V fragment of dims block db for the keys of MFMA u: 16-byte unit
-  // (block 2u + (lq >> 1), dim 16db + lr, half (lq & 1) ^ (lr >> 3 & 1))
-  const int vhalf = (lq & 1) ^ ((lr >> 3) & 1);
+  // (2 (16db + lr) + (lq & 1) + 16 (lq >> 1)) mod 256 of block 2u + (lq >> 1)
+  const int vunit = 2 * lr + (lq & 1) + 16 * (lq >> 1);
 
   for (int t = 0; t < ntiles; ++t) {
     // tile t's loads (this wave's) are done; then every wave's, and every
     // wave has finished tile t - 1, whose stage the next load reuses
-    if (t + 2 < ntiles) wait_vm<8>();
-    else if (t + 1 < ntiles) wait_vm<4>();
+    if (t + 2 < ntiles) wait_vm<2 * kLoadsPerTile>();
+    else if (t + 1 < ntiles) wait_vm<kLoadsPerTile>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -321,8 +334,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int unit = tid + e * kThreads;  // [block][dim][half']
-        const int a = unit >> 8, d = (unit >> 1) & (kD - 1), hs = unit & 1;
-        const int key0 = t * kBN + 16 * a + 8 * (hs ^ ((d >> 3) & 1));
+        const int a = unit >> 8, hs = unit & 1;  // block, half (8 keys) of the unit
+        const int key0 = t * kBN + 16 * a + 8 * hs;
         if (key0 + 8 > Lc) vw[unit] = mask_unit(vw[unit], key0, Lc);
       }
       __syncthreads();
@@ -330,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
 
     // S^T[key][row] = K . Q^T (raw scores).  The K fragments of MFMA kb + 1
     // are read while kb's products run.
-    f32x4 sacc[4][2];
+    f32x4 sacc[4][kRB];
     half8_t kf[2][4];
     auto read_k = [&](int kb, half8_t* f) {
       const int a = 2 * (kb >> 1) + ka;
@@ -343,13 +356,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       if (kb < 3) read_k(kb + 1, kf[(kb + 1) & 1]);
-      sacc[kb][0] = (f32x4)0.f;
-      sacc[kb][1] = (f32x4)0.f;
 #pragma unroll
-      for (int kd = 0; kd < 4; ++kd) {
-        sacc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb & 1][kd], qf[0][kd], sacc[kb][0], 0, 0, 0);
-        sacc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb & 1][kd], qf[1][kd], sacc[kb][1], 0, 0, 0);
-      }
+      for (int rb = 0; rb < kRB; ++rb) sacc[kb][rb] = (f32x4)0.f;
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb & 1][kd], qf[rb][kd], sacc[kb][rb], 0, 0, 0);
     }
     // the first two V fragment pairs are read during the softmax
     half8_t vf[3][2];
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int a = 2 * u + (lq >> 1);
-        f[u] = __builtin_bit_cast(half8_t, vl[a * kUnitsPerBlock + (16 * db + lr) * 2 + vhalf]);
+        f[u] = __builtin_bit_cast(half8_t, vl[a * kUnitsPerBlock + ((32 * db + vunit) & (kUnitsPerBlock - 1))]);
       }
     };
     read_v(0, vf[0]);
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kRB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 
@@ -381,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
       for (int kb = 0; kb < 4; ++kb) {
         const int key0 = t * kBN + 16 * (2 * (kb >> 1) + (lq >> 1)) + 8 * (lq & 1) + 4 * (kb & 1);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (key0 + i > prow[rb]) sacc[kb][rb][i] = -INFINITY;
@@ -392,18 +405,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
     // running maximum is only raised when some score exceeds it by more than
     // kSlack; both the numerator and the denominator use the same (possibly
     // stale) maximum, so the quotient is unchanged.
-    float mloc[2];
+    float mloc[kRB];
+    bool raise = false;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       const f32x4 s0 = sacc[0][rb], s1 = sacc[1][rb], s2 = sacc[2][rb], s3 = sacc[3][rb];
       const float a0 = max3f(s0[0], s0[1], s0[2]), a1 = max3f(s0[3], s1[0], s1[1]);
       const float a2 = max3f(s1[2], s1[3], s2[0]), a3 = max3f(s2[1], s2[2], s2[3]);
       const float a4 = max3f(s3[0], s3[1], s3[2]);
       mloc[rb] = max3f(max3f(a0, a1, a2), max3f(a3, a4, s3[3]), a0);
+      raise = raise || mloc[rb] > m_lim[rb];
     }
-    if (__any(mloc[0] > m_lim[0] || mloc[1] > m_lim[1])) {
+    if (__any(raise)) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         const float mx = max_xor16(max_xor32(mloc[rb]));
         const float m_new = fmaxf(m_raw[rb], mx);  // finite: key 0 is in tile 0 for every row
         const float alpha = __builtin_amdgcn_exp2f((m_raw[rb] - m_new) * scale_log2);
@@ -418,9 +433,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
 
     // pb[u][rb]: B operand of the second product, keys 8(lq & 1) .. +7 of
     // block 2u + (lq >> 1) = scores (kb = 2u, i = 0..3), (kb = 2u + 1, i = 0..3)
-    half8_t pb[2][2];
+    half8_t pb[2][kRB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -444,16 +459,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
       if (db + 2 < 8) read_v(db + 2, vf[(db + 2) % 3]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        oacc[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % 3][u], pb[u][0], oacc[db][0], 0, 0, 0);
-        oacc[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % 3][u], pb[u][1], oacc[db][1], 0, 0, 0);
-      }
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % 3][u], pb[u][rb], oacc[db][rb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const float l = sum_xor16(sum_xor32(l_run[rb]));
     const float inv = 1.f / l;
     const int r = wrow0 + 16 * rb + lr;
