@@ -14,8 +14,11 @@ Inputs are synthetic and resident in HBM before timing.  Each timed step
 rotates over --layers copies of the arena (a layer's worth each) so repeated
 steps cannot be served from the 256 MB Infinity Cache.
 
-`roofline` refers to the dominant kernel call (paged_attention_decode), timed
-with HIP events on the stream it is launched on.  `cpu_baseline` times the CPU
+`roofline` refers to the dominant kernel call (paged_attention_decode): its
+average duration over --steps calls issued back to back (rotating the arena
+copies) between two HIP events on the stream it is launched on
+(`avg_launch_ms`); `avg_launch_ms_isolated` is the mean of per-call events
+inside the timed steps, which adds the event and launch gaps of one call.  `cpu_baseline` times the CPU
 oracle on the same decode workload.
 """
 from __future__ import annotations
@@ -54,6 +57,22 @@ def time_steps(torch, run_step, kernel_events, steps, warmup):
     return (t1 - t0) * 1e3 / steps, sum(ker_ms) / len(ker_ms)
 
 
+def time_back_to_back(torch, call, n):
+    """Average duration of one call over n calls issued back to back between two
+    HIP events on the stream the kernels are launched on."""
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        call(i)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        call(i)
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def make_layers(torch, dw, n):
     layers = [(dw.k_arena, dw.v_arena)]
     for _ in range(n - 1):
@@ -79,9 +98,15 @@ def bench_decode(torch, args):
         b.record()
         events.append((a, b))
 
-    ms_step, ms_kernel = time_steps(torch, run, events, args.steps, args.warmup)
+    ms_step, ms_call = time_steps(torch, run, events, args.steps, args.warmup)
+
+    def call(i):
+        k, v = layers[i % len(layers)]
+        dw.decode(k_arena=k, v_arena=v)
+
+    ms_kernel = time_back_to_back(torch, call, args.steps)
     nbytes = dw.decode_bytes()
-    return w, dw, ms_step, ms_kernel, nbytes
+    return w, dw, ms_step, ms_kernel, ms_call, nbytes
 
 
 def bench_chunk(torch, args):
@@ -102,8 +127,14 @@ def bench_chunk(torch, args):
         b.record()
         events.append((a, b))
 
-    ms_step, ms_kernel = time_steps(torch, run, events, args.steps, args.warmup)
-    return w, dw, ms_step, ms_kernel, dw.chunk_flops()
+    ms_step, ms_call = time_steps(torch, run, events, args.steps, args.warmup)
+
+    def call(i):
+        k, v = layers[i % len(layers)]
+        dw.chunk(k_arena=k, v_arena=v)
+
+    ms_kernel = time_back_to_back(torch, call, args.steps)
+    return w, dw, ms_step, ms_kernel, ms_call, dw.chunk_flops()
 
 
 def cpu_baseline(w, target_s):
@@ -173,13 +204,13 @@ def main():
         del src, dst
     if args.no_decode:
         args.no_cpu_baseline = True
-        wc, dwc, ms_cstep, ms_chunk, flops = bench_chunk(torch, args)
+        wc, dwc, ms_cstep, ms_chunk, ms_ccall, flops = bench_chunk(torch, args)
         log(f"chunk: step {ms_cstep:.4f} ms, kernel {ms_chunk:.4f} ms, "
             f"{flops / (ms_chunk * 1e-3) / 1e12:.1f} TFLOP/s kernel")
         return
 
     from paged_kv_chunked_amd.rocprof_summary import load_traffic
-    w, dw, ms_step, ms_dec, nbytes = bench_decode(torch, args)
+    w, dw, ms_step, ms_dec, ms_dcall, nbytes = bench_decode(torch, args)
     value = nbytes / (ms_step * 1e-3) / 1e9
     achieved = nbytes / (ms_dec * 1e-3) / 1e9
     log(f"decode: step {ms_step:.4f} ms, kernel {ms_dec:.4f} ms, {nbytes / 1e6:.1f} MB "
@@ -216,10 +247,11 @@ def main():
             "traffic": load_traffic(TRAFFIC, "paged_attention_decode"),
             "algorithmic_bytes_per_launch": nbytes,
             "avg_launch_ms": round(ms_dec, 5),
+            "avg_launch_ms_isolated": round(ms_dcall, 5),
         },
     }
     if not args.no_chunk:
-        wc, dwc, ms_cstep, ms_chunk, flops = bench_chunk(torch, args)
+        wc, dwc, ms_cstep, ms_chunk, ms_ccall, flops = bench_chunk(torch, args)
         tf_kernel = flops / (ms_chunk * 1e-3) / 1e12
         tf_step = flops / (ms_cstep * 1e-3) / 1e12
         log(f"chunk: step {ms_cstep:.4f} ms, kernel {ms_chunk:.4f} ms, {flops / 1e9:.1f} GFLOP "
@@ -240,6 +272,7 @@ def main():
                 "traffic": load_traffic(TRAFFIC, "paged_attention_chunk"),
                 "algorithmic_flops_per_launch": flops,
                 "avg_launch_ms": round(ms_chunk, 5),
+                "avg_launch_ms_isolated": round(ms_ccall, 5),
             },
         }
         del dwc
