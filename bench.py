@@ -10,6 +10,9 @@ Default run (N = 1):
   * chunk prefill (reported under "chunk_prefill"): 8 sequences with cached
     prefixes 16*U{0..224} and a 512-token chunk each; a step = restore q +
     kv_append_rope + paged_attention_chunk; TFLOP/s over visible pairs.
+  * swap (reported under "swap"): 1024 blocks (64 MiB) of the decode batch out
+    to pinned host memory and back (pkv_swap_out / pkv_swap_in), beside a
+    plain contiguous copy of the same size in each direction.
 Inputs are synthetic and resident in HBM before timing.  Each timed step
 rotates over --layers copies of the arena (a layer's worth each) so repeated
 steps cannot be served from the 256 MB Infinity Cache.
@@ -137,6 +140,47 @@ def bench_chunk(torch, args):
     return w, dw, ms_step, ms_kernel, ms_call, dw.chunk_flops()
 
 
+def bench_swap(torch, dw, reps=5):
+    """Preemption by swapping: the blocks of the decode batch's longest
+    sequences (1024 blocks, 64 MiB) out to pinned host memory and back, against
+    a plain contiguous copy of the same size in each direction."""
+    import numpy as np
+    import paged_kv_chunked_amd as pkv
+    order = np.argsort(-dw.dec_lens_host)
+    ids = []
+    for r in order:
+        n = -(-int(dw.dec_lens_host[r]) // 16)
+        ids.extend(int(b) for b in dw.bt_host[r, :n])
+        if len(ids) >= 1024:
+            break
+    ids = torch.tensor(ids[:1024], dtype=torch.int32, device=dw.device)
+    nbytes = pkv.pkv_swap_bytes(dw.g, ids.shape[0])
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dev = torch.empty(nbytes, dtype=torch.uint8, device=dw.device)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+    res = {
+        "blocks": int(ids.shape[0]),
+        "bytes": nbytes,
+        "swap_out_GBps": timed(lambda: pkv.pkv_swap_out(dw.g, dw.k_arena, dw.v_arena, ids, host)),
+        "swap_in_GBps": timed(lambda: pkv.pkv_swap_in(dw.g, dw.k_arena, dw.v_arena, ids, host)),
+        "copy_d2h_GBps": timed(lambda: host.copy_(dev, non_blocking=True)),
+        "copy_h2d_GBps": timed(lambda: dev.copy_(host, non_blocking=True)),
+    }
+    return {k: (round(v, 2) if isinstance(v, float) else v) for k, v in res.items()}
+
+
 def cpu_baseline(w, target_s):
     """The oracle (numpy fp64) on the decode workload: append + attention for
     every decode row, repeated until about target_s seconds have passed."""
@@ -175,6 +219,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4,
                     help="arena copies rotated over (Infinity Cache guard)")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-swap", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -250,6 +295,9 @@ def main():
             "avg_launch_ms_isolated": round(ms_dcall, 5),
         },
     }
+    if not args.no_swap:
+        out["swap"] = bench_swap(torch, dw)
+        log(f"swap: {out['swap']}")
     if not args.no_chunk:
         wc, dwc, ms_cstep, ms_chunk, ms_ccall, flops = bench_chunk(torch, args)
         tf_kernel = flops / (ms_chunk * 1e-3) / 1e12

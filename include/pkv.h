@@ -190,6 +190,34 @@ pkv_status pkv_copy_blocks(const pkv_geom* geom, void* k_arena, void* v_arena,
                            const int32_t* src_dst, int32_t n, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pkv_swap_out / pkv_swap_in — preemption by swapping (part 3 section 5: when
+ * memory is short a running sequence is preempted; recomputing its KV cache
+ * is too expensive, so its blocks are swapped out of the arena and restored
+ * later).
+ * pkv_swap_out copies, bit for bit, block ids[i]'s K tile and V tile (all KV
+ * heads, all 16 slots) to buf at byte offset i * 2T (K tile) and
+ * i * 2T + T (V tile), T = num_kv_heads * 16 * head_dim * element size;
+ * pkv_swap_in copies them back into block ids[i] of the arenas.  The arena
+ * layouts are unchanged, so a sequence restored into different blocks is the
+ * same sequence once its block-table row names the new ids.
+ * ids        device int32 [n]; ids outside [0, num_blocks) are skipped (their
+ *            buf slots are left unchanged / their tiles are not written).
+ *            Swap-in ids must be distinct.
+ * buf        device-accessible memory of pkv_swap_bytes(n) bytes, 16-byte
+ *            aligned: pinned host memory (hipHostMalloc) for a swap to the
+ *            host, or device memory.  buf_bytes is its size.
+ * PKV_ERR_WORKSPACE if buf_bytes is too small; PKV_ERR_RANGE if buf is not
+ * 16-byte aligned.  Asynchronous on `stream`; the caller synchronises before
+ * reading buf on the host or reusing the swapped-out blocks.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_swap_bytes(const pkv_geom* geom, int32_t n, size_t* bytes);
+pkv_status pkv_swap_out(const pkv_geom* geom, const void* k_arena, const void* v_arena,
+                        const int32_t* ids, int32_t n, void* buf, size_t buf_bytes,
+                        void* stream);
+pkv_status pkv_swap_in(const pkv_geom* geom, void* k_arena, void* v_arena, const int32_t* ids,
+                       int32_t n, const void* buf, size_t buf_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Host block pool (part 3 sections 1 and 3).  The free list starts as
  * [0, 1, ..., N-1]; allocation pops from its end (highest id first); a block
  * whose count drops to 0 is pushed on the end and is the next one allocated.
@@ -211,6 +239,15 @@ int32_t pkv_pool_num_free(const pkv_pool* pool);
 int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t id); /* -1 if out of range */
 /* Copies the free list, bottom first, into out[0..cap); *n = its length. */
 pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+/* Admission rule of continuous batching (part 3 section 5): a new sequence
+ * needing new_need blocks is admitted only if
+ *   free + evictable >= active_reserved + new_need,
+ * free = the pool's free blocks, evictable = blocks the prefix cache could
+ * release, active_reserved = blocks the running sequences still have to
+ * allocate to finish.  Returns 1 (admit), 0 (do not), -1 (NULL pool or a
+ * negative count). */
+int32_t pkv_pool_can_admit(const pkv_pool* pool, int64_t evictable, int64_t active_reserved,
+                           int64_t new_need);
 
 /* Host check of table copies: every row with length L > 0 needs
  * ceil(L/16) <= max_blocks_per_seq entries, each in [0, num_blocks). */

@@ -55,6 +55,25 @@ class Arena:
         self.k[dst] = self.k[src]
         self.v[dst] = self.v[src]
 
+    def swap_out(self, ids):
+        """[K3] section 5, preemption by swapping: the tiles of blocks ``ids``
+        (all KV heads, all 16 slots) packed block after block, K tile then V
+        tile, as raw bytes (the layout pkv_swap_out documents)."""
+        out = []
+        for b in ids:
+            out.append(np.ascontiguousarray(self.k[b]).view(np.uint8).ravel())
+            out.append(np.ascontiguousarray(self.v[b]).view(np.uint8).ravel())
+        return np.concatenate(out) if out else np.zeros(0, np.uint8)
+
+    def swap_in(self, ids, packed: np.ndarray) -> None:
+        """Inverse of swap_out: tile i of ``packed`` goes back into block ids[i]."""
+        kt = self.k[0].nbytes
+        vt = self.v[0].nbytes
+        for i, b in enumerate(ids):
+            base = i * (kt + vt)
+            self.k[b] = packed[base:base + kt].view(self.k.dtype).reshape(self.k.shape[1:])
+            self.v[b] = packed[base + kt:base + kt + vt].view(self.v.dtype).reshape(self.v.shape[1:])
+
     def gather(self, table_row, length: int):
         """Dense K, V [length][Hkv][D] of one sequence (the copy the method avoids)."""
         blk, slot = slots(table_row, 0, length)

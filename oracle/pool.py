@@ -10,6 +10,9 @@ that block before writing it.
 Reading of the copy-on-write order (the pages give none): if the block is
 shared (count > 1), pop a fresh block, (the caller copies the data), then drop
 one reference to the old block.  A block with count 1 is written in place.
+
+[K3] section 5 "Continuous Batching and Admission Control": a new sequence is
+admitted only if free + evictable >= active_reserved + new_need.
 """
 from __future__ import annotations
 
@@ -68,3 +71,9 @@ class Pool:
     @property
     def num_free(self) -> int:
         return len(self.free)
+
+
+def can_admit(free: int, evictable: int, active_reserved: int, new_need: int) -> bool:
+    """[K3] section 5: strict admission, so that admitted sequences can always
+    finish (no memory deadlock)."""
+    return free + evictable >= active_reserved + new_need

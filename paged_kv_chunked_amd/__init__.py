@@ -64,6 +64,9 @@ _SIGS = {
                                              _I32, _I32, _I32, ctypes.c_float, _P,
                                              ctypes.c_size_t, _P]),
     "pkv_copy_blocks": (ctypes.c_int, [_PG, _P, _P, _P, _I32, _P]),
+    "pkv_swap_bytes": (ctypes.c_int, [_PG, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_swap_out": (ctypes.c_int, [_PG, _P, _P, _P, _I32, _P, ctypes.c_size_t, _P]),
+    "pkv_swap_in": (ctypes.c_int, [_PG, _P, _P, _P, _I32, _P, ctypes.c_size_t, _P]),
     "pkv_pool_create": (_P, [_I32]),
     "pkv_pool_destroy": (None, [_P]),
     "pkv_pool_alloc": (ctypes.c_int, [_P, _PI32]),
@@ -74,6 +77,7 @@ _SIGS = {
     "pkv_pool_num_free": (_I32, [_P]),
     "pkv_pool_refcount": (_I32, [_P, _I32]),
     "pkv_pool_free_list": (ctypes.c_int, [_P, _P, _I32, _PI32]),
+    "pkv_pool_can_admit": (_I32, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
     "pkv_validate_tables": (ctypes.c_int, [_PG, _P, _I32, _P, _I32]),
     "pkv_f64_to_f16_host": (ctypes.c_int, [_P, _P, ctypes.c_int64]),
 }
@@ -217,6 +221,30 @@ def pkv_copy_blocks(g: Geom, k_arena, v_arena, src_dst, stream=None) -> None:
                                  src_dst.shape[0], _stream(stream)), "pkv_copy_blocks")
 
 
+def pkv_swap_bytes(g: Geom, n: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().pkv_swap_bytes(ctypes.byref(g), n, ctypes.byref(out)), "pkv_swap_bytes")
+    return out.value
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def pkv_swap_out(g: Geom, k_arena, v_arena, ids, buf, stream=None) -> None:
+    """Blocks ids (device int32 [n]) -> buf (pinned host or device tensor of
+    pkv_swap_bytes(n) bytes)."""
+    _check(lib().pkv_swap_out(ctypes.byref(g), _ptr(k_arena), _ptr(v_arena), _ptr(ids),
+                              ids.shape[0], _ptr(buf), _nbytes(buf), _stream(stream)),
+           "pkv_swap_out")
+
+
+def pkv_swap_in(g: Geom, k_arena, v_arena, ids, buf, stream=None) -> None:
+    _check(lib().pkv_swap_in(ctypes.byref(g), _ptr(k_arena), _ptr(v_arena), _ptr(ids),
+                             ids.shape[0], _ptr(buf), _nbytes(buf), _stream(stream)),
+           "pkv_swap_in")
+
+
 def pkv_validate_tables(g: Geom, block_table_host, lens_host) -> None:
     """Host (numpy int32) copies of a block table [S][max_blocks] and lengths [S]."""
     _check(lib().pkv_validate_tables(ctypes.byref(g), block_table_host.ctypes.data,
@@ -273,6 +301,12 @@ class Pool:
 
     def refcount(self, b: int) -> int:
         return lib().pkv_pool_refcount(self._h, b)
+
+    def can_admit(self, evictable: int, active_reserved: int, new_need: int) -> bool:
+        r = lib().pkv_pool_can_admit(self._h, evictable, active_reserved, new_need)
+        if r < 0:
+            raise PkvError(4, "pkv_pool_can_admit")
+        return bool(r)
 
     def free_list(self):
         import numpy as np

@@ -122,4 +122,39 @@ pkv_status pkv_copy_blocks(const pkv_geom* geom, void* k_arena, void* v_arena,
                                             (hipStream_t)stream));
 }
 
+pkv_status pkv_swap_bytes(const pkv_geom* geom, int32_t n, size_t* bytes) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (!bytes) return PKV_ERR_NULL;
+  if (n < 0) return PKV_ERR_RANGE;
+  *bytes = (size_t)n * 2 * pkv::swap_tile_bytes(*geom);
+  return PKV_OK;
+}
+
+static pkv_status swap_common(const pkv_geom* geom, void* k_arena, void* v_arena,
+                              const int32_t* ids, int32_t n, void* buf, size_t buf_bytes,
+                              bool swap_in, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (n < 0) return PKV_ERR_RANGE;
+  if (n == 0) return PKV_OK;
+  if (!k_arena || !v_arena || !ids || !buf) return PKV_ERR_NULL;
+  if (((uintptr_t)buf & 15) != 0) return PKV_ERR_RANGE;  // 16-byte units
+  if (buf_bytes < (size_t)n * 2 * pkv::swap_tile_bytes(*geom)) return PKV_ERR_WORKSPACE;
+  return hip_status(pkv::launch_swap_blocks(*geom, k_arena, v_arena, ids, n, buf, swap_in,
+                                            (hipStream_t)stream));
+}
+
+pkv_status pkv_swap_out(const pkv_geom* geom, const void* k_arena, const void* v_arena,
+                        const int32_t* ids, int32_t n, void* buf, size_t buf_bytes,
+                        void* stream) {
+  return swap_common(geom, (void*)k_arena, (void*)v_arena, ids, n, buf, buf_bytes, false,
+                     stream);
+}
+
+pkv_status pkv_swap_in(const pkv_geom* geom, void* k_arena, void* v_arena, const int32_t* ids,
+                       int32_t n, const void* buf, size_t buf_bytes, void* stream) {
+  return swap_common(geom, k_arena, v_arena, ids, n, (void*)buf, buf_bytes, true, stream);
+}
+
 }  // extern "C"

@@ -165,6 +165,12 @@ pkv_status pkv_pool_cow(pkv_pool* p, int32_t id, int32_t* out_id, int32_t* copie
 
 int32_t pkv_pool_num_free(const pkv_pool* p) { return p ? (int32_t)p->free_list.size() : -1; }
 
+int32_t pkv_pool_can_admit(const pkv_pool* p, int64_t evictable, int64_t active_reserved,
+                           int64_t new_need) {
+  if (!p || evictable < 0 || active_reserved < 0 || new_need < 0) return -1;
+  return (int64_t)p->free_list.size() + evictable >= active_reserved + new_need ? 1 : 0;
+}
+
 int32_t pkv_pool_refcount(const pkv_pool* p, int32_t id) {
   if (!p || !in_range(p, id)) return -1;
   return p->rc[id];

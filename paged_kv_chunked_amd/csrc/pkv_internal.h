@@ -99,5 +99,9 @@ hipError_t launch_attend_generic(const pkv_geom& g, float* out, const void* q,
 
 hipError_t launch_copy_blocks(const pkv_geom& g, void* k_arena, void* v_arena,
                               const int32_t* src_dst, int n, hipStream_t stream);
+size_t swap_tile_bytes(const pkv_geom& g);
+hipError_t launch_swap_blocks(const pkv_geom& g, void* k_arena, void* v_arena,
+                              const int32_t* ids, int n, void* buf, bool swap_in,
+                              hipStream_t stream);
 
 }  // namespace pkv

@@ -256,3 +256,31 @@ def test_entry_point_errors(lib):
     g32 = _geom(dtype=1)   # fp32 storage runs the generic kernel: no schedule
     assert pkv.paged_attention_chunk_workspace_bytes(g32, 2, 100, 500) == 0
     assert lib.pkv_status_string(5) == b"workspace missing or too small"
+
+
+def test_pool_admission_matches_oracle(lib):
+    from oracle import pool as opool
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        N = int(rng.integers(1, 50))
+        p = pkv.Pool(N)
+        taken = int(rng.integers(0, N + 1))
+        for _ in range(taken):
+            p.alloc()
+        ev, res, need = (int(x) for x in rng.integers(0, 30, size=3))
+        assert p.can_admit(ev, res, need) == opool.can_admit(N - taken, ev, res, need)
+    with pytest.raises(pkv.PkvError):
+        pkv.Pool(4).can_admit(-1, 0, 0)
+
+
+def test_swap_entry_point_errors(lib):
+    g = _geom()
+    gp = ctypes.byref(g)
+    tile = 8 * 16 * 128 * 2
+    assert pkv.pkv_swap_bytes(g, 3) == 3 * 2 * tile
+    # n == 0 is a no-op; nulls, a short or misaligned buffer are rejected before any launch
+    assert lib.pkv_swap_out(gp, None, None, None, 0, None, 0, None) == 0
+    assert lib.pkv_swap_out(gp, FAKE, FAKE, None, 2, FAKE, 2 * 2 * tile, None) == 1
+    assert lib.pkv_swap_in(gp, FAKE, FAKE, FAKE, 2, FAKE, 2 * 2 * tile - 1, None) == 5
+    assert lib.pkv_swap_in(gp, FAKE, FAKE, FAKE, 2, ctypes.c_void_p(0x1008), 2 * 2 * tile, None) == 4
+    assert lib.pkv_swap_out(gp, FAKE, FAKE, FAKE, -1, FAKE, 0, None) == 4

@@ -130,3 +130,74 @@ def test_symbolic_arena_tracks_copies():
     s.copy_block(4, 1)
     src, tok = s.provenance([5, 1], 20)
     assert (src == 3).all() and (tok == np.arange(20)).all()
+
+
+# ---- [K3] section 5: preemption by swapping, admission control -------------
+
+def test_swap_roundtrip_relocates_sequence():
+    """A sequence swapped out and restored into other blocks reads back the
+    same K/V through its new block table (the arena layout is unchanged)."""
+    rng = np.random.default_rng(7)
+    a = arena.Arena(12, 2, 16, np.float16)
+    a.k[:] = rng.standard_normal(a.k.shape).astype(np.float16)
+    a.v[:] = rng.standard_normal(a.v.shape).astype(np.float16)
+    old, new, L = [5, 2, 9], [1, 11, 0], 40
+    packed = a.swap_out(old)
+    b = arena.Arena(12, 2, 16, np.float16)          # all NaN
+    b.swap_in(new, packed)
+    k0, v0 = a.gather(old, L)
+    k1, v1 = b.gather(new, L)
+    assert np.array_equal(k0.view(np.uint16), k1.view(np.uint16))
+    assert np.array_equal(v0.view(np.uint16), v1.view(np.uint16))
+    # blocks not named are untouched (still NaN)
+    assert np.isnan(b.k[3]).all() and np.isnan(b.v[3]).all()
+
+
+@pytest.mark.parametrize("dtype,esize", [(np.float16, 2), (np.float32, 4)])
+def test_swap_size_is_kv_bytes_per_token(dtype, esize):
+    """[K3] section 1: KV bytes per token and layer = 2 x KV heads x head dim x
+    bytes per element; a swapped block carries 16 tokens of it."""
+    H, D, n = 8, 128, 3
+    a = arena.Arena(4, H, D, dtype)
+    a.k[:] = 0
+    a.v[:] = 0
+    assert a.swap_out([0, 3, 1]).size == n * 16 * (2 * H * D * esize)
+
+
+def test_admission_rule_prevents_deadlock():
+    """[K3] section 5: admitting only when free + evictable >= active_reserved +
+    new_need means the admitted sequences can always be driven to completion:
+    in random interleavings of block allocations no allocation ever fails."""
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        N = int(rng.integers(8, 40))
+        p = pool.Pool(N)
+        active = {}          # seq -> blocks still to allocate
+        held = {}
+        seq = 0
+        for _ in range(200):
+            if rng.random() < 0.4:
+                need = int(rng.integers(1, N // 2 + 1))
+                reserved = sum(active.values())
+                if pool.can_admit(p.num_free, 0, reserved, need):
+                    active[seq], held[seq] = need, []
+                    seq += 1
+            elif active:
+                s = int(rng.choice(list(active)))
+                held[s].append(p.alloc())        # must never raise
+                active[s] -= 1
+                if active[s] == 0:               # finished: free everything
+                    for b in held.pop(s):
+                        p.decref(b)
+                    del active[s]
+    # and the rule is tight: without it the same demand can run out of blocks
+    p = pool.Pool(4)
+    with pytest.raises(pool.OutOfBlocks):
+        for _ in range(5):
+            p.alloc()
+
+
+def test_admission_boundary():
+    assert pool.can_admit(3, 1, 2, 2)        # equality admits
+    assert not pool.can_admit(3, 1, 2, 3)
+    assert pool.can_admit(0, 5, 0, 5)        # evictable blocks count
