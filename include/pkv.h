@@ -64,12 +64,23 @@ typedef enum pkv_status {
   PKV_ERR_HIP = 8         /* a HIP runtime call or kernel launch failed */
 } pkv_status;
 
-typedef enum pkv_dtype { PKV_F16 = 0, PKV_F32 = 1 } pkv_dtype;
+/* PKV_I8KV: q, k, v (inputs) and the rotated q are fp16; the arenas hold the
+ * K and V of every (token, KV head) vector as INT8 codes with one fp16 scale
+ * (part 3 section 2's group codec with group = one head vector of head_dim
+ * values: s = fp16(fp32(max |x|) / 127), floored at 2^-24; code =
+ * round-half-even(fp32(x) / fp32(s)); x_hat = code * s, |x - x_hat| <= s/2),
+ * x being the value an fp16 arena would hold.  Tile of one (block, head),
+ * 16 * head_dim + 32 bytes:
+ *   K  int8 codes [head_dim/16][16][16] (16-byte pieces of 16 dims, the 16
+ *      keys of a piece contiguous), then fp16 scales [16] (slot order)
+ *   V  int8 codes [head_dim][16], then fp16 scales [16]
+ * head_dim must be a multiple of 16. */
+typedef enum pkv_dtype { PKV_F16 = 0, PKV_F32 = 1, PKV_I8KV = 2 } pkv_dtype;
 
 /* Geometry of one layer's arena.  block_size must be 16; head_dim a multiple of
- * x (8 for fp16, 4 for fp32) and <= 256; num_q_heads a multiple of
- * num_kv_heads; dtype is the storage dtype of q, k, v and both arenas (IEEE
- * binary16 or binary32). */
+ * x (8 for fp16, 4 for fp32, 16 for PKV_I8KV) and <= 256; num_q_heads a
+ * multiple of num_kv_heads; dtype is the storage dtype of q, k, v and both
+ * arenas (IEEE binary16 or binary32), or PKV_I8KV (fp16 q/k/v, INT8 arenas). */
 typedef struct pkv_geom {
   int32_t num_blocks;
   int32_t block_size;

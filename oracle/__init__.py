@@ -17,6 +17,8 @@ Sources, the Kshipra blog series:
        section 3 "Radix-Tree Prefix Cache": shared blocks kept alive by
          reference counts; a block that diverges is copied before it is
          written                                          -> pool
+       section 2 "INT4 Quantization and the Scale Bug": group quantization
+         with one FP16 scale used to encode and decode   -> quant
        section 4 "Chunked Prefill": online softmax over blocks read in place,
          RoPE at absolute positions P onward, causal mask over the chunk,
          result identical to dense masked attention       -> rope, attention
@@ -24,10 +26,12 @@ Sources, the Kshipra blog series:
 Modules:
   rope       closed-form rotary embedding, cos/sin tables from libm in fp64
   pool       LIFO free list + reference counts + copy-on-write
-  arena      block-arena writes/gathers, materialised or symbolic
+  arena      block-arena writes/gathers, materialised (fp16/fp32 or
+             group-quantized) or symbolic
+  quant      group quantization codec (INT8/INT4 codes, FP16 scale)
   attention  dense gather, masked score matrix, two-pass softmax in fp64
   script     runs a workload's pool script and step on the above
 
 Parity pins for every function live in tests/test_oracle_*.py.
 """
-from . import rope, pool, arena, attention, script  # noqa: F401
+from . import rope, pool, arena, attention, quant, script  # noqa: F401

@@ -81,6 +81,67 @@ class Arena:
         return K.reshape(length, K.shape[1], -1), self.v[blk, :, :, slot]
 
 
+class QuantArena:
+    """Arena of group-quantized K/V ([K3] section 2's codec applied per (token,
+    KV head) vector, see quant.py).  Codes and scales are kept apart here; the
+    byte image of a (block, head) tile is ``tile_bytes``:
+      K tile  int8 codes [D/16][16][16] (16-byte pieces of 16 dims, keys
+              grouped by piece as in the fp16 K layout), then 16 fp16 scales
+      V tile  int8 codes [D][16] (head-dim-major), then 16 fp16 scales
+    Unwritten slots hold all-ones bytes (code -1, scale NaN), so a read of one
+    is NaN."""
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, bits: int = 8):
+        self.bits = bits
+        H, D = num_kv_heads, head_dim
+        self.kq = np.full((num_blocks, H, D // 16, BLOCK, 16), -1, np.int8)
+        self.vq = np.full((num_blocks, H, D, BLOCK), -1, np.int8)
+        self.ks = np.full((num_blocks, H, BLOCK), 0xFFFF, np.uint16).view(np.float16)
+        self.vs = np.full((num_blocks, H, BLOCK), 0xFFFF, np.uint16).view(np.float16)
+
+    def write(self, table_row, start: int, k_store: np.ndarray, v_store: np.ndarray) -> None:
+        """k_store, v_store [n][Hkv][D] fp16 (what an fp16 cache would hold)."""
+        from . import quant
+        n, H, D = k_store.shape
+        blk, slot = slots(table_row, start, n)
+        kq, ks = quant.encode(k_store, self.bits)
+        vq, vs = quant.encode(v_store, self.bits)
+        self.kq[blk, :, :, slot, :] = kq.reshape(n, H, D // 16, 16)
+        self.ks[blk, :, slot] = ks
+        self.vq[blk, :, :, slot] = vq
+        self.vs[blk, :, slot] = vs
+
+    def copy_block(self, src: int, dst: int) -> None:
+        for a in (self.kq, self.vq, self.ks, self.vs):
+            a[dst] = a[src]
+
+    def gather(self, table_row, length: int):
+        """Dequantized K, V [length][Hkv][D] in fp64."""
+        from . import quant
+        blk, slot = slots(table_row, 0, length)
+        kq = self.kq[blk, :, :, slot, :].reshape(length, self.kq.shape[1], -1)
+        return (quant.decode(kq, self.ks[blk, :, slot]),
+                quant.decode(self.vq[blk, :, :, slot], self.vs[blk, :, slot]))
+
+    def swap_out(self, ids):
+        """[K3] section 5 swapping: per block, the K tiles then the V tiles as
+        bytes (every head's codes followed by its 16 scales)."""
+        out = []
+        for b in ids:
+            out.append(self.tile_bytes("k", b))
+            out.append(self.tile_bytes("v", b))
+        return np.concatenate(out) if out else np.zeros(0, np.uint8)
+
+    def tile_bytes(self, which: str, block: int) -> np.ndarray:
+        """Byte image of every head's tile of ``block`` (K or V), heads in order."""
+        q, sc = (self.kq, self.ks) if which == "k" else (self.vq, self.vs)
+        parts = []
+        for h in range(q.shape[1]):
+            parts.append(np.ascontiguousarray(q[block, h]).view(np.uint8).ravel())
+            parts.append(np.ascontiguousarray(sc[block, h]).view(np.uint8).ravel())
+        return np.concatenate(parts)
+
+
 class SymbolicArena:
     """Per (block, slot): the source that wrote it and the token index inside it."""
 

@@ -26,6 +26,7 @@ from . import arena as _arena
 from . import attention as _attention
 from . import pool as _pool
 from . import rope as _rope
+from . import quant as _quant
 
 STEP_SOURCE = 1 << 40     # symbolic source ids >= this are step rows
 
@@ -46,8 +47,12 @@ def rope_tables(w, max_pos: Optional[int] = None):
 def run_script(w, materialize: bool = True, cos_sin=None) -> State:
     p = _pool.Pool(w.num_blocks)
     tables: Dict[int, List[int]] = {s: [] for s in range(w.num_pool_seqs)}
-    ar = (_arena.Arena(w.num_blocks, w.num_kv_heads, w.head_dim, w.np_dtype)
-          if materialize else _arena.SymbolicArena(w.num_blocks))
+    if not materialize:
+        ar = _arena.SymbolicArena(w.num_blocks)
+    elif getattr(w, "kv_bits", 0):
+        ar = _arena.QuantArena(w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_bits)
+    else:
+        ar = _arena.Arena(w.num_blocks, w.num_kv_heads, w.head_dim, w.np_dtype)
     cos, sin = cos_sin if cos_sin is not None else rope_tables(w)
     copies = []
     for op in w.script:
@@ -152,6 +157,8 @@ def sequence_kv(w, state: State, row: int, length: Optional[int] = None, cos_sin
             start = fills[int(source)][3]
         K[sel] = _rope.rotate_store(k[t], start + t, cos, sin, w.np_dtype)
         V[sel] = v[t]
+    if getattr(w, "kv_bits", 0):   # the cache holds the codes of these values
+        return _quant.roundtrip(K, w.kv_bits), _quant.roundtrip(V, w.kv_bits)
     return K, V
 
 

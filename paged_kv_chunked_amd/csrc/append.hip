@@ -78,6 +78,120 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(
   }
 }
 
+// Group quantization of one (token, KV head) vector, Kshipra part 3 section
+// 2's codec: scale s = fp16(fp32(amax) / 127) (floored at the smallest
+// positive fp16), codes round-half-even(fp32(x) / fp32(s)) -- the same fp16
+// scale used to encode and to decode.  One wave per vector; lane l holds
+// elements l, l + 64, l + 128, l + 192 (those below D).
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+__device__ inline _Float16 group_scale(float amax) {
+  const _Float16 s = (_Float16)(amax / 127.f);
+  const _Float16 smin = __builtin_bit_cast(_Float16, (uint16_t)1);  // 2^-24
+  return s < smin ? smin : s;
+}
+
+__device__ inline int8_t encode8(float x, float s) {
+  const float r = __builtin_rintf(x / s);
+  return (int8_t)fminf(fmaxf(r, -127.f), 127.f);
+}
+
+// kv_append_rope for INT8 arenas (q, k, v fp16).  Tile of one (block, head):
+// K codes [D/16][16][16] then 16 fp16 scales; V codes [D][16] then 16 fp16
+// scales.  k is rotated and rounded to fp16 exactly as for an fp16 arena, then
+// quantized.
+__global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
+    const _Float16* q, _Float16* q_out, const _Float16* __restrict__ k,
+    const _Float16* __restrict__ v, uint8_t* __restrict__ k_arena, uint8_t* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
+    int num_seqs, const double2* __restrict__ cs, int rope_max_pos, int num_blocks, int Hq,
+    int Hkv, int D) {
+  const int t = blockIdx.x;
+  const int b = find_seq(cu_q_lens, num_seqs, t);
+  const int pos = chunk_start[b] + (t - cu_q_lens[b]);
+  if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
+  const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];
+  const int slot = pos & 15;
+  const int half = D >> 1;
+  const double2* row = cs + (size_t)pos * half;
+
+  if (q != nullptr) {
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < Hq * half; idx += kThreads) {
+      const int h = idx / half, i = idx - h * half;
+      const size_t base = ((size_t)t * Hq + h) * D;
+      const double2 c = row[i];
+      double o0, o1;
+      rope_pair((double)q[base + i], (double)q[base + i + half], c.x, c.y, o0, o1);
+      q_out[base + i] = store_f64<_Float16>(o0);
+      q_out[base + i + half] = store_f64<_Float16>(o1);
+    }
+  }
+  if (blk < 0 || blk >= num_blocks) return;
+  const size_t tile_bytes = (size_t)kBlock * D + 2 * kBlock;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int kWaves = kThreads / 64;
+  // K: wave w quantizes heads w, w + kWaves, ...; lane l rotates the pairs
+  // (l, l + half) and (l + 64, l + 64 + half) that exist
+  for (int h = wave; h < Hkv; h += kWaves) {
+    const _Float16* kp = k + ((size_t)t * Hkv + h) * D;
+    float x[4];
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = lane + 64 * u;
+      x[2 * u] = x[2 * u + 1] = 0.f;
+      if (i < half) {
+        const double2 c = row[i];
+        double o0, o1;
+        rope_pair((double)kp[i], (double)kp[i + half], c.x, c.y, o0, o1);
+        x[2 * u] = (float)store_f64<_Float16>(o0);
+        x[2 * u + 1] = (float)store_f64<_Float16>(o1);
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * u]), fabsf(x[2 * u + 1])));
+      }
+    }
+    const _Float16 sh = group_scale(wave_max(amax));
+    const float s = (float)sh;
+    uint8_t* tile = k_arena + ((size_t)blk * Hkv + h) * tile_bytes;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = lane + 64 * u;
+      if (i < half) {
+        const int d0 = i, d1 = i + half;
+        tile[(d0 >> 4) * 256 + slot * 16 + (d0 & 15)] = (uint8_t)encode8(x[2 * u], s);
+        tile[(d1 >> 4) * 256 + slot * 16 + (d1 & 15)] = (uint8_t)encode8(x[2 * u + 1], s);
+      }
+    }
+    if (lane == 0) *(_Float16*)(tile + (size_t)kBlock * D + 2 * slot) = sh;
+  }
+  // V: lane l holds elements l, l + 64, l + 128, l + 192
+  for (int h = wave; h < Hkv; h += kWaves) {
+    const _Float16* vp = v + ((size_t)t * Hkv + h) * D;
+    float x[4];
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      x[u] = d < D ? (float)vp[d] : 0.f;
+      amax = fmaxf(amax, fabsf(x[u]));
+    }
+    const _Float16 sh = group_scale(wave_max(amax));
+    const float s = (float)sh;
+    uint8_t* tile = v_arena + ((size_t)blk * Hkv + h) * tile_bytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      if (d < D) tile[d * kBlock + slot] = (uint8_t)encode8(x[u], s);
+    }
+    if (lane == 0) *(_Float16*)(tile + (size_t)kBlock * D + 2 * slot) = sh;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, const void* k,
@@ -87,6 +201,14 @@ hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, con
                               int num_seqs, int num_tokens, const void* rope_table,
                               int rope_max_pos, hipStream_t stream) {
   const dim3 grid(num_tokens), block(kThreads);
+  if (g.dtype == PKV_I8KV) {
+    hipLaunchKernelGGL(append_rope_i8_kernel, grid, block, 0, stream, (const _Float16*)q,
+                       (_Float16*)q_out, (const _Float16*)k, (const _Float16*)v,
+                       (uint8_t*)k_arena, (uint8_t*)v_arena, block_table, max_blocks, cu_q_lens,
+                       chunk_start, num_seqs, (const double2*)rope_table, rope_max_pos,
+                       g.num_blocks, g.num_q_heads, g.num_kv_heads, g.head_dim);
+    return hipGetLastError();
+  }
   if (g.dtype == PKV_F16) {
     hipLaunchKernelGGL(append_rope_kernel<_Float16>, grid, block, 0, stream,
                        (const _Float16*)q, (_Float16*)q_out, (const _Float16*)k,

@@ -63,10 +63,7 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(uint4* __restrict__ k_
 
 }  // namespace
 
-size_t swap_tile_bytes(const pkv_geom& g) {
-  const size_t elt = g.dtype == PKV_F16 ? 2 : 4;
-  return (size_t)g.num_kv_heads * kBlock * g.head_dim * elt;
-}
+size_t swap_tile_bytes(const pkv_geom& g) { return (size_t)g.num_kv_heads * kv_tile_bytes(g); }
 
 hipError_t launch_swap_blocks(const pkv_geom& g, void* k_arena, void* v_arena,
                               const int32_t* ids, int n, void* buf, bool swap_in,
@@ -84,8 +81,7 @@ hipError_t launch_swap_blocks(const pkv_geom& g, void* k_arena, void* v_arena,
 
 hipError_t launch_copy_blocks(const pkv_geom& g, void* k_arena, void* v_arena,
                               const int32_t* src_dst, int n, hipStream_t stream) {
-  const size_t elt = g.dtype == PKV_F16 ? 2 : 4;
-  const size_t vecs = (size_t)g.num_kv_heads * kBlock * g.head_dim * elt / 16;
+  const size_t vecs = (size_t)g.num_kv_heads * kv_tile_bytes(g) / 16;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(256), 0, stream, (uint4*)k_arena,
                      (uint4*)v_arena, src_dst, vecs, g.num_blocks);
   return hipGetLastError();

@@ -1,5 +1,6 @@
-// Generic paged attention: any storage dtype, head_dim <= 256, any query/KV
-// head ratio.  One workgroup per (row, query head) walks the row's blocks in
+// Generic paged attention: any storage dtype (INT8 arenas dequantized element
+// by element, x_hat = code * scale, exact in fp32), head_dim <= 256, any
+// query/KV head ratio.  One workgroup per (row, query head) walks the row's blocks in
 // place through the block table with the online-softmax merge of Kshipra
 // part 3, section 4 (running max, rescaled denominator and accumulator, then
 // out = o / l).  It serves the shapes the tuned kernels do not cover (fp32
@@ -11,10 +12,46 @@ namespace {
 
 constexpr int kThreads = 128;
 
+// Element (d, slot) of a K / V tile of the arena, as a float.
 template <typename T>
+struct TileReader {
+  const T* kt;
+  const T* vt;
+  __device__ TileReader(const void* k_arena, const void* v_arena, int blk, int Hkv, int g, int D)
+      : kt((const T*)k_arena + ((size_t)blk * Hkv + g) * kBlock * D),
+        vt((const T*)v_arena + ((size_t)blk * Hkv + g) * D * kBlock) {}
+  __device__ float k(int d, int slot, int D) const {
+    constexpr int x = 16 / sizeof(T);  // K tile layout [D/x][16][x]
+    (void)D;
+    return (float)kt[((d / x) * kBlock + slot) * x + d % x];
+  }
+  __device__ float v(int d, int slot) const { return (float)vt[d * kBlock + slot]; }
+};
+// INT8 tiles: codes then 16 fp16 scales (16 * D + 32 bytes per (block, head))
+struct TileReaderI8 {
+  const uint8_t* kt;
+  const uint8_t* vt;
+  int D;
+  __device__ TileReaderI8(const void* k_arena, const void* v_arena, int blk, int Hkv, int g, int D_)
+      : D(D_) {
+    const size_t tb = (size_t)kBlock * D_ + 2 * kBlock;
+    kt = (const uint8_t*)k_arena + ((size_t)blk * Hkv + g) * tb;
+    vt = (const uint8_t*)v_arena + ((size_t)blk * Hkv + g) * tb;
+  }
+  __device__ float k(int d, int slot, int) const {
+    const float code = (float)(int8_t)kt[(d >> 4) * 256 + slot * 16 + (d & 15)];
+    return code * (float)((const _Float16*)(kt + (size_t)kBlock * D))[slot];
+  }
+  __device__ float v(int d, int slot) const {
+    const float code = (float)(int8_t)vt[d * kBlock + slot];
+    return code * (float)((const _Float16*)(vt + (size_t)kBlock * D))[slot];
+  }
+};
+
+template <typename T, typename Reader>
 __global__ __launch_bounds__(kThreads) void attend_generic_kernel(
-    float* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_arena,
-    const T* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,
+    float* __restrict__ out, const T* __restrict__ q, const void* __restrict__ k_arena,
+    const void* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ chunk_start, int num_seqs, float scale, int num_blocks, int Hq,
     int Hkv, int D) {
@@ -50,13 +87,11 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(
   for (int n = 0; n < nblk; ++n) {
     int blk = bt[n];
     if (blk < 0 || blk >= num_blocks) blk = 0;
-    const T* kt = k_arena + ((size_t)blk * Hkv + g) * kBlock * D;
-    const T* vt = v_arena + ((size_t)blk * Hkv + g) * D * kBlock;
+    const Reader tr(k_arena, v_arena, blk, Hkv, g, D);
     const int tok = n * kBlock + jl;
     float part = 0.f;
-    constexpr int x = 16 / sizeof(T);  // K tile layout [D/x][16][x]
     if (tok < L)
-      for (int d = sub; d < D; d += 8) part += qs[d] * (float)kt[((d / x) * kBlock + jl) * x + d % x];
+      for (int d = sub; d < D; d += 8) part += qs[d] * tr.k(d, jl, D);
     part += __shfl_xor(part, 1, 8);
     part += __shfl_xor(part, 2, 8);
     part += __shfl_xor(part, 4, 8);
@@ -71,8 +106,8 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(
     for (int j = 0; j < nvalid; ++j) {
       const float p = expf(sc[j] - m_new);
       psum += p;
-      if (tid < D) a0 += p * (float)vt[tid * kBlock + j];
-      if (tid + kThreads < D) a1 += p * (float)vt[(tid + kThreads) * kBlock + j];
+      if (tid < D) a0 += p * tr.v(tid, j);
+      if (tid + kThreads < D) a1 += p * tr.v(tid + kThreads, j);
     }
     l = l * alpha + psum;
     acc0 = a0;
@@ -94,14 +129,19 @@ hipError_t launch_attend_generic(const pkv_geom& g, float* out, const void* q,
                                  const int32_t* chunk_start, int num_seqs, int num_rows,
                                  float scale, hipStream_t stream) {
   const dim3 grid(num_rows, g.num_q_heads), block(kThreads);
-  if (g.dtype == PKV_F16) {
-    hipLaunchKernelGGL(attend_generic_kernel<_Float16>, grid, block, 0, stream, out,
-                       (const _Float16*)q, (const _Float16*)k_arena, (const _Float16*)v_arena,
+  if (g.dtype == PKV_I8KV) {
+    hipLaunchKernelGGL((attend_generic_kernel<_Float16, TileReaderI8>), grid, block, 0, stream,
+                       out, (const _Float16*)q, k_arena, v_arena, block_table, max_blocks,
+                       context_lens, cu_q_lens, chunk_start, num_seqs, scale, g.num_blocks,
+                       g.num_q_heads, g.num_kv_heads, g.head_dim);
+  } else if (g.dtype == PKV_F16) {
+    hipLaunchKernelGGL((attend_generic_kernel<_Float16, TileReader<_Float16>>), grid, block, 0,
+                       stream, out, (const _Float16*)q, k_arena, v_arena,
                        block_table, max_blocks, context_lens, cu_q_lens, chunk_start, num_seqs,
                        scale, g.num_blocks, g.num_q_heads, g.num_kv_heads, g.head_dim);
   } else {
-    hipLaunchKernelGGL(attend_generic_kernel<float>, grid, block, 0, stream, out,
-                       (const float*)q, (const float*)k_arena, (const float*)v_arena,
+    hipLaunchKernelGGL((attend_generic_kernel<float, TileReader<float>>), grid, block, 0,
+                       stream, out, (const float*)q, k_arena, v_arena,
                        block_table, max_blocks, context_lens, cu_q_lens, chunk_start, num_seqs,
                        scale, g.num_blocks, g.num_q_heads, g.num_kv_heads, g.head_dim);
   }

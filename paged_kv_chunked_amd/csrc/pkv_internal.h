@@ -64,6 +64,12 @@ __device__ inline int find_seq(const int32_t* __restrict__ cu, int num_seqs, int
   return lo;
 }
 
+// Bytes of one (block, KV head) tile of either arena.
+inline size_t kv_tile_bytes(const pkv_geom& g) {
+  if (g.dtype == PKV_I8KV) return (size_t)kBlock * g.head_dim + 2 * kBlock;
+  return (size_t)kBlock * g.head_dim * (g.dtype == PKV_F16 ? 2 : 4);
+}
+
 // ---- launchers (defined in the kernel translation units) -------------------
 hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, const void* k,
                               const void* v, void* k_arena, void* v_arena,

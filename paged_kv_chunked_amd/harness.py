@@ -17,7 +17,7 @@ from typing import Dict, List
 
 import numpy as np
 
-from . import (BLOCK_SIZE, F16, F32, Pool, geom, kv_append_rope, paged_attention_chunk,
+from . import (BLOCK_SIZE, F16, F32, I8KV, Pool, geom, kv_append_rope, paged_attention_chunk,
                paged_attention_chunk_workspace_bytes,
                paged_attention_decode, paged_attention_decode_workspace_bytes, pkv_copy_blocks,
                pkv_rope_table_bytes, pkv_rope_table_init)
@@ -84,21 +84,38 @@ class DeviceWorkload:
         self.w = w
         self.device = torch.device(device)
         self.tdtype = torch.float16 if w.dtype == "f16" else torch.float32
+        self.kv_bits = getattr(w, "kv_bits", 0)
         self.g = geom(w.num_blocks, w.num_kv_heads, w.num_q_heads, w.head_dim,
-                      F16 if w.dtype == "f16" else F32)
+                      I8KV if self.kv_bits == 8 else F16 if w.dtype == "f16" else F32)
         self.threads = threads
         self.scale = default_scale(w.head_dim)
         N, H, D = w.num_blocks, w.num_kv_heads, w.head_dim
         x = 16 // (2 if w.dtype == "f16" else 4)   # elements per 16-byte piece of K
+        if self.kv_bits == 8:
+            # INT8 tiles: codes, then 16 fp16 scales; unwritten = all-ones bytes
+            # (scale NaN), as in the oracle's quantized arena
+            tile = BLOCK_SIZE * D + 2 * BLOCK_SIZE
+            self.k_arena = torch.full((N, H, tile), 255, dtype=torch.uint8, device=self.device)
+            self.v_arena = torch.full((N, H, tile), 255, dtype=torch.uint8, device=self.device)
+        else:
+            self._fp_arenas(N, H, D, x)
+        self._finish_init(w, fill_batch, rope_max_pos)
+
+    def _fp_arenas(self, N, H, D, x):
+        torch = _torch()
         self.k_arena = torch.full((N, H, D // x, BLOCK_SIZE, x), float("nan"), dtype=self.tdtype,
                                   device=self.device)
         self.v_arena = torch.full((N, H, D, BLOCK_SIZE), float("nan"), dtype=self.tdtype,
                                   device=self.device)
+
+    def _finish_init(self, w, fill_batch, rope_max_pos):
+        torch = _torch()
+        D = w.head_dim
         self.rope_max_pos = rope_max_pos or w.max_position
         nbytes = pkv_rope_table_bytes(D, self.rope_max_pos)
         self.rope = torch.empty(nbytes // 8, dtype=torch.float64, device=self.device)
         pkv_rope_table_init(self.rope, w.theta, D, self.rope_max_pos)
-        self.pool = Pool(N)
+        self.pool = Pool(w.num_blocks)
         self.tables: Dict[int, List[int]] = {s: [] for s in range(w.num_pool_seqs)}
         self.copies = []
         self._run_script(fill_batch)
@@ -251,7 +268,10 @@ class DeviceWorkload:
             return 0
         w = self.w
         elt = 2 if w.dtype == "f16" else 4
-        per_tok = 2 * w.num_kv_heads * w.head_dim * elt
+        if self.kv_bits == 8:   # codes plus the fp16 scale of each head vector
+            per_tok = 2 * w.num_kv_heads * (w.head_dim + 2)
+        else:
+            per_tok = 2 * w.num_kv_heads * w.head_dim * elt
         seen = {}
         for r, L in zip(self.dec_rows, self.dec_lens_host):
             t = self.tables[w.step[r].seq]

@@ -1,0 +1,106 @@
+"""Pins of the oracle's group-quantization codec (oracle/quant.py) and of the
+quantized arena, against what Kshipra part 3, section 2 fixes: one FP16 scale
+per group used to encode and to decode, rounding to the nearest step, the
+reconstruction bound |x - x_hat| <= s / 2, the failure of that bound when the
+codes come from the FP32 scale (the pages' bug, about |q| * 2^-11 * s beyond
+s / 2), and the cost of 4 + 16/128 = 4.125 bits per value (about 26% of FP16)
+for INT4 with groups of 128."""
+import numpy as np
+import pytest
+
+from oracle import arena, quant
+
+
+def _groups(rng, n, d=128):
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    x[rng.random((n, d)) < 0.01] *= 8.0           # heavy tail, as the long workload's keys
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_reconstruction_bound(bits):
+    x = _groups(np.random.default_rng(1), 4000)
+    q, s = quant.encode(x, bits)
+    err = np.abs(x.astype(np.float64) - quant.decode(q, s))
+    half = s.astype(np.float64)[:, None] / 2
+    assert (err <= half).all()
+    assert np.abs(q).max() == quant.QMAX[bits]     # the largest value maps to the top code
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_codes_are_the_nearest_step_brute_force(bits):
+    """Every code is the integer step nearest x / s (ties to even), checked by
+    trying all codes."""
+    rng = np.random.default_rng(2)
+    x = _groups(rng, 40, d=16)
+    q, s = quant.encode(x, bits)
+    qmax = quant.QMAX[bits]
+    cand = np.arange(-qmax, qmax + 1, dtype=np.float64)
+    for g in range(x.shape[0]):
+        r = x[g].astype(np.float32) / s[g].astype(np.float32)   # the fp32 quotient
+        d = np.abs(r.astype(np.float64)[:, None] - cand[None, :])
+        best = d.min(axis=1)
+        for i in range(x.shape[1]):
+            winners = cand[d[i] == best[i]]
+            expect = winners[0] if winners.size == 1 else winners[winners % 2 == 0][0]
+            assert q[g, i] == expect
+
+
+def test_fp32_scale_breaks_the_bound_by_the_pages_margin():
+    """The pages' bug: codes from the FP32 scale, decoding with its FP16
+    rounding.  The bound fails, by at most |q| * 2^-11 * s (about 0.06 s for
+    INT8); encoding with the FP16 scale (the fix) keeps it."""
+    x = _groups(np.random.default_rng(3), 4000)
+    qb, sb = quant.encode_with_fp32_scale(x, 8)
+    s64 = sb.astype(np.float64)[:, None]
+    err = np.abs(x.astype(np.float64) - quant.decode(qb, sb))
+    assert (err > s64 / 2).any()
+    excess = (err - s64 / 2) / s64
+    assert excess.max() <= 127 * 2.0 ** -11 * 1.01
+    assert excess.max() > 0.02
+    q, s = quant.encode(x, 8)
+    assert (np.abs(x.astype(np.float64) - quant.decode(q, s)) <= s.astype(np.float64)[:, None] / 2).all()
+
+
+def test_bits_per_value_from_the_pages():
+    assert quant.bits_per_value(4, 128) == 4.125
+    assert abs(quant.bits_per_value(4, 128) / 16 - 0.26) < 0.005
+    assert quant.bits_per_value(8, 128) == 8.125
+
+
+def test_special_groups():
+    # all zeros: zero codes, exact zeros back
+    z = np.zeros((1, 128), np.float16)
+    q, s = quant.encode(z)
+    assert (q == 0).all() and (quant.decode(q, s) == 0).all()
+    # a group whose scale is exact: amax = 127 * 2^-3 gives s = 2^-3 and every
+    # multiple of 2^-3 in range reconstructs exactly
+    x = (np.arange(-127, 129, 2)[:128] * 0.125).astype(np.float16)[None]
+    x[0, 0] = np.float16(-127 * 0.125)
+    q, s = quant.encode(x)
+    assert s[0] == np.float16(0.125)
+    assert np.array_equal(quant.decode(q, s)[0], x[0].astype(np.float64))
+    # a single non-zero value: top code, reconstructed within half a step
+    y = np.zeros((1, 128), np.float16)
+    y[0, 5] = np.float16(-3.3)
+    q, s = quant.encode(y)
+    assert q[0, 5] == -127 and abs(quant.decode(q, s)[0, 5] - float(y[0, 5])) <= float(s[0]) / 2
+
+
+def test_quant_arena_gather_is_codec_roundtrip_and_tile_size():
+    rng = np.random.default_rng(4)
+    H, D = 2, 32
+    a = arena.QuantArena(6, H, D)
+    k = _groups(rng, 20 * H, D).reshape(20, H, D)
+    v = _groups(rng, 20 * H, D).reshape(20, H, D)
+    table = [4, 1]
+    a.write(table, 0, k, v)
+    K, V = a.gather(table, 20)
+    assert np.array_equal(K, quant.roundtrip(k))
+    assert np.array_equal(V, quant.roundtrip(v))
+    # unwritten slots read as NaN
+    K2, _ = a.gather([4, 1], 32)
+    assert np.isnan(K2[20:]).all()
+    # the byte image of one block's K tiles: per head 16 * D codes + 16 fp16 scales
+    assert a.tile_bytes("k", 4).size == H * (16 * D + 32)
+    assert a.swap_out([4, 1]).size == 2 * 2 * H * (16 * D + 32)
