@@ -10,6 +10,8 @@ Default run (N = 1):
   * chunk prefill (reported under "chunk_prefill"): 8 sequences with cached
     prefixes 16*U{0..224} and a 512-token chunk each; a step = restore q +
     kv_append_rope + paged_attention_chunk; TFLOP/s over visible pairs.
+  * decode over INT8 arenas (reported under "decode_int8"): the same batch with
+    K/V cached as INT8 codes plus one fp16 scale per (token, KV head) vector.
   * swap (reported under "swap"): 1024 blocks (64 MiB) of the decode batch out
     to pinned host memory and back (pkv_swap_out / pkv_swap_in), beside a
     plain contiguous copy of the same size in each direction.
@@ -83,9 +85,12 @@ def make_layers(torch, dw, n):
     return layers
 
 
-def bench_decode(torch, args):
+def bench_decode(torch, args, kv_bits=0):
+    import dataclasses
     from paged_kv_chunked_amd import harness, workloads
     w = workloads.decode_batch()
+    if kv_bits:
+        w = dataclasses.replace(w, kv_bits=kv_bits)
     log(f"decode set-up: {w.num_blocks} blocks")
     dw = harness.DeviceWorkload(w)
     layers = make_layers(torch, dw, args.layers)
@@ -220,6 +225,7 @@ def main():
                     help="arena copies rotated over (Infinity Cache guard)")
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-swap", action="store_true")
+    ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -298,6 +304,31 @@ def main():
     if not args.no_swap:
         out["swap"] = bench_swap(torch, dw)
         log(f"swap: {out['swap']}")
+    if not args.no_int8:
+        _, dw8, ms_step8, ms_dec8, ms_dcall8, nbytes8 = bench_decode(torch, args, kv_bits=8)
+        ach8 = nbytes8 / (ms_dec8 * 1e-3) / 1e9
+        tokens = int(sum(dw8.dec_lens_host))
+        log(f"decode int8: kernel {ms_dec8:.4f} ms, {nbytes8 / 1e6:.1f} MB -> {ach8:.0f} GB/s")
+        out["decode_int8"] = {
+            "workload": "the decode workload over INT8 arenas (codes + one fp16 scale per "
+                        "(token, KV head) vector)",
+            "context_tokens_per_s": round(tokens / (ms_dec8 * 1e-3), 1),
+            "speedup_vs_fp16_arena": round(ms_dec / ms_dec8, 3),
+            "ms_per_step": round(ms_step8, 5),
+            "roofline": {
+                "kernel": "paged_attention_decode (decode_split_i8_kernel + decode_combine_kernel)",
+                "bound": "hbm",
+                "achieved": round(ach8, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(ach8 / PEAK_HBM_GBS, 4),
+                "traffic": None,
+                "algorithmic_bytes_per_launch": nbytes8,
+                "avg_launch_ms": round(ms_dec8, 5),
+                "avg_launch_ms_isolated": round(ms_dcall8, 5),
+            },
+        }
+        del dw8
     if not args.no_chunk:
         wc, dwc, ms_cstep, ms_chunk, ms_ccall, flops = bench_chunk(torch, args)
         tf_kernel = flops / (ms_chunk * 1e-3) / 1e12

@@ -283,6 +283,221 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
   }
 }
 
+// ---- INT8 arenas (PKV_I8KV) -------------------------------------------------
+// Same split-KV structure for arenas holding INT8 codes with one fp16 scale per
+// (token, KV head) vector (tile: codes, then 16 scales).  Half the bytes per
+// token, so twice the tokens per second at the same HBM rate.
+//   * K rows of the first product are permuted: row m of MFMA u is token
+//     8((m >> 2) & 1) + 4u + (m & 3) of block A (m < 8) or B (m >= 8), so a
+//     lane's 8 scores for head ln are 8 consecutive tokens of one block -- one
+//     8-byte load of V codes per head dim.  The head dims of the contraction
+//     are permuted too (MFMA kd, lane group lq: dims 16(4(kd >> 1) + lq) +
+//     8(kd & 1) .. +8), so one 16-byte load of K codes feeds two MFMAs; the
+//     queries are loaded in the same order.
+//   * codes become fp16 exactly (byte b: fp16 bits 0x6400 | (b ^ 0x80) =
+//     1024 + b + 128, minus 1152), the K scale multiplies the score, and the V
+//     scale is folded into the probability: P^T holds fp16(p * s_v * 2^6), the
+//     2^6 keeping small weights out of fp16 subnormals (undone at the end).
+constexpr float kPvBoost = 64.f;
+#ifndef PKV_DECODE_I8_AHEAD
+#define PKV_DECODE_I8_AHEAD 1
+#endif
+constexpr int kI8Ahead = PKV_DECODE_I8_AHEAD;  // pairs in flight behind the computed one
+
+struct PairI8 {
+  u32x4 k[2][2];  // [u][j]: 16 codes (dims 16(4j + lq) .. +16) of the lane's key row
+  u32x2 v[8];     // [db]: 8 codes of dim 16db + ln, the lane's 8 keys
+  u32x4 ks, vs;   // fp16 scales of the lane's 8 keys (K, V)
+};
+
+__device__ inline half8_t codes_to_half(uint32_t lo, uint32_t hi) {
+  const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+  const uint32_t c = 0x64646464u;
+  // byte selectors: result bytes [a0, 0x64, a1, 0x64] etc. (perm indexes the
+  // 8 bytes {src1 (0..3), src0 (4..7)})
+  const uint32_t w0 = __builtin_amdgcn_perm(c, a, 0x05010400u);
+  const uint32_t w1 = __builtin_amdgcn_perm(c, a, 0x05030402u);
+  const uint32_t w2 = __builtin_amdgcn_perm(c, b, 0x05010400u);
+  const uint32_t w3 = __builtin_amdgcn_perm(c, b, 0x05030402u);
+  half8_t h = __builtin_bit_cast(half8_t, u32x4{w0, w1, w2, w3});
+  return h - (half8_t)(_Float16)1152.f;
+}
+
+__device__ inline PairI8 load_pair_i8(const uint8_t* __restrict__ k_arena,
+                                      const uint8_t* __restrict__ v_arena, int blk_a, int blk_b,
+                                      int Hkv, int g, int ln, int lq) {
+  constexpr size_t kTile = (size_t)kBlock * kD + 2 * kBlock;
+  PairI8 pr;
+  // K row of this lane (MFMA row ln) for MFMA u: block A or B by ln >> 3
+  const uint8_t* kt = k_arena + ((size_t)((ln >> 3) ? blk_b : blk_a) * Hkv + g) * kTile;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int slot = 8 * ((ln >> 2) & 1) + 4 * u + (ln & 3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pr.k[u][j] = __builtin_nontemporal_load((const u32x4*)(kt + (4 * j + lq) * 256 + slot * 16));
+  }
+  // the lane's keys (as head ln of the scores): block lq >> 1, tokens 8(lq & 1) .. +8
+  const size_t tv = ((size_t)((lq >> 1) ? blk_b : blk_a) * Hkv + g) * kTile;
+  const uint8_t* vt = v_arena + tv;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    pr.v[db] = __builtin_nontemporal_load((const u32x2*)(vt + (16 * db + ln) * kBlock + 8 * (lq & 1)));
+  pr.ks = __builtin_nontemporal_load((const u32x4*)(k_arena + tv + kBlock * kD + 16 * (lq & 1)));
+  pr.vs = __builtin_nontemporal_load((const u32x4*)(vt + kBlock * kD + 16 * (lq & 1)));
+  return pr;
+}
+
+__global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_split_i8_kernel(
+    float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const _Float16* __restrict__ q,
+    const uint8_t* __restrict__ k_arena, const uint8_t* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks) {
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.z * kDecodeWavesPerWG + (threadIdx.x >> 6);
+  if (g >= Hkv) return;
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 15, lq = lane >> 4;
+  const int Hq = Hkv * kG;
+  const int blk0 = split * kSB;
+  int my_blk = 0;
+  if (lane < kSB && blk0 + lane < max_blocks)
+    my_blk = block_table[(size_t)b * max_blocks + blk0 + lane];
+  // Q^T (B operand) in the permuted dim order: MFMA kd, lane group lq holds
+  // dims 16(4(kd >> 1) + lq) + 8(kd & 1) .. +8 of head g*4+ln
+  half8_t qb[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd)
+    qb[kd] = ln < kG ? *(const half8_t*)(q + ((size_t)b * Hq + g * kG + ln) * kD +
+                                         16 * (4 * (kd >> 1) + lq) + 8 * (kd & 1))
+                     : (half8_t)(_Float16)0.f;
+  const int L = min(min(context_lens[b], max_blocks * kBlock), nsplit_max * kDecodeSplit);
+  if (L <= 0) {
+    if (split == 0 && ln < kG) {
+      float* o = out + ((size_t)b * Hq + g * kG + ln) * kD + 4 * lq;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f32x4*)(o + 16 * db) = (f32x4)0.f;
+    }
+    return;
+  }
+  const int nb_seq = (L + kBlock - 1) / kBlock;
+  if (blk0 >= nb_seq) return;
+  const int nb = min(kSB, nb_seq - blk0);
+  const int nsplit = (nb_seq + kSB - 1) / kSB;
+  const int npairs = (nb + 1) >> 1;
+  if (lane >= nb || my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
+
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = (f32x4)0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto pair_ids = [&](int p, int& a, int& c) {
+    a = __builtin_amdgcn_readlane(my_blk, 2 * p);
+    c = 2 * p + 1 < nb ? __builtin_amdgcn_readlane(my_blk, 2 * p + 1) : a;
+  };
+  auto compute = [&](const PairI8& pr, int p) {
+    f32x4 s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = (f32x4)0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 c = pr.k[u][j];
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_half(c.x, c.y), qb[2 * j], s[u], 0, 0, 0);
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_half(c.z, c.w), qb[2 * j + 1], s[u], 0, 0, 0);
+      }
+    }
+    // element e = 4u + i of this lane: token 8(lq & 1) + e of block lq >> 1
+    const half8_t ksc = __builtin_bit_cast(half8_t, pr.ks);
+    const half8_t vsc = __builtin_bit_cast(half8_t, pr.vs);
+    const int tok0 = (blk0 + 2 * p + (lq >> 1)) * kBlock + 8 * (lq & 1);
+    const int nvalid = L - tok0;  // keys e < nvalid exist
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = e < nvalid ? s[e >> 2][e & 3] * ((float)ksc[e] * scale_log2) : -INFINITY;
+      sv[e] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: the first key of a split is real
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    }
+    m_run = m_new;
+    half8_t pb;
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);  // 0 for keys past the end
+      lsum += pe;
+      // past the end the V scale may be NaN (unwritten slot): select, not multiply
+      pb[e] = e < nvalid ? (_Float16)(pe * ((float)vsc[e] * kPvBoost)) : (_Float16)0.f;
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const u32x2 c = pr.v[db];
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_half(c.x, c.y), pb, o[db], 0, 0, 0);
+    }
+  };
+
+  // kI8Ahead pairs are kept in flight behind the one being computed (same
+  // unconditional-prefetch scheme as the fp16 kernel).  One measured best:
+  // two or three cost registers (occupancy 3 -> 2) and ran 4-6% slower.
+  constexpr int kAhead = kI8Ahead;
+  PairI8 buf[kAhead + 1];
+#pragma unroll
+  for (int p = 0; p < kAhead; ++p) {
+    int ba, bb;
+    pair_ids(min(p, npairs - 1), ba, bb);
+    buf[p] = load_pair_i8(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+  }
+#pragma unroll
+  for (int p = 0; p < kSB / 2; ++p) {
+    if (p + kAhead < kSB / 2) {
+      int ba, bb;
+      pair_ids(min(p + kAhead, npairs - 1), ba, bb);
+      buf[(p + kAhead) % (kAhead + 1)] = load_pair_i8(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (p < npairs) compute(buf[p % (kAhead + 1)], p);
+  }
+
+  float l_row = l_run;
+  l_row += __shfl_xor(l_row, 16);
+  l_row += __shfl_xor(l_row, 32);
+  const int hq = g * kG + ln;
+  const float unboost = 1.f / kPvBoost;
+  if (nsplit == 1) {
+    if (ln < kG) {
+      const float inv = unboost / l_row;
+      float* dst = out + ((size_t)b * Hq + hq) * kD + 4 * lq;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * inv;
+    }
+    return;
+  }
+  if (ln < kG) {
+    const size_t part = ((size_t)b * nsplit_max + split) * Hq + hq;
+    float* dst = ws_o + part * kD + 4 * lq;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * unboost;
+    if (lq == 0) {
+      ws_ml[2 * part] = m_run;
+      ws_ml[2 * part + 1] = l_row;
+    }
+  }
+}
+
 // Log-sum-exp merge of the splits of the 4 query heads of one (sequence b, KV
 // head g): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
 // M = max_s m_s.  The split weights are computed once into LDS; then each
@@ -347,7 +562,8 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 }  // namespace
 
 bool decode_fast_path(const pkv_geom& g) {
-  return g.dtype == PKV_F16 && g.head_dim == kD && g.num_q_heads == kG * g.num_kv_heads;
+  return (g.dtype == PKV_F16 || g.dtype == PKV_I8KV) && g.head_dim == kD &&
+         g.num_q_heads == kG * g.num_kv_heads;
 }
 
 // Workspace: [partial o: S x nsplit x Hq x D floats][partial (m, l): S x nsplit x
@@ -391,10 +607,16 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
   // index across all XCDs; the extra column of workgroups exits at once.
   const int gx = nsplit | 1;
   const dim3 grid(gx, num_seqs, zg);
-  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64 * wpg), 0, stream,
-                     out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
-                     (const _Float16*)v_arena, block_table, max_blocks, context_lens,
-                     scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
+  if (g.dtype == PKV_I8KV)
+    hipLaunchKernelGGL(decode_split_i8_kernel, grid, dim3(64 * wpg), 0, stream,
+                       out, ws_o, ws_ml, (const _Float16*)q, (const uint8_t*)k_arena,
+                       (const uint8_t*)v_arena, block_table, max_blocks, context_lens,
+                       scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
+  else
+    hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64 * wpg), 0, stream,
+                       out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
+                       (const _Float16*)v_arena, block_table, max_blocks, context_lens,
+                       scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit <= 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(g.num_kv_heads, num_seqs), dim3(kCombineThreads),

@@ -12,6 +12,7 @@ decode and chunk workloads are compared in full; the mixed and long-context
 workloads on sampled sequences and rows (their K/V regenerated and rotated by
 the oracle for just those sequences).
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -68,6 +69,15 @@ class Errors:
         assert mean <= MEAN_ABS, (name, mean)
 
 
+def quant_image(a, which):
+    """Byte image [N][Hkv][16 D + 32] of the oracle's quantized arena (codes,
+    then the 16 fp16 scales of each (block, head) tile)."""
+    q, sc = (a.kq, a.ks) if which == "k" else (a.vq, a.vs)
+    N, H = q.shape[:2]
+    return np.concatenate([np.ascontiguousarray(q).reshape(N, H, -1).view(np.uint8),
+                           np.ascontiguousarray(sc).view(np.uint8).reshape(N, H, -1)], axis=2)
+
+
 def run_case(w, full_arena=True, dec_sample=None, chunk_sample=None):
     """Runs workload w on the GPU and checks it against the oracle."""
     say(f"{w.name}: set-up (blocks={w.num_blocks}, step rows={len(w.step)})")
@@ -81,7 +91,10 @@ def run_case(w, full_arena=True, dec_sample=None, chunk_sample=None):
     assert np.array_equal(dw.bt_host, oscript.block_table(w, st))
     q_rot = oscript.append_step(w, st)
     assert np.array_equal(bits(dw.q.cpu().numpy()), bits(q_rot)), "rotated q differs"
-    if full_arena:
+    if full_arena and w.kv_bits:
+        assert np.array_equal(dw.k_arena.cpu().numpy(), quant_image(st.arena, "k")), "K arena differs"
+        assert np.array_equal(dw.v_arena.cpu().numpy(), quant_image(st.arena, "v")), "V arena differs"
+    elif full_arena:
         assert np.array_equal(bits(dw.k_arena.cpu().numpy()), bits(st.arena.k)), "K arena differs"
         assert np.array_equal(bits(dw.v_arena.cpu().numpy()), bits(st.arena.v)), "V arena differs"
     errs = Errors()
@@ -89,7 +102,7 @@ def run_case(w, full_arena=True, dec_sample=None, chunk_sample=None):
     dec_rows = dw.dec_rows if dec_sample is None else dec_sample
     for r in dec_rows:
         s = w.step[r]
-        if not full_arena:  # the sampled sequence's arena blocks, bit for bit
+        if not full_arena and not w.kv_bits:  # the sampled sequence's arena blocks, bit for bit
             K, V = oscript.sequence_kv(w, st, r)
             L = s.start + 1
             tab = torch.tensor(dw.tables[s.seq][:-(-L // 16)], device=dw.device)
@@ -143,6 +156,11 @@ def generic_shape(name, dtype, hq, hkv, d):
     return workloads.build(name, 13, dtype, hq, hkv, d, 1.0e4, seqs, max_blocks_per_seq=24)
 
 
+def i8(w):
+    """The same workload over INT8 arenas (codes + fp16 scale per head vector)."""
+    return dataclasses.replace(w, name=w.name + "_i8", kv_bits=8)
+
+
 SMALL = {
     "tiny_f32": workloads.tiny,
     "small_decode": small_decode,
@@ -152,6 +170,11 @@ SMALL = {
     "generic_f16_g2": lambda: generic_shape("generic_f16_g2", "f16", 8, 4, 128),
     "generic_f16_g8": lambda: generic_shape("generic_f16_g8", "f16", 16, 2, 128),
     "generic_f32_d128": lambda: generic_shape("generic_f32_d128", "f32", 8, 2, 128),
+    "small_decode_i8": lambda: i8(small_decode()),
+    "small_chunk_i8": lambda: i8(small_chunk()),
+    "small_mixed_i8": lambda: i8(small_mixed()),
+    "generic_i8_d64": lambda: i8(generic_shape("generic_i8_d64", "f16", 8, 2, 64)),
+    "generic_i8_g2": lambda: i8(generic_shape("generic_i8_g2", "f16", 8, 4, 128)),
 }
 
 
@@ -170,6 +193,10 @@ def test_decode_full():
 
 def test_chunk_full():
     run_case(workloads.chunk_batch())
+
+
+def test_decode_full_i8():
+    run_case(i8(workloads.decode_batch()))
 
 
 def test_mixed_full_sampled():
