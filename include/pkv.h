@@ -260,6 +260,39 @@ pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, i
 int32_t pkv_pool_can_admit(const pkv_pool* pool, int64_t evictable, int64_t active_reserved,
                            int64_t new_need);
 
+/* ---------------------------------------------------------------------------
+ * Radix-tree prefix cache over the pool's blocks (part 3 section 3: KV blocks
+ * live in a radix tree keyed by token blocks; a new request reuses every
+ * matching block; reference counts keep shared blocks alive; under memory
+ * pressure the least recently used leaf is evicted, the tree being re-scanned
+ * on every iteration so a parent that becomes a leaf is considered).
+ * A node is one full block of 16 token ids; the tree owns one reference to
+ * its block.  Host-only, not thread-safe; the pool must outlive the tree.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_radix pkv_radix;
+pkv_radix* pkv_radix_create(pkv_pool* pool);  /* NULL if pool is NULL */
+void pkv_radix_destroy(pkv_radix* r);          /* drops the tree's references */
+/* Longest cached prefix of whole blocks of tokens[0..n): writes up to cap of
+ * its block ids to blocks and returns its length in blocks (-1 on bad
+ * arguments).  Marks the matched nodes as used now; takes no reference (a
+ * request adopting the blocks increfs them). */
+int32_t pkv_radix_match(pkv_radix* r, const int32_t* tokens, int32_t n, int32_t* blocks,
+                        int32_t cap);
+/* Caches the n / 16 whole blocks of tokens[0..n), held in blocks[i] (live
+ * pool blocks): each block not yet in the tree becomes a node and the tree
+ * increfs it; existing nodes keep their block.  All-or-nothing on
+ * PKV_ERR_RANGE / PKV_ERR_REFCOUNT (a new block id out of range or free). */
+pkv_status pkv_radix_insert(pkv_radix* r, const int32_t* tokens, int32_t n,
+                            const int32_t* blocks);
+/* Frees up to target blocks, one least recently used evictable leaf at a time
+ * (a leaf whose block the tree alone holds; ties: older node first); returns
+ * how many were freed (-1 on bad arguments). */
+int32_t pkv_radix_evict(pkv_radix* r, int32_t target);
+/* Blocks repeated eviction could free: nodes the tree alone holds whose
+ * whole subtree is evictable (the "evictable" of pkv_pool_can_admit). */
+int32_t pkv_radix_evictable(const pkv_radix* r);
+int32_t pkv_radix_num_nodes(const pkv_radix* r);
+
 /* Host check of table copies: every row with length L > 0 needs
  * ceil(L/16) <= max_blocks_per_seq entries, each in [0, num_blocks). */
 pkv_status pkv_validate_tables(const pkv_geom* geom, const int32_t* h_block_table,

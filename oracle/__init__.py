@@ -16,7 +16,10 @@ Sources, the Kshipra blog series:
          free list, GQA-aware sizing                      -> pool, arena
        section 3 "Radix-Tree Prefix Cache": shared blocks kept alive by
          reference counts; a block that diverges is copied before it is
-         written                                          -> pool
+         written; least-recently-used leaf eviction that re-scans the tree
+                                                          -> pool, radix
+       section 5 "Continuous Batching and Admission Control": admission
+         rule; preemption by swapping blocks out         -> pool, arena
        section 2 "INT4 Quantization and the Scale Bug": group quantization
          with one FP16 scale used to encode and decode   -> quant
        section 4 "Chunked Prefill": online softmax over blocks read in place,
@@ -25,7 +28,8 @@ Sources, the Kshipra blog series:
 
 Modules:
   rope       closed-form rotary embedding, cos/sin tables from libm in fp64
-  pool       LIFO free list + reference counts + copy-on-write
+  pool       LIFO free list + reference counts + copy-on-write + admission
+  radix      radix-tree prefix cache with re-scanning LRU eviction
   arena      block-arena writes/gathers, materialised (fp16/fp32 or
              group-quantized) or symbolic
   quant      group quantization codec (INT8/INT4 codes, FP16 scale)
@@ -34,4 +38,4 @@ Modules:
 
 Parity pins for every function live in tests/test_oracle_*.py.
 """
-from . import rope, pool, arena, attention, quant, script  # noqa: F401
+from . import rope, pool, arena, attention, quant, radix, script  # noqa: F401

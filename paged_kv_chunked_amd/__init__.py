@@ -78,6 +78,13 @@ _SIGS = {
     "pkv_pool_refcount": (_I32, [_P, _I32]),
     "pkv_pool_free_list": (ctypes.c_int, [_P, _P, _I32, _PI32]),
     "pkv_pool_can_admit": (_I32, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
+    "pkv_radix_create": (_P, [_P]),
+    "pkv_radix_destroy": (None, [_P]),
+    "pkv_radix_match": (_I32, [_P, _P, _I32, _P, _I32]),
+    "pkv_radix_insert": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "pkv_radix_evict": (_I32, [_P, _I32]),
+    "pkv_radix_evictable": (_I32, [_P]),
+    "pkv_radix_num_nodes": (_I32, [_P]),
     "pkv_validate_tables": (ctypes.c_int, [_PG, _P, _I32, _P, _I32]),
     "pkv_f64_to_f16_host": (ctypes.c_int, [_P, _P, ctypes.c_int64]),
 }
@@ -316,3 +323,50 @@ class Pool:
         _check(lib().pkv_pool_free_list(self._h, out.ctypes.data, n.value, ctypes.byref(n)),
                "pkv_pool_free_list")
         return out
+
+
+class Radix:
+    """The library's radix-tree prefix cache (pkv_radix_*) over a Pool."""
+
+    def __init__(self, pool: "Pool"):
+        self.pool = pool  # keeps the pool alive for the tree's lifetime
+        self._h = lib().pkv_radix_create(pool._h)
+        if not self._h:
+            raise PkvError(1, "pkv_radix_create")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.pkv_radix_destroy(h)
+
+    def match(self, tokens):
+        import numpy as np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cap = t.size // BLOCK_SIZE
+        out = np.empty(max(cap, 1), np.int32)
+        m = lib().pkv_radix_match(self._h, t.ctypes.data, t.size, out.ctypes.data, cap)
+        if m < 0:
+            raise PkvError(4, "pkv_radix_match")
+        return out[:m].copy()
+
+    def insert(self, tokens, blocks) -> None:
+        import numpy as np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        b = np.ascontiguousarray(blocks, dtype=np.int32)
+        if b.size < t.size // BLOCK_SIZE:
+            raise ValueError("one block id per whole block of tokens")
+        _check(lib().pkv_radix_insert(self._h, t.ctypes.data, t.size, b.ctypes.data),
+               "pkv_radix_insert")
+
+    def evict(self, target: int) -> int:
+        r = lib().pkv_radix_evict(self._h, target)
+        if r < 0:
+            raise PkvError(4, "pkv_radix_evict")
+        return r
+
+    def evictable(self) -> int:
+        return lib().pkv_radix_evictable(self._h)
+
+    @property
+    def num_nodes(self) -> int:
+        return lib().pkv_radix_num_nodes(self._h)

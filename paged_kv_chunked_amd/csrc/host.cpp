@@ -1,5 +1,8 @@
-// Host side of libpkv: block pool, RoPE table, validation, status strings.
+// Host side of libpkv: block pool, radix-tree prefix cache, RoPE table,
+// validation, status strings.
+#include <array>
 #include <cmath>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -184,6 +187,199 @@ pkv_status pkv_pool_free_list(const pkv_pool* p, int32_t* out, int32_t cap, int3
   for (int32_t i = 0; i < len && i < cap; ++i) out[i] = p->free_list[i];
   return PKV_OK;
 }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Radix-tree prefix cache (Kshipra part 3, section 3).  Node 0 is the root;
+// every other live node is one full block of 16 token ids and holds one
+// reference to its physical block in the pool.  Children are found by a
+// linear scan of the parent's child list (fan-out is small: distinct
+// continuations of one prefix).
+namespace {
+struct RadixNode {
+  std::array<int32_t, PKV_BLOCK_SIZE> key;
+  int32_t block = -1;
+  int32_t parent = -1;
+  uint64_t last = 0;    // clock of the last match / insert that touched it
+  int64_t serial = -1;  // creation order (LRU tie-break)
+  bool alive = false;
+  std::vector<int32_t> children;
+};
+}  // namespace
+
+struct pkv_radix {
+  pkv_pool* pool = nullptr;
+  std::vector<RadixNode> nodes;
+  std::vector<int32_t> free_nodes;
+  uint64_t clock = 0;
+  int64_t serial = 0;
+  int32_t live = 0;
+};
+
+namespace {
+int32_t find_child(const pkv_radix* r, int32_t node, const int32_t* key) {
+  for (int32_t c : r->nodes[node].children)
+    if (std::memcmp(r->nodes[c].key.data(), key, sizeof(int32_t) * PKV_BLOCK_SIZE) == 0)
+      return c;
+  return -1;
+}
+
+bool only_tree_holds(const pkv_radix* r, int32_t node) {
+  const int32_t b = r->nodes[node].block;
+  return r->pool->rc[b] == 1;
+}
+
+void remove_node(pkv_radix* r, int32_t node) {
+  RadixNode& n = r->nodes[node];
+  std::vector<int32_t>& sib = r->nodes[n.parent].children;
+  for (size_t i = 0; i < sib.size(); ++i)
+    if (sib[i] == node) {
+      sib.erase(sib.begin() + i);
+      break;
+    }
+  n.alive = false;
+  n.children.clear();
+  r->free_nodes.push_back(node);
+  --r->live;
+}
+}  // namespace
+
+extern "C" {
+
+pkv_radix* pkv_radix_create(pkv_pool* pool) {
+  if (!pool) return nullptr;
+  pkv_radix* r = new (std::nothrow) pkv_radix;
+  if (!r) return nullptr;
+  r->pool = pool;
+  r->nodes.resize(1);
+  r->nodes[0].alive = true;
+  return r;
+}
+
+void pkv_radix_destroy(pkv_radix* r) {
+  if (!r) return;
+  for (size_t i = 1; i < r->nodes.size(); ++i)
+    if (r->nodes[i].alive) pkv_pool_decref(r->pool, r->nodes[i].block);
+  delete r;
+}
+
+int32_t pkv_radix_match(pkv_radix* r, const int32_t* tokens, int32_t n, int32_t* blocks,
+                        int32_t cap) {
+  if (!r || n < 0 || (n > 0 && !tokens) || cap < 0 || (cap > 0 && !blocks)) return -1;
+  ++r->clock;
+  int32_t node = 0, m = 0;
+  for (int32_t i = 0; i + PKV_BLOCK_SIZE <= n; i += PKV_BLOCK_SIZE) {
+    const int32_t c = find_child(r, node, tokens + i);
+    if (c < 0) break;
+    r->nodes[c].last = r->clock;
+    if (m < cap) blocks[m] = r->nodes[c].block;
+    ++m;
+    node = c;
+  }
+  return m;
+}
+
+pkv_status pkv_radix_insert(pkv_radix* r, const int32_t* tokens, int32_t n,
+                            const int32_t* blocks) {
+  if (!r) return PKV_ERR_NULL;
+  if (n < 0) return PKV_ERR_RANGE;
+  const int32_t nb = n / PKV_BLOCK_SIZE;
+  if (nb > 0 && (!tokens || !blocks)) return PKV_ERR_NULL;
+  // validate first: every block that would become a new node must be live
+  {
+    int32_t node = 0, i = 0;
+    for (; i < nb; ++i) {
+      const int32_t c = find_child(r, node, tokens + (size_t)i * PKV_BLOCK_SIZE);
+      if (c < 0) break;
+      node = c;
+    }
+    for (; i < nb; ++i) {
+      const int32_t b = blocks[i];
+      if (!in_range(r->pool, b)) return PKV_ERR_RANGE;
+      if (r->pool->rc[b] < 1) return PKV_ERR_REFCOUNT;
+    }
+  }
+  try {
+    ++r->clock;
+    int32_t node = 0;
+    for (int32_t i = 0; i < nb; ++i) {
+      const int32_t* key = tokens + (size_t)i * PKV_BLOCK_SIZE;
+      int32_t c = find_child(r, node, key);
+      if (c < 0) {
+        if (!r->free_nodes.empty()) {
+          c = r->free_nodes.back();
+          r->free_nodes.pop_back();
+        } else {
+          c = (int32_t)r->nodes.size();
+          r->nodes.emplace_back();
+        }
+        RadixNode& nn = r->nodes[c];
+        std::memcpy(nn.key.data(), key, sizeof(int32_t) * PKV_BLOCK_SIZE);
+        nn.block = blocks[i];
+        nn.parent = node;
+        nn.serial = r->serial++;
+        nn.alive = true;
+        r->nodes[node].children.push_back(c);
+        ++r->live;
+        pkv_pool_incref(r->pool, blocks[i]);
+      }
+      r->nodes[c].last = r->clock;
+      node = c;
+    }
+  } catch (const std::bad_alloc&) {
+    return PKV_ERR_NOMEM;
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_radix_evict(pkv_radix* r, int32_t target) {
+  if (!r || target < 0) return -1;
+  int32_t freed = 0;
+  while (freed < target) {
+    // re-scan for the least recently used evictable leaf every iteration
+    int32_t best = -1;
+    for (size_t i = 1; i < r->nodes.size(); ++i) {
+      const RadixNode& n = r->nodes[i];
+      if (!n.alive || !n.children.empty() || !only_tree_holds(r, (int32_t)i)) continue;
+      if (best < 0 || n.last < r->nodes[best].last ||
+          (n.last == r->nodes[best].last && n.serial < r->nodes[best].serial))
+        best = (int32_t)i;
+    }
+    if (best < 0) break;  // nothing evictable left
+    const int32_t b = r->nodes[best].block;
+    remove_node(r, best);
+    pkv_pool_decref(r->pool, b);
+    ++freed;
+  }
+  return freed;
+}
+
+int32_t pkv_radix_evictable(const pkv_radix* r) {
+  if (!r) return -1;
+  // post-order over the tree: a node counts if the tree alone holds its block
+  // and its whole subtree counts
+  std::vector<int32_t> order;
+  std::vector<int32_t> stack{0};
+  while (!stack.empty()) {
+    const int32_t n = stack.back();
+    stack.pop_back();
+    order.push_back(n);
+    for (int32_t c : r->nodes[n].children) stack.push_back(c);
+  }
+  std::vector<char> whole(r->nodes.size(), 1);
+  int32_t count = 0;
+  for (size_t k = order.size(); k-- > 1;) {  // children before parents; skip the root
+    const int32_t n = order[k];
+    bool ok = only_tree_holds(r, n);
+    for (int32_t c : r->nodes[n].children) ok = ok && whole[c];
+    whole[n] = ok;
+    count += ok;
+  }
+  return count;
+}
+
+int32_t pkv_radix_num_nodes(const pkv_radix* r) { return r ? r->live : -1; }
 
 // ---------------------------------------------------------------------------
 pkv_status pkv_validate_tables(const pkv_geom* g, const int32_t* bt, int32_t max_blocks,
