@@ -186,6 +186,36 @@ def bench_swap(torch, dw, reps=5):
     return {k: (round(v, 2) if isinstance(v, float) else v) for k, v in res.items()}
 
 
+def bench_shared(torch, args):
+    """Decode over a shared prefix: 64 sequences continuing one 4096-token
+    prompt, through paged_attention_decode and paged_attention_decode_shared
+    (the prompt's whole splits read once per 4 rows)."""
+    from paged_kv_chunked_amd import harness, workloads
+    w = workloads.shared_prefix_decode()
+    log(f"shared-prefix decode set-up: {w.num_blocks} blocks")
+    dw = harness.DeviceWorkload(w)
+    dw.step()
+    ms_plain = time_back_to_back(torch, lambda i: dw.decode(), args.steps)
+    ms_shared = time_back_to_back(torch, lambda i: dw.decode_shared(), args.steps)
+    nbytes = dw.decode_bytes()
+    tokens = int(sum(dw.dec_lens_host))
+    res = {
+        "workload": "shared_prefix_decode: 64 sequences forked from one 4096-token prompt, "
+                    "own tokens U[1,512], Hq 32 / Hkv 8, head_dim 128, fp16",
+        "groups": int(len(dw.dec_group_start) - 1),
+        "shared_splits": int(dw.dec_max_skip),
+        "context_tokens": tokens,
+        "unique_bytes": nbytes,
+        "ms_decode": round(ms_plain, 5),
+        "ms_decode_shared": round(ms_shared, 5),
+        "speedup": round(ms_plain / ms_shared, 3),
+        "context_tokens_per_s_shared": round(tokens / (ms_shared * 1e-3), 1),
+        "unique_GBps_shared": round(nbytes / (ms_shared * 1e-3) / 1e9, 1),
+    }
+    del dw
+    return res
+
+
 def cpu_baseline(w, target_s):
     """The oracle (numpy fp64) on the decode workload: append + attention for
     every decode row, repeated until about target_s seconds have passed."""
@@ -226,6 +256,7 @@ def main():
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-swap", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
+    ap.add_argument("--no-shared", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -329,6 +360,9 @@ def main():
             },
         }
         del dw8
+    if not args.no_shared:
+        out["decode_shared_prefix"] = bench_shared(torch, args)
+        log(f"shared-prefix decode: {out['decode_shared_prefix']}")
     if not args.no_chunk:
         wc, dwc, ms_cstep, ms_chunk, ms_ccall, flops = bench_chunk(torch, args)
         tf_kernel = flops / (ms_chunk * 1e-3) / 1e12

@@ -167,6 +167,31 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
                                   size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * paged_attention_decode_shared — paged_attention_decode for a batch in which
+ * groups of rows share a cached prefix (part 3 section 3: requests that share
+ * a prefix reuse its blocks, kept alive by reference counts).  The shared
+ * splits are read once for up to 4 rows at a time instead of once per row;
+ * the result is bit for bit that of paged_attention_decode.
+ * group_start  device int32 [num_groups+1], nondecreasing within
+ *              [0, num_seqs]: group i is rows group_start[i] .. [i+1]-1.
+ * row_skip     device int32 [num_seqs]: s_i for every row of group i, 0 for
+ *              rows in no group.  Contract: the rows of group i have the same
+ *              block-table entries for logical blocks 0 .. 24*s_i - 1 (the
+ *              first s_i 384-token splits) and context lengths > 384*s_i.
+ * max_skip     host bound of row_skip; max_group_size host bound of a group's
+ *              row count.  Other arguments as for paged_attention_decode.
+ * num_groups == 0 is plain paged_attention_decode.  Arenas other than fp16
+ * with head_dim 128 and 4 query heads per KV head compute every split per
+ * row (same result).
+ * ------------------------------------------------------------------------- */
+pkv_status paged_attention_decode_shared(
+    const pkv_geom* geom, void* out, int32_t out_dtype, const void* q, const void* k_arena,
+    const void* v_arena, const int32_t* block_table, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len, float scale,
+    const int32_t* group_start, const int32_t* row_skip, int32_t num_groups, int32_t max_skip,
+    int32_t max_group_size, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * paged_attention_chunk — prefill chunks (part 3 section 4).
  * Sequence b has C_b = cu_q_lens[b+1] - cu_q_lens[b] new rows at absolute
  * positions P_b .. P_b + C_b - 1 (P_b = chunk_start[b]); its cached prefix and

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 F16, F32, I8KV = 0, 1, 2
 BLOCK_SIZE = 16
+DECODE_SPLIT = 384   # tokens per decode split (fixed by the library, see pkv.h)
 
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_DTYPE",
           4: "PKV_ERR_RANGE", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_NOMEM",
@@ -58,6 +59,9 @@ _SIGS = {
                                                               ctypes.POINTER(ctypes.c_size_t)]),
     "paged_attention_decode": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _I32,
                                               _I32, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "paged_attention_decode_shared": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P,
+                                                     _I32, _I32, ctypes.c_float, _P, _P, _I32,
+                                                     _I32, _I32, _P, ctypes.c_size_t, _P]),
     "paged_attention_chunk_workspace_bytes": (ctypes.c_int, [_PG, _I32, _I32, _I32,
                                                              ctypes.POINTER(ctypes.c_size_t)]),
     "paged_attention_chunk": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32,
@@ -191,6 +195,21 @@ def paged_attention_decode(g: Geom, out, q, k_arena, v_arena, block_table, conte
                                         max_context_len, scale, _ptr(workspace), ws_bytes,
                                         _stream(stream)),
            "paged_attention_decode")
+
+
+def paged_attention_decode_shared(g: Geom, out, q, k_arena, v_arena, block_table, context_lens,
+                                  max_context_len: int, scale: float, group_start, row_skip,
+                                  max_skip: int, max_group_size: int, workspace=None,
+                                  stream=None) -> None:
+    """paged_attention_decode with groups of rows sharing their leading splits
+    (group_start: device int32 [G+1]; row_skip: device int32 [num_seqs])."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attention_decode_shared(
+        ctypes.byref(g), _ptr(out), F32, _ptr(q), _ptr(k_arena), _ptr(v_arena),
+        _ptr(block_table), block_table.shape[1], _ptr(context_lens), context_lens.shape[0],
+        max_context_len, scale, _ptr(group_start), _ptr(row_skip), group_start.shape[0] - 1,
+        max_skip, max_group_size, _ptr(workspace), ws_bytes, _stream(stream)),
+        "paged_attention_decode_shared")
 
 
 def paged_attention_chunk_workspace_bytes(g: Geom, num_seqs: int, num_tokens: int,

@@ -75,6 +75,31 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
                                        (hipStream_t)stream));
 }
 
+pkv_status paged_attention_decode_shared(
+    const pkv_geom* geom, void* out, int32_t out_dtype, const void* q, const void* k_arena,
+    const void* v_arena, const int32_t* block_table, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len, float scale,
+    const int32_t* group_start, const int32_t* row_skip, int32_t num_groups, int32_t max_skip,
+    int32_t max_group_size, void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_groups < 0 || max_skip < 0 || max_group_size < 0) return PKV_ERR_RANGE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_arena || !v_arena || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (num_groups > 0 && (!group_start || !row_skip)) return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || max_context_len < 1 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return PKV_ERR_RANGE;
+  const size_t need = pkv::decode_workspace_bytes(*geom, num_seqs, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  const pkv::DecodeGroups groups{group_start, row_skip, num_groups, max_skip, max_group_size};
+  return hip_status(pkv::launch_decode(*geom, (float*)out, q, k_arena, v_arena, block_table,
+                                       max_blocks_per_seq, context_lens, num_seqs,
+                                       max_context_len, scale, workspace, workspace_bytes,
+                                       (hipStream_t)stream, num_groups > 0 ? &groups : nullptr));
+}
+
 pkv_status paged_attention_chunk_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
                                                  int32_t num_tokens, int32_t max_context_len,
                                                  size_t* bytes) {

@@ -133,10 +133,13 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
     const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
-    int num_blocks) {
+    int num_blocks, const int32_t* __restrict__ row_skip) {
   const int split = blockIdx.x, b = blockIdx.y;
   const int g = blockIdx.z * kDecodeWavesPerWG + (threadIdx.x >> 6);
   if (g >= Hkv) return;
+  // splits below row_skip[b] are computed by decode_shared_kernel, once for
+  // every sequence sharing them
+  if (row_skip != nullptr && split < row_skip[b]) return;
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
@@ -193,18 +196,20 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
     // element e of this lane: token 4lq + (e & 3) of block A (e < 4) or B
     const int tok_a = (blk0 + 2 * p) * kBlock + 4 * lq;
     const int nva = L - tok_a, nvb = nva - kBlock;  // valid elements of A / B
-    float sv[8];
+    // The base-2 exponent of key e is fma(score_e, scale_log2, -m): one
+    // rounding, written out so that no kernel leaves it to the compiler's
+    // contraction choices (decode_shared_kernel must round it identically).
+    // The running max is taken over raw scores and scaled once (scale_log2 >
+    // 0 and rounding is monotone, so this is the max of the scaled scores).
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const bool ok = e < 4 ? e < nva : e - 4 < nvb;
-      const float x = ok ? s[e >> 2][e & 3] * scale_log2 : -INFINITY;
-      sv[e] = x;
-      mx = fmaxf(mx, x);
+      mx = fmaxf(mx, ok ? s[e >> 2][e & 3] : -INFINITY);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: the first key of a split is real
+    const float m_new = fmaxf(m_run, mx * scale_log2);  // finite: the first key of a split is real
     if (__any(m_new > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -216,7 +221,9 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
     float lsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m_new);
+      const bool ok = e < 4 ? e < nva : e - 4 < nvb;
+      const float arg = ok ? __builtin_fmaf(s[e >> 2][e & 3], scale_log2, -m_new) : -INFINITY;
+      const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(arg);
       pb[e] = ph;
       lsum += (float)ph;
     }
@@ -273,6 +280,123 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
   }
   if (ln < kG) {
     const size_t part = ((size_t)b * nsplit_max + split) * Hq + hq;
+    float* dst = ws_o + part * kD + 4 * lq;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db];
+    if (lq == 0) {
+      ws_ml[2 * part] = m_run;
+      ws_ml[2 * part + 1] = l_row;
+    }
+  }
+}
+
+// ---- splits shared by several sequences ---------------------------------------
+// Kshipra part 3, section 3: sequences that share a cached prefix share its
+// physical blocks.  For a group of rows whose first `skip` splits are the same
+// blocks, decode_shared_kernel reads each of those splits once for up to 4
+// rows at a time: the 16 columns of the first product, of which the per-row
+// kernel fills 4 (one row's 4 query heads), carry 4 rows x 4 heads.  Column
+// ln is row 4 * quad + (ln >> 2), head ln & 3.  Every column is computed with
+// the same instructions, operand layouts and order as the per-row kernel, so
+// the partials -- and the merged output -- are bit for bit those of
+// paged_attention_decode.  All keys of a shared split are real (a member's
+// own token comes after the shared prefix), so there is no mask.
+__global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_shared_kernel(
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, const _Float16* __restrict__ q,
+    const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ group_start, const int32_t* __restrict__ row_skip,
+    float scale_log2, int Hkv, int nsplit_max, int num_blocks, int zheads, int num_seqs) {
+  const int split = blockIdx.x, gi = blockIdx.y;
+  const int quad = blockIdx.z / zheads;
+  const int g = (blockIdx.z - quad * zheads) * kDecodeWavesPerWG + (threadIdx.x >> 6);
+  if (g >= Hkv) return;
+  // rows of the group, clamped to the batch (a bad table cannot address
+  // memory outside the buffers)
+  const int r0 = max(0, group_start[gi]), r1 = min(num_seqs, group_start[gi + 1]);
+  const int first = r0 + 4 * quad;
+  if (first >= r1) return;
+  const int skip = min(row_skip[r0], nsplit_max);
+  if (split >= skip) return;
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 15, lq = lane >> 4;
+  const int Hq = Hkv * kG;
+  const int blk0 = split * kSB;
+  const int row = first + (ln >> 2);  // this column's sequence
+  const bool col_ok = row < r1;
+  int my_blk = 0;
+  if (lane < kSB && blk0 + lane < max_blocks)
+    my_blk = block_table[(size_t)r0 * max_blocks + blk0 + lane];  // the group's shared blocks
+  if (my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
+  half8_t qb[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd)
+    qb[kd] = col_ok ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + (ln & 3)) * kD + 32 * kd + 8 * lq)
+                    : (half8_t)(_Float16)0.f;
+  constexpr int npairs = kSB / 2;  // a shared split is whole
+
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = (f32x4)0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto compute = [&](const Pair& pr) {
+    f32x4 s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = (f32x4)0.f;
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr.k[u][kd], qb[kd], s[u], 0, 0, 0);
+    }
+    // same rounding steps as decode_split_kernel: max of raw scores scaled
+    // once, exponent fma(score, scale_log2, -m)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[e >> 2][e & 3]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    }
+    m_run = m_new;
+    half8_t pb;
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 ph =
+          (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 2][e & 3], scale_log2, -m_new));
+      pb[e] = ph;
+      lsum += (float)ph;
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr.v[db], pb, o[db], 0, 0, 0);
+  };
+
+  Pair buf[2];
+  buf[0] = load_pair(k_arena, v_arena, __builtin_amdgcn_readlane(my_blk, 0),
+                     __builtin_amdgcn_readlane(my_blk, 1), Hkv, g, ln, lq);
+#pragma unroll
+  for (int p = 0; p < npairs; ++p) {
+    if (p + 1 < npairs) {
+      buf[(p + 1) & 1] = load_pair(k_arena, v_arena, __builtin_amdgcn_readlane(my_blk, 2 * p + 2),
+                                   __builtin_amdgcn_readlane(my_blk, 2 * p + 3), Hkv, g, ln, lq);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    compute(buf[p & 1]);
+  }
+
+  float l_row = l_run;
+  l_row += __shfl_xor(l_row, 16);
+  l_row += __shfl_xor(l_row, 32);
+  if (col_ok) {
+    const size_t part = ((size_t)row * nsplit_max + split) * Hq + g * kG + (ln & 3);
     float* dst = ws_o + part * kD + 4 * lq;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db];
@@ -583,7 +707,7 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
                          const void* v_arena, const int32_t* block_table, int max_blocks,
                          const int32_t* context_lens, int num_seqs, int max_context_len,
                          float scale, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, const DecodeGroups* groups) {
   if (!decode_fast_path(g))
     return launch_attend_generic(g, out, q, k_arena, v_arena, block_table, max_blocks,
                                  context_lens, nullptr, nullptr, num_seqs, num_seqs, scale,
@@ -607,6 +731,19 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
   // index across all XCDs; the extra column of workgroups exits at once.
   const int gx = nsplit | 1;
   const dim3 grid(gx, num_seqs, zg);
+  // shared splits (fp16 arenas; other dtypes compute every split per row)
+  const bool shared = groups != nullptr && g.dtype == PKV_F16 && nsplit > 1 &&
+                      groups->num_groups > 0 && groups->max_skip > 0 && groups->max_group_size > 0;
+  if (shared) {
+    const int quads = (groups->max_group_size + 3) / 4;
+    const dim3 sgrid(min(groups->max_skip, nsplit), groups->num_groups, quads * zg);
+    hipLaunchKernelGGL(decode_shared_kernel, sgrid, dim3(64 * wpg), 0, stream, ws_o, ws_ml,
+                       (const _Float16*)q, (const _Float16*)k_arena, (const _Float16*)v_arena,
+                       block_table, max_blocks, groups->group_start, groups->row_skip,
+                       scale_log2, g.num_kv_heads, nsplit, g.num_blocks, zg, num_seqs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (g.dtype == PKV_I8KV)
     hipLaunchKernelGGL(decode_split_i8_kernel, grid, dim3(64 * wpg), 0, stream,
                        out, ws_o, ws_ml, (const _Float16*)q, (const uint8_t*)k_arena,
@@ -616,7 +753,8 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
     hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64 * wpg), 0, stream,
                        out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
                        (const _Float16*)v_arena, block_table, max_blocks, context_lens,
-                       scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
+                       scale_log2, g.num_kv_heads, nsplit, g.num_blocks,
+                       shared ? groups->row_skip : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit <= 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(g.num_kv_heads, num_seqs), dim3(kCombineThreads),

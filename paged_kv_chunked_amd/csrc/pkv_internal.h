@@ -80,11 +80,21 @@ hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, con
 
 bool decode_fast_path(const pkv_geom& g);
 size_t decode_workspace_bytes(const pkv_geom& g, int num_seqs, int max_context_len);
+// Rows sharing their leading splits (decode_shared_kernel).  Device arrays:
+// group_start [num_groups + 1] (group i = rows group_start[i] .. [i+1]),
+// row_skip [num_seqs] (leading splits of the row computed with its group).
+struct DecodeGroups {
+  const int32_t* group_start;
+  const int32_t* row_skip;
+  int num_groups;
+  int max_skip;        // host bound of row_skip
+  int max_group_size;  // host bound of a group's row count
+};
 hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const void* k_arena,
                          const void* v_arena, const int32_t* block_table, int max_blocks,
                          const int32_t* context_lens, int num_seqs, int max_context_len,
                          float scale, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+                         hipStream_t stream, const DecodeGroups* groups = nullptr);
 
 bool chunk_fast_path(const pkv_geom& g);
 size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens);

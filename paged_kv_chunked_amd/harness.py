@@ -17,8 +17,8 @@ from typing import Dict, List
 
 import numpy as np
 
-from . import (BLOCK_SIZE, F16, F32, I8KV, Pool, geom, kv_append_rope, paged_attention_chunk,
-               paged_attention_chunk_workspace_bytes,
+from . import (BLOCK_SIZE, DECODE_SPLIT, F16, F32, I8KV, Pool, geom, kv_append_rope, paged_attention_chunk,
+               paged_attention_chunk_workspace_bytes, paged_attention_decode_shared,
                paged_attention_decode, paged_attention_decode_workspace_bytes, pkv_copy_blocks,
                pkv_rope_table_bytes, pkv_rope_table_init)
 from . import workloads as _wl
@@ -35,10 +35,11 @@ def default_scale(head_dim: int) -> float:
 
 
 def run_pool_script(w: _wl.Workload, pool: Pool, tables: Dict[int, List[int]],
-                    on_fill=None, on_copy=None):
+                    on_fill=None, on_copy=None, on_release=None):
     """Executes the workload's pool script on the library pool, appending to
     ``tables`` (sequence -> physical block ids).  ``on_fill(op)`` is called for
-    each fill and ``on_copy(src, dst)`` for each copy-on-write copy, in script
+    each fill, ``on_copy(src, dst)`` for each copy-on-write copy and
+    ``on_release(seq)`` before a sequence's blocks are given back, in script
     order.  Returns the list of (src, dst) copies."""
     copies = []
     for op in w.script:
@@ -69,12 +70,42 @@ def run_pool_script(w: _wl.Workload, pool: Pool, tables: Dict[int, List[int]],
                 copies.append((old, new))
             tables[seq][logical] = new
         elif kind == "release":
+            if on_release is not None:
+                on_release(op[1])
             for b in tables[op[1]]:
                 pool.decref(b)
             tables[op[1]] = []
         else:
             raise ValueError(kind)
     return copies
+
+
+def decode_groups(bt: np.ndarray, lens: np.ndarray, split: int = DECODE_SPLIT):
+    """Groups of consecutive decode rows whose leading whole splits are the
+    same physical blocks: (group_start int32 [G+1], row_skip int32 [rows]).
+    A row's skip s satisfies lens > split * s (its own token comes later);
+    single rows form groups with skip 0."""
+    n = len(lens)
+    spb = split // BLOCK_SIZE
+    own = (np.asarray(lens, np.int64) - 1) // split     # whole splits before the last key
+    starts, skip = [0], np.zeros(n, np.int32)
+    i = 0
+    while i < n:
+        j, s = i + 1, int(own[i])
+        while j < n and s > 0:
+            same = 0
+            while same < min(s, int(own[j])) and np.array_equal(
+                    bt[i, same * spb:(same + 1) * spb], bt[j, same * spb:(same + 1) * spb]):
+                same += 1
+            if same == 0:
+                break
+            s = same
+            j += 1
+        if j - i > 1:
+            skip[i:j] = s
+        starts.append(j)
+        i = j
+    return np.asarray(starts, np.int32), skip
 
 
 class DeviceWorkload:
@@ -162,8 +193,13 @@ class DeviceWorkload:
             pair = torch.tensor([[old, new]], dtype=torch.int32, device=self.device)
             pkv_copy_blocks(self.g, self.k_arena, self.v_arena, pair)
 
+        def on_release(seq):
+            # a queued fill of this sequence reads its table when flushed
+            if any(op[2] == seq for op in pending):
+                flush()
+
         self.copies = run_pool_script(w, self.pool, self.tables, on_fill=on_fill,
-                                      on_copy=on_copy)
+                                      on_copy=on_copy, on_release=on_release)
         flush()
 
     def block_table_host(self) -> np.ndarray:
@@ -210,10 +246,14 @@ class DeviceWorkload:
             self.dec_lens = torch.from_numpy(lens).to(dev)
             self.dec_max_len = int(lens.max())
             ws = paged_attention_decode_workspace_bytes(self.g, len(dec), self.dec_max_len)
-            # zero-filled once: the decode merge counters must start at zero
             self.dec_ws = (torch.zeros(max(ws, 4) // 4, dtype=torch.float32, device=dev)
                            if ws else None)
             self.dec_out = torch.empty((len(dec), Hq, D), dtype=torch.float32, device=dev)
+            gs, skip = decode_groups(self.bt_host[r0:r1], lens)
+            self.dec_group_start = torch.from_numpy(gs).to(dev)
+            self.dec_row_skip = torch.from_numpy(skip).to(dev)
+            self.dec_max_skip = int(skip.max()) if skip.size else 0
+            self.dec_max_group = int(np.diff(gs).max()) if gs.size > 1 else 1
         if chk:
             r0, r1 = chk[0], chk[-1] + 1
             t0, t1 = int(cu[r0]), int(cu[r1])
@@ -244,6 +284,18 @@ class DeviceWorkload:
                                    self.v_arena if v_arena is None else v_arena,
                                    self.dec_bt, self.dec_lens, self.dec_max_len, self.scale,
                                    self.dec_ws, stream=stream)
+
+    def decode_shared(self, stream=None, k_arena=None, v_arena=None):
+        """The decode rows through paged_attention_decode_shared (shared leading
+        splits of consecutive rows read once per 4 rows)."""
+        if self.dec_rows:
+            paged_attention_decode_shared(self.g, self.dec_out, self.dec_q,
+                                          self.k_arena if k_arena is None else k_arena,
+                                          self.v_arena if v_arena is None else v_arena,
+                                          self.dec_bt, self.dec_lens, self.dec_max_len, self.scale,
+                                          self.dec_group_start, self.dec_row_skip,
+                                          self.dec_max_skip, self.dec_max_group, self.dec_ws,
+                                          stream=stream)
 
     def chunk(self, stream=None, k_arena=None, v_arena=None):
         if self.chunk_rows:

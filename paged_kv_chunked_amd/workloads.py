@@ -316,12 +316,45 @@ def long_context(num_decodes: int = 32, context: int = 32768, chunk: int = 4096,
                  boost_prob=0.01, shuffle_rng=rng)
 
 
+def shared_prefix_decode(num_seqs: int = 64, prefix: int = 4096, lo: int = 1, hi: int = 512,
+                         seed: int = 1006) -> Workload:
+    """Decodes that all continue one cached prompt (Kshipra part 3, section 3:
+    many requests share a prefix such as a system prompt): a parent holding
+    ``prefix`` tokens (whole blocks) is forked ``num_seqs`` times and
+    released, then each child appends its own U[lo, hi] tokens and decodes
+    one more.  Hq 32 / Hkv 8, D 128, fp16, theta 5e5, arena = total + 10 %."""
+    assert prefix % BLOCK_SIZE == 0
+    rng = np.random.default_rng(seed)
+    own = rng.integers(lo, hi, size=num_seqs, endpoint=True)
+    seqs = [(prefix + int(n) - 1, 1) for n in own]   # decode token at prefix + n - 1
+    parent = num_seqs
+    pblocks = prefix // BLOCK_SIZE
+    need = [_blocks(p + c) - pblocks for p, c in seqs]
+    num_blocks = int(math.ceil(1.1 * (sum(need) + pblocks)))
+    script = [("shuffle", rng.permutation(num_blocks).astype(np.int64)),
+              ("alloc", np.full(pblocks, parent, np.int64)),
+              ("fill", 0, parent, 0, prefix)]
+    for b in range(num_seqs):
+        script.append(("fork", b, parent))
+    script.append(("release", parent))
+    script.append(("alloc", _round_robin(need, range(num_seqs))))
+    for b, (p, c) in enumerate(seqs):
+        if p > prefix:
+            script.append(("fill", 1 + b, b, prefix, p - prefix))
+    step = tuple(StepSeq(b, p, c) for b, (p, c) in enumerate(seqs))
+    return Workload(name="shared_prefix_decode", seed=seed, dtype="f16", num_q_heads=32,
+                    num_kv_heads=8, head_dim=128, theta=5.0e5, num_blocks=num_blocks,
+                    max_blocks_per_seq=_blocks(prefix + hi), num_pool_seqs=num_seqs + 1,
+                    script=script, step=step)
+
+
 NAMED = {
     "tiny": tiny,
     "decode": decode_batch,
     "chunk": chunk_batch,
     "mixed": mixed_step,
     "long": long_context,
+    "shared": shared_prefix_decode,
 }
 
 
