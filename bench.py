@@ -353,7 +353,7 @@ def main():
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",
                 "frac": round(ach8 / PEAK_HBM_GBS, 4),
-                "traffic": None,
+                "traffic": load_traffic(TRAFFIC, "paged_attention_decode_i8"),
                 "algorithmic_bytes_per_launch": nbytes8,
                 "avg_launch_ms": round(ms_dec8, 5),
                 "avg_launch_ms_isolated": round(ms_dcall8, 5),

@@ -1,8 +1,8 @@
 """Summaries of rocprofv3 result databases for profiles/.
 
-    python -m paged_kv_chunked_amd.rocprof_summary stats DB OUT.md --command "..."
-        per-kernel dispatch count and average / min / max / total duration
-        (a --kernel-trace --stats run).
+    python -m paged_kv_chunked_amd.rocprof_summary stats DB OUT.md --command "..." [--note ...]
+        dispatch count and average / min / max / total duration per (kernel,
+        grid) (a --kernel-trace --stats run).
     python -m paged_kv_chunked_amd.rocprof_summary traffic FETCH_DB WRITE_DB OUT.json \
             --copy-mib N --command "..."
         HBM bytes per dispatch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE).
@@ -10,7 +10,9 @@
         that bench.py --calibrate-copy-mib N performs first (the first
         __amd_rocclr_copyBuffer dispatch): scale = N MiB / counter value.  The
         record stores the SHA-256 of the kernel sources, so bench.py only uses
-        it while those sources are unchanged.
+        it while those sources are unchanged.  Dispatches are averaged per
+        kernel name, so the profiled command must run each kernel on one
+        workload only (bench.py --no-shared --no-swap).
 
 rocprofv3 writes one SQLite database per process; its ``kernels`` and
 ``pmc_events`` views are read here.
@@ -31,6 +33,8 @@ CSRC = os.path.join(HERE, "csrc")
 CALLS = {
     "paged_attention_decode": (("decode_split_kernel", "decode_combine_kernel"),
                                ("decode.hip", "pkv_internal.h")),
+    "paged_attention_decode_i8": (("decode_split_i8_kernel", "decode_combine_kernel"),
+                                  ("decode.hip", "pkv_internal.h")),
     "paged_attention_chunk": (("chunk_mfma_kernel",), ("chunk.hip", "pkv_internal.h")),
     "kv_append_rope": (("append_rope_kernel",), ("append.hip", "pkv_internal.h")),
 }
@@ -46,19 +50,22 @@ def sources_sha(files) -> str:
 
 def kernel_rows(db):
     c = sqlite3.connect(db)
-    return c.execute("select name, duration from kernels").fetchall()
+    return c.execute("select name, grid_x, grid_y, grid_z, duration from kernels").fetchall()
 
 
-def stats(db, out, command):
+def stats(db, out, command, notes=()):
+    """One line per (kernel, grid): launches of one kernel on different
+    workloads have different grids and are kept apart."""
     agg = collections.defaultdict(list)
-    for name, dur in kernel_rows(db):
-        agg[name].append(dur)
-    lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
-             "| kernel | calls | avg (us) | min (us) | max (us) | total (ms) |",
-             "|---|---|---|---|---|---|"]
-    for name, durs in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+    for name, gx, gy, gz, dur in kernel_rows(db):
+        agg[(name, f"{gx}x{gy}x{gz}")].append(dur)
+    lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", ""]
+    lines += [f"- {n}" for n in notes] + ([""] if notes else [])
+    lines += ["| kernel | grid (threads) | calls | avg (us) | min (us) | max (us) | total (ms) |",
+              "|---|---|---|---|---|---|---|"]
+    for (name, grid), durs in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         short = name if len(name) < 110 else name[:107] + "..."
-        lines.append(f"| `{short}` | {len(durs)} | {sum(durs) / len(durs) / 1e3:.2f} | "
+        lines.append(f"| `{short}` | {grid} | {len(durs)} | {sum(durs) / len(durs) / 1e3:.2f} | "
                      f"{min(durs) / 1e3:.2f} | {max(durs) / 1e3:.2f} | {sum(durs) / 1e6:.3f} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -120,6 +127,7 @@ def main():
     a.add_argument("db")
     a.add_argument("out")
     a.add_argument("--command", required=True)
+    a.add_argument("--note", action="append", default=[])
     b = sub.add_parser("traffic")
     b.add_argument("fetch_db")
     b.add_argument("write_db")
@@ -128,7 +136,7 @@ def main():
     b.add_argument("--command", required=True)
     args = ap.parse_args()
     if args.cmd == "stats":
-        stats(args.db, args.out, args.command)
+        stats(args.db, args.out, args.command, args.note)
     else:
         traffic(args.fetch_db, args.write_db, args.out, args.copy_mib, args.command)
 
