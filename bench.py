@@ -216,6 +216,43 @@ def bench_shared(torch, args):
     return res
 
 
+def bench_mixed(torch, args):
+    """One continuous-batching step (4 chunks of 256 + 1024 decodes, 16 of them
+    sharing a prefix): the separate chunk and decode calls, back to back,
+    against one paged_attention_mixed call.  The step's roofline is the sum of
+    the decode bytes at HBM peak and the chunk flops at fp16 MFMA peak (no
+    credit for overlapping them)."""
+    from paged_kv_chunked_amd import harness, workloads
+    w = workloads.mixed_step()
+    log(f"mixed step set-up: {w.num_blocks} blocks")
+    dw = harness.DeviceWorkload(w)
+    dw.step()
+    dw.mixed()
+    ms_sep = time_back_to_back(torch, lambda i: (dw.chunk(), dw.decode()), max(args.steps // 5, 5))
+    ms_mix = time_back_to_back(torch, lambda i: dw.mixed(), max(args.steps // 5, 5))
+    nbytes, flops = dw.decode_bytes(), dw.chunk_flops()
+    roof_ms = (nbytes / (PEAK_HBM_GBS * 1e9) + flops / (PEAK_F16_TFLOPS * 1e12)) * 1e3
+    res = {
+        "workload": "mixed_step: 4 chunks x 256 rows (P = 16*U{0..496}) + 1024 decodes "
+                    "(contexts U[256,8192], 16 sharing a 1024-token prefix), Hq 32 / Hkv 8, "
+                    "head_dim 128, fp16",
+        "decode_bytes": nbytes,
+        "chunk_flops": flops,
+        "ms_separate_calls": round(ms_sep, 5),
+        "ms_mixed_call": round(ms_mix, 5),
+        "speedup": round(ms_sep / ms_mix, 3),
+        "roofline": {
+            "kernel": "paged_attention_mixed (mixed_order_kernel + mixed_kernel + "
+                      "decode_combine_kernel)",
+            "bound": "hbm+mfma",
+            "roofline_ms": round(roof_ms, 5),
+            "frac": round(roof_ms / ms_mix, 4),
+        },
+    }
+    del dw
+    return res
+
+
 def cpu_baseline(w, target_s):
     """The oracle (numpy fp64) on the decode workload: append + attention for
     every decode row, repeated until about target_s seconds have passed."""
@@ -257,6 +294,7 @@ def main():
     ap.add_argument("--no-swap", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-shared", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -363,6 +401,9 @@ def main():
     if not args.no_shared:
         out["decode_shared_prefix"] = bench_shared(torch, args)
         log(f"shared-prefix decode: {out['decode_shared_prefix']}")
+    if not args.no_mixed:
+        out["mixed_step"] = bench_mixed(torch, args)
+        log(f"mixed step: {out['mixed_step']}")
     if not args.no_chunk:
         wc, dwc, ms_cstep, ms_chunk, ms_ccall, flops = bench_chunk(torch, args)
         tf_kernel = flops / (ms_chunk * 1e-3) / 1e12

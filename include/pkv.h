@@ -202,12 +202,41 @@ pkv_status paged_attention_decode_shared(
  * q            device [num_tokens][Hq][D], already rotated.
  * max_q_len    host upper bound of C_b; max_context_len host upper bound of
  *              P_b + C_b, <= max_blocks_per_seq * 16.
- * workspace    as for decode (current kernels need 0 bytes).
+ * workspace    device memory of paged_attention_chunk_workspace_bytes()
+ *              bytes (the schedule of the tuned kernel: one int32 per
+ *              (sequence, 64-row tile)); PKV_ERR_WORKSPACE if missing or short.
  * ------------------------------------------------------------------------- */
 pkv_status paged_attention_chunk_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
                                                  int32_t num_tokens, int32_t max_context_len,
                                                  size_t* bytes);
 pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                 const void* q, const void* k_arena, const void* v_arena,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* cu_q_lens, const int32_t* chunk_start,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                                 int32_t max_context_len, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * paged_attention_mixed — one continuous-batching step (part 3 section 5: each
+ * step mixes prefill chunks and decode tokens under a token budget) in one
+ * attention launch.  Arguments, layouts and result are those of
+ * paged_attention_chunk; a sequence with C_b = 1 is a decode (its row sees
+ * keys 0 .. P_b, computed in 384-token splits exactly as
+ * paged_attention_decode computes a row of context P_b + 1), a sequence with
+ * C_b >= 2 a prefill chunk (computed exactly as paged_attention_chunk does).
+ * Results are bit for bit those of the two stand-alone calls.
+ * workspace    device memory of paged_attention_mixed_workspace_bytes()
+ *              bytes: the schedule and the decode partials.  Sized from
+ *              num_seqs, num_tokens and max_context_len; PKV_ERR_WORKSPACE if
+ *              missing or short.
+ * Other shapes (not fp16 / head_dim 128 / 4 query heads per KV head) run the
+ * generic kernel over every row, as paged_attention_chunk does.
+ * ------------------------------------------------------------------------- */
+pkv_status paged_attention_mixed_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
+                                                 int32_t num_tokens, int32_t max_context_len,
+                                                 size_t* bytes);
+pkv_status paged_attention_mixed(const pkv_geom* geom, void* out, int32_t out_dtype,
                                  const void* q, const void* k_arena, const void* v_arena,
                                  const int32_t* block_table, int32_t max_blocks_per_seq,
                                  const int32_t* cu_q_lens, const int32_t* chunk_start,

@@ -67,6 +67,11 @@ _SIGS = {
     "paged_attention_chunk": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32,
                                              _I32, _I32, _I32, ctypes.c_float, _P,
                                              ctypes.c_size_t, _P]),
+    "paged_attention_mixed_workspace_bytes": (ctypes.c_int, [_PG, _I32, _I32, _I32,
+                                                             ctypes.POINTER(ctypes.c_size_t)]),
+    "paged_attention_mixed": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32,
+                                             _I32, _I32, _I32, ctypes.c_float, _P,
+                                             ctypes.c_size_t, _P]),
     "pkv_copy_blocks": (ctypes.c_int, [_PG, _P, _P, _P, _I32, _P]),
     "pkv_swap_bytes": (ctypes.c_int, [_PG, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_swap_out": (ctypes.c_int, [_PG, _P, _P, _P, _I32, _P, ctypes.c_size_t, _P]),
@@ -240,6 +245,37 @@ def paged_attention_chunk(g: Geom, out, q, k_arena, v_arena, block_table, cu_q_l
                                        q.shape[0], max_q_len, max_context_len, scale,
                                        _ptr(workspace), ws_bytes, _stream(stream)),
            "paged_attention_chunk")
+
+
+def paged_attention_mixed_workspace_bytes(g: Geom, num_seqs: int, num_tokens: int,
+                                          max_context_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().paged_attention_mixed_workspace_bytes(ctypes.byref(g), num_seqs, num_tokens,
+                                                       max_context_len, ctypes.byref(n)),
+           "paged_attention_mixed_workspace_bytes")
+    return n.value
+
+
+def paged_attention_mixed(g: Geom, out, q, k_arena, v_arena, block_table, cu_q_lens,
+                          chunk_start, max_q_len: int, max_context_len: int, scale: float,
+                          workspace=None, stream=None) -> None:
+    """One varlen batch of prefill chunks and decodes (sequences of one row) in
+    one attention launch; arguments as paged_attention_chunk.  ``workspace``:
+    a device tensor of at least paged_attention_mixed_workspace_bytes(...)
+    bytes; None makes a fresh one from torch's allocator."""
+    if workspace is None:
+        need = paged_attention_mixed_workspace_bytes(g, chunk_start.shape[0], q.shape[0],
+                                                     max_context_len)
+        if need:
+            import torch
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attention_mixed(ctypes.byref(g), _ptr(out), F32, _ptr(q), _ptr(k_arena),
+                                       _ptr(v_arena), _ptr(block_table), block_table.shape[1],
+                                       _ptr(cu_q_lens), _ptr(chunk_start), chunk_start.shape[0],
+                                       q.shape[0], max_q_len, max_context_len, scale,
+                                       _ptr(workspace), ws_bytes, _stream(stream)),
+           "paged_attention_mixed")
 
 
 def pkv_copy_blocks(g: Geom, k_arena, v_arena, src_dst, stream=None) -> None:

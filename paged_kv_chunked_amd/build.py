@@ -21,12 +21,17 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = "gfx950"
-SOURCES = ["host.cpp", "api.hip", "append.hip", "decode.hip", "chunk.hip", "generic.hip",
-           "copy.hip"]
+SOURCES = ["host.cpp", "api.hip", "append.hip", "decode.hip", "chunk.hip", "mixed.hip",
+           "generic.hip", "copy.hip"]
 # Per-file device flags.  The chunk kernel never lets a NaN reach a max (masked
 # scores are replaced by -inf with a select, V past the sequence is zeroed as
-# integers), so its device code may drop the quieting of max operands.
-EXTRA_DEVICE_FLAGS = {"chunk.hip": ["-fno-honor-nans"]}
+# integers), so its device code may drop the quieting of max operands.  The
+# mixed-batch kernel runs the same chunk code and is built the same way; its
+# work-queue atomic must stay a plain atomic whose result is awaited only where
+# it is used (the compiler's wave aggregation of atomics would wait at once);
+# that backend option is passed to the compiler as is.
+EXTRA_DEVICE_FLAGS = {"chunk.hip": ["-fno-honor-nans"], "mixed.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"mixed.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def hipcc() -> str:
@@ -49,6 +54,7 @@ def _compile(src: str) -> str:
         cmd[1:1] = ["-x", "hip"]
     for f in EXTRA_DEVICE_FLAGS.get(src, []):
         cmd += ["-Xarch_device", f]
+    cmd += EXTRA_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -136,6 +136,42 @@ pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dt
                                       workspace_bytes, (hipStream_t)stream));
 }
 
+pkv_status paged_attention_mixed_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
+                                                 int32_t num_tokens, int32_t max_context_len,
+                                                 size_t* bytes) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (!bytes) return PKV_ERR_NULL;
+  if (num_seqs < 0 || num_tokens < 0 || max_context_len < 0) return PKV_ERR_RANGE;
+  *bytes = pkv::mixed_workspace_bytes(*geom, num_seqs, num_tokens, max_context_len);
+  return PKV_OK;
+}
+
+pkv_status paged_attention_mixed(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                 const void* q, const void* k_arena, const void* v_arena,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* cu_q_lens, const int32_t* chunk_start,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                                 int32_t max_context_len, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0) return PKV_ERR_RANGE;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_arena || !v_arena || !block_table || !cu_q_lens || !chunk_start)
+    return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || max_q_len < 1 || max_context_len < max_q_len ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return PKV_ERR_RANGE;
+  const size_t need = pkv::mixed_workspace_bytes(*geom, num_seqs, num_tokens, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  return hip_status(pkv::launch_mixed(*geom, (float*)out, q, k_arena, v_arena, block_table,
+                                      max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs,
+                                      num_tokens, max_q_len, max_context_len, scale, workspace,
+                                      workspace_bytes, (hipStream_t)stream));
+}
+
 pkv_status pkv_copy_blocks(const pkv_geom* geom, void* k_arena, void* v_arena,
                            const int32_t* src_dst, int32_t n, void* stream) {
   pkv_status st = check_geom(geom);

@@ -1,0 +1,387 @@
+// Core of the tuned chunk prefill: one (sequence, 64-row tile, KV head) unit,
+// used by paged_attention_chunk and by the mixed-batch kernel (the design is
+// described at the top of chunk.hip).  A workgroup of kThreads runs one unit;
+// the unit owns the workgroup's 128 KiB of LDS.
+#pragma once
+
+#include "fp16_shape.h"
+
+namespace pkv {
+namespace {
+
+#ifndef PKV_CHUNK_RB
+#define PKV_CHUNK_RB 2
+#endif
+constexpr int kRB = PKV_CHUNK_RB;  // 16-row blocks per wave
+constexpr int kBM = 16 * kRB;      // rows per wave
+constexpr int kRows = 64;          // chunk rows per workgroup
+constexpr int kRowGroups = kRows / kBM;  // waves per query head in a workgroup
+constexpr int kBN = 64;            // keys per tile (4 arena blocks)
+constexpr int kWaves = kG * kRowGroups;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLoadsPerTile = 2 * 16 / kWaves;  // direct-to-LDS loads per wave per tile
+constexpr int kStages = 4;         // LDS ring depth (tiles)
+constexpr int kUnitsPerBlock = kBlock * kD * 2 / 16;  // 16-byte units in one (block, head) tile
+constexpr int kStageUnits = 2 * 4 * kUnitsPerBlock;    // K and V of 4 blocks
+
+// Reductions over the four lanes {l, l^16, l^32, l^48} that hold one row,
+// through the gfx950 cross-row lane swaps (no LDS round trip).
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Three-way maximum as one v_max3_f32.  fmaxf would first quiet each operand
+// (the compiler cannot tell that matrix-core results are never signalling
+// NaNs), doubling the instruction count of the row maximum.
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// One 16-byte direct-to-LDS load per lane: lane i's 16 bytes from `src` land
+// at LDS byte address lds + 16 i.  Issued from asm so that the compiler does
+// not drain the vector-memory counter before every LDS read; the kernel waits
+// for these loads itself (wait_vm) before the barrier that publishes a tile.
+__device__ inline void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// How far (log2 units) a row's running maximum may lag the true maximum before
+// the accumulator is rescaled: probabilities stay <= 2^8, well inside fp16.
+constexpr float kSlack = 8.f;
+
+// Work of row tile rt of sequence b, in 64-key tiles (0 if the tile is empty).
+// The same arithmetic decides the tile loop of the attention kernel.
+__device__ inline int chunk_item_cost(const int32_t* __restrict__ cu_q_lens,
+                                      const int32_t* __restrict__ chunk_start, int b, int rt,
+                                      int max_blocks, int num_tokens) {
+  const int row0 = cu_q_lens[b];
+  const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
+  if (rt * kRows >= C) return 0;
+  const int P = chunk_start[b];
+  const int Lc = min(P + C, max_blocks * kBlock);
+  if (Lc <= 0) return 0;
+  const int kend = min(Lc, P + min(C, rt * kRows + kRows));
+  return max(1, (kend + kBN - 1) / kBN);
+}
+
+// Zero the halves of a 16-byte V unit (8 consecutive keys key0..key0+7) whose
+// key is >= limit.
+__device__ inline u32x4 mask_unit(u32x4 x, int key0, int limit) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int k = key0 + 2 * c;
+    uint32_t w = x[c];
+    if (k >= limit) w = 0u;
+    else if (k + 1 >= limit) w &= 0xFFFFu;
+    x[c] = w;
+  }
+  return x;
+}
+
+// Row tile rt of sequence b for KV head g.
+__device__ __forceinline__ void chunk_tile_unit(
+    float* __restrict__ out, const _Float16* __restrict__ q,
+    const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
+    float scale_log2, int Hkv, int num_blocks, int num_tokens, int b, int rt, int g) {
+  const int row0 = cu_q_lens[b];
+  const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
+  if (rt * kRows >= C) return;
+  const int P = chunk_start[b];
+  const int Lc = min(P + C, max_blocks * kBlock);  // keys that exist
+  if (Lc <= 0) return;
+  // the wave index is made visibly uniform, so block-table reads indexed by
+  // it are scalar loads (they must not add to the vector-memory count)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int Hq = Hkv * kG;
+  const int h = g * kG + (wave & 3);
+  const int wrow0 = rt * kRows + kBM * (wave >> 2);  // (kRowGroups waves per head)  // first chunk row of this wave
+
+  // 4 stages x (K: 4 blocks x 256 units, then V: 4 blocks x 256 units)
+  __shared__ u32x4 ring[kStages * kStageUnits];  // 128 KiB
+
+  const int row_hi = min(C, rt * kRows + kRows);
+  const int kend = min(Lc, P + row_hi);  // keys [0, kend) are visible to some row
+  const int ntiles = (kend + kBN - 1) / kBN;
+  const int nblk_seq = (Lc + kBlock - 1) / kBlock;
+  const int32_t* bt = block_table + (size_t)b * max_blocks;
+
+  // Tile loads.  Each block's K and V tiles are 4 quarters of 1 KiB; wave w
+  // moves quarters w * kQuarters .. +kQuarters-1 of the 16 (block = index / 4);
+  // a lane's unit goes to position pos of the block's 256 units:
+  //   K: pos = piece * 16 + slot', fetched from slot' ^ 4 in odd blocks, so
+  //      the two blocks an operand read touches use disjoint banks;
+  //   V: pos = (dim * 2 + half + 16 (block & 1)) mod 256: the odd blocks'
+  //      units are rotated by 16, so the two blocks an operand read touches
+  //      use disjoint banks (measured conflict-free on gfx950).
+  // Past the sequence's last block the id of that last block is used (its
+  // contents never reach the output: scores masked, V zeroed).
+  constexpr int kQuarters = 16 / kWaves;  // 1 KiB quarters of block tiles per wave
+  const int dma_blk = (wave * kQuarters) >> 2;
+  const uint32_t ring_lds =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)ring;
+  auto issue_tile = [&](int t) {
+    int blk = bt[min(t * 4 + dma_blk, nblk_seq - 1)];
+    blk = (blk < 0 || blk >= num_blocks) ? 0 : blk;
+    const u32x4* kt = (const u32x4*)k_arena + ((size_t)blk * Hkv + g) * kUnitsPerBlock;
+    const u32x4* vt = (const u32x4*)v_arena + ((size_t)blk * Hkv + g) * kUnitsPerBlock;
+    const uint32_t st = ring_lds + (uint32_t)((t % kStages) * kStageUnits * 16);
+#pragma unroll
+    for (int j = 0; j < kQuarters; ++j) {
+      const int qq = (wave * kQuarters + j) & 3;
+      const int pos = qq * 64 + lane;
+      const uint32_t off = (uint32_t)((dma_blk * kUnitsPerBlock + qq * 64) * 16);
+      dma16(kt + (pos ^ (4 * (dma_blk & 1))), __builtin_amdgcn_readfirstlane(st + off));
+      dma16(vt + ((pos - 16 * (dma_blk & 1)) & (kUnitsPerBlock - 1)),
+            __builtin_amdgcn_readfirstlane(st + 4 * kUnitsPerBlock * 16 + off));
+    }
+  };
+
+  // Q^T as the B operand: qf[rb][kd] = Q[row wrow0 + 16rb + lr][dims 32kd + 8lq .. +8]
+  half8_t qf[kRB][4];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int r = wrow0 + 16 * rb + lr;
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) {
+      if (r < C) {
+        qf[rb][kd] = __builtin_bit_cast(
+            half8_t, *(const u32x4*)(q + ((size_t)(row0 + r) * Hq + h) * kD + 32 * kd + 8 * lq));
+      } else {
+        qf[rb][kd] = (half8_t)(_Float16)0.f;
+      }
+    }
+  }
+  // every query load is complete before the first tile load is issued, so the
+  // tile waits below count tile loads only
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+  if (ntiles > 2) issue_tile(2);
+
+  // absolute positions of this lane's two rows (rows past the chunk borrow the
+  // last valid position so they stay finite; they are never stored)
+  int prow[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) prow[rb] = min(P + wrow0 + 16 * rb + lr, Lc - 1);
+  const int first_pos = P + wrow0;  // smallest row position of this wave
+
+  f32x4 oacc[8][kRB];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) oacc[db][rb] = (f32x4)0.f;
+  // Per row: running maximum of the raw scores, the raw score above which
+  // the accumulator must be rescaled, -max * scale_log2, and the denominator.
+  float m_raw[kRB], m_lim[kRB], m_off[kRB], l_run[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    m_raw[rb] = -INFINITY;
+    m_lim[rb] = -INFINITY;
+    m_off[rb] = 0.f;
+    l_run[rb] = 0.f;
+  }
+  const float slack_raw = kSlack / scale_log2;
+  const half2_t ones = {(_Float16)1.f, (_Float16)1.f};
+
+  // Operand addresses (16-byte units within a stage).  K fragment of MFMA kb,
+  // dim piece 4kd + lq: MFMA row m = lr holds key slot
+  // 8((m >> 2) & 1) + 4(kb & 1) + (m & 3) of block 2(kb >> 1) + (m >> 3).
+  const int ka = lr >> 3;  // block offset within the pair of blocks
+  const int kslot0 = 8 * ((lr >> 2) & 1) + (lr & 3);
+  // V fragment of dims block db for the keys of MFMA u: 16-byte unit
+  // (2 (16db + lr) + (lq & 1) + 16 (lq >> 1)) mod 256 of block 2u + (lq >> 1)
+  const int vunit = 2 * lr + (lq & 1) + 16 * (lq >> 1);
+
+  for (int t = 0; t < ntiles; ++t) {
+    // tile t's loads (this wave's) are done; then every wave's, and every
+    // wave has finished tile t - 1, whose stage the next load reuses
+    if (t + 2 < ntiles) wait_vm<2 * kLoadsPerTile>();
+    else if (t + 1 < ntiles) wait_vm<kLoadsPerTile>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 3 < ntiles) issue_tile(t + 3);
+    const u32x4* kl = ring + (t % kStages) * kStageUnits;
+    const u32x4* vl = kl + 4 * kUnitsPerBlock;
+    if (t * kBN + kBN > Lc) {
+      // last tile: zero V of keys past the sequence (2 units per thread)
+      u32x4* vw = ring + (t % kStages) * kStageUnits + 4 * kUnitsPerBlock;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int unit = tid + e * kThreads;  // [block][dim][half']
+        const int a = unit >> 8, hs = unit & 1;  // block, half (8 keys) of the unit
+        const int key0 = t * kBN + 16 * a + 8 * hs;
+        if (key0 + 8 > Lc) vw[unit] = mask_unit(vw[unit], key0, Lc);
+      }
+      __syncthreads();
+    }
+
+    // S^T[key][row] = K . Q^T (raw scores).  The K fragments of MFMA kb + 1
+    // are read while kb's products run.
+    f32x4 sacc[4][kRB];
+    half8_t kf[2][4];
+    auto read_k = [&](int kb, half8_t* f) {
+      const int a = 2 * (kb >> 1) + ka;
+      const int s = (kslot0 + 4 * (kb & 1)) ^ (4 * (a & 1));
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd)
+        f[kd] = __builtin_bit_cast(half8_t, kl[a * kUnitsPerBlock + (4 * kd + lq) * 16 + s]);
+    };
+    read_k(0, kf[0]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb < 3) read_k(kb + 1, kf[(kb + 1) & 1]);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) sacc[kb][rb] = (f32x4)0.f;
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb & 1][kd], qf[rb][kd], sacc[kb][rb], 0, 0, 0);
+    }
+    // the first two V fragment pairs are read during the softmax
+    half8_t vf[3][2];
+    auto read_v = [&](int db, half8_t* f) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int a = 2 * u + (lq >> 1);
+        f[u] = __builtin_bit_cast(half8_t, vl[a * kUnitsPerBlock + ((32 * db + vunit) & (kUnitsPerBlock - 1))]);
+      }
+    };
+    read_v(0, vf[0]);
+    read_v(1, vf[1]);
+    // Instruction order of this block: each LDS read is issued about two
+    // products ahead of the first product that needs it, so the read latency
+    // hides behind matrix-core work (the scheduler would otherwise place
+    // every read right before its use).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kRB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+
+    // Causal mask (and keys past the sequence) only where the tile reaches
+    // past this wave's smallest row position.  Score (kb, i) of this lane is
+    // key 16(2(kb >> 1) + (lq >> 1)) + 8(lq & 1) + 4(kb & 1) + i of the tile.
+    if (t * kBN + kBN - 1 > first_pos || t * kBN + kBN > Lc) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key0 = t * kBN + 16 * (2 * (kb >> 1) + (lq >> 1)) + 8 * (lq & 1) + 4 * (kb & 1);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + i > prow[rb]) sacc[kb][rb][i] = -INFINITY;
+      }
+    }
+
+    // online softmax per row (this lane: rows 16rb + lr, 16 keys each).  The
+    // running maximum is only raised when some score exceeds it by more than
+    // kSlack; both the numerator and the denominator use the same (possibly
+    // stale) maximum, so the quotient is unchanged.
+    float mloc[kRB];
+    bool raise = false;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const f32x4 s0 = sacc[0][rb], s1 = sacc[1][rb], s2 = sacc[2][rb], s3 = sacc[3][rb];
+      const float a0 = max3f(s0[0], s0[1], s0[2]), a1 = max3f(s0[3], s1[0], s1[1]);
+      const float a2 = max3f(s1[2], s1[3], s2[0]), a3 = max3f(s2[1], s2[2], s2[3]);
+      const float a4 = max3f(s3[0], s3[1], s3[2]);
+      mloc[rb] = max3f(max3f(a0, a1, a2), max3f(a3, a4, s3[3]), a0);
+      raise = raise || mloc[rb] > m_lim[rb];
+    }
+    if (__any(raise)) {
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const float mx = max_xor16(max_xor32(mloc[rb]));
+        const float m_new = fmaxf(m_raw[rb], mx);  // finite: key 0 is in tile 0 for every row
+        const float alpha = __builtin_amdgcn_exp2f((m_raw[rb] - m_new) * scale_log2);
+        m_raw[rb] = m_new;
+        m_lim[rb] = m_new + slack_raw;
+        m_off[rb] = -m_new * scale_log2;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[db][rb] *= alpha;
+      }
+    }
+
+    // pb[u][rb]: B operand of the second product, keys 8(lq & 1) .. +7 of
+    // block 2u + (lq >> 1) = scores (kb = 2u, i = 0..3), (kb = 2u + 1, i = 0..3)
+    half8_t pb[2][kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const half2_t ph = {
+              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i], scale_log2, m_off[rb])),
+              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i + 1], scale_log2, m_off[rb]))};
+          lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
+          pb[kb >> 1][rb][4 * (kb & 1) + i] = ph[0];
+          pb[kb >> 1][rb][4 * (kb & 1) + i + 1] = ph[1];
+        }
+      l_run[rb] += lsum;
+    }
+
+    // O^T[dim][row] += V^T[dim][key] . P^T[key][row].  The V fragments of dims
+    // block db + 2 are read before block db's four products (scheduling
+    // barriers keep that order).
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      if (db + 2 < 8) read_v(db + 2, vf[(db + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % 3][u], pb[u][rb], oacc[db][rb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float l = sum_xor16(sum_xor32(l_run[rb]));
+    const float inv = 1.f / l;
+    const int r = wrow0 + 16 * rb + lr;
+    if (r < C) {
+      float* dst = out + ((size_t)(row0 + r) * Hq + h) * kD + 4 * lq;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const f32x4 v = oacc[db][rb] * inv;
+        *(f32x4*)(dst + 16 * db) = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace pkv

@@ -96,9 +96,28 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
                          float scale, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, const DecodeGroups* groups = nullptr);
 
+// Merge of decode split partials (decode_combine_kernel): decode rows, or the
+// one-row sequences of a varlen batch when cu_q_lens != nullptr (lens then
+// holds chunk starts).
+hipError_t launch_decode_combine(const pkv_geom& g, float* out, const float* ws_o,
+                                 const float* ws_ml, const int32_t* lens,
+                                 const int32_t* cu_q_lens, int num_tokens, int max_blocks,
+                                 int num_seqs, int nsplit_max, hipStream_t stream);
+
 bool chunk_fast_path(const pkv_geom& g);
 size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens);
 hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
+                        const void* v_arena, const int32_t* block_table, int max_blocks,
+                        const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
+                        int num_tokens, int max_q_len, int max_context_len, float scale,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+// One attention launch for a varlen batch of prefill chunks and decodes
+// (sequences of one row), with a schedule and decode partials in the workspace.
+bool mixed_fast_path(const pkv_geom& g);
+size_t mixed_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens,
+                             int max_context_len);
+hipError_t launch_mixed(const pkv_geom& g, float* out, const void* q, const void* k_arena,
                         const void* v_arena, const int32_t* block_table, int max_blocks,
                         const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
                         int num_tokens, int max_q_len, int max_context_len, float scale,

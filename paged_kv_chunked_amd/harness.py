@@ -19,6 +19,7 @@ import numpy as np
 
 from . import (BLOCK_SIZE, DECODE_SPLIT, F16, F32, I8KV, Pool, geom, kv_append_rope, paged_attention_chunk,
                paged_attention_chunk_workspace_bytes, paged_attention_decode_shared,
+               paged_attention_mixed, paged_attention_mixed_workspace_bytes,
                paged_attention_decode, paged_attention_decode_workspace_bytes, pkv_copy_blocks,
                pkv_rope_table_bytes, pkv_rope_table_init)
 from . import workloads as _wl
@@ -229,10 +230,12 @@ class DeviceWorkload:
 
         dec = w.decode_rows()
         chk = w.chunk_rows()
-        # decode rows and chunk rows must each be contiguous in the step
-        for rows in (dec, chk):
-            if rows and rows != list(range(rows[0], rows[-1] + 1)):
-                raise ValueError("step rows of one kind must be contiguous")
+        # the separate decode and chunk calls need the rows of each kind to be
+        # contiguous in the step; paged_attention_mixed takes any order
+        self.split_ok = all(not rows or rows == list(range(rows[0], rows[-1] + 1))
+                            for rows in (dec, chk))
+        if not self.split_ok:
+            dec, chk = [], []
         self.dec_rows, self.chunk_rows = dec, chk
         Hq, D = w.num_q_heads, w.head_dim
         if dec:
@@ -277,7 +280,12 @@ class DeviceWorkload:
                        self.bt, self.cu, self.starts, self.rope, self.rope_max_pos,
                        q_out=self.q, stream=stream)
 
+    def _need_split(self):
+        if not self.split_ok:
+            raise ValueError("step rows of one kind must be contiguous for the separate calls")
+
     def decode(self, stream=None, k_arena=None, v_arena=None):
+        self._need_split()
         if self.dec_rows:
             paged_attention_decode(self.g, self.dec_out, self.dec_q,
                                    self.k_arena if k_arena is None else k_arena,
@@ -297,7 +305,28 @@ class DeviceWorkload:
                                           self.dec_max_skip, self.dec_max_group, self.dec_ws,
                                           stream=stream)
 
+    def mixed(self, stream=None, k_arena=None, v_arena=None):
+        """Every step row (chunks and decodes) through paged_attention_mixed,
+        into ``mix_out`` [num_tokens][Hq][D] (buffers made on first use)."""
+        torch = _torch()
+        w = self.w
+        if not hasattr(self, "mix_out"):
+            counts = np.diff(self.cu_host).astype(np.int64)
+            T = int(self.cu_host[-1])
+            self.mix_max_q = int(counts.max())
+            self.mix_max_ctx = int((self.starts_host + counts).max())
+            self.mix_out = torch.empty((T, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                                       device=self.device)
+            ws = paged_attention_mixed_workspace_bytes(self.g, len(w.step), T, self.mix_max_ctx)
+            self.mix_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=self.device)
+        paged_attention_mixed(self.g, self.mix_out, self.q,
+                              self.k_arena if k_arena is None else k_arena,
+                              self.v_arena if v_arena is None else v_arena,
+                              self.bt, self.cu, self.starts, self.mix_max_q, self.mix_max_ctx,
+                              self.scale, self.mix_ws, stream=stream)
+
     def chunk(self, stream=None, k_arena=None, v_arena=None):
+        self._need_split()
         if self.chunk_rows:
             paged_attention_chunk(self.g, self.chunk_out, self.chunk_q,
                                   self.k_arena if k_arena is None else k_arena,

@@ -1,0 +1,142 @@
+"""GPU: paged_attention_mixed, one attention launch for a continuous-batching
+step of prefill chunks and decodes (Kshipra part 3, section 5).
+
+Its decode rows (sequences with one new row) must be bit for bit those of
+paged_attention_decode and its chunk rows those of paged_attention_chunk,
+which the parity tests check against the oracle; rows are also checked against
+the oracle here, and batches whose kinds interleave (which the separate calls
+cannot take as one batch) against the oracle alone.
+"""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_chunked_amd as pkv  # noqa: E402
+from oracle import script as oscript  # noqa: E402
+from paged_kv_chunked_amd import harness, workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.fail("libpkv.so is not built")
+    pkv.lib()
+
+
+def say(msg):
+    print(f"[gpu-mixed] {msg}", flush=True)
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def oracle_rows(w, dw, rows, st=None, q_rot=None):
+    """max / mean |mixed - oracle| over step rows ``rows`` (every query row)."""
+    if st is None:
+        st = oscript.run_script(w, materialize=False)
+        q_rot = oscript.append_step(w, st)
+    cu = dw.cu_host
+    got = dw.mix_out.cpu().numpy()
+    worst, tot, n = 0.0, 0.0, 0
+    for r in rows:
+        exp = oscript.attend_row(w, st, r, q_rot[cu[r]:cu[r + 1]], dw.scale)
+        d = np.abs(got[cu[r]:cu[r + 1]].astype(np.float64) - exp)
+        worst, tot, n = max(worst, float(d.max())), tot + float(d.sum()), n + d.size
+    return worst, tot / max(n, 1)
+
+
+def check_against_split_calls(w, sample_rows=None):
+    say(f"{w.name}: set-up (blocks={w.num_blocks}, step rows={len(w.step)})")
+    dw = harness.DeviceWorkload(w)
+    dw.step()
+    dw.mixed()
+    torch.cuda.synchronize()
+    mix = dw.mix_out.cpu().numpy()
+    cu = dw.cu_host
+    say(f"{w.name}: {len(dw.dec_rows)} decode rows, {len(dw.chunk_rows)} chunks")
+    if dw.dec_rows:
+        dec = dw.dec_out.cpu().numpy()
+        for i, r in enumerate(dw.dec_rows):
+            assert np.array_equal(bits(mix[cu[r]]), bits(dec[i])), ("decode row", r)
+    if dw.chunk_rows:
+        chk = dw.chunk_out.cpu().numpy()
+        t0, t1 = cu[dw.chunk_rows[0]], cu[dw.chunk_rows[-1] + 1]
+        assert np.array_equal(bits(mix[t0:t1]), bits(chk)), "chunk rows"
+    rows = range(len(w.step)) if sample_rows is None else sample_rows
+    worst, mean = oracle_rows(w, dw, rows)
+    say(f"{w.name}: oracle max {worst:.2e} mean {mean:.2e}")
+    assert worst <= 2e-3 and mean <= 2e-4
+    # a second call (the schedule and its queue counter are rebuilt) gives the
+    # same bits
+    dw.mix_out.fill_(float("nan"))
+    dw.mixed()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(dw.mix_out.cpu().numpy()), bits(mix))
+    return dw
+
+
+def test_small_mixed():
+    check_against_split_calls(workloads.mixed_step(num_chunks=2, chunk=96, num_decodes=40,
+                                                   lo=1, hi=1200, num_sharers=5,
+                                                   shared_prefix=256, parent_tokens=264))
+
+
+def test_decodes_only():
+    lens = [1, 2, 15, 16, 17, 383, 384, 385, 768, 769, 1000, 1600, 2049]
+    check_against_split_calls(workloads.build("mixed_decodes_only", 21, "f16", 32, 8, 128,
+                                              5.0e5, [(L - 1, 1) for L in lens],
+                                              max_blocks_per_seq=130))
+
+
+def test_chunks_only_and_one_row_sequence():
+    seqs = [(0, 1), (0, 33), (48, 16), (5, 70), (100, 129), (0, 200), (300, 64), (17, 5)]
+    check_against_split_calls(workloads.build("mixed_chunks", 22, "f16", 32, 8, 128, 5.0e5,
+                                              seqs, max_blocks_per_seq=40))
+
+
+def test_short_contexts_need_no_merge():
+    """Every context fits one 384-token split: no partials, no combine."""
+    seqs = [(10, 1), (383, 1), (200, 1), (0, 40), (64, 100)]
+    check_against_split_calls(workloads.build("mixed_one_split", 23, "f16", 32, 8, 128, 5.0e5,
+                                              seqs, max_blocks_per_seq=30))
+
+
+def test_sixteen_kv_heads():
+    """Hkv 16: decode units cover the KV heads in two groups of 8 waves."""
+    seqs = [(700, 1), (1500, 1), (30, 1), (0, 70), (400, 33)]
+    check_against_split_calls(workloads.build("mixed_hkv16", 24, "f16", 64, 16, 128, 5.0e5,
+                                              seqs, max_blocks_per_seq=100))
+
+
+def test_interleaved_kinds_against_oracle():
+    seqs = [(300, 1), (0, 70), (1000, 1), (48, 16), (2000, 1), (5, 2), (0, 1), (800, 130)]
+    w = workloads.build("mixed_interleaved", 25, "f16", 32, 8, 128, 5.0e5, seqs,
+                        max_blocks_per_seq=130)
+    say(f"{w.name}: set-up")
+    dw = harness.DeviceWorkload(w)
+    assert not dw.split_ok
+    dw.append()
+    dw.mixed()
+    torch.cuda.synchronize()
+    worst, mean = oracle_rows(w, dw, range(len(seqs)))
+    say(f"{w.name}: oracle max {worst:.2e} mean {mean:.2e}")
+    assert worst <= 2e-3 and mean <= 2e-4
+
+
+def test_mixed_full():
+    """The 2048-token-budget step: 4 chunks of 256 + 1024 decodes (16 sharing a
+    prefix); every row bit for bit against the separate calls, sampled rows
+    against the oracle."""
+    w = workloads.mixed_step()
+    rng = np.random.default_rng(3)
+    sample = sorted(set(w.chunk_rows()[:1] +
+                        rng.choice(w.decode_rows(), size=8, replace=False).tolist()))
+    check_against_split_calls(w, sample_rows=sample)
