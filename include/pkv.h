@@ -69,12 +69,17 @@ typedef enum pkv_status {
  * (part 3 section 2's group codec with group = one head vector of head_dim
  * values: s = fp16(fp32(max |x|) / 127), floored at 2^-24; code =
  * round-half-even(fp32(x) / fp32(s)); x_hat = code * s, |x - x_hat| <= s/2),
- * x being the value an fp16 arena would hold.  Tile of one (block, head),
- * 16 * head_dim + 32 bytes:
+ * x being the value an fp16 arena would hold.  Tile of one (block, head):
+ * 16 * head_dim + 32 bytes rounded up to a multiple of 128 (2176 at head_dim
+ * 128), so every tile starts on a 128-byte line:
  *   K  int8 codes [head_dim/16][16][16] (16-byte pieces of 16 dims, the 16
- *      keys of a piece contiguous), then fp16 scales [16] (slot order)
- *   V  int8 codes [head_dim][16], then fp16 scales [16]
- * head_dim must be a multiple of 16. */
+ *      keys of a piece contiguous; the key of slot s sits at position s with
+ *      bits 2 and 3 exchanged: positions 0..7 hold slots 0-3 and 8-11,
+ *      positions 8..15 slots 4-7 and 12-15), then fp16 scales [16] (slot
+ *      order), then padding
+ *   V  int8 codes [head_dim][16] (slot order), then fp16 scales [16], then
+ *      padding
+ * Padding bytes are never written or read.  head_dim must be a multiple of 16. */
 typedef enum pkv_dtype { PKV_F16 = 0, PKV_F32 = 1, PKV_I8KV = 2 } pkv_dtype;
 
 /* Geometry of one layer's arena.  block_size must be 16; head_dim a multiple of

@@ -81,13 +81,29 @@ class Arena:
         return K.reshape(length, K.shape[1], -1), self.v[blk, :, :, slot]
 
 
+def quant_tile_size(head_dim: int) -> int:
+    """Bytes of one (block, head) tile: 16 * D codes + 16 fp16 scales, rounded
+    up to whole 128-byte lines (the library's layout)."""
+    return (16 * head_dim + 32 + 127) // 128 * 128
+
+
+def kpos(slot):
+    """Stored position of the key in ``slot`` among the 16 of a K piece: bits
+    2 and 3 exchanged (the library's layout)."""
+    slot = np.asarray(slot)
+    return (slot & 3) | ((slot >> 1) & 4) | ((slot << 1) & 8)
+
+
 class QuantArena:
     """Arena of group-quantized K/V ([K3] section 2's codec applied per (token,
-    KV head) vector, see quant.py).  Codes and scales are kept apart here; the
-    byte image of a (block, head) tile is ``tile_bytes``:
-      K tile  int8 codes [D/16][16][16] (16-byte pieces of 16 dims, keys
-              grouped by piece as in the fp16 K layout), then 16 fp16 scales
-      V tile  int8 codes [D][16] (head-dim-major), then 16 fp16 scales
+    KV head) vector, see quant.py).  Codes and scales are kept apart here, in
+    slot order; the byte image of a (block, head) tile (``tile_bytes``,
+    ``image``) follows the library's documented layout, quant_tile_size bytes:
+      K tile  int8 codes [D/16][16][16] (16-byte pieces of 16 dims; the key of
+              slot s at position kpos(s)), then 16 fp16 scales (slot order)
+      V tile  int8 codes [D][16] (head-dim-major, slot order), then 16 fp16
+              scales
+      then padding up to the tile size (never written: all-ones bytes).
     Unwritten slots hold all-ones bytes (code -1, scale NaN), so a read of one
     is NaN."""
 
@@ -125,21 +141,31 @@ class QuantArena:
 
     def swap_out(self, ids):
         """[K3] section 5 swapping: per block, the K tiles then the V tiles as
-        bytes (every head's codes followed by its 16 scales)."""
+        bytes (every head's tile image: codes, 16 scales, padding)."""
         out = []
         for b in ids:
             out.append(self.tile_bytes("k", b))
             out.append(self.tile_bytes("v", b))
         return np.concatenate(out) if out else np.zeros(0, np.uint8)
 
+    def image(self, which: str, blocks=None) -> np.ndarray:
+        """Byte image [N][Hkv][tile] of the K or V arena (of ``blocks`` only if
+        given)."""
+        q, sc = (self.kq, self.ks) if which == "k" else (self.vq, self.vs)
+        if blocks is not None:
+            q, sc = q[blocks], sc[blocks]
+        N, H = q.shape[:2]
+        if which == "k":                    # slot s to position kpos(s)
+            q = q[:, :, :, np.argsort(kpos(np.arange(BLOCK))), :]
+        codes = np.ascontiguousarray(q).reshape(N, H, -1).view(np.uint8)
+        scales = np.ascontiguousarray(sc).view(np.uint8).reshape(N, H, -1)
+        pad = quant_tile_size(q.shape[2] * 16 if which == "k" else q.shape[2]) \
+            - codes.shape[2] - scales.shape[2]
+        return np.concatenate([codes, scales, np.full((N, H, pad), 0xFF, np.uint8)], axis=2)
+
     def tile_bytes(self, which: str, block: int) -> np.ndarray:
         """Byte image of every head's tile of ``block`` (K or V), heads in order."""
-        q, sc = (self.kq, self.ks) if which == "k" else (self.vq, self.vs)
-        parts = []
-        for h in range(q.shape[1]):
-            parts.append(np.ascontiguousarray(q[block, h]).view(np.uint8).ravel())
-            parts.append(np.ascontiguousarray(sc[block, h]).view(np.uint8).ravel())
-        return np.concatenate(parts)
+        return self.image(which, [block]).ravel()
 
 
 class SymbolicArena:

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
     }
   }
   if (blk < 0 || blk >= num_blocks) return;
-  const size_t tile_bytes = (size_t)kBlock * D + 2 * kBlock;
+  const size_t tile_bytes = i8_tile_bytes(D);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int kWaves = kThreads / 64;
   // K: wave w quantizes heads w, w + kWaves, ...; lane l rotates the pairs
@@ -163,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
       const int i = lane + 64 * u;
       if (i < half) {
         const int d0 = i, d1 = i + half;
-        tile[(d0 >> 4) * 256 + slot * 16 + (d0 & 15)] = (uint8_t)encode8(x[2 * u], s);
-        tile[(d1 >> 4) * 256 + slot * 16 + (d1 & 15)] = (uint8_t)encode8(x[2 * u + 1], s);
+        tile[(d0 >> 4) * 256 + i8_kpos(slot) * 16 + (d0 & 15)] = (uint8_t)encode8(x[2 * u], s);
+        tile[(d1 >> 4) * 256 + i8_kpos(slot) * 16 + (d1 & 15)] = (uint8_t)encode8(x[2 * u + 1], s);
       }
     }
     if (lane == 0) *(_Float16*)(tile + (size_t)kBlock * D + 2 * slot) = sh;

@@ -185,7 +185,10 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
 //     8-byte load of V codes per head dim.  The head dims of the contraction
 //     are permuted too (MFMA kd, lane group lq: dims 16(4(kd >> 1) + lq) +
 //     8(kd & 1) .. +8), so one 16-byte load of K codes feeds two MFMAs; the
-//     queries are loaded in the same order.
+//     queries are loaded in the same order.  The arena stores the tokens an
+//     MFMA reads together contiguously (i8_kpos) and pads tiles to whole
+//     128-byte lines, so every load instruction reads whole lines (measured
+//     16% faster than the unpadded slot-order layout).
 //   * codes become fp16 exactly (byte b: fp16 bits 0x6400 | (b ^ 0x80) =
 //     1024 + b + 128, minus 1152), the K scale multiplies the score, and the V
 //     scale is folded into the probability: P^T holds fp16(p * s_v * 2^6), the
@@ -218,13 +221,15 @@ __device__ inline half8_t codes_to_half(uint32_t lo, uint32_t hi) {
 __device__ inline PairI8 load_pair_i8(const uint8_t* __restrict__ k_arena,
                                       const uint8_t* __restrict__ v_arena, int blk_a, int blk_b,
                                       int Hkv, int g, int ln, int lq) {
-  constexpr size_t kTile = (size_t)kBlock * kD + 2 * kBlock;
+  constexpr size_t kTile = i8_tile_bytes(kD);
   PairI8 pr;
   // K row of this lane (MFMA row ln) for MFMA u: block A or B by ln >> 3
   const uint8_t* kt = k_arena + ((size_t)((ln >> 3) ? blk_b : blk_a) * Hkv + g) * kTile;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int slot = 8 * ((ln >> 2) & 1) + 4 * u + (ln & 3);
+    // the lane's token 8((ln >> 2) & 1) + 4u + (ln & 3) is stored at position
+    // 8u + (ln & 7): MFMA u reads one 128-byte run per (block, piece)
+    const int slot = 8 * u + (ln & 7);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       pr.k[u][j] = __builtin_nontemporal_load((const u32x4*)(kt + (4 * j + lq) * 256 + slot * 16));
@@ -240,7 +245,17 @@ __device__ inline PairI8 load_pair_i8(const uint8_t* __restrict__ k_arena,
   return pr;
 }
 
-__global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_split_i8_kernel(
+// Waves per workgroup and minimum resident waves per SIMD of the INT8 split
+// kernel (its own register budget differs from the fp16 kernel's).
+#ifndef PKV_DECODE_I8_WAVES_PER_WG
+#define PKV_DECODE_I8_WAVES_PER_WG 8
+#endif
+#ifndef PKV_DECODE_I8_WAVES_PER_SIMD
+#define PKV_DECODE_I8_WAVES_PER_SIMD 2
+#endif
+constexpr int kI8WavesPerWG = PKV_DECODE_I8_WAVES_PER_WG;
+
+__global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) void decode_split_i8_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q,
     const uint8_t* __restrict__ k_arena, const uint8_t* __restrict__ v_arena,
@@ -248,7 +263,7 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
     const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
     int num_blocks) {
   const int split = blockIdx.x, b = blockIdx.y;
-  const int g = blockIdx.z * kDecodeWavesPerWG + (threadIdx.x >> 6);
+  const int g = blockIdx.z * kI8WavesPerWG + (threadIdx.x >> 6);
   if (g >= Hkv) return;
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, lq = lane >> 4;
@@ -525,17 +540,20 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (g.dtype == PKV_I8KV)
-    hipLaunchKernelGGL(decode_split_i8_kernel, grid, dim3(64 * wpg), 0, stream,
+  if (g.dtype == PKV_I8KV) {
+    const int wpg8 = g.num_kv_heads < kI8WavesPerWG ? g.num_kv_heads : kI8WavesPerWG;
+    const dim3 grid8(gx, num_seqs, (g.num_kv_heads + kI8WavesPerWG - 1) / kI8WavesPerWG);
+    hipLaunchKernelGGL(decode_split_i8_kernel, grid8, dim3(64 * wpg8), 0, stream,
                        out, ws_o, ws_ml, (const _Float16*)q, (const uint8_t*)k_arena,
                        (const uint8_t*)v_arena, block_table, max_blocks, context_lens,
                        scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
-  else
+  } else {
     hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64 * wpg), 0, stream,
                        out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
                        (const _Float16*)v_arena, block_table, max_blocks, context_lens,
                        scale_log2, g.num_kv_heads, nsplit, g.num_blocks,
                        shared ? groups->row_skip : nullptr);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit <= 1) return e;
   return launch_decode_combine(g, out, ws_o, ws_ml, context_lens, nullptr, 0, max_blocks, num_seqs,

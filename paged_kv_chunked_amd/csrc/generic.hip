@@ -27,19 +27,20 @@ struct TileReader {
   }
   __device__ float v(int d, int slot) const { return (float)vt[d * kBlock + slot]; }
 };
-// INT8 tiles: codes then 16 fp16 scales (16 * D + 32 bytes per (block, head))
+// INT8 tiles: codes then 16 fp16 scales, padded to 128-byte lines; K keys at
+// their stored positions i8_kpos(slot)
 struct TileReaderI8 {
   const uint8_t* kt;
   const uint8_t* vt;
   int D;
   __device__ TileReaderI8(const void* k_arena, const void* v_arena, int blk, int Hkv, int g, int D_)
       : D(D_) {
-    const size_t tb = (size_t)kBlock * D_ + 2 * kBlock;
+    const size_t tb = i8_tile_bytes(D_);
     kt = (const uint8_t*)k_arena + ((size_t)blk * Hkv + g) * tb;
     vt = (const uint8_t*)v_arena + ((size_t)blk * Hkv + g) * tb;
   }
   __device__ float k(int d, int slot, int) const {
-    const float code = (float)(int8_t)kt[(d >> 4) * 256 + slot * 16 + (d & 15)];
+    const float code = (float)(int8_t)kt[(d >> 4) * 256 + i8_kpos(slot) * 16 + (d & 15)];
     return code * (float)((const _Float16*)(kt + (size_t)kBlock * D))[slot];
   }
   __device__ float v(int d, int slot) const {

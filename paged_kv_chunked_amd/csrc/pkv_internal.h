@@ -64,9 +64,20 @@ __device__ inline int find_seq(const int32_t* __restrict__ cu, int num_seqs, int
   return lo;
 }
 
+// INT8 tiles: codes then 16 fp16 scales, padded to whole 128-byte lines.
+__host__ __device__ constexpr size_t i8_tile_bytes(int head_dim) {
+  return ((size_t)kBlock * head_dim + 2 * kBlock + 127) / 128 * 128;
+}
+// Stored position of slot s among the 16 keys of an INT8 K piece: bits 2 and 3
+// exchanged, so that the slots {0-3, 8-11} and {4-7, 12-15} the decode kernel
+// reads together are each one contiguous 128-byte run.
+__host__ __device__ constexpr int i8_kpos(int s) {
+  return (s & 3) | ((s >> 1) & 4) | ((s << 1) & 8);
+}
+
 // Bytes of one (block, KV head) tile of either arena.
 inline size_t kv_tile_bytes(const pkv_geom& g) {
-  if (g.dtype == PKV_I8KV) return (size_t)kBlock * g.head_dim + 2 * kBlock;
+  if (g.dtype == PKV_I8KV) return i8_tile_bytes(g.head_dim);
   return (size_t)kBlock * g.head_dim * (g.dtype == PKV_F16 ? 2 : 4);
 }
 

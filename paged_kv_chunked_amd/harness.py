@@ -124,9 +124,10 @@ class DeviceWorkload:
         N, H, D = w.num_blocks, w.num_kv_heads, w.head_dim
         x = 16 // (2 if w.dtype == "f16" else 4)   # elements per 16-byte piece of K
         if self.kv_bits == 8:
-            # INT8 tiles: codes, then 16 fp16 scales; unwritten = all-ones bytes
-            # (scale NaN), as in the oracle's quantized arena
-            tile = BLOCK_SIZE * D + 2 * BLOCK_SIZE
+            # INT8 tiles: codes, then 16 fp16 scales, padded to 128-byte lines;
+            # unwritten = all-ones bytes (scale NaN), as in the oracle's
+            # quantized arena
+            tile = (BLOCK_SIZE * D + 2 * BLOCK_SIZE + 127) // 128 * 128
             self.k_arena = torch.full((N, H, tile), 255, dtype=torch.uint8, device=self.device)
             self.v_arena = torch.full((N, H, tile), 255, dtype=torch.uint8, device=self.device)
         else:

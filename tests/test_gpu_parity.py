@@ -70,12 +70,8 @@ class Errors:
 
 
 def quant_image(a, which):
-    """Byte image [N][Hkv][16 D + 32] of the oracle's quantized arena (codes,
-    then the 16 fp16 scales of each (block, head) tile)."""
-    q, sc = (a.kq, a.ks) if which == "k" else (a.vq, a.vs)
-    N, H = q.shape[:2]
-    return np.concatenate([np.ascontiguousarray(q).reshape(N, H, -1).view(np.uint8),
-                           np.ascontiguousarray(sc).view(np.uint8).reshape(N, H, -1)], axis=2)
+    """Byte image [N][Hkv][tile] of the oracle's quantized arena."""
+    return a.image(which)
 
 
 def run_case(w, full_arena=True, dec_sample=None, chunk_sample=None):

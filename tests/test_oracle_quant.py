@@ -101,6 +101,20 @@ def test_quant_arena_gather_is_codec_roundtrip_and_tile_size():
     # unwritten slots read as NaN
     K2, _ = a.gather([4, 1], 32)
     assert np.isnan(K2[20:]).all()
-    # the byte image of one block's K tiles: per head 16 * D codes + 16 fp16 scales
-    assert a.tile_bytes("k", 4).size == H * (16 * D + 32)
-    assert a.swap_out([4, 1]).size == 2 * 2 * H * (16 * D + 32)
+    # the byte image of one block's K tiles: per head 16 * D codes + 16 fp16
+    # scales, padded to whole 128-byte lines
+    tile = arena.quant_tile_size(D)
+    assert tile == 640 and arena.quant_tile_size(128) == 2176
+    assert a.tile_bytes("k", 4).size == H * tile
+    assert a.swap_out([4, 1]).size == 2 * 2 * H * tile
+    # K codes of slot s at position kpos(s) (bits 2 and 3 exchanged), V codes
+    # and both scale arrays in slot order, padding never written
+    assert [int(x) for x in arena.kpos(np.arange(16))] == [0, 1, 2, 3, 8, 9, 10, 11,
+                                                           4, 5, 6, 7, 12, 13, 14, 15]
+    img_k, img_v = a.image("k")[4, 0], a.image("v")[4, 0]
+    piece = img_k[:16 * D].reshape(D // 16, 16, 16)
+    assert np.array_equal(piece[:, 8], a.kq[4, 0, :, 4].view(np.uint8))   # slot 4 at position 8
+    assert np.array_equal(piece[:, 4], a.kq[4, 0, :, 8].view(np.uint8))   # slot 8 at position 4
+    assert np.array_equal(img_v[:16 * D].reshape(D, 16), a.vq[4, 0].view(np.uint8))
+    assert np.array_equal(img_k[16 * D:16 * D + 32].view(np.float16), a.ks[4, 0])
+    assert (img_k[16 * D + 32:] == 0xFF).all() and (img_v[16 * D + 32:] == 0xFF).all()
