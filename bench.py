@@ -373,31 +373,32 @@ def main():
     if not args.no_swap:
         out["swap"] = bench_swap(torch, dw)
         log(f"swap: {out['swap']}")
-    if not args.no_int8:
-        _, dw8, ms_step8, ms_dec8, ms_dcall8, nbytes8 = bench_decode(torch, args, kv_bits=8)
-        ach8 = nbytes8 / (ms_dec8 * 1e-3) / 1e9
-        tokens = int(sum(dw8.dec_lens_host))
-        log(f"decode int8: kernel {ms_dec8:.4f} ms, {nbytes8 / 1e6:.1f} MB -> {ach8:.0f} GB/s")
-        out["decode_int8"] = {
-            "workload": "the decode workload over INT8 arenas (codes + one fp16 scale per "
+    for bits in (() if args.no_int8 else (8, 4)):
+        _, dwq, ms_stepq, ms_decq, ms_dcallq, nbytesq = bench_decode(torch, args, kv_bits=bits)
+        achq = nbytesq / (ms_decq * 1e-3) / 1e9
+        tokens = int(sum(dwq.dec_lens_host))
+        log(f"decode int{bits}: kernel {ms_decq:.4f} ms, {nbytesq / 1e6:.1f} MB -> {achq:.0f} GB/s")
+        out[f"decode_int{bits}"] = {
+            "workload": f"the decode workload over INT{bits} arenas (codes + one fp16 scale per "
                         "(token, KV head) vector)",
-            "context_tokens_per_s": round(tokens / (ms_dec8 * 1e-3), 1),
-            "speedup_vs_fp16_arena": round(ms_dec / ms_dec8, 3),
-            "ms_per_step": round(ms_step8, 5),
+            "context_tokens_per_s": round(tokens / (ms_decq * 1e-3), 1),
+            "speedup_vs_fp16_arena": round(ms_dec / ms_decq, 3),
+            "ms_per_step": round(ms_stepq, 5),
             "roofline": {
-                "kernel": "paged_attention_decode (decode_split_i8_kernel + decode_combine_kernel)",
+                "kernel": f"paged_attention_decode (decode_split_i{bits}_kernel + "
+                          "decode_combine_kernel)",
                 "bound": "hbm",
-                "achieved": round(ach8, 1),
+                "achieved": round(achq, 1),
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",
-                "frac": round(ach8 / PEAK_HBM_GBS, 4),
-                "traffic": load_traffic(TRAFFIC, "paged_attention_decode_i8"),
-                "algorithmic_bytes_per_launch": nbytes8,
-                "avg_launch_ms": round(ms_dec8, 5),
-                "avg_launch_ms_isolated": round(ms_dcall8, 5),
+                "frac": round(achq / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic(TRAFFIC, f"paged_attention_decode_i{bits}"),
+                "algorithmic_bytes_per_launch": nbytesq,
+                "avg_launch_ms": round(ms_decq, 5),
+                "avg_launch_ms_isolated": round(ms_dcallq, 5),
             },
         }
-        del dw8
+        del dwq
     if not args.no_shared:
         out["decode_shared_prefix"] = bench_shared(torch, args)
         log(f"shared-prefix decode: {out['decode_shared_prefix']}")

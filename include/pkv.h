@@ -79,13 +79,26 @@ typedef enum pkv_status {
  *      order), then padding
  *   V  int8 codes [head_dim][16] (slot order), then fp16 scales [16], then
  *      padding
- * Padding bytes are never written or read.  head_dim must be a multiple of 16. */
-typedef enum pkv_dtype { PKV_F16 = 0, PKV_F32 = 1, PKV_I8KV = 2 } pkv_dtype;
+ * Padding bytes are never written or read.  head_dim must be a multiple of 16.
+ *
+ * PKV_I4KV: the same with 4-bit codes (s = fp16(fp32(max |x|) / 7), codes in
+ * [-7, 7], stored as their two's-complement low 4 bits, two per byte, low
+ * nibble first).  Tile of one (block, head): 8 * head_dim codes bytes + 32,
+ * rounded up to a multiple of 128 (1152 at head_dim 128):
+ *   K  [head_dim/16 pieces][16 records][8 bytes]: the key of slot s has record
+ *      2 r + u, r = 4 ((s >> 3) & 1) + (s & 3), u = (s >> 2) & 1; byte i of a
+ *      record holds dims 16p + i (low) and 16p + 8 + i (high); then fp16
+ *      scales [16] (slot order), then padding
+ *   V  [head_dim][8 bytes]: byte 4g + i holds slots 8g + i (low) and
+ *      8g + 4 + i (high); then fp16 scales [16], then padding
+ * head_dim must be a multiple of 32. */
+typedef enum pkv_dtype { PKV_F16 = 0, PKV_F32 = 1, PKV_I8KV = 2, PKV_I4KV = 3 } pkv_dtype;
 
 /* Geometry of one layer's arena.  block_size must be 16; head_dim a multiple of
- * x (8 for fp16, 4 for fp32, 16 for PKV_I8KV) and <= 256; num_q_heads a
- * multiple of num_kv_heads; dtype is the storage dtype of q, k, v and both
- * arenas (IEEE binary16 or binary32), or PKV_I8KV (fp16 q/k/v, INT8 arenas). */
+ * x (8 for fp16, 4 for fp32, 16 for PKV_I8KV, 32 for PKV_I4KV) and <= 256;
+ * num_q_heads a multiple of num_kv_heads; dtype is the storage dtype of q, k,
+ * v and both arenas (IEEE binary16 or binary32), or PKV_I8KV / PKV_I4KV (fp16
+ * q/k/v, INT8 / INT4 arenas). */
 typedef struct pkv_geom {
   int32_t num_blocks;
   int32_t block_size;

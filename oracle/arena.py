@@ -81,10 +81,19 @@ class Arena:
         return K.reshape(length, K.shape[1], -1), self.v[blk, :, :, slot]
 
 
-def quant_tile_size(head_dim: int) -> int:
-    """Bytes of one (block, head) tile: 16 * D codes + 16 fp16 scales, rounded
-    up to whole 128-byte lines (the library's layout)."""
-    return (16 * head_dim + 32 + 127) // 128 * 128
+def quant_tile_size(head_dim: int, bits: int = 8) -> int:
+    """Bytes of one (block, head) tile: the 16 * D codes (bits each) + 16 fp16
+    scales, rounded up to whole 128-byte lines (the library's layout)."""
+    return (16 * head_dim * bits // 8 + 32 + 127) // 128 * 128
+
+
+def k4_record(slot):
+    """INT4 K: index of the 8-byte record of the key in ``slot`` among the 16
+    of a 16-dim piece (the library's layout): 2 r + u with r = 4 ((s >> 3) & 1)
+    + (s & 3) and u = (s >> 2) & 1, so the two keys one lane of the decode
+    kernel reads (u = 0, 1) are adjacent."""
+    slot = np.asarray(slot)
+    return 2 * (4 * ((slot >> 3) & 1) + (slot & 3)) + ((slot >> 2) & 1)
 
 
 def kpos(slot):
@@ -104,6 +113,13 @@ class QuantArena:
       V tile  int8 codes [D][16] (head-dim-major, slot order), then 16 fp16
               scales
       then padding up to the tile size (never written: all-ones bytes).
+    With 4 bits, codes are packed two per byte (low nibble first, each the
+    code's two's-complement low 4 bits):
+      K tile  [D/16][16 records of 8 bytes] (record k4_record(s) of slot s;
+              byte i holds dims 16p + i and 16p + 8 + i), then 16 fp16 scales
+      V tile  [D][8 bytes] (byte 4g + i of a dim holds slots 8g + i and
+              8g + 4 + i, so 8 consecutive slots are 4 bytes in order), then
+              16 fp16 scales
     Unwritten slots hold all-ones bytes (code -1, scale NaN), so a read of one
     is NaN."""
 
@@ -155,12 +171,22 @@ class QuantArena:
         if blocks is not None:
             q, sc = q[blocks], sc[blocks]
         N, H = q.shape[:2]
-        if which == "k":                    # slot s to position kpos(s)
-            q = q[:, :, :, np.argsort(kpos(np.arange(BLOCK))), :]
-        codes = np.ascontiguousarray(q).reshape(N, H, -1).view(np.uint8)
+        D = q.shape[2] * 16 if which == "k" else q.shape[2]
+        if self.bits == 8:
+            if which == "k":                # slot s to position kpos(s)
+                q = q[:, :, :, np.argsort(kpos(np.arange(BLOCK))), :]
+            codes = np.ascontiguousarray(q).reshape(N, H, -1).view(np.uint8)
+        else:
+            nib = q.view(np.uint8) & 0x0F   # two's-complement low 4 bits
+            if which == "k":                # [piece][record][byte i]: dims i, 8 + i
+                rec = nib[:, :, :, np.argsort(k4_record(np.arange(BLOCK))), :]
+                packed = rec[..., :8] | (rec[..., 8:] << 4)
+            else:                           # [dim][byte 4g + i]: slots 8g + i, 8g + 4 + i
+                n = nib.reshape(nib.shape[:-1] + (2, 2, 4))     # [.., g, half, i]
+                packed = (n[..., 0, :] | (n[..., 1, :] << 4)).reshape(nib.shape[:-1] + (8,))
+            codes = np.ascontiguousarray(packed).reshape(N, H, -1)
         scales = np.ascontiguousarray(sc).view(np.uint8).reshape(N, H, -1)
-        pad = quant_tile_size(q.shape[2] * 16 if which == "k" else q.shape[2]) \
-            - codes.shape[2] - scales.shape[2]
+        pad = quant_tile_size(D, self.bits) - codes.shape[2] - scales.shape[2]
         return np.concatenate([codes, scales, np.full((N, H, pad), 0xFF, np.uint8)], axis=2)
 
     def tile_bytes(self, which: str, block: int) -> np.ndarray:

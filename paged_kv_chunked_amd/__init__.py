@@ -16,7 +16,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-F16, F32, I8KV = 0, 1, 2
+F16, F32, I8KV, I4KV = 0, 1, 2, 3
 BLOCK_SIZE = 16
 DECODE_SPLIT = 384   # tokens per decode split (fixed by the library, see pkv.h)
 

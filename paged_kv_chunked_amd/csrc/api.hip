@@ -9,9 +9,13 @@ pkv_status check_geom(const pkv_geom* g) {
   if (g->block_size != PKV_BLOCK_SIZE) return PKV_ERR_SHAPE;
   if (g->num_blocks < 1 || g->num_kv_heads < 1 || g->num_q_heads < 1) return PKV_ERR_SHAPE;
   if (g->num_q_heads % g->num_kv_heads) return PKV_ERR_SHAPE;
-  if (g->dtype != PKV_F16 && g->dtype != PKV_F32 && g->dtype != PKV_I8KV) return PKV_ERR_DTYPE;
-  // head_dim: a whole number of 16-byte pieces (the K tile layout), <= 256
-  const int piece = g->dtype == PKV_F16 ? 8 : g->dtype == PKV_F32 ? 4 : 16;
+  if (g->dtype != PKV_F16 && g->dtype != PKV_F32 && g->dtype != PKV_I8KV &&
+      g->dtype != PKV_I4KV)
+    return PKV_ERR_DTYPE;
+  // head_dim: a whole number of 16-byte pieces (the K tile layout), <= 256;
+  // INT4 pairs dims i and i + 8 of 16-dim pieces in both halves of a head
+  const int piece = g->dtype == PKV_F16 ? 8 : g->dtype == PKV_F32 ? 4
+                    : g->dtype == PKV_I8KV ? 16 : 32;
   if (g->head_dim < piece || g->head_dim % piece || g->head_dim > 256) return PKV_ERR_SHAPE;
   return PKV_OK;
 }

@@ -192,6 +192,144 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
   }
 }
 
+// Group quantization to 4 bits: s = fp16(fp32(amax) / 7) (floored at the
+// smallest positive fp16), codes in [-7, 7] stored as two's-complement
+// nibbles.
+__device__ inline _Float16 group_scale4(float amax) {
+  const _Float16 s = (_Float16)(amax / 7.f);
+  const _Float16 smin = __builtin_bit_cast(_Float16, (uint16_t)1);  // 2^-24
+  return s < smin ? smin : s;
+}
+
+__device__ inline int encode4(float x, float s) {
+  const float r = __builtin_rintf(x / s);
+  return (int)fminf(fmaxf(r, -7.f), 7.f);
+}
+
+// kv_append_rope for INT4 arenas.  K: byte i of a key's 8-byte record in a
+// 16-dim piece holds dims i and i + 8 -- lanes i and i + 8 of the wave, joined
+// with one shuffle.  V: the byte of a head dim that holds slot s also holds
+// slot s ^ 4; when both tokens are in this call the one with bit 2 clear
+// writes the byte, otherwise the token present merges its nibble into the
+// stored byte.  No byte is written by two workgroups of one call.
+__global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
+    const _Float16* q, _Float16* q_out, const _Float16* __restrict__ k,
+    const _Float16* __restrict__ v, uint8_t* __restrict__ k_arena, uint8_t* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
+    int num_seqs, int num_tokens, const double2* __restrict__ cs, int rope_max_pos,
+    int num_blocks, int Hq, int Hkv, int D) {
+  const int t = blockIdx.x;
+  const int b = find_seq(cu_q_lens, num_seqs, t);
+  const int row0 = cu_q_lens[b];
+  const int P = chunk_start[b];
+  const int pos = P + (t - row0);
+  if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
+  const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];
+  const int slot = pos & 15;
+  const int half = D >> 1;
+  const double2* row = cs + (size_t)pos * half;
+
+  if (q != nullptr) {
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < Hq * half; idx += kThreads) {
+      const int h = idx / half, i = idx - h * half;
+      const size_t base = ((size_t)t * Hq + h) * D;
+      const double2 c = row[i];
+      double o0, o1;
+      rope_pair((double)q[base + i], (double)q[base + i + half], c.x, c.y, o0, o1);
+      q_out[base + i] = store_f64<_Float16>(o0);
+      q_out[base + i + half] = store_f64<_Float16>(o1);
+    }
+  }
+  if (blk < 0 || blk >= num_blocks) return;
+  const size_t tile_bytes = i4_tile_bytes(D);
+  const size_t codes = (size_t)kBlock * D / 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int kWaves = kThreads / 64;
+  const int krec = i4_krec(slot);
+  for (int h = wave; h < Hkv; h += kWaves) {
+    const _Float16* kp = k + ((size_t)t * Hkv + h) * D;
+    float x[4];
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = lane + 64 * u;
+      x[2 * u] = x[2 * u + 1] = 0.f;
+      if (i < half) {
+        const double2 c = row[i];
+        double o0, o1;
+        rope_pair((double)kp[i], (double)kp[i + half], c.x, c.y, o0, o1);
+        x[2 * u] = (float)store_f64<_Float16>(o0);
+        x[2 * u + 1] = (float)store_f64<_Float16>(o1);
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * u]), fabsf(x[2 * u + 1])));
+      }
+    }
+    const _Float16 sh = group_scale4(wave_max(amax));
+    const float s = (float)sh;
+    uint8_t* tile = k_arena + ((size_t)blk * Hkv + h) * tile_bytes;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = lane + 64 * u;
+      const int c0 = i < half ? encode4(x[2 * u], s) : 0;
+      const int c1 = i < half ? encode4(x[2 * u + 1], s) : 0;
+      const int p0 = __shfl_down(c0, 8), p1 = __shfl_down(c1, 8);  // dims i + 8, i + 8 + half
+      if (i < half && (i & 8) == 0) {  // half is a multiple of 16: i + half has bit 3 clear too
+        const int d0 = i, d1 = i + half;
+        tile[(d0 >> 4) * 128 + krec * 8 + (d0 & 7)] = (uint8_t)((c0 & 15) | ((p0 & 15) << 4));
+        tile[(d1 >> 4) * 128 + krec * 8 + (d1 & 7)] = (uint8_t)((c1 & 15) | ((p1 & 15) << 4));
+      }
+    }
+    if (lane == 0) *(_Float16*)(tile + codes + 2 * slot) = sh;
+  }
+  // V: the token sharing this token's bytes, and which of the two writes them
+  const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
+  const int ppos = pos ^ 4;
+  const bool partner_in = ppos >= P && ppos < P + C;
+  const bool leader = (pos & 4) == 0 || !partner_in;
+  const int tp = t + (ppos - pos);
+  const int vbyte = i4_vbyte(slot), vhigh = i4_vhigh(slot);
+  for (int h = wave; h < Hkv; h += kWaves) {
+    const _Float16* vp = v + ((size_t)t * Hkv + h) * D;
+    float x[4];
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      x[u] = d < D ? (float)vp[d] : 0.f;
+      amax = fmaxf(amax, fabsf(x[u]));
+    }
+    const _Float16 sh = group_scale4(wave_max(amax));
+    const float s = (float)sh;
+    uint8_t* tile = v_arena + ((size_t)blk * Hkv + h) * tile_bytes;
+    if (lane == 0) *(_Float16*)(tile + codes + 2 * slot) = sh;
+    if (!leader) continue;  // the partner's workgroup writes the shared bytes
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    float sp = 1.f;
+    if (partner_in) {
+      const _Float16* pp = v + ((size_t)tp * Hkv + h) * D;
+      float pmax = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = lane + 64 * u;
+        y[u] = d < D ? (float)pp[d] : 0.f;
+        pmax = fmaxf(pmax, fabsf(y[u]));
+      }
+      sp = (float)group_scale4(wave_max(pmax));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      if (d >= D) continue;
+      uint8_t* at = tile + (size_t)d * 8 + vbyte;
+      const int own = encode4(x[u], s) & 15;
+      // the other nibble: the partner's code, or what the byte holds already
+      const int other = partner_in ? (encode4(y[u], sp) & 15) : (vhigh ? (*at & 15) : (*at >> 4));
+      *at = (uint8_t)(vhigh ? (other | (own << 4)) : (own | (other << 4)));
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, const void* k,
@@ -201,6 +339,14 @@ hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, con
                               int num_seqs, int num_tokens, const void* rope_table,
                               int rope_max_pos, hipStream_t stream) {
   const dim3 grid(num_tokens), block(kThreads);
+  if (g.dtype == PKV_I4KV) {
+    hipLaunchKernelGGL(append_rope_i4_kernel, grid, block, 0, stream, (const _Float16*)q,
+                       (_Float16*)q_out, (const _Float16*)k, (const _Float16*)v,
+                       (uint8_t*)k_arena, (uint8_t*)v_arena, block_table, max_blocks, cu_q_lens,
+                       chunk_start, num_seqs, num_tokens, (const double2*)rope_table,
+                       rope_max_pos, g.num_blocks, g.num_q_heads, g.num_kv_heads, g.head_dim);
+    return hipGetLastError();
+  }
   if (g.dtype == PKV_I8KV) {
     hipLaunchKernelGGL(append_rope_i8_kernel, grid, block, 0, stream, (const _Float16*)q,
                        (_Float16*)q_out, (const _Float16*)k, (const _Float16*)v,

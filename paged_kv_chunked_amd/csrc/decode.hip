@@ -245,8 +245,86 @@ __device__ inline PairI8 load_pair_i8(const uint8_t* __restrict__ k_arena,
   return pr;
 }
 
-// Waves per workgroup and minimum resident waves per SIMD of the INT8 split
-// kernel (its own register budget differs from the fp16 kernel's).
+// INT4 arenas (PKV_I4KV): the same kernel over 4-bit codes.  A lane's 16-byte
+// K load holds its two keys' records (MFMA u = 0, 1) of one 16-dim piece: low
+// nibbles are dims 0-7, high nibbles dims 8-15 of the piece, so each MFMA
+// operand is one mask per word.  A 4-byte V load holds the lane's 8 keys of
+// one head dim (low nibbles keys 0-3, high nibbles keys 4-7).  Nibbles become
+// fp16 exactly: (n ^ 8) + 1024 - 1032.
+struct PairI4 {
+  u32x4 k[2];     // [j]: records (u = 0: x, y; u = 1: z, w) of piece 4j + lq
+  uint32_t v[8];  // [db]: 8 codes of dim 16db + ln, the lane's 8 keys
+  u32x4 ks, vs;   // fp16 scales of the lane's 8 keys (K, V)
+};
+
+// 8 nibbles (the low nibble of each byte of lo, then of hi) as fp16 codes
+__device__ inline half8_t nibbles_to_half(uint32_t lo, uint32_t hi) {
+  const uint32_t a = (lo & 0x0F0F0F0Fu) ^ 0x08080808u, b = (hi & 0x0F0F0F0Fu) ^ 0x08080808u;
+  const uint32_t c = 0x64646464u;
+  const uint32_t w0 = __builtin_amdgcn_perm(c, a, 0x05010400u);
+  const uint32_t w1 = __builtin_amdgcn_perm(c, a, 0x05030402u);
+  const uint32_t w2 = __builtin_amdgcn_perm(c, b, 0x05010400u);
+  const uint32_t w3 = __builtin_amdgcn_perm(c, b, 0x05030402u);
+  half8_t h = __builtin_bit_cast(half8_t, u32x4{w0, w1, w2, w3});
+  return h - (half8_t)(_Float16)1032.f;
+}
+
+__device__ inline PairI4 load_pair_i4(const uint8_t* __restrict__ k_arena,
+                                      const uint8_t* __restrict__ v_arena, int blk_a, int blk_b,
+                                      int Hkv, int g, int ln, int lq) {
+  constexpr size_t kTile = i4_tile_bytes(kD);
+  PairI4 pr;
+  // the lane's key row (MFMA row ln) lives in block A or B by ln >> 3; its
+  // records for u = 0, 1 are 16 bytes at record 2 (ln & 7)
+  const uint8_t* kt = k_arena + ((size_t)((ln >> 3) ? blk_b : blk_a) * Hkv + g) * kTile;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    pr.k[j] = __builtin_nontemporal_load((const u32x4*)(kt + (4 * j + lq) * 128 + (ln & 7) * 16));
+  const size_t tv = ((size_t)((lq >> 1) ? blk_b : blk_a) * Hkv + g) * kTile;
+  const uint8_t* vt = v_arena + tv;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    pr.v[db] = __builtin_nontemporal_load((const uint32_t*)(vt + (16 * db + ln) * 8 + 4 * (lq & 1)));
+  pr.ks = __builtin_nontemporal_load((const u32x4*)(k_arena + tv + kBlock * kD / 2 + 16 * (lq & 1)));
+  pr.vs = __builtin_nontemporal_load((const u32x4*)(vt + kBlock * kD / 2 + 16 * (lq & 1)));
+  return pr;
+}
+
+// The two code widths as traits of one split kernel: the pair type, its load,
+// and the MFMA operands (K operand of MFMA u, contraction step kd; V operand
+// of dims block db).
+struct CodesI8 {
+  using Pair = PairI8;
+  __device__ static Pair load(const uint8_t* k, const uint8_t* v, int a, int b, int Hkv, int g,
+                              int ln, int lq) {
+    return load_pair_i8(k, v, a, b, Hkv, g, ln, lq);
+  }
+  __device__ static half8_t kop(const Pair& pr, int u, int kd) {
+    const u32x4 c = pr.k[u][kd >> 1];
+    return (kd & 1) ? codes_to_half(c.z, c.w) : codes_to_half(c.x, c.y);
+  }
+  __device__ static half8_t vop(const Pair& pr, int db) {
+    return codes_to_half(pr.v[db].x, pr.v[db].y);
+  }
+};
+struct CodesI4 {
+  using Pair = PairI4;
+  __device__ static Pair load(const uint8_t* k, const uint8_t* v, int a, int b, int Hkv, int g,
+                              int ln, int lq) {
+    return load_pair_i4(k, v, a, b, Hkv, g, ln, lq);
+  }
+  __device__ static half8_t kop(const Pair& pr, int u, int kd) {
+    const u32x4 c = pr.k[kd >> 1];
+    const uint32_t w0 = u ? c.z : c.x, w1 = u ? c.w : c.y;
+    return (kd & 1) ? nibbles_to_half(w0 >> 4, w1 >> 4) : nibbles_to_half(w0, w1);
+  }
+  __device__ static half8_t vop(const Pair& pr, int db) {
+    return nibbles_to_half(pr.v[db], pr.v[db] >> 4);
+  }
+};
+
+// Waves per workgroup and minimum resident waves per SIMD of the quantized
+// split kernels (their register budget differs from the fp16 kernel's).
 #ifndef PKV_DECODE_I8_WAVES_PER_WG
 #define PKV_DECODE_I8_WAVES_PER_WG 8
 #endif
@@ -255,7 +333,8 @@ __device__ inline PairI8 load_pair_i8(const uint8_t* __restrict__ k_arena,
 #endif
 constexpr int kI8WavesPerWG = PKV_DECODE_I8_WAVES_PER_WG;
 
-__global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) void decode_split_i8_kernel(
+template <class Codes>
+__device__ __forceinline__ void decode_split_q(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q,
     const uint8_t* __restrict__ k_arena, const uint8_t* __restrict__ v_arena,
@@ -305,17 +384,15 @@ __global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) v
     a = __builtin_amdgcn_readlane(my_blk, 2 * p);
     c = 2 * p + 1 < nb ? __builtin_amdgcn_readlane(my_blk, 2 * p + 1) : a;
   };
-  auto compute = [&](const PairI8& pr, int p) {
+  using Pair = typename Codes::Pair;
+  auto compute = [&](const Pair& pr, int p) {
     f32x4 s[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       s[u] = (f32x4)0.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const u32x4 c = pr.k[u][j];
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_half(c.x, c.y), qb[2 * j], s[u], 0, 0, 0);
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_half(c.z, c.w), qb[2 * j + 1], s[u], 0, 0, 0);
-      }
+      for (int kd = 0; kd < 4; ++kd)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Codes::kop(pr, u, kd), qb[kd], s[u], 0, 0, 0);
     }
     // element e = 4u + i of this lane: token 8(lq & 1) + e of block lq >> 1
     const half8_t ksc = __builtin_bit_cast(half8_t, pr.ks);
@@ -351,29 +428,27 @@ __global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) v
     }
     l_run += lsum;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const u32x2 c = pr.v[db];
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_half(c.x, c.y), pb, o[db], 0, 0, 0);
-    }
+    for (int db = 0; db < 8; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Codes::vop(pr, db), pb, o[db], 0, 0, 0);
   };
 
   // kI8Ahead pairs are kept in flight behind the one being computed (same
   // unconditional-prefetch scheme as the fp16 kernel).  One measured best:
   // two or three cost registers (occupancy 3 -> 2) and ran 4-6% slower.
   constexpr int kAhead = kI8Ahead;
-  PairI8 buf[kAhead + 1];
+  Pair buf[kAhead + 1];
 #pragma unroll
   for (int p = 0; p < kAhead; ++p) {
     int ba, bb;
     pair_ids(min(p, npairs - 1), ba, bb);
-    buf[p] = load_pair_i8(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+    buf[p] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
   }
 #pragma unroll
   for (int p = 0; p < kSB / 2; ++p) {
     if (p + kAhead < kSB / 2) {
       int ba, bb;
       pair_ids(min(p + kAhead, npairs - 1), ba, bb);
-      buf[(p + kAhead) % (kAhead + 1)] = load_pair_i8(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+      buf[(p + kAhead) % (kAhead + 1)] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (p < npairs) compute(buf[p % (kAhead + 1)], p);
@@ -403,6 +478,26 @@ __global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) v
       ws_ml[2 * part + 1] = l_row;
     }
   }
+}
+
+__global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) void decode_split_i8_kernel(
+    float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const _Float16* __restrict__ q, const uint8_t* __restrict__ k_arena,
+    const uint8_t* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks) {
+  decode_split_q<CodesI8>(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks,
+                          context_lens, scale_log2, Hkv, nsplit_max, num_blocks);
+}
+
+__global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) void decode_split_i4_kernel(
+    float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const _Float16* __restrict__ q, const uint8_t* __restrict__ k_arena,
+    const uint8_t* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks) {
+  decode_split_q<CodesI4>(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks,
+                          context_lens, scale_log2, Hkv, nsplit_max, num_blocks);
 }
 
 // Log-sum-exp merge of the splits of the 4 query heads of one (sequence b, KV
@@ -482,7 +577,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 }  // namespace
 
 bool decode_fast_path(const pkv_geom& g) {
-  return (g.dtype == PKV_F16 || g.dtype == PKV_I8KV) && g.head_dim == kD &&
+  return (g.dtype == PKV_F16 || g.dtype == PKV_I8KV || g.dtype == PKV_I4KV) && g.head_dim == kD &&
          g.num_q_heads == kG * g.num_kv_heads;
 }
 
@@ -540,10 +635,11 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (g.dtype == PKV_I8KV) {
+  if (g.dtype == PKV_I8KV || g.dtype == PKV_I4KV) {
     const int wpg8 = g.num_kv_heads < kI8WavesPerWG ? g.num_kv_heads : kI8WavesPerWG;
     const dim3 grid8(gx, num_seqs, (g.num_kv_heads + kI8WavesPerWG - 1) / kI8WavesPerWG);
-    hipLaunchKernelGGL(decode_split_i8_kernel, grid8, dim3(64 * wpg8), 0, stream,
+    hipLaunchKernelGGL(g.dtype == PKV_I8KV ? decode_split_i8_kernel : decode_split_i4_kernel,
+                       grid8, dim3(64 * wpg8), 0, stream,
                        out, ws_o, ws_ml, (const _Float16*)q, (const uint8_t*)k_arena,
                        (const uint8_t*)v_arena, block_table, max_blocks, context_lens,
                        scale_log2, g.num_kv_heads, nsplit, g.num_blocks);

@@ -49,6 +49,33 @@ struct TileReaderI8 {
   }
 };
 
+// INT4 tiles: two codes per byte (two's-complement nibbles), then 16 fp16
+// scales, padded to 128-byte lines; K records i4_krec(slot) of 8 bytes per
+// 16-dim piece (byte i: dims i, i + 8), V bytes i4_vbyte(slot) per dim.
+struct TileReaderI4 {
+  const uint8_t* kt;
+  const uint8_t* vt;
+  int D;
+  __device__ TileReaderI4(const void* k_arena, const void* v_arena, int blk, int Hkv, int g, int D_)
+      : D(D_) {
+    const size_t tb = i4_tile_bytes(D_);
+    kt = (const uint8_t*)k_arena + ((size_t)blk * Hkv + g) * tb;
+    vt = (const uint8_t*)v_arena + ((size_t)blk * Hkv + g) * tb;
+  }
+  __device__ static float nibble(uint8_t byte, int high) {
+    const int n = high ? byte >> 4 : byte & 15;
+    return (float)((n ^ 8) - 8);
+  }
+  __device__ float k(int d, int slot, int) const {
+    const uint8_t byte = kt[(d >> 4) * 128 + i4_krec(slot) * 8 + (d & 7)];
+    return nibble(byte, (d >> 3) & 1) * (float)((const _Float16*)(kt + (size_t)kBlock * D / 2))[slot];
+  }
+  __device__ float v(int d, int slot) const {
+    const uint8_t byte = vt[(size_t)d * 8 + i4_vbyte(slot)];
+    return nibble(byte, i4_vhigh(slot)) * (float)((const _Float16*)(vt + (size_t)kBlock * D / 2))[slot];
+  }
+};
+
 template <typename T, typename Reader>
 __global__ __launch_bounds__(kThreads) void attend_generic_kernel(
     float* __restrict__ out, const T* __restrict__ q, const void* __restrict__ k_arena,
@@ -130,7 +157,12 @@ hipError_t launch_attend_generic(const pkv_geom& g, float* out, const void* q,
                                  const int32_t* chunk_start, int num_seqs, int num_rows,
                                  float scale, hipStream_t stream) {
   const dim3 grid(num_rows, g.num_q_heads), block(kThreads);
-  if (g.dtype == PKV_I8KV) {
+  if (g.dtype == PKV_I4KV) {
+    hipLaunchKernelGGL((attend_generic_kernel<_Float16, TileReaderI4>), grid, block, 0, stream,
+                       out, (const _Float16*)q, k_arena, v_arena, block_table, max_blocks,
+                       context_lens, cu_q_lens, chunk_start, num_seqs, scale, g.num_blocks,
+                       g.num_q_heads, g.num_kv_heads, g.head_dim);
+  } else if (g.dtype == PKV_I8KV) {
     hipLaunchKernelGGL((attend_generic_kernel<_Float16, TileReaderI8>), grid, block, 0, stream,
                        out, (const _Float16*)q, k_arena, v_arena, block_table, max_blocks,
                        context_lens, cu_q_lens, chunk_start, num_seqs, scale, g.num_blocks,

@@ -75,9 +75,24 @@ __host__ __device__ constexpr int i8_kpos(int s) {
   return (s & 3) | ((s >> 1) & 4) | ((s << 1) & 8);
 }
 
+// INT4 tiles: 4-bit codes (two per byte) then 16 fp16 scales, padded to
+// whole 128-byte lines.
+__host__ __device__ constexpr size_t i4_tile_bytes(int head_dim) {
+  return ((size_t)kBlock * head_dim / 2 + 2 * kBlock + 127) / 128 * 128;
+}
+// INT4 K: 8-byte record of slot s within a 16-dim piece, so that the two keys
+// one decode lane reads (s and s + 4 within a group of 8) are adjacent.
+__host__ __device__ constexpr int i4_krec(int s) {
+  return 2 * (4 * ((s >> 3) & 1) + (s & 3)) + ((s >> 2) & 1);
+}
+// INT4 V: byte of slot s within a head dim's 8 bytes, and its nibble.
+__host__ __device__ constexpr int i4_vbyte(int s) { return 4 * (s >> 3) + (s & 3); }
+__host__ __device__ constexpr int i4_vhigh(int s) { return (s >> 2) & 1; }
+
 // Bytes of one (block, KV head) tile of either arena.
 inline size_t kv_tile_bytes(const pkv_geom& g) {
   if (g.dtype == PKV_I8KV) return i8_tile_bytes(g.head_dim);
+  if (g.dtype == PKV_I4KV) return i4_tile_bytes(g.head_dim);
   return (size_t)kBlock * g.head_dim * (g.dtype == PKV_F16 ? 2 : 4);
 }
 

@@ -17,7 +17,7 @@ from typing import Dict, List
 
 import numpy as np
 
-from . import (BLOCK_SIZE, DECODE_SPLIT, F16, F32, I8KV, Pool, geom, kv_append_rope, paged_attention_chunk,
+from . import (BLOCK_SIZE, DECODE_SPLIT, F16, F32, I4KV, I8KV, Pool, geom, kv_append_rope, paged_attention_chunk,
                paged_attention_chunk_workspace_bytes, paged_attention_decode_shared,
                paged_attention_mixed, paged_attention_mixed_workspace_bytes,
                paged_attention_decode, paged_attention_decode_workspace_bytes, pkv_copy_blocks,
@@ -118,16 +118,17 @@ class DeviceWorkload:
         self.tdtype = torch.float16 if w.dtype == "f16" else torch.float32
         self.kv_bits = getattr(w, "kv_bits", 0)
         self.g = geom(w.num_blocks, w.num_kv_heads, w.num_q_heads, w.head_dim,
-                      I8KV if self.kv_bits == 8 else F16 if w.dtype == "f16" else F32)
+                      I8KV if self.kv_bits == 8 else I4KV if self.kv_bits == 4
+                      else F16 if w.dtype == "f16" else F32)
         self.threads = threads
         self.scale = default_scale(w.head_dim)
         N, H, D = w.num_blocks, w.num_kv_heads, w.head_dim
         x = 16 // (2 if w.dtype == "f16" else 4)   # elements per 16-byte piece of K
-        if self.kv_bits == 8:
-            # INT8 tiles: codes, then 16 fp16 scales, padded to 128-byte lines;
-            # unwritten = all-ones bytes (scale NaN), as in the oracle's
+        if self.kv_bits:
+            # INT8 / INT4 tiles: codes, then 16 fp16 scales, padded to 128-byte
+            # lines; unwritten = all-ones bytes (scale NaN), as in the oracle's
             # quantized arena
-            tile = (BLOCK_SIZE * D + 2 * BLOCK_SIZE + 127) // 128 * 128
+            tile = (BLOCK_SIZE * D * self.kv_bits // 8 + 2 * BLOCK_SIZE + 127) // 128 * 128
             self.k_arena = torch.full((N, H, tile), 255, dtype=torch.uint8, device=self.device)
             self.v_arena = torch.full((N, H, tile), 255, dtype=torch.uint8, device=self.device)
         else:
@@ -350,8 +351,8 @@ class DeviceWorkload:
             return 0
         w = self.w
         elt = 2 if w.dtype == "f16" else 4
-        if self.kv_bits == 8:   # codes plus the fp16 scale of each head vector
-            per_tok = 2 * w.num_kv_heads * (w.head_dim + 2)
+        if self.kv_bits:   # codes plus the fp16 scale of each head vector
+            per_tok = 2 * w.num_kv_heads * (w.head_dim * self.kv_bits // 8 + 2)
         else:
             per_tok = 2 * w.num_kv_heads * w.head_dim * elt
         seen = {}

@@ -36,6 +36,8 @@ CALLS = {
     "paged_attention_decode": (("decode_split_kernel", "decode_combine_kernel"), _DECODE_SRC),
     "paged_attention_decode_i8": (("decode_split_i8_kernel", "decode_combine_kernel"),
                                   _DECODE_SRC),
+    "paged_attention_decode_i4": (("decode_split_i4_kernel", "decode_combine_kernel"),
+                                  _DECODE_SRC),
     "paged_attention_chunk": (("chunk_mfma_kernel",), _CHUNK_SRC),
     "paged_attention_mixed": (("mixed_kernel", "mixed_order_kernel"),
                               ("mixed.hip",) + _CHUNK_SRC[1:] + _DECODE_SRC[:2]),

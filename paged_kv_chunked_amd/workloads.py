@@ -69,7 +69,7 @@ class Workload:
     boost_prob: float = 0.0
     boost: float = 8.0
     block_size: int = BLOCK_SIZE
-    kv_bits: int = 0          # 0: K/V cached in the storage dtype; 8: INT8 codes + fp16 scales
+    kv_bits: int = 0          # 0: K/V cached in the storage dtype; 8 / 4: INT8 / INT4 codes + fp16 scales
 
     # ---- derived sizes -------------------------------------------------
     @property

@@ -157,6 +157,11 @@ def i8(w):
     return dataclasses.replace(w, name=w.name + "_i8", kv_bits=8)
 
 
+def i4(w):
+    """The same workload over INT4 arenas (4-bit codes + fp16 scale per head vector)."""
+    return dataclasses.replace(w, name=w.name + "_i4", kv_bits=4)
+
+
 SMALL = {
     "tiny_f32": workloads.tiny,
     "small_decode": small_decode,
@@ -171,6 +176,11 @@ SMALL = {
     "small_mixed_i8": lambda: i8(small_mixed()),
     "generic_i8_d64": lambda: i8(generic_shape("generic_i8_d64", "f16", 8, 2, 64)),
     "generic_i8_g2": lambda: i8(generic_shape("generic_i8_g2", "f16", 8, 4, 128)),
+    "small_decode_i4": lambda: i4(small_decode()),
+    "small_chunk_i4": lambda: i4(small_chunk()),
+    "small_mixed_i4": lambda: i4(small_mixed()),
+    "generic_i4_d64": lambda: i4(generic_shape("generic_i4_d64", "f16", 8, 2, 64)),
+    "generic_i4_g2": lambda: i4(generic_shape("generic_i4_g2", "f16", 8, 4, 128)),
 }
 
 
@@ -193,6 +203,10 @@ def test_chunk_full():
 
 def test_decode_full_i8():
     run_case(i8(workloads.decode_batch()))
+
+
+def test_decode_full_i4():
+    run_case(i4(workloads.decode_batch()))
 
 
 def test_mixed_full_sampled():

@@ -194,6 +194,7 @@ def _geom(**kw):
     (dict(block_size=32), 2), (dict(num_q_heads=30), 2), (dict(head_dim=130 * 2), 2),
     (dict(head_dim=3), 2), (dict(head_dim=12), 2), (dict(head_dim=6, dtype=1), 2),
     (dict(num_blocks=0), 2), (dict(dtype=7), 3), (dict(num_kv_heads=0), 2),
+    (dict(head_dim=40, dtype=2), 2), (dict(head_dim=48, dtype=3), 2),
 ])
 def test_bad_geometry_rejected(lib, kw, code):
     g = _geom(**kw)

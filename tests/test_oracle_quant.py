@@ -118,3 +118,40 @@ def test_quant_arena_gather_is_codec_roundtrip_and_tile_size():
     assert np.array_equal(img_v[:16 * D].reshape(D, 16), a.vq[4, 0].view(np.uint8))
     assert np.array_equal(img_k[16 * D:16 * D + 32].view(np.float16), a.ks[4, 0])
     assert (img_k[16 * D + 32:] == 0xFF).all() and (img_v[16 * D + 32:] == 0xFF).all()
+
+
+def test_int4_tile_image_layout():
+    """INT4 arena image: K records per 16-dim piece at k4_record(slot) (the two
+    keys a decode lane reads for MFMA u = 0, 1 adjacent), each byte holding dims
+    i (low nibble) and 8 + i; V byte 4g + i holding slots 8g + i and 8g + 4 + i; codes as
+    two's-complement nibbles; scales in slot order; padding to 128-byte lines."""
+    rng = np.random.default_rng(6)
+    H, D = 1, 32
+    a = arena.QuantArena(3, H, D, bits=4)
+    k = _groups(rng, 16 * H, D).reshape(16, H, D)
+    v = _groups(rng, 16 * H, D).reshape(16, H, D)
+    a.write([2], 0, k, v)
+    assert arena.quant_tile_size(D, 4) == 384 and arena.quant_tile_size(128, 4) == 1152
+    rec = arena.k4_record(np.arange(16))
+    assert sorted(rec.tolist()) == list(range(16))
+    assert [int(x) for x in rec[[0, 4, 1, 5, 8, 12]]] == [0, 1, 2, 3, 8, 9]
+    img_k, img_v = a.image("k")[2, 0], a.image("v")[2, 0]
+    qk, _ = quant.encode(k, 4)                     # [16 slots][H][D]
+    qv, _ = quant.encode(v, 4)
+    for s in range(16):
+        for p in range(D // 16):
+            for i in range(8):
+                byte = int(img_k[p * 128 + int(rec[s]) * 8 + i])
+                lo, hi = byte & 15, byte >> 4
+                assert lo == int(qk[s, 0, 16 * p + i]) & 15
+                assert hi == int(qk[s, 0, 16 * p + 8 + i]) & 15
+    for d in range(D):
+        for g in range(2):
+            for i in range(4):
+                byte = int(img_v[d * 8 + 4 * g + i])
+                assert byte & 15 == int(qv[8 * g + i, 0, d]) & 15
+                assert byte >> 4 == int(qv[8 * g + 4 + i, 0, d]) & 15
+    assert np.array_equal(img_k[8 * D:8 * D + 32].view(np.float16), a.ks[2, 0])
+    assert (img_k[8 * D + 32:] == 0xFF).all()
+    # unwritten blocks: all-ones bytes
+    assert (a.image("k")[0] == 0xFF).all() and (a.image("v")[1] == 0xFF).all()
