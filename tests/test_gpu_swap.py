@@ -1,12 +1,14 @@
 """GPU: preemption by swapping (Kshipra part 3, section 5).
 
-A decode batch runs; one sequence's blocks are swapped out to pinned host
-memory (pkv_swap_out), compared bit for bit with the oracle's packed tiles,
+A decode batch runs (fp16, INT8 and INT4 arenas); one sequence's blocks are
+swapped out to pinned host memory (pkv_swap_out), compared bit for bit with
+the oracle's packed tiles,
 its old blocks are overwritten, and the tiles are swapped back in
 (pkv_swap_in) into freshly allocated blocks.  With the block-table row
 pointing at the new blocks, the decode output must be bit for bit the output
 before preemption (the kernels never depend on physical block ids).
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -34,9 +36,11 @@ def say(msg):
     print(f"[gpu-swap] {msg}", flush=True)
 
 
-def test_swap_out_in_roundtrip_bitwise():
-    w = workloads.decode_batch(num_seqs=8, lo=100, hi=900, seed=2024)
-    say("set-up")
+@pytest.mark.parametrize("kv_bits", [0, 8, 4])
+def test_swap_out_in_roundtrip_bitwise(kv_bits):
+    w = dataclasses.replace(workloads.decode_batch(num_seqs=8, lo=100, hi=900, seed=2024),
+                            kv_bits=kv_bits)
+    say(f"set-up (kv_bits={kv_bits})")
     dw = harness.DeviceWorkload(w)
     dw.step()
     torch.cuda.synchronize()
@@ -60,7 +64,8 @@ def test_swap_out_in_roundtrip_bitwise():
     assert np.array_equal(buf.numpy(), exp)
 
     # the sequence is preempted: it is restored into other blocks, and its
-    # old blocks are overwritten (all-ones bytes: NaN in fp16) and freed
+    # old blocks are overwritten (all-ones bytes: NaN in fp16, NaN scales in
+    # quantized arenas) and freed
     assert dw.pool.num_free >= nblk
     new = np.array([dw.pool.alloc() for _ in range(nblk)], dtype=np.int32)[::-1].copy()
     assert not set(new.tolist()) & set(old.tolist())

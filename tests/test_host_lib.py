@@ -285,3 +285,55 @@ def test_swap_entry_point_errors(lib):
     assert lib.pkv_swap_in(gp, FAKE, FAKE, FAKE, 2, FAKE, 2 * 2 * tile - 1, None) == 5
     assert lib.pkv_swap_in(gp, FAKE, FAKE, FAKE, 2, ctypes.c_void_p(0x1008), 2 * 2 * tile, None) == 4
     assert lib.pkv_swap_out(gp, FAKE, FAKE, FAKE, -1, FAKE, 0, None) == 4
+
+
+def test_mixed_entry_point_errors(lib):
+    g = _geom()
+    gp = ctypes.byref(g)
+    args = lambda out, dt, ws, wsb, **kw: (gp, out, dt, FAKE, FAKE, FAKE, FAKE, kw.get("mb", 64),
+                                           FAKE, FAKE, kw.get("S", 2), kw.get("T", 100),
+                                           kw.get("mq", 64), kw.get("mc", 500), 0.1, ws, wsb, None)
+    # empty batches are a no-op; nulls, the output dtype, a context longer than
+    # the table and a short workspace are rejected before any launch
+    assert lib.paged_attention_mixed(gp, None, 1, None, None, None, None, 4, None, None, 0, 0, 16,
+                                     64, 0.1, None, 0, None) == 0
+    assert lib.paged_attention_mixed(*args(None, 1, FAKE, 1 << 30)) == 1
+    assert lib.paged_attention_mixed(*args(FAKE, 0, FAKE, 1 << 30)) == 3
+    assert lib.paged_attention_mixed(*args(FAKE, 1, FAKE, 1 << 30, mc=64 * 16 + 1)) == 4
+    assert lib.paged_attention_mixed(*args(FAKE, 1, FAKE, 1 << 30, mq=501)) == 4
+    need = pkv.paged_attention_mixed_workspace_bytes(g, 2, 100, 500)
+    # schedule (4 header ints + 2 x 2 row tiles + 2 x 2 splits, 256-aligned) +
+    # the decode partials of 2 sequences x 2 splits
+    parts = 2 * 32 * 2
+    assert need == 256 + (-(-parts * 128 * 4 // 256) * 256 + parts * 2 * 4)
+    assert lib.paged_attention_mixed(*args(FAKE, 1, FAKE, need - 1)) == 5
+    assert lib.paged_attention_mixed(*args(FAKE, 1, None, need)) == 5
+    # one split per context: the schedule only
+    assert pkv.paged_attention_mixed_workspace_bytes(g, 2, 100, 384) == 256
+    # fp32 storage runs the generic kernel: no workspace
+    assert pkv.paged_attention_mixed_workspace_bytes(_geom(dtype=1), 2, 100, 500) == 0
+
+
+def test_decode_shared_entry_point_errors(lib):
+    g = _geom()
+    gp = ctypes.byref(g)
+    need = pkv.paged_attention_decode_workspace_bytes(g, 3, 1000)
+
+    def call(out=FAKE, dt=1, gs=FAKE, rs=FAKE, ng=1, mskip=2, mgs=3, ws=FAKE, wsb=None, mc=1000):
+        return lib.paged_attention_decode_shared(gp, out, dt, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3,
+                                                 mc, 0.1, gs, rs, ng, mskip, mgs, ws,
+                                                 need if wsb is None else wsb, None)
+    assert call(out=None) == 1
+    assert call(gs=None) == 1 and call(rs=None) == 1
+    assert call(dt=0) == 3
+    assert call(ng=-1) == 4 and call(mskip=-1) == 4 and call(mgs=-1) == 4
+    assert call(mc=64 * 16 + 1) == 4
+    assert call(wsb=need - 1) == 5 and call(ws=None) == 5
+
+
+@pytest.mark.parametrize("dtype,tile", [(0, 16 * 128 * 2), (2, 2176), (3, 1152)])
+def test_swap_bytes_per_storage(lib, dtype, tile):
+    """Swap buffers hold whole tiles: fp16 4 KiB, INT8 and INT4 tiles padded
+    to 128-byte lines (codes + 16 scales)."""
+    g = _geom(dtype=dtype)
+    assert pkv.pkv_swap_bytes(g, 5) == 5 * 2 * 8 * tile
