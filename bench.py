@@ -22,9 +22,10 @@ steps cannot be served from the 256 MB Infinity Cache.
 `roofline` refers to the dominant kernel call (paged_attention_decode): its
 average duration over --steps calls issued back to back (rotating the arena
 copies) between two HIP events on the stream it is launched on
-(`avg_launch_ms`); `avg_launch_ms_isolated` is the mean of per-call events
-inside the timed steps, which adds the event and launch gaps of one call.  `cpu_baseline` times the CPU
-oracle on the same decode workload.
+(`avg_launch_ms`); `avg_launch_ms_isolated` is the mean of per-call events in
+a separate pass of the same steps (an event record adds a gap to the stream,
+so the timed steps carry no events).  `cpu_baseline` times the CPU oracle on
+the same decode workload.
 """
 from __future__ import annotations
 
@@ -48,18 +49,29 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_steps(torch, run_step, kernel_events, steps, warmup):
+def time_steps(torch, run_step, steps, warmup, run_step_events=None, kernel_events=None):
+    """ms per step over ``steps`` plain steps after ``warmup`` untimed ones,
+    bracketed by synchronisations.  Then, if given, the same number of steps
+    with HIP events around the attention call (instrumentation only: an event
+    record adds a gap to the stream, so it stays out of the timed steps) give
+    the mean duration of one isolated call."""
     for i in range(warmup):
         run_step(i)
     torch.cuda.synchronize()
-    kernel_events.clear()
     t0 = time.perf_counter()
     for i in range(steps):
         run_step(warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ker_ms = [a.elapsed_time(b) for a, b in kernel_events]
-    return (t1 - t0) * 1e3 / steps, sum(ker_ms) / len(ker_ms)
+    ms_call = None
+    if run_step_events is not None:
+        kernel_events.clear()
+        for i in range(steps):
+            run_step_events(i)
+        torch.cuda.synchronize()
+        ker_ms = [a.elapsed_time(b) for a, b in kernel_events]
+        ms_call = sum(ker_ms) / len(ker_ms)
+    return (t1 - t0) * 1e3 / steps, ms_call
 
 
 def time_back_to_back(torch, call, n):
@@ -99,6 +111,11 @@ def bench_decode(torch, args, kv_bits=0):
     def run(i):
         k, v = layers[i % len(layers)]
         dw.append(k_arena=k, v_arena=v)
+        dw.decode(k_arena=k, v_arena=v)
+
+    def run_events(i):
+        k, v = layers[i % len(layers)]
+        dw.append(k_arena=k, v_arena=v)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -106,7 +123,7 @@ def bench_decode(torch, args, kv_bits=0):
         b.record()
         events.append((a, b))
 
-    ms_step, ms_call = time_steps(torch, run, events, args.steps, args.warmup)
+    ms_step, ms_call = time_steps(torch, run, args.steps, args.warmup, run_events, events)
 
     def call(i):
         k, v = layers[i % len(layers)]
@@ -128,6 +145,11 @@ def bench_chunk(torch, args):
     def run(i):
         k, v = layers[i % len(layers)]
         dw.append(k_arena=k, v_arena=v)
+        dw.chunk(k_arena=k, v_arena=v)
+
+    def run_events(i):
+        k, v = layers[i % len(layers)]
+        dw.append(k_arena=k, v_arena=v)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -135,7 +157,7 @@ def bench_chunk(torch, args):
         b.record()
         events.append((a, b))
 
-    ms_step, ms_call = time_steps(torch, run, events, args.steps, args.warmup)
+    ms_step, ms_call = time_steps(torch, run, args.steps, args.warmup, run_events, events)
 
     def call(i):
         k, v = layers[i % len(layers)]

@@ -3,12 +3,12 @@
 // section 4 "Chunked Prefill": RoPE at absolute positions P onward).
 //
 // Arena layouts: K [block][head][D/x][16][x] with x = 16 bytes of elements,
-// V [block][head][D][16].  One 256-thread workgroup per new token; each thread
-// owns whole rotation pairs (i, i + D/2), so an in-place q rotation is
-// race-free.  The rotation runs in fp64 with fused multiply-add disabled and is
-// rounded once to the storage dtype (fp16: f64_to_f16_bits; fp32: the
-// hardware's round-to-nearest-even convert), so the stored values are exactly
-// determined by the inputs.
+// V [block][head][D][16].  One or (small batches) four 256-thread workgroups
+// per new token, each with an even share of its work; each thread owns whole rotation pairs
+// (i, i + D/2), so an in-place q rotation is race-free.  The rotation runs in fp64 with fused multiply-add disabled and is
+// rounded once to the storage dtype (fp16: round-to-odd to fp32, then to
+// nearest-even; fp32: the hardware's round-to-nearest-even convert), so the
+// stored values are exactly determined by the inputs.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -17,8 +17,17 @@ namespace {
 constexpr int kThreads = 256;
 
 template <typename T> __device__ inline T store_f64(double x);
+// fp64 -> fp16 with one rounding (to nearest, ties to even): the value is
+// rounded to fp32 with round-to-odd (toward zero, then the last bit set if the
+// conversion was inexact) and that to fp16 to nearest-even.  Rounding to odd
+// in a format of at least 2p + 2 bits (24 >= 2 * 11 + 2) and then to nearest
+// gives the correctly rounded result (Boldo and Melquiond, "Emulation of FMA
+// and correctly rounded sums: proved algorithms using rounding to odd").
+// Matches f64_to_f16_bits, the definition-based conversion the host side uses.
 template <> __device__ inline _Float16 store_f64<_Float16>(double x) {
-  return __builtin_bit_cast(_Float16, f64_to_f16_bits(x));
+  float f = __double2float_rz(x);
+  if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return (_Float16)f;
 }
 template <> __device__ inline float store_f64<float>(double x) { return (float)x; }
 
@@ -29,6 +38,65 @@ __device__ inline void rope_pair(double x0, double x1, double c, double s, doubl
   o1 = x1 * c + x0 * s;
 }
 
+// The query pairs (i, i + D/2) of one token that this thread rotates: the
+// first kQBatch are loaded into registers before the token's position is
+// looked up (their addresses depend on the token index only), so those loads
+// overlap the lookup chain instead of following it.  q may alias q_out: every
+// pair is read and written by one thread, and a thread reads its pairs before
+// writing any of them.
+constexpr int kQBatch = 8;
+template <typename T>
+struct QRotation {
+  T lo[kQBatch], hi[kQBatch];
+  int n0, n, half;  // pairs [n0, n) of the token are this workgroup's
+  size_t tok;       // element offset of the token's first query head
+  // k_tok: the token's k, read instead when there is no q to rotate, so the
+  // loads need no branch (values past the end are never used)
+  __device__ void load(const T* q, const T* k_tok, int t, int Hq, int D, int slice,
+                       int slices) {
+    half = D >> 1;
+    const int total = q != nullptr ? Hq * half : 0;
+    n0 = (int)((long)total * slice / slices);
+    n = (int)((long)total * (slice + 1) / slices);
+    tok = (size_t)t * Hq * D;
+    const T* src = q != nullptr ? q + tok : k_tok;
+    // unconditional loads (indices past the end read the last pair, unused),
+    // so that they are all in flight together
+#pragma unroll
+    for (int j = 0; j < kQBatch; ++j) {
+      const int idx = min(n0 + (int)threadIdx.x + j * kThreads, max(n - 1, 0));
+      const int h = idx / half, i = idx - h * half;
+      lo[j] = src[(size_t)h * D + i];
+      hi[j] = src[(size_t)h * D + i + half];
+    }
+  }
+  __device__ void finish(const T* q, T* q_out, const double2* __restrict__ row, int D) {
+#pragma unroll
+    for (int j = 0; j < kQBatch; ++j) {
+      const int idx = n0 + threadIdx.x + j * kThreads;
+      if (idx < n) {
+        const int h = idx / half, i = idx - h * half;
+        const size_t base = tok + (size_t)h * D;
+        const double2 c = row[i];
+        double o0, o1;
+        rope_pair((double)lo[j], (double)hi[j], c.x, c.y, o0, o1);
+        q_out[base + i] = store_f64<T>(o0);
+        q_out[base + i + half] = store_f64<T>(o1);
+      }
+    }
+    // heads beyond the register batch (more than kQBatch * kThreads pairs)
+    for (int idx = n0 + threadIdx.x + kQBatch * kThreads; idx < n; idx += kThreads) {
+      const int h = idx / half, i = idx - h * half;
+      const size_t base = tok + (size_t)h * D;
+      const double2 c = row[i];
+      double o0, o1;
+      rope_pair((double)q[base + i], (double)q[base + i + half], c.x, c.y, o0, o1);
+      q_out[base + i] = store_f64<T>(o0);
+      q_out[base + i + half] = store_f64<T>(o1);
+    }
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void append_rope_kernel(
     const T* q, T* q_out, const T* __restrict__ k,
@@ -38,44 +106,68 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(
     int num_seqs, const double2* __restrict__ cs, int rope_max_pos, int num_blocks, int Hq,
     int Hkv, int D) {
   const int t = blockIdx.x;
+  const int half = D >> 1;
+  // workgroup blockIdx.y of gridDim.y takes an even share of the token's q
+  // pairs, k pairs and v elements
+  const int sl = blockIdx.y, S = gridDim.y;
+  // the token's q, k and v are requested before its position is looked up
+  QRotation<T> qr;
+  qr.load(q, k + (size_t)t * Hkv * D, t, Hq, D, sl, S);
+  constexpr int kKB = 2, kVB = 4;
+  const int nk0 = (int)((long)Hkv * half * sl / S), nk = (int)((long)Hkv * half * (sl + 1) / S);
+  const int nv0 = (int)((long)Hkv * D * sl / S), nv = (int)((long)Hkv * D * (sl + 1) / S);
+  T klo[kKB], khi[kKB], vv[kVB];
+#pragma unroll
+  for (int j = 0; j < kKB; ++j) {  // unconditional, as for q
+    const int idx = min(nk0 + (int)threadIdx.x + j * kThreads, nk - 1);
+    const int h = idx / half, i = idx - h * half;
+    const T* kp = k + ((size_t)t * Hkv + h) * D;
+    klo[j] = kp[i];
+    khi[j] = kp[i + half];
+  }
+#pragma unroll
+  for (int j = 0; j < kVB; ++j)
+    vv[j] = v[(size_t)t * Hkv * D + min(nv0 + (int)threadIdx.x + j * kThreads, nv - 1)];
   const int b = find_seq(cu_q_lens, num_seqs, t);
   const int pos = chunk_start[b] + (t - cu_q_lens[b]);
   if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
   const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];
   const int slot = pos & 15;
-  const int half = D >> 1;
   const double2* row = cs + (size_t)pos * half;
 
-  if (q != nullptr) {
-#pragma unroll 4
-    for (int idx = threadIdx.x; idx < Hq * half; idx += kThreads) {
-      const int h = idx / half, i = idx - h * half;
-      const size_t base = ((size_t)t * Hq + h) * D;
-      const double2 c = row[i];
-      double o0, o1;
-      rope_pair((double)q[base + i], (double)q[base + i + half], c.x, c.y, o0, o1);
-      q_out[base + i] = store_f64<T>(o0);
-      q_out[base + i + half] = store_f64<T>(o1);
-    }
-  }
+  qr.finish(q, q_out, row, D);
   if (blk < 0 || blk >= num_blocks) return;
   constexpr int x = 16 / sizeof(T);  // K tile layout [D/x][16][x]
-#pragma unroll 2
-  for (int idx = threadIdx.x; idx < Hkv * half; idx += kThreads) {
+  auto put_k = [&](int idx, T a, T c_hi) {
     const int h = idx / half, i = idx - h * half;
-    const T* kp = k + ((size_t)t * Hkv + h) * D;
     const double2 c = row[i];
     double o0, o1;
-    rope_pair((double)kp[i], (double)kp[i + half], c.x, c.y, o0, o1);
+    rope_pair((double)a, (double)c_hi, c.x, c.y, o0, o1);
     T* tile = k_arena + ((size_t)blk * Hkv + h) * kBlock * D;
     tile[((i / x) * kBlock + slot) * x + i % x] = store_f64<T>(o0);
     tile[(((i + half) / x) * kBlock + slot) * x + (i + half) % x] = store_f64<T>(o1);
+  };
+#pragma unroll
+  for (int j = 0; j < kKB; ++j) {
+    const int idx = nk0 + threadIdx.x + j * kThreads;
+    if (idx < nk) put_k(idx, klo[j], khi[j]);
   }
-#pragma unroll 4
-  for (int idx = threadIdx.x; idx < Hkv * D; idx += kThreads) {
+  for (int idx = nk0 + threadIdx.x + kKB * kThreads; idx < nk; idx += kThreads) {
+    const int h = idx / half, i = idx - h * half;
+    const T* kp = k + ((size_t)t * Hkv + h) * D;
+    put_k(idx, kp[i], kp[i + half]);
+  }
+  auto put_v = [&](int idx, T val) {
     const int h = idx / D, d = idx - h * D;
-    v_arena[(((size_t)blk * Hkv + h) * D + d) * kBlock + slot] = v[((size_t)t * Hkv + h) * D + d];
+    v_arena[(((size_t)blk * Hkv + h) * D + d) * kBlock + slot] = val;
+  };
+#pragma unroll
+  for (int j = 0; j < kVB; ++j) {
+    const int idx = nv0 + threadIdx.x + j * kThreads;
+    if (idx < nv) put_v(idx, vv[j]);
   }
+  for (int idx = nv0 + threadIdx.x + kVB * kThreads; idx < nv; idx += kThreads)
+    put_v(idx, v[(size_t)t * Hkv * D + idx]);
 }
 
 // Group quantization of one (token, KV head) vector, Kshipra part 3 section
@@ -112,6 +204,11 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
     int num_seqs, const double2* __restrict__ cs, int rope_max_pos, int num_blocks, int Hq,
     int Hkv, int D) {
   const int t = blockIdx.x;
+  // workgroup blockIdx.y of gridDim.y takes an even share of the q pairs and
+  // the KV heads blockIdx.y * kWaves + wave, + gridDim.y * kWaves, ...
+  const int sl = blockIdx.y, S = gridDim.y;
+  QRotation<_Float16> qr;
+  qr.load(q, k + (size_t)t * Hkv * D, t, Hq, D, sl, S);  // before the position lookup
   const int b = find_seq(cu_q_lens, num_seqs, t);
   const int pos = chunk_start[b] + (t - cu_q_lens[b]);
   if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
@@ -120,25 +217,14 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
   const int half = D >> 1;
   const double2* row = cs + (size_t)pos * half;
 
-  if (q != nullptr) {
-#pragma unroll 4
-    for (int idx = threadIdx.x; idx < Hq * half; idx += kThreads) {
-      const int h = idx / half, i = idx - h * half;
-      const size_t base = ((size_t)t * Hq + h) * D;
-      const double2 c = row[i];
-      double o0, o1;
-      rope_pair((double)q[base + i], (double)q[base + i + half], c.x, c.y, o0, o1);
-      q_out[base + i] = store_f64<_Float16>(o0);
-      q_out[base + i + half] = store_f64<_Float16>(o1);
-    }
-  }
+  qr.finish(q, q_out, row, D);
   if (blk < 0 || blk >= num_blocks) return;
   const size_t tile_bytes = i8_tile_bytes(D);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int kWaves = kThreads / 64;
   // K: wave w quantizes heads w, w + kWaves, ...; lane l rotates the pairs
   // (l, l + half) and (l + 64, l + 64 + half) that exist
-  for (int h = wave; h < Hkv; h += kWaves) {
+  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
     const _Float16* kp = k + ((size_t)t * Hkv + h) * D;
     float x[4];
     float amax = 0.f;
@@ -170,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
     if (lane == 0) *(_Float16*)(tile + (size_t)kBlock * D + 2 * slot) = sh;
   }
   // V: lane l holds elements l, l + 64, l + 128, l + 192
-  for (int h = wave; h < Hkv; h += kWaves) {
+  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
     const _Float16* vp = v + ((size_t)t * Hkv + h) * D;
     float x[4];
     float amax = 0.f;
@@ -220,6 +306,11 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
     int num_seqs, int num_tokens, const double2* __restrict__ cs, int rope_max_pos,
     int num_blocks, int Hq, int Hkv, int D) {
   const int t = blockIdx.x;
+  // workgroup blockIdx.y of gridDim.y takes an even share of the q pairs and
+  // the KV heads blockIdx.y * kWaves + wave, + gridDim.y * kWaves, ...
+  const int sl = blockIdx.y, S = gridDim.y;
+  QRotation<_Float16> qr;
+  qr.load(q, k + (size_t)t * Hkv * D, t, Hq, D, sl, S);  // before the position lookup
   const int b = find_seq(cu_q_lens, num_seqs, t);
   const int row0 = cu_q_lens[b];
   const int P = chunk_start[b];
@@ -230,25 +321,14 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
   const int half = D >> 1;
   const double2* row = cs + (size_t)pos * half;
 
-  if (q != nullptr) {
-#pragma unroll 4
-    for (int idx = threadIdx.x; idx < Hq * half; idx += kThreads) {
-      const int h = idx / half, i = idx - h * half;
-      const size_t base = ((size_t)t * Hq + h) * D;
-      const double2 c = row[i];
-      double o0, o1;
-      rope_pair((double)q[base + i], (double)q[base + i + half], c.x, c.y, o0, o1);
-      q_out[base + i] = store_f64<_Float16>(o0);
-      q_out[base + i + half] = store_f64<_Float16>(o1);
-    }
-  }
+  qr.finish(q, q_out, row, D);
   if (blk < 0 || blk >= num_blocks) return;
   const size_t tile_bytes = i4_tile_bytes(D);
   const size_t codes = (size_t)kBlock * D / 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int kWaves = kThreads / 64;
   const int krec = i4_krec(slot);
-  for (int h = wave; h < Hkv; h += kWaves) {
+  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
     const _Float16* kp = k + ((size_t)t * Hkv + h) * D;
     float x[4];
     float amax = 0.f;
@@ -289,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
   const bool leader = (pos & 4) == 0 || !partner_in;
   const int tp = t + (ppos - pos);
   const int vbyte = i4_vbyte(slot), vhigh = i4_vhigh(slot);
-  for (int h = wave; h < Hkv; h += kWaves) {
+  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
     const _Float16* vp = v + ((size_t)t * Hkv + h) * D;
     float x[4];
     float amax = 0.f;
@@ -338,7 +418,13 @@ hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, con
                               const int32_t* cu_q_lens, const int32_t* chunk_start,
                               int num_seqs, int num_tokens, const void* rope_table,
                               int rope_max_pos, hipStream_t stream) {
-  const dim3 grid(num_tokens), block(kThreads);
+  // Small batches (decode steps) spread each token over 4 workgroups: their
+  // append is latency-bound, and shorter per-workgroup chains help (10.8 ->
+  // 6.0 us for 64 tokens).  Large batches already fill the chip with one
+  // workgroup per token, and slicing them only adds lookups (58 -> 75 us for
+  // 4096 tokens).
+  const int slices = num_tokens < 512 ? 4 : 1;
+  const dim3 grid(num_tokens, slices), block(kThreads);
   if (g.dtype == PKV_I4KV) {
     hipLaunchKernelGGL(append_rope_i4_kernel, grid, block, 0, stream, (const _Float16*)q,
                        (_Float16*)q_out, (const _Float16*)k, (const _Float16*)v,
