@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(
   T klo[kKB], khi[kKB], vv[kVB];
 #pragma unroll
   for (int j = 0; j < kKB; ++j) {  // unconditional, as for q
-    const int idx = min(nk0 + (int)threadIdx.x + j * kThreads, nk - 1);
+    const int idx = max(min(nk0 + (int)threadIdx.x + j * kThreads, nk - 1), 0);
     const int h = idx / half, i = idx - h * half;
     const T* kp = k + ((size_t)t * Hkv + h) * D;
     klo[j] = kp[i];
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(
   }
 #pragma unroll
   for (int j = 0; j < kVB; ++j)
-    vv[j] = v[(size_t)t * Hkv * D + min(nv0 + (int)threadIdx.x + j * kThreads, nv - 1)];
+    vv[j] = v[(size_t)t * Hkv * D + max(min(nv0 + (int)threadIdx.x + j * kThreads, nv - 1), 0)];
   const int b = find_seq(cu_q_lens, num_seqs, t);
   const int pos = chunk_start[b] + (t - cu_q_lens[b]);
   if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
@@ -168,6 +168,98 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(
   }
   for (int idx = nv0 + threadIdx.x + kVB * kThreads; idx < nv; idx += kThreads)
     put_v(idx, v[(size_t)t * Hkv * D + idx]);
+}
+
+// Vector form for head dims whose halves are whole 16-byte pieces (the
+// tuned shapes): a thread rotates one piece of x = 16 / sizeof(T) pairs --
+// dims i0 .. i0+x-1 with their partners i0+D/2 .. -- with two 16-byte loads
+// and two 16-byte stores, for q and for k; a k piece is exactly one 16-byte
+// slot of the K tile.  V keeps element stores (its tile is head-dim-major).
+// The first piece of each kind and the first v elements are loaded before the
+// position lookup, as in the scalar form.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void append_rope_vec_kernel(
+    const T* q, T* q_out, const T* __restrict__ k, const T* __restrict__ v,
+    T* __restrict__ k_arena, T* __restrict__ v_arena, const int32_t* __restrict__ block_table,
+    int max_blocks, const int32_t* __restrict__ cu_q_lens,
+    const int32_t* __restrict__ chunk_start, int num_seqs, const double2* __restrict__ cs,
+    int rope_max_pos, int num_blocks, int Hq, int Hkv, int D) {
+  constexpr int x = 16 / sizeof(T);
+  typedef T vecT __attribute__((ext_vector_type(x)));
+  const int t = blockIdx.x, sl = blockIdx.y, S = gridDim.y;
+  const int half = D >> 1, cph = half / x;  // pieces per half head
+  auto share = [&](int n, int& lo, int& hi) {
+    lo = (int)((long)n * sl / S);
+    hi = (int)((long)n * (sl + 1) / S);
+  };
+  int nq0, nq, nk0, nk, nv0, nv;
+  share(q != nullptr ? Hq * cph : 0, nq0, nq);
+  share(Hkv * cph, nk0, nk);
+  share(Hkv * D, nv0, nv);
+  const size_t qtok = (size_t)t * Hq * D, ktok = (size_t)t * Hkv * D;
+  // first pieces, unconditionally (a clamped index past the end is unused)
+  const T* qsrc = q != nullptr ? q + qtok : k + ktok;
+  auto piece_ptr = [&](const T* base, int idx) { return base + (idx / cph) * D + (idx % cph) * x; };
+  const int iq = min(nq0 + (int)threadIdx.x, max(nq - 1, 0));
+  const int ik = max(min(nk0 + (int)threadIdx.x, nk - 1), 0);  // a share may be empty
+  const vecT qlo = *(const vecT*)piece_ptr(qsrc, iq), qhi = *(const vecT*)(piece_ptr(qsrc, iq) + half);
+  const vecT klo = *(const vecT*)piece_ptr(k + ktok, ik), khi = *(const vecT*)(piece_ptr(k + ktok, ik) + half);
+  constexpr int kVB = 4;
+  T vv[kVB];
+#pragma unroll
+  for (int j = 0; j < kVB; ++j)
+    vv[j] = v[ktok + max(min(nv0 + (int)threadIdx.x + j * kThreads, nv - 1), 0)];
+
+  const int b = find_seq(cu_q_lens, num_seqs, t);
+  const int pos = chunk_start[b] + (t - cu_q_lens[b]);
+  if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
+  const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];
+  const int slot = pos & 15;
+  const double2* row = cs + (size_t)pos * half;
+
+  auto rotate = [&](vecT lo, vecT hi, int c, vecT& olo, vecT& ohi) {
+#pragma unroll
+    for (int e = 0; e < x; ++e) {
+      const double2 r = row[c * x + e];
+      double o0, o1;
+      rope_pair((double)lo[e], (double)hi[e], r.x, r.y, o0, o1);
+      olo[e] = store_f64<T>(o0);
+      ohi[e] = store_f64<T>(o1);
+    }
+  };
+  // q: in place allowed (each piece is read and written by one thread, which
+  // reads it before writing)
+  for (int idx = nq0 + threadIdx.x; idx < nq; idx += kThreads) {
+    const vecT lo = idx == iq ? qlo : *(const vecT*)piece_ptr(q + qtok, idx);
+    const vecT hi = idx == iq ? qhi : *(const vecT*)(piece_ptr(q + qtok, idx) + half);
+    vecT olo, ohi;
+    rotate(lo, hi, idx % cph, olo, ohi);
+    T* dst = q_out + qtok + (idx / cph) * D + (idx % cph) * x;
+    *(vecT*)dst = olo;
+    *(vecT*)(dst + half) = ohi;
+  }
+  if (blk < 0 || blk >= num_blocks) return;
+  for (int idx = nk0 + threadIdx.x; idx < nk; idx += kThreads) {
+    const vecT lo = idx == ik ? klo : *(const vecT*)piece_ptr(k + ktok, idx);
+    const vecT hi = idx == ik ? khi : *(const vecT*)(piece_ptr(k + ktok, idx) + half);
+    const int h = idx / cph, c = idx % cph;
+    vecT olo, ohi;
+    rotate(lo, hi, c, olo, ohi);
+    T* tile = k_arena + ((size_t)blk * Hkv + h) * kBlock * D;  // [D/x][16][x]
+    *(vecT*)(tile + (c * kBlock + slot) * x) = olo;
+    *(vecT*)(tile + ((c + cph) * kBlock + slot) * x) = ohi;
+  }
+  auto put_v = [&](int idx, T val) {
+    const int h = idx / D, d = idx - h * D;
+    v_arena[(((size_t)blk * Hkv + h) * D + d) * kBlock + slot] = val;
+  };
+#pragma unroll
+  for (int j = 0; j < kVB; ++j) {
+    const int idx = nv0 + threadIdx.x + j * kThreads;
+    if (idx < nv) put_v(idx, vv[j]);
+  }
+  for (int idx = nv0 + threadIdx.x + kVB * kThreads; idx < nv; idx += kThreads)
+    put_v(idx, v[ktok + idx]);
 }
 
 // Group quantization of one (token, KV head) vector, Kshipra part 3 section
@@ -441,7 +533,20 @@ hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, con
                        g.num_blocks, g.num_q_heads, g.num_kv_heads, g.head_dim);
     return hipGetLastError();
   }
-  if (g.dtype == PKV_F16) {
+  const bool vec = (g.head_dim / 2) % (g.dtype == PKV_F16 ? 8 : 4) == 0;
+  if (g.dtype == PKV_F16 && vec) {
+    hipLaunchKernelGGL(append_rope_vec_kernel<_Float16>, grid, block, 0, stream,
+                       (const _Float16*)q, (_Float16*)q_out, (const _Float16*)k,
+                       (const _Float16*)v, (_Float16*)k_arena, (_Float16*)v_arena, block_table,
+                       max_blocks, cu_q_lens, chunk_start, num_seqs, (const double2*)rope_table,
+                       rope_max_pos, g.num_blocks, g.num_q_heads, g.num_kv_heads, g.head_dim);
+  } else if (g.dtype == PKV_F32 && vec) {
+    hipLaunchKernelGGL(append_rope_vec_kernel<float>, grid, block, 0, stream, (const float*)q,
+                       (float*)q_out, (const float*)k, (const float*)v, (float*)k_arena,
+                       (float*)v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
+                       num_seqs, (const double2*)rope_table, rope_max_pos, g.num_blocks,
+                       g.num_q_heads, g.num_kv_heads, g.head_dim);
+  } else if (g.dtype == PKV_F16) {
     hipLaunchKernelGGL(append_rope_kernel<_Float16>, grid, block, 0, stream,
                        (const _Float16*)q, (_Float16*)q_out, (const _Float16*)k,
                        (const _Float16*)v, (_Float16*)k_arena, (_Float16*)v_arena, block_table,
