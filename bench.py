@@ -250,8 +250,12 @@ def bench_mixed(torch, args):
     dw = harness.DeviceWorkload(w)
     dw.step()
     dw.mixed()
-    ms_sep = time_back_to_back(torch, lambda i: (dw.chunk(), dw.decode()), max(args.steps // 5, 5))
-    ms_mix = time_back_to_back(torch, lambda i: dw.mixed(), max(args.steps // 5, 5))
+    n = max(args.steps // 5, 5)
+    ms_sep = time_back_to_back(torch, lambda i: (dw.chunk(), dw.decode()), n)
+    ms_mix = time_back_to_back(torch, lambda i: dw.mixed(), n)
+    # the whole step: the 2048 new tokens appended, then the attention
+    ms_sep_step = time_back_to_back(torch, lambda i: (dw.append(), dw.chunk(), dw.decode()), n)
+    ms_mix_step = time_back_to_back(torch, lambda i: (dw.append(), dw.mixed()), n)
     nbytes, flops = dw.decode_bytes(), dw.chunk_flops()
     roof_ms = (nbytes / (PEAK_HBM_GBS * 1e9) + flops / (PEAK_F16_TFLOPS * 1e12)) * 1e3
     res = {
@@ -263,6 +267,8 @@ def bench_mixed(torch, args):
         "ms_separate_calls": round(ms_sep, 5),
         "ms_mixed_call": round(ms_mix, 5),
         "speedup": round(ms_sep / ms_mix, 3),
+        "ms_step_append_separate_calls": round(ms_sep_step, 5),
+        "ms_step_append_mixed_call": round(ms_mix_step, 5),
         "roofline": {
             "kernel": "paged_attention_mixed (mixed_order_kernel + mixed_kernel + "
                       "decode_combine_kernel)",

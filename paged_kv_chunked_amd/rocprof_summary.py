@@ -12,7 +12,7 @@
         record stores the SHA-256 of the kernel sources, so bench.py only uses
         it while those sources are unchanged.  Dispatches are averaged per
         kernel name, so the profiled command must run each kernel on one
-        workload only (bench.py --no-shared --no-swap).
+        workload only (bench.py --no-shared --no-swap --no-mixed).
 
 rocprofv3 writes one SQLite database per process; its ``kernels`` and
 ``pmc_events`` views are read here.
