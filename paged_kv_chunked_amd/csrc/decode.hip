@@ -74,10 +74,19 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
     const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ group_start, const int32_t* __restrict__ row_skip,
-    float scale_log2, int Hkv, int nsplit_max, int num_blocks, int zheads, int num_seqs) {
-  const int split = blockIdx.x, gi = blockIdx.y;
-  const int quad = blockIdx.z / zheads;
-  const int g = (blockIdx.z - quad * zheads) * kDecodeWavesPerWG + (threadIdx.x >> 6);
+    float scale_log2, int Hkv, int nsplit_max, int num_blocks, int zheads, int num_seqs,
+    int nsx8, int quads) {
+  // Linear workgroup i = ((group * zheads + z) * quads + quad) * nsx8 + split,
+  // nsx8 a multiple of 8: workgroups are dealt to the 8 XCDs by i mod 8, so
+  // every quad (and group) reading split s runs on XCD s mod 8, close in time,
+  // and the split's blocks come from HBM into that XCD's L2 once.
+  int i = blockIdx.x;
+  const int split = i % nsx8;
+  i /= nsx8;
+  const int quad = i % quads;
+  i /= quads;
+  const int zh = i % zheads, gi = i / zheads;
+  const int g = zh * kDecodeWavesPerWG + (threadIdx.x >> 6);
   if (g >= Hkv) return;
   // rows of the group, clamped to the batch (a bad table cannot address
   // memory outside the buffers)
@@ -627,11 +636,14 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
                       groups->num_groups > 0 && groups->max_skip > 0 && groups->max_group_size > 0;
   if (shared) {
     const int quads = (groups->max_group_size + 3) / 4;
-    const dim3 sgrid(min(groups->max_skip, nsplit), groups->num_groups, quads * zg);
-    hipLaunchKernelGGL(decode_shared_kernel, sgrid, dim3(64 * wpg), 0, stream, ws_o, ws_ml,
-                       (const _Float16*)q, (const _Float16*)k_arena, (const _Float16*)v_arena,
-                       block_table, max_blocks, groups->group_start, groups->row_skip,
-                       scale_log2, g.num_kv_heads, nsplit, g.num_blocks, zg, num_seqs);
+    const int nsx8 = (min(groups->max_skip, nsplit) + 7) / 8 * 8;
+    const long nwg = (long)nsx8 * quads * zg * groups->num_groups;
+    if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(decode_shared_kernel, dim3((unsigned)nwg), dim3(64 * wpg), 0, stream, ws_o,
+                       ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
+                       (const _Float16*)v_arena, block_table, max_blocks, groups->group_start,
+                       groups->row_skip, scale_log2, g.num_kv_heads, nsplit, g.num_blocks, zg,
+                       num_seqs, nsx8, quads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
