@@ -140,3 +140,53 @@ def test_mixed_full():
     sample = sorted(set(w.chunk_rows()[:1] +
                         rng.choice(w.decode_rows(), size=8, replace=False).tolist()))
     check_against_split_calls(w, sample_rows=sample)
+
+
+def test_empty_sequences_change_nothing():
+    """Sequences with no new rows (a repeated cu_q_lens entry) anywhere in the
+    batch leave every output bit of paged_attention_chunk and
+    paged_attention_mixed unchanged."""
+    seqs = [(300, 1), (0, 70), (1000, 1), (48, 16)]
+    w = workloads.build("mixed_empty", 26, "f16", 32, 8, 128, 5.0e5, seqs,
+                        max_blocks_per_seq=70)
+    say(f"{w.name}: set-up")
+    dw = harness.DeviceWorkload(w)
+    dw.append()
+    dw.mixed()
+    torch.cuda.synchronize()
+    ref = dw.mix_out.clone()
+    # insert empty sequences before, between and after the real ones
+    cu = dw.cu_host.tolist()
+    starts = dw.starts_host.tolist()
+    bt = dw.bt_host
+    order = [None, 0, None, 1, 2, None, 3, None]
+    cu2, st2, rows = [0], [], []
+    for o in order:
+        if o is None:
+            cu2.append(cu2[-1])
+            st2.append(0)
+            rows.append(np.full(bt.shape[1], -1, np.int32))
+        else:
+            cu2.append(cu2[-1] + cu[o + 1] - cu[o])
+            st2.append(starts[o])
+            rows.append(bt[o])
+    dev = dw.device
+    cu2 = torch.tensor(cu2, dtype=torch.int32, device=dev)
+    st2 = torch.tensor(st2, dtype=torch.int32, device=dev)
+    bt2 = torch.from_numpy(np.stack(rows)).to(dev)
+    out = torch.full_like(ref, float("nan"))
+    pkv.paged_attention_mixed(dw.g, out, dw.q, dw.k_arena, dw.v_arena, bt2, cu2, st2,
+                              dw.mix_max_q, dw.mix_max_ctx, dw.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out.cpu().numpy()), bits(ref.cpu().numpy()))
+    # the chunk call over the same batch: compare with its own run without the
+    # empty sequences
+    cu1 = torch.tensor(cu, dtype=torch.int32, device=dev)
+    ref_c = torch.full_like(ref, float("nan"))
+    pkv.paged_attention_chunk(dw.g, ref_c, dw.q, dw.k_arena, dw.v_arena, dw.bt, cu1, dw.starts,
+                              dw.mix_max_q, dw.mix_max_ctx, dw.scale)
+    out_c = torch.full_like(ref, float("nan"))
+    pkv.paged_attention_chunk(dw.g, out_c, dw.q, dw.k_arena, dw.v_arena, bt2, cu2, st2,
+                              dw.mix_max_q, dw.mix_max_ctx, dw.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out_c.cpu().numpy()), bits(ref_c.cpu().numpy()))
