@@ -281,6 +281,36 @@ def bench_mixed(torch, args):
     return res
 
 
+def bench_long(torch, args):
+    """The long-context step: 32 decodes at context 32768 and one 4096-token
+    chunk at P = 28672 over a 68 750-block arena (4.5 GB per K/V pair of
+    arenas, beyond the Infinity Cache by itself), each call against its own
+    roofline."""
+    from paged_kv_chunked_amd import harness, workloads
+    w = workloads.long_context()
+    log(f"long-context set-up: {w.num_blocks} blocks")
+    dw = harness.DeviceWorkload(w)
+    dw.step()
+    n = max(args.steps // 5, 5)
+    ms_dec = time_back_to_back(torch, lambda i: dw.decode(), n)
+    ms_chk = time_back_to_back(torch, lambda i: dw.chunk(), n)
+    ms_step = time_back_to_back(torch, lambda i: dw.step(), n)
+    nbytes, flops = dw.decode_bytes(), dw.chunk_flops()
+    res = {
+        "workload": "long_llama3_8b: 32 decodes at 32768 + one 4096-token chunk at P = 28672, "
+                    "Hq 32 / Hkv 8, head_dim 128, fp16, 68750-block arena, 1% of keys x8",
+        "decode": {"ms": round(ms_dec, 5), "bytes": nbytes,
+                   "GBps": round(nbytes / (ms_dec * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(nbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "chunk": {"ms": round(ms_chk, 5), "flops": flops,
+                  "TFLOPs": round(flops / (ms_chk * 1e-3) / 1e12, 1),
+                  "frac_mfma": round(flops / (ms_chk * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)},
+        "ms_step_append_chunk_decode": round(ms_step, 5),
+    }
+    del dw
+    return res
+
+
 def cpu_baseline(w, target_s):
     """The oracle (numpy fp64) on the decode workload: append + attention for
     every decode row, repeated until about target_s seconds have passed."""
@@ -323,6 +353,7 @@ def main():
     ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-shared", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -433,6 +464,9 @@ def main():
     if not args.no_mixed:
         out["mixed_step"] = bench_mixed(torch, args)
         log(f"mixed step: {out['mixed_step']}")
+    if not args.no_long:
+        out["long_context"] = bench_long(torch, args)
+        log(f"long context: {out['long_context']}")
     if not args.no_chunk:
         wc, dwc, ms_cstep, ms_chunk, ms_ccall, flops = bench_chunk(torch, args)
         tf_kernel = flops / (ms_chunk * 1e-3) / 1e12
