@@ -509,13 +509,18 @@ __global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) v
                           context_lens, scale_log2, Hkv, nsplit_max, num_blocks);
 }
 
-// Log-sum-exp merge of the splits of the 4 query heads of one (sequence b, KV
-// head g): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
-// M = max_s m_s.  The split weights are computed once into LDS; then each
-// thread accumulates 2 head dims of one head over the splits with independent
-// 8-byte loads.
-constexpr int kCombineThreads = 256;
-constexpr int kCombineMaxSplits = 512;  // LDS capacity; longer rows loop
+// Log-sum-exp merge of the splits of one (sequence b, query head h):
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// One wave per query head (the 4 heads of KV head g form a workgroup), each
+// lane 2 head dims; every lane forms the split weights itself from the (m, l)
+// pairs, so there is no cross-lane or LDS traffic.  The first kCombineEager
+// splits' partials are requested before the context length arrives (the
+// workspace holds nsplit_max splits per sequence, so these reads stay inside
+// it; the slots past a sequence's own splits are never used), leaving one
+// memory round trip for sequences with at most that many splits.  Longer rows
+// are merged kCombineEager splits at a time under a running maximum.
+constexpr int kCombineThreads = 64 * kG;
+constexpr int kCombineEager = 16;
 
 // Sequence b's output row is b and its context context_lens[b]; with a varlen
 // batch (cu_q_lens != nullptr) only sequences of one row are decodes, their
@@ -526,6 +531,21 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const int32_t* __restrict__ context_lens, int max_blocks, int Hq, int nsplit_max,
     const int32_t* __restrict__ cu_q_lens, int num_tokens) {
   const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int hh = tid >> 6, d = 2 * (tid & 63);  // head within the group, 2 dims
+  // partial (b, split s, head h) sits at ((b * nsplit_max + s) * Hq + h)
+  const size_t part0 = (size_t)b * nsplit_max * Hq + g * kG + hh;
+  const float* ml = ws_ml + 2 * part0;
+  const float* po = ws_o + part0 * kD + d;
+  float2 mlv[kCombineEager], ov[kCombineEager];
+  const int ne = min(kCombineEager, nsplit_max);
+#pragma unroll
+  for (int s = 0; s < kCombineEager; ++s) {
+    if (s < ne) {
+      mlv[s] = *(const float2*)(ml + (size_t)2 * s * Hq);
+      ov[s] = *(const float2*)(po + (size_t)s * Hq * kD);
+    }
+  }
   int row = b, len = 0;
   if (cu_q_lens != nullptr) {
     row = cu_q_lens[b];
@@ -537,50 +557,42 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   const int L = min(min(len, max_blocks * kBlock), nsplit_max * kDecodeSplit);
   const int nsplit = (L + kDecodeSplit - 1) / kDecodeSplit;
   if (nsplit <= 1) return;
-  __shared__ float w_lds[kG][kCombineMaxSplits];
-  __shared__ float inv_den[kG];
-  const int tid = threadIdx.x;
-  const int hh = tid >> 6, d = 2 * (tid & 63);  // head within the group, 2 dims
-  // partial (b, split s, head h) sits at ((b * nsplit_max + s) * Hq + h)
-  const size_t part0 = (size_t)b * nsplit_max * Hq + g * kG + hh;
-  const size_t pstride = Hq;  // between consecutive splits of one head
-  const float* ml = ws_ml + 2 * part0;
-  const float* po = ws_o + part0 * kD + d;
-  float a0 = 0.f, a1 = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += kCombineMaxSplits) {
-    const int ns = min(kCombineMaxSplits, nsplit - s0);
-    // wave hh: running max and denominator of head hh over this range
-    float M = -INFINITY;
-    for (int s = tid & 63; s < nsplit; s += 64) M = fmaxf(M, ml[2 * s * pstride]);
+  float M = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineEager) {
+    if (s0 > 0) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float den = 0.f;
-    for (int s = tid & 63; s < ns; s += 64) {
-      const float w = exp2f(ml[2 * (s0 + s) * pstride] - M);
-      w_lds[hh][s] = w;
-      den += w * ml[2 * (s0 + s) * pstride + 1];
+      for (int s = 0; s < kCombineEager; ++s) {
+        if (s0 + s < nsplit) {
+          mlv[s] = *(const float2*)(ml + (size_t)2 * (s0 + s) * Hq);
+          ov[s] = *(const float2*)(po + (size_t)(s0 + s) * Hq * kD);
+        }
+      }
     }
-    if (s0 == 0) {
-      for (int s = ns + (tid & 63); s < nsplit; s += 64)
-        den += exp2f(ml[2 * s * pstride] - M) * ml[2 * s * pstride + 1];
+    const int ns = min(kCombineEager, nsplit - s0);
+    float Mc = M;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-      if ((tid & 63) == 0) inv_den[hh] = 1.f / den;
+    for (int s = 0; s < kCombineEager; ++s)
+      if (s < ns) Mc = fmaxf(Mc, mlv[s].x);
+    if (s0 > 0) {
+      const float r = exp2f(M - Mc);
+      den *= r;
+      a0 *= r;
+      a1 *= r;
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) {
-      const float w = w_lds[hh][s];
-      const float2 o2 = *(const float2*)(po + (size_t)(s0 + s) * pstride * kD);
-      a0 += w * o2.x;
-      a1 += w * o2.y;
+    M = Mc;
+#pragma unroll
+    for (int s = 0; s < kCombineEager; ++s) {
+      if (s < ns) {
+        const float w = exp2f(mlv[s].x - M);
+        den += w * mlv[s].y;
+        a0 += w * ov[s].x;
+        a1 += w * ov[s].y;
+      }
     }
-    __syncthreads();
   }
+  const float inv = 1.f / den;
   float* dst = out + ((size_t)row * Hq + g * kG + hh) * kD + d;
-  const float inv = inv_den[hh];
-  dst[0] = a0 * inv;
-  dst[1] = a1 * inv;
+  *(float2*)dst = make_float2(a0 * inv, a1 * inv);
 }
 
 }  // namespace
