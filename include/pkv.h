@@ -89,8 +89,12 @@ typedef enum pkv_status {
  *      2 r + u, r = 4 ((s >> 3) & 1) + (s & 3), u = (s >> 2) & 1; byte i of a
  *      record holds dims 16p + i (low) and 16p + 8 + i (high); then fp16
  *      scales [16] (slot order), then padding
- *   V  [head_dim][8 bytes]: byte 4g + i holds slots 8g + i (low) and
- *      8g + 4 + i (high); then fp16 scales [16], then padding
+ *   V  head dims in groups of 64 (the last of 32 if head_dim is not a
+ *      multiple of 64); group j (G = 4 blocks of 16 dims, or 2) holds
+ *      [half h][dim & 15][block (dim >> 4) & 3] words of 4 bytes at
+ *      512 j + 4 ((16 h + (dim & 15)) G + ((dim >> 4) & 3)); byte i of the word
+ *      of half h holds slots 8h + i (low) and 8h + 4 + i (high); then fp16
+ *      scales [16], then padding
  * head_dim must be a multiple of 32. */
 typedef enum pkv_dtype { PKV_F16 = 0, PKV_F32 = 1, PKV_I8KV = 2, PKV_I4KV = 3 } pkv_dtype;
 

@@ -96,6 +96,16 @@ def k4_record(slot):
     return 2 * (4 * ((slot >> 3) & 1) + (slot & 3)) + ((slot >> 2) & 1)
 
 
+def v4_byte(d, slot, head_dim: int):
+    """INT4 V: offset of the byte holding head dim ``d`` of the key in
+    ``slot`` (the library's layout, see QuantArena); its nibble is the high
+    one when (slot >> 2) & 1."""
+    d, slot = np.asarray(d), np.asarray(slot)
+    j = d >> 6
+    G = np.where(head_dim - 64 * j >= 64, 4, 2)
+    return 512 * j + 4 * (((slot >> 3) * 16 + (d & 15)) * G + ((d >> 4) & 3)) + (slot & 3)
+
+
 def kpos(slot):
     """Stored position of the key in ``slot`` among the 16 of a K piece: bits
     2 and 3 exchanged (the library's layout)."""
@@ -117,9 +127,13 @@ class QuantArena:
     code's two's-complement low 4 bits):
       K tile  [D/16][16 records of 8 bytes] (record k4_record(s) of slot s;
               byte i holds dims 16p + i and 16p + 8 + i), then 16 fp16 scales
-      V tile  [D][8 bytes] (byte 4g + i of a dim holds slots 8g + i and
-              8g + 4 + i, so 8 consecutive slots are 4 bytes in order), then
-              16 fp16 scales
+      V tile  head dims in groups of 64 (the last of 32 when D is not a
+              multiple of 64); group j of G 16-dim blocks is [half h][d & 15]
+              [block (d >> 4) & 3] words of 4 bytes at 512 j + 4 ((16 h +
+              (d & 15)) G + ((d >> 4) & 3)) (v4_byte); byte i of the word of
+              half h holds slots 8h + i (low nibble) and 8h + 4 + i (high),
+              so 8 consecutive slots are 4 bytes in order; then 16 fp16
+              scales
     Unwritten slots hold all-ones bytes (code -1, scale NaN), so a read of one
     is NaN."""
 
@@ -181,9 +195,13 @@ class QuantArena:
             if which == "k":                # [piece][record][byte i]: dims i, 8 + i
                 rec = nib[:, :, :, np.argsort(k4_record(np.arange(BLOCK))), :]
                 packed = rec[..., :8] | (rec[..., 8:] << 4)
-            else:                           # [dim][byte 4g + i]: slots 8g + i, 8g + 4 + i
-                n = nib.reshape(nib.shape[:-1] + (2, 2, 4))     # [.., g, half, i]
-                packed = (n[..., 0, :] | (n[..., 1, :] << 4)).reshape(nib.shape[:-1] + (8,))
+            else:                           # word of (dim, half h): byte i = slots 8h + i, 8h + 4 + i
+                n = nib.reshape(nib.shape[:-1] + (2, 2, 4))     # [N][H][D][h][hi][i]
+                words = n[..., 0, :] | (n[..., 1, :] << 4)      # [N][H][D][h][i]
+                blocks = words.reshape(N, H, D // 16, 16, 2, 4)  # [N][H][db][d & 15][h][i]
+                groups = [blocks[:, :, b0:b0 + 4].transpose(0, 1, 4, 3, 2, 5).reshape(N, H, -1)
+                          for b0 in range(0, D // 16, 4)]       # [h][d & 15][db & 3][i]
+                packed = np.concatenate(groups, axis=2)
             codes = np.ascontiguousarray(packed).reshape(N, H, -1)
         scales = np.ascontiguousarray(sc).view(np.uint8).reshape(N, H, -1)
         pad = quant_tile_size(D, self.bits) - codes.shape[2] - scales.shape[2]

@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
   const bool partner_in = ppos >= P && ppos < P + C;
   const bool leader = (pos & 4) == 0 || !partner_in;
   const int tp = t + (ppos - pos);
-  const int vbyte = i4_vbyte(slot), vhigh = i4_vhigh(slot);
+  const int vhigh = i4_vhigh(slot);
   for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
     const _Float16* vp = v + ((size_t)t * Hkv + h) * D;
     float x[4];
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
     for (int u = 0; u < 4; ++u) {
       const int d = lane + 64 * u;
       if (d >= D) continue;
-      uint8_t* at = tile + (size_t)d * 8 + vbyte;
+      uint8_t* at = tile + i4_vbyte(d, slot, D);
       const int own = encode4(x[u], s) & 15;
       // the other nibble: the partner's code, or what the byte holds already
       const int other = partner_in ? (encode4(y[u], sp) & 15) : (vhigh ? (*at & 15) : (*at >> 4));

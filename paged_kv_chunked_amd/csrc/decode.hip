@@ -291,9 +291,17 @@ __device__ inline PairI4 load_pair_i4(const uint8_t* __restrict__ k_arena,
     pr.k[j] = __builtin_nontemporal_load((const u32x4*)(kt + (4 * j + lq) * 128 + (ln & 7) * 16));
   const size_t tv = ((size_t)((lq >> 1) ? blk_b : blk_a) * Hkv + g) * kTile;
   const uint8_t* vt = v_arena + tv;
+  // V: the lane's 8 keys (half lq & 1 of its block) for dims 16db + ln, four
+  // dim blocks per 16-byte load (i4_vbyte with D = 128)
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
-    pr.v[db] = __builtin_nontemporal_load((const uint32_t*)(vt + (16 * db + ln) * 8 + 4 * (lq & 1)));
+  for (int j = 0; j < 2; ++j) {
+    const u32x4 w =
+        __builtin_nontemporal_load((const u32x4*)(vt + ((2 * j + (lq & 1)) * 16 + ln) * 16));
+    pr.v[4 * j] = w.x;
+    pr.v[4 * j + 1] = w.y;
+    pr.v[4 * j + 2] = w.z;
+    pr.v[4 * j + 3] = w.w;
+  }
   pr.ks = __builtin_nontemporal_load((const u32x4*)(k_arena + tv + kBlock * kD / 2 + 16 * (lq & 1)));
   pr.vs = __builtin_nontemporal_load((const u32x4*)(vt + kBlock * kD / 2 + 16 * (lq & 1)));
   return pr;

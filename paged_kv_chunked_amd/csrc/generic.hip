@@ -51,7 +51,7 @@ struct TileReaderI8 {
 
 // INT4 tiles: two codes per byte (two's-complement nibbles), then 16 fp16
 // scales, padded to 128-byte lines; K records i4_krec(slot) of 8 bytes per
-// 16-dim piece (byte i: dims i, i + 8), V bytes i4_vbyte(slot) per dim.
+// 16-dim piece (byte i: dims i, i + 8), V byte i4_vbyte(d, slot, D).
 struct TileReaderI4 {
   const uint8_t* kt;
   const uint8_t* vt;
@@ -71,7 +71,7 @@ struct TileReaderI4 {
     return nibble(byte, (d >> 3) & 1) * (float)((const _Float16*)(kt + (size_t)kBlock * D / 2))[slot];
   }
   __device__ float v(int d, int slot) const {
-    const uint8_t byte = vt[(size_t)d * 8 + i4_vbyte(slot)];
+    const uint8_t byte = vt[i4_vbyte(d, slot, D)];
     return nibble(byte, i4_vhigh(slot)) * (float)((const _Float16*)(vt + (size_t)kBlock * D / 2))[slot];
   }
 };

@@ -85,8 +85,17 @@ __host__ __device__ constexpr size_t i4_tile_bytes(int head_dim) {
 __host__ __device__ constexpr int i4_krec(int s) {
   return 2 * (4 * ((s >> 3) & 1) + (s & 3)) + ((s >> 2) & 1);
 }
-// INT4 V: byte of slot s within a head dim's 8 bytes, and its nibble.
-__host__ __device__ constexpr int i4_vbyte(int s) { return 4 * (s >> 3) + (s & 3); }
+// INT4 V: byte holding the code of slot s for head dim d (head_dim D, a
+// multiple of 32), and its nibble.  Head dims go in groups of 64 (the last
+// may hold 32); a group of G 16-dim blocks is [key half s >> 3][d & 15][block
+// (d >> 4) & 3] words of 4 bytes, byte i of a word holding slots 8h + i (low
+// nibble) and 8h + 4 + i (high).  One 16-byte load then gives a decode lane
+// the 8 keys of one half for 4 dim blocks.
+__host__ __device__ constexpr int i4_vbyte(int d, int s, int D) {
+  return 512 * (d >> 6) +
+         4 * (((s >> 3) * 16 + (d & 15)) * (D - 64 * (d >> 6) >= 64 ? 4 : 2) + ((d >> 4) & 3)) +
+         (s & 3);
+}
 __host__ __device__ constexpr int i4_vhigh(int s) { return (s >> 2) & 1; }
 
 // Bytes of one (block, KV head) tile of either arena.

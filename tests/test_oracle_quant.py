@@ -120,18 +120,20 @@ def test_quant_arena_gather_is_codec_roundtrip_and_tile_size():
     assert (img_k[16 * D + 32:] == 0xFF).all() and (img_v[16 * D + 32:] == 0xFF).all()
 
 
-def test_int4_tile_image_layout():
+@pytest.mark.parametrize("D", [32, 96, 128])
+def test_int4_tile_image_layout(D):
     """INT4 arena image: K records per 16-dim piece at k4_record(slot) (the two
     keys a decode lane reads for MFMA u = 0, 1 adjacent), each byte holding dims
-    i (low nibble) and 8 + i; V byte 4g + i holding slots 8g + i and 8g + 4 + i; codes as
+    i (low nibble) and 8 + i; V words of 4 bytes per (dim, key half) grouped by
+    64 dims, byte i of half h holding slots 8h + i and 8h + 4 + i; codes as
     two's-complement nibbles; scales in slot order; padding to 128-byte lines."""
     rng = np.random.default_rng(6)
-    H, D = 1, 32
+    H = 1
     a = arena.QuantArena(3, H, D, bits=4)
     k = _groups(rng, 16 * H, D).reshape(16, H, D)
     v = _groups(rng, 16 * H, D).reshape(16, H, D)
     a.write([2], 0, k, v)
-    assert arena.quant_tile_size(D, 4) == 384 and arena.quant_tile_size(128, 4) == 1152
+    assert arena.quant_tile_size(32, 4) == 384 and arena.quant_tile_size(128, 4) == 1152
     rec = arena.k4_record(np.arange(16))
     assert sorted(rec.tolist()) == list(range(16))
     assert [int(x) for x in rec[[0, 4, 1, 5, 8, 12]]] == [0, 1, 2, 3, 8, 9]
@@ -145,12 +147,19 @@ def test_int4_tile_image_layout():
                 lo, hi = byte & 15, byte >> 4
                 assert lo == int(qk[s, 0, 16 * p + i]) & 15
                 assert hi == int(qk[s, 0, 16 * p + 8 + i]) & 15
+    # V: every code byte is used exactly once; group j of G dim blocks at 512 j
+    offs = arena.v4_byte(np.arange(D)[:, None], np.arange(16)[None, :], D)
+    assert np.array_equal(offs, arena.v4_byte(np.arange(D)[:, None], np.arange(16)[None, :] ^ 4, D))
+    assert sorted(set(offs.ravel().tolist())) == list(range(8 * D))
     for d in range(D):
-        for g in range(2):
+        j, G = d // 64, (4 if D - 64 * (d // 64) >= 64 else 2)
+        for h in range(2):
             for i in range(4):
-                byte = int(img_v[d * 8 + 4 * g + i])
-                assert byte & 15 == int(qv[8 * g + i, 0, d]) & 15
-                assert byte >> 4 == int(qv[8 * g + 4 + i, 0, d]) & 15
+                at = 512 * j + 4 * ((16 * h + d % 16) * G + (d // 16) % 4) + i
+                assert int(offs[d, 8 * h + i]) == at
+                byte = int(img_v[at])
+                assert byte & 15 == int(qv[8 * h + i, 0, d]) & 15
+                assert byte >> 4 == int(qv[8 * h + 4 + i, 0, d]) & 15
     assert np.array_equal(img_k[8 * D:8 * D + 32].view(np.float16), a.ks[2, 0])
     assert (img_k[8 * D + 32:] == 0xFF).all()
     # unwritten blocks: all-ones bytes
