@@ -257,9 +257,10 @@ __device__ inline PairI8 load_pair_i8(const uint8_t* __restrict__ k_arena,
 // INT4 arenas (PKV_I4KV): the same kernel over 4-bit codes.  A lane's 16-byte
 // K load holds its two keys' records (MFMA u = 0, 1) of one 16-dim piece: low
 // nibbles are dims 0-7, high nibbles dims 8-15 of the piece, so each MFMA
-// operand is one mask per word.  A 4-byte V load holds the lane's 8 keys of
-// one head dim (low nibbles keys 0-3, high nibbles keys 4-7).  Nibbles become
-// fp16 exactly: (n ^ 8) + 1024 - 1032.
+// operand is one mask per word.  Each 4-byte word of V holds the lane's 8
+// keys of one head dim (low nibbles keys 0-3, high nibbles keys 4-7), and one
+// 16-byte V load brings the words of four dim blocks.  Nibbles become fp16
+// exactly: (n ^ 8) + 1024 - 1032.
 struct PairI4 {
   u32x4 k[2];     // [j]: records (u = 0: x, y; u = 1: z, w) of piece 4j + lq
   uint32_t v[8];  // [db]: 8 codes of dim 16db + ln, the lane's 8 keys
