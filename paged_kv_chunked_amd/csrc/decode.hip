@@ -521,40 +521,44 @@ __global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) v
 // Log-sum-exp merge of the splits of one (sequence b, query head h):
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 // One wave per query head (the 4 heads of KV head g form a workgroup), each
-// lane 2 head dims; every lane forms the split weights itself from the (m, l)
-// pairs, so there is no cross-lane or LDS traffic.  The first kCombineEager
-// splits' partials are requested before the context length arrives (the
-// workspace holds nsplit_max splits per sequence, so these reads stay inside
-// it; the slots past a sequence's own splits are never used), leaving one
-// memory round trip for sequences with at most that many splits.  Longer rows
-// are merged kCombineEager splits at a time under a running maximum.
+// lane 2 head dims.  Lane i holds the (m, l) of splits i, i + 64, ...; M and
+// the denominator are wave reductions, and each split's weight reaches every
+// lane through a lane read (no LDS, no barrier).  The (m, l) of the first 64
+// splits and the partial o of the first kPre splits are requested before the
+// context length arrives (the workspace holds nsplit_max splits per sequence,
+// so these reads stay inside it; slots past a sequence's own splits are never
+// used).  kPre = kCombineChunk suits small batches (one memory round trip per
+// row of up to that many splits); for batches whose partials are large the
+// launcher takes kPre = 2, every merged row having at least two splits, so
+// unused slots are not fetched.
 constexpr int kCombineThreads = 64 * kG;
-constexpr int kCombineEager = 16;
+constexpr int kCombineChunk = 16;
+// partial bytes of a batch above which the combine prefetches 2 splits only
+constexpr size_t kCombineEagerBytes = (size_t)64 << 20;
 
 // Sequence b's output row is b and its context context_lens[b]; with a varlen
 // batch (cu_q_lens != nullptr) only sequences of one row are decodes, their
 // output row is cu_q_lens[b] and context_lens holds chunk starts (context
 // chunk_start[b] + 1).
+template <int kPre>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     float* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
     const int32_t* __restrict__ context_lens, int max_blocks, int Hq, int nsplit_max,
     const int32_t* __restrict__ cu_q_lens, int num_tokens) {
+  static_assert(kPre >= 1 && kPre <= kCombineChunk, "prefetch within the first batch");
   const int g = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int hh = tid >> 6, d = 2 * (tid & 63);  // head within the group, 2 dims
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int hh = tid >> 6, d = 2 * lane;  // head within the group, 2 dims
   // partial (b, split s, head h) sits at ((b * nsplit_max + s) * Hq + h)
   const size_t part0 = (size_t)b * nsplit_max * Hq + g * kG + hh;
   const float* ml = ws_ml + 2 * part0;
   const float* po = ws_o + part0 * kD + d;
-  float2 mlv[kCombineEager], ov[kCombineEager];
-  const int ne = min(kCombineEager, nsplit_max);
+  float2 ml0 = make_float2(-INFINITY, 0.f);
+  if (lane < nsplit_max) ml0 = *(const float2*)(ml + (size_t)2 * lane * Hq);
+  float2 ov[kCombineChunk];
 #pragma unroll
-  for (int s = 0; s < kCombineEager; ++s) {
-    if (s < ne) {
-      mlv[s] = *(const float2*)(ml + (size_t)2 * s * Hq);
-      ov[s] = *(const float2*)(po + (size_t)s * Hq * kD);
-    }
-  }
+  for (int s = 0; s < kPre; ++s)
+    if (s < nsplit_max) ov[s] = *(const float2*)(po + (size_t)s * Hq * kD);
   int row = b, len = 0;
   if (cu_q_lens != nullptr) {
     row = cu_q_lens[b];
@@ -566,36 +570,40 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   const int L = min(min(len, max_blocks * kBlock), nsplit_max * kDecodeSplit);
   const int nsplit = (L + kDecodeSplit - 1) / kDecodeSplit;
   if (nsplit <= 1) return;
-  float M = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += kCombineEager) {
-    if (s0 > 0) {
 #pragma unroll
-      for (int s = 0; s < kCombineEager; ++s) {
-        if (s0 + s < nsplit) {
-          mlv[s] = *(const float2*)(ml + (size_t)2 * (s0 + s) * Hq);
-          ov[s] = *(const float2*)(po + (size_t)(s0 + s) * Hq * kD);
-        }
+  for (int s = kPre; s < kCombineChunk; ++s)
+    if (s < nsplit) ov[s] = *(const float2*)(po + (size_t)s * Hq * kD);
+
+  float M = lane < nsplit ? ml0.x : -INFINITY;
+  for (int s = lane + 64; s < nsplit; s += 64) M = fmaxf(M, ml[(size_t)2 * s * Hq]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float w0 = lane < nsplit ? exp2f(ml0.x - M) : 0.f;
+  float den = lane < nsplit ? w0 * ml0.y : 0.f;
+  for (int s = lane + 64; s < nsplit; s += 64)
+    den += exp2f(ml[(size_t)2 * s * Hq] - M) * ml[(size_t)2 * s * Hq + 1];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+
+  float a0 = 0.f, a1 = 0.f;
+  for (int c0 = 0; c0 < nsplit; c0 += 64) {
+    // this lane's weight in the 64 splits from c0 (split c0 + lane)
+    const float wc = c0 == 0 ? w0
+                     : (c0 + lane < nsplit ? exp2f(ml[(size_t)2 * (c0 + lane) * Hq] - M) : 0.f);
+    const int nc = min(64, nsplit - c0);
+    for (int j0 = 0; j0 < nc; j0 += kCombineChunk) {
+      if (c0 + j0 > 0) {
+#pragma unroll
+        for (int s = 0; s < kCombineChunk; ++s)
+          if (j0 + s < nc) ov[s] = *(const float2*)(po + (size_t)(c0 + j0 + s) * Hq * kD);
       }
-    }
-    const int ns = min(kCombineEager, nsplit - s0);
-    float Mc = M;
 #pragma unroll
-    for (int s = 0; s < kCombineEager; ++s)
-      if (s < ns) Mc = fmaxf(Mc, mlv[s].x);
-    if (s0 > 0) {
-      const float r = exp2f(M - Mc);
-      den *= r;
-      a0 *= r;
-      a1 *= r;
-    }
-    M = Mc;
-#pragma unroll
-    for (int s = 0; s < kCombineEager; ++s) {
-      if (s < ns) {
-        const float w = exp2f(mlv[s].x - M);
-        den += w * mlv[s].y;
-        a0 += w * ov[s].x;
-        a1 += w * ov[s].y;
+      for (int s = 0; s < kCombineChunk; ++s) {
+        if (j0 + s < nc) {
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), j0 + s));
+          a0 += w * ov[s].x;
+          a1 += w * ov[s].y;
+        }
       }
     }
   }
@@ -693,9 +701,16 @@ hipError_t launch_decode_combine(const pkv_geom& g, float* out, const float* ws_
                                  const float* ws_ml, const int32_t* lens,
                                  const int32_t* cu_q_lens, int num_tokens, int max_blocks,
                                  int num_seqs, int nsplit_max, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(g.num_kv_heads, num_seqs), dim3(kCombineThreads),
-                     0, stream, out, ws_o, ws_ml, lens, max_blocks, g.num_q_heads, nsplit_max,
-                     cu_q_lens, num_tokens);
+  const size_t partial_bytes =
+      (size_t)num_seqs * g.num_q_heads * nsplit_max * (kD + 2) * sizeof(float);
+  if (partial_bytes <= kCombineEagerBytes)
+    hipLaunchKernelGGL(decode_combine_kernel<kCombineChunk>, dim3(g.num_kv_heads, num_seqs),
+                       dim3(kCombineThreads), 0, stream, out, ws_o, ws_ml, lens, max_blocks,
+                       g.num_q_heads, nsplit_max, cu_q_lens, num_tokens);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<2>, dim3(g.num_kv_heads, num_seqs),
+                       dim3(kCombineThreads), 0, stream, out, ws_o, ws_ml, lens, max_blocks,
+                       g.num_q_heads, nsplit_max, cu_q_lens, num_tokens);
   return hipGetLastError();
 }
 

@@ -58,12 +58,33 @@ def kernel_rows(db):
     return c.execute("select name, grid_x, grid_y, grid_z, duration from kernels").fetchall()
 
 
+def split_clusters(durs, ratio=3.0):
+    """Durations of one (kernel, grid) cut at every gap where the next-longer
+    launch takes more than ``ratio`` times as long: two workloads that happen
+    to launch the same grid (a short and a long one) get separate lines."""
+    durs = sorted(durs)
+    groups, cur = [], [durs[0]]
+    for a, b in zip(durs, durs[1:]):
+        if b > ratio * a:
+            groups.append(cur)
+            cur = []
+        cur.append(b)
+    return groups + [cur]
+
+
 def stats(db, out, command, notes=()):
     """One line per (kernel, grid): launches of one kernel on different
-    workloads have different grids and are kept apart."""
-    agg = collections.defaultdict(list)
+    workloads have different grids and are kept apart.  A (kernel, grid) whose
+    launch durations fall into clusters more than 3x apart is listed once per
+    cluster (grid marked #1, #2, ... from the shortest)."""
+    raw = collections.defaultdict(list)
     for name, gx, gy, gz, dur in kernel_rows(db):
-        agg[(name, f"{gx}x{gy}x{gz}")].append(dur)
+        raw[(name, f"{gx}x{gy}x{gz}")].append(dur)
+    agg = {}
+    for (name, grid), durs in raw.items():
+        groups = split_clusters(durs)
+        for i, grp in enumerate(groups):
+            agg[(name, grid if len(groups) == 1 else f"{grid} #{i + 1}")] = grp
     lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", ""]
     lines += [f"- {n}" for n in notes] + ([""] if notes else [])
     lines += ["| kernel | grid (threads) | calls | avg (us) | min (us) | max (us) | total (ms) |",

@@ -181,6 +181,10 @@ SMALL = {
     "small_mixed_i4": lambda: i4(small_mixed()),
     "generic_i4_d64": lambda: i4(generic_shape("generic_i4_d64", "f16", 8, 2, 64)),
     "generic_i4_g2": lambda: i4(generic_shape("generic_i4_g2", "f16", 8, 4, 128)),
+    # head dims that end in a short group: INT4 V words of 2 dim blocks, INT8 K
+    # with an odd number of 16-dim pieces
+    "generic_i4_d96": lambda: i4(generic_shape("generic_i4_d96", "f16", 8, 2, 96)),
+    "generic_i8_d48": lambda: i8(generic_shape("generic_i8_d48", "f16", 8, 2, 48)),
 }
 
 
