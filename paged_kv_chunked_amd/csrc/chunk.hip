@@ -24,8 +24,9 @@
 //     arena's V row;
 //   * online softmax in fp32 (scores in log2 units), P rounded to fp16 for the
 //     second product, and the denominator summed from those rounded values so
-//     the weights still add up to one; the running maximum is only moved when
-//     a score exceeds it by a margin (quotient unchanged, see kSlack);
+//     the weights still add up to one; a row's running maximum is only moved
+//     when one of its scores exceeds it by a margin (quotient unchanged, see
+//     kSlack);
 //   * the causal mask is applied only on tiles that reach past a wave's first
 //     row position; V slots past the sequence's length are zeroed in LDS in
 //     the last tile (p = 0 there, but 0 * NaN would not be 0).

@@ -301,10 +301,12 @@ __device__ __forceinline__ void chunk_tile_unit(
       }
     }
 
-    // online softmax per row (this lane: rows 16rb + lr, 16 keys each).  The
-    // running maximum is only raised when some score exceeds it by more than
-    // kSlack; both the numerator and the denominator use the same (possibly
-    // stale) maximum, so the quotient is unchanged.
+    // online softmax per row (this lane: rows 16rb + lr, 16 keys each).  A
+    // row's running maximum is only raised when one of its scores exceeds it
+    // by more than kSlack; both the numerator and the denominator use the same
+    // (possibly stale) maximum, so the quotient is unchanged.  The decision is
+    // each row's own (rows whose maximum stays get alpha = 1 exactly), so a
+    // row's arithmetic does not depend on which rows share its wave.
     float mloc[kRB];
     bool raise = false;
 #pragma unroll
@@ -320,8 +322,10 @@ __device__ __forceinline__ void chunk_tile_unit(
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         const float mx = max_xor16(max_xor32(mloc[rb]));
-        const float m_new = fmaxf(m_raw[rb], mx);  // finite: key 0 is in tile 0 for every row
-        const float alpha = __builtin_amdgcn_exp2f((m_raw[rb] - m_new) * scale_log2);
+        // finite when raised: key 0 is in tile 0 for every row
+        const float m_new = mx > m_lim[rb] ? mx : m_raw[rb];
+        const float alpha =
+            mx > m_lim[rb] ? __builtin_amdgcn_exp2f((m_raw[rb] - m_new) * scale_log2) : 1.f;
         m_raw[rb] = m_new;
         m_lim[rb] = m_new + slack_raw;
         m_off[rb] = -m_new * scale_log2;
@@ -382,6 +386,7 @@ __device__ __forceinline__ void chunk_tile_unit(
     }
   }
 }
+
 
 }  // namespace
 }  // namespace pkv
