@@ -128,8 +128,9 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(
 #pragma unroll
   for (int j = 0; j < kVB; ++j)
     vv[j] = v[(size_t)t * Hkv * D + max(min(nv0 + (int)threadIdx.x + j * kThreads, nv - 1), 0)];
-  const int b = find_seq(cu_q_lens, num_seqs, t);
-  const int pos = chunk_start[b] + (t - cu_q_lens[b]);
+  int row0, P;
+  const int b = find_seq_start(cu_q_lens, chunk_start, num_seqs, t, row0, P);
+  const int pos = P + (t - row0);
   if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
   const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];
   const int slot = pos & 15;
@@ -210,8 +211,9 @@ __global__ __launch_bounds__(kThreads) void append_rope_vec_kernel(
   for (int j = 0; j < kVB; ++j)
     vv[j] = v[ktok + max(min(nv0 + (int)threadIdx.x + j * kThreads, nv - 1), 0)];
 
-  const int b = find_seq(cu_q_lens, num_seqs, t);
-  const int pos = chunk_start[b] + (t - cu_q_lens[b]);
+  int row0, P;
+  const int b = find_seq_start(cu_q_lens, chunk_start, num_seqs, t, row0, P);
+  const int pos = P + (t - row0);
   if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
   const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];
   const int slot = pos & 15;
@@ -301,8 +303,9 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
   const int sl = blockIdx.y, S = gridDim.y;
   QRotation<_Float16> qr;
   qr.load(q, k + (size_t)t * Hkv * D, t, Hq, D, sl, S);  // before the position lookup
-  const int b = find_seq(cu_q_lens, num_seqs, t);
-  const int pos = chunk_start[b] + (t - cu_q_lens[b]);
+  int row0, P;
+  const int b = find_seq_start(cu_q_lens, chunk_start, num_seqs, t, row0, P);
+  const int pos = P + (t - row0);
   if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
   const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];
   const int slot = pos & 15;
@@ -403,9 +406,8 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
   const int sl = blockIdx.y, S = gridDim.y;
   QRotation<_Float16> qr;
   qr.load(q, k + (size_t)t * Hkv * D, t, Hq, D, sl, S);  // before the position lookup
-  const int b = find_seq(cu_q_lens, num_seqs, t);
-  const int row0 = cu_q_lens[b];
-  const int P = chunk_start[b];
+  int row0, P;
+  const int b = find_seq_start(cu_q_lens, chunk_start, num_seqs, t, row0, P);
   const int pos = P + (t - row0);
   if (pos < 0 || pos >= rope_max_pos || (pos >> 4) >= max_blocks) return;
   const int blk = block_table[(size_t)b * max_blocks + (pos >> 4)];

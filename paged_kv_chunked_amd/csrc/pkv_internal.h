@@ -64,6 +64,33 @@ __device__ inline int find_seq(const int32_t* __restrict__ cu, int num_seqs, int
   return lo;
 }
 
+// find_seq for the append kernels, which also need the row's sequence start
+// row0 = cu[b] and chunk start P = start[b]: the final round (at most 64
+// candidates, one per lane) loads each candidate's start beside its cu, so the
+// lookup of a batch of up to 64 sequences is one dependent load, not two.
+__device__ inline int find_seq_start(const int32_t* __restrict__ cu,
+                                     const int32_t* __restrict__ start, int num_seqs, int t,
+                                     int& row0, int& P) {
+  int lo = 0, hi = num_seqs;  // the answer lies in [lo, hi); cu[lo] <= t
+  const int lane = threadIdx.x & 63;
+  while (hi - lo > 64) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const unsigned long long m = __ballot(idx < hi && cu[idx] <= t);
+    if (m == 0) break;  // only if cu[0] > t (caller contract violation)
+    lo += (63 - __clzll(m)) * step;
+    hi = min(hi, lo + step);
+  }
+  const int idx = lo + lane;
+  const bool in = idx < hi;
+  const int c = in ? cu[idx] : 0, p = in ? start[idx] : 0;
+  const unsigned long long m = __ballot(in && c <= t);
+  const int l = m ? 63 - __clzll(m) : 0;  // lane 0 (= lo) on a contract violation
+  row0 = __builtin_amdgcn_readlane(c, l);
+  P = __builtin_amdgcn_readlane(p, l);
+  return lo + l;
+}
+
 // INT8 tiles: codes then 16 fp16 scales, padded to whole 128-byte lines.
 __host__ __device__ constexpr size_t i8_tile_bytes(int head_dim) {
   return ((size_t)kBlock * head_dim + 2 * kBlock + 127) / 128 * 128;
