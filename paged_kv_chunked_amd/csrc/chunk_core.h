@@ -161,6 +161,11 @@ __device__ __forceinline__ void chunk_tile_unit(
     }
   };
 
+  // The first tile's loads go out before the queries' so the two latencies
+  // overlap; then every query load (and the first tile) is complete before
+  // the next tile loads are issued, so the tile waits below count tile loads
+  // only.
+  issue_tile(0);
   // Q^T as the B operand: qf[rb][kd] = Q[row wrow0 + 16rb + lr][dims 32kd + 8lq .. +8]
   half8_t qf[kRB][4];
 #pragma unroll
@@ -176,10 +181,7 @@ __device__ __forceinline__ void chunk_tile_unit(
       }
     }
   }
-  // every query load is complete before the first tile load is issued, so the
-  // tile waits below count tile loads only
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  issue_tile(0);
   if (ntiles > 1) issue_tile(1);
   if (ntiles > 2) issue_tile(2);
 
