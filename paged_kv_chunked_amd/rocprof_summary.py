@@ -3,6 +3,10 @@
     python -m paged_kv_chunked_amd.rocprof_summary stats DB OUT.md --command "..." [--note ...]
         dispatch count and average / min / max / total duration per (kernel,
         grid) (a --kernel-trace --stats run).
+    python -m paged_kv_chunked_amd.rocprof_summary counters DB OUT.json --kernel NAME ... \
+            --command "..." [--simds 1024] [--flops F]
+        per-dispatch averages of the counters of a --pmc run for the named
+        kernels, with MFMA busy % and MFMA flops where those counters exist.
     python -m paged_kv_chunked_amd.rocprof_summary traffic FETCH_DB WRITE_DB OUT.json \
             --copy-mib N --command "..."
         HBM bytes per dispatch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE).
@@ -133,6 +137,63 @@ def traffic(fetch_db, write_db, out, copy_mib, command):
         json.dump(rec, fh, indent=1)
 
 
+def counters(db, out, command, kernels, simds, flops=None):
+    """Per-dispatch averages of every counter of a --pmc run for each kernel
+    whose name contains one of ``kernels`` (dispatches on different grids, or
+    in duration clusters more than 3x apart, listed apart), with the
+    kernel-trace duration of the same dispatches, and where the counters are
+    present:
+      mfma_busy_pct = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES
+                      / (GRBM_GUI_ACTIVE * simds) * 100
+      mfma_f16_flop = SQ_INSTS_VALU_MFMA_MOPS_F16 * 512 (products issued,
+                      masked work included), and its ratio to ``flops`` (the
+                      algorithmic flops of one dispatch of the named kernel).
+    """
+    c = sqlite3.connect(db)
+    disp = {}
+    for did, name, gx, gy, gz, dur in c.execute(
+            "select dispatch_id, name, grid_x, grid_y, grid_z, duration from kernels"):
+        disp[did] = (name, f"{gx}x{gy}x{gz}", dur)
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    for did, name, cname, v in c.execute(
+            "select dispatch_id, name, counter_name, counter_value from pmc_events"):
+        vals[did][cname] += v
+    groups = collections.defaultdict(list)
+    for did, cv in vals.items():
+        name, grid, dur = disp.get(did, (None, None, None))
+        if name is None or not any(k in name for k in kernels):
+            continue
+        groups[(name, grid)].append((dur, cv))
+    split = {}
+    for (name, grid), rows in groups.items():
+        clusters = split_clusters([d for d, _ in rows])
+        for i, cl in enumerate(clusters):
+            lo, hi = cl[0], cl[-1]
+            split[(name, grid if len(clusters) == 1 else f"{grid} #{i + 1}")] = [
+                r for r in rows if lo <= r[0] <= hi]
+    rec = {"command": command, "simds": simds, "kernels": []}
+    for (name, grid), rows in sorted(split.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        n = len(rows)
+        avg = collections.defaultdict(float)
+        for _, cv in rows:
+            for k, v in cv.items():
+                avg[k] += v / n
+        entry = {"kernel": name, "grid": grid, "dispatches": n,
+                 "avg_duration_us": sum(d for d, _ in rows) / n / 1e3,
+                 "counters_per_dispatch": dict(sorted(avg.items()))}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg.get("GRBM_GUI_ACTIVE"):
+            entry["mfma_busy_pct"] = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (
+                avg["GRBM_GUI_ACTIVE"] * simds)
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in avg:
+            entry["mfma_f16_flop"] = avg["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512.0
+            if flops:
+                entry["mfma_f16_flop_over_algorithmic"] = entry["mfma_f16_flop"] / flops
+        rec["kernels"].append(entry)
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
 def load_traffic(path, call):
     """Bytes per call (fetch + write) if the record matches the current sources."""
     try:
@@ -149,6 +210,13 @@ def load_traffic(path, call):
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("counters")
+    a.add_argument("db")
+    a.add_argument("out")
+    a.add_argument("--command", required=True)
+    a.add_argument("--kernel", action="append", required=True)
+    a.add_argument("--simds", type=int, default=1024)
+    a.add_argument("--flops", type=float, default=None)
     a = sub.add_parser("stats")
     a.add_argument("db")
     a.add_argument("out")
@@ -163,6 +231,8 @@ def main():
     args = ap.parse_args()
     if args.cmd == "stats":
         stats(args.db, args.out, args.command, args.note)
+    elif args.cmd == "counters":
+        counters(args.db, args.out, args.command, args.kernel, args.simds, args.flops)
     else:
         traffic(args.fetch_db, args.write_db, args.out, args.copy_mib, args.command)
 

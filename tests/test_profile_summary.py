@@ -30,3 +30,38 @@ def test_traffic_record_needs_matching_sources(tmp_path):
     rec["calls"][call]["sources_sha256"] = "0" * 64
     path.write_text(json.dumps(rec))
     assert rs.load_traffic(str(path), call) is None
+
+
+def _fake_db(path, dispatches):
+    """A database with the two rocprofv3 views the summaries read."""
+    import sqlite3
+    c = sqlite3.connect(path)
+    c.execute("create table kernels (dispatch_id, name, grid_x, grid_y, grid_z, duration)")
+    c.execute("create table pmc_events (dispatch_id, name, counter_name, counter_value)")
+    for did, name, grid, dur, cnt in dispatches:
+        c.execute("insert into kernels values (?, ?, ?, 1, 1, ?)", (did, name, grid, dur))
+        for k, v in cnt.items():  # two rows per counter (per-instance values are summed)
+            c.execute("insert into pmc_events values (?, ?, ?, ?)", (did, name, k, v / 2))
+            c.execute("insert into pmc_events values (?, ?, ?, ?)", (did, name, k, v / 2))
+    c.commit()
+
+
+def test_counters_derive_mfma_busy_and_flops(tmp_path):
+    cnt = {"SQ_VALU_MFMA_BUSY_CYCLES": 512.0 * 1000, "GRBM_GUI_ACTIVE": 1000.0,
+           "SQ_INSTS_VALU_MFMA_MOPS_F16": 2.0e6}
+    long_cnt = dict(cnt, GRBM_GUI_ACTIVE=4000.0)
+    db = str(tmp_path / "run.db")
+    _fake_db(db, [(1, "chunk_mfma_kernel", 512, 140_000.0, cnt),
+                  (2, "chunk_mfma_kernel", 512, 150_000.0, cnt),
+                  (3, "chunk_mfma_kernel", 512, 1_700_000.0, long_cnt),  # same grid, 10x longer
+                  (4, "other_kernel", 64, 5_000.0, cnt)])
+    rec = rs.counters(db, str(tmp_path / "out.json"), "cmd", ["chunk_mfma"], simds=1024,
+                      flops=1.0e9)
+    ks = rec["kernels"]
+    assert [k["grid"] for k in ks] == ["512x1x1 #1", "512x1x1 #2"]
+    short = ks[0]
+    assert short["dispatches"] == 2 and short["avg_duration_us"] == 145.0
+    assert short["mfma_busy_pct"] == 50.0          # 512e3 / (1000 * 1024)
+    assert short["mfma_f16_flop"] == 2.0e6 * 512
+    assert short["mfma_f16_flop_over_algorithmic"] == 2.0e6 * 512 / 1.0e9
+    assert ks[1]["mfma_busy_pct"] == 12.5
