@@ -137,27 +137,35 @@ def traffic(fetch_db, write_db, out, copy_mib, command):
         json.dump(rec, fh, indent=1)
 
 
-def counters(db, out, command, kernels, simds, flops=None):
+def counters(db, out, command, kernels, simds, flops=None, notes=()):
     """Per-dispatch averages of every counter of a --pmc run for each kernel
     whose name contains one of ``kernels`` (dispatches on different grids, or
     in duration clusters more than 3x apart, listed apart), with the
     kernel-trace duration of the same dispatches, and where the counters are
     present:
       mfma_busy_pct = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES
-                      / (GRBM_GUI_ACTIVE * simds) * 100
+                      / (max over XCDs of GRBM_GUI_ACTIVE * simds) * 100
       mfma_f16_flop = SQ_INSTS_VALU_MFMA_MOPS_F16 * 512 (products issued,
-                      masked work included), and its ratio to ``flops`` (the
-                      algorithmic flops of one dispatch of the named kernel).
+                      masked work included), and its ratio to the algorithmic
+                      flops of one dispatch: ``flops`` maps a row's grid label
+                      (e.g. "262144x1x1 #1") to them.
     """
+    flops = flops or {}
     c = sqlite3.connect(db)
     disp = {}
     for did, name, gx, gy, gz, dur in c.execute(
             "select dispatch_id, name, grid_x, grid_y, grid_z, duration from kernels"):
         disp[did] = (name, f"{gx}x{gy}x{gz}", dur)
+    # one row per hardware instance: SQ counters come per shader engine and are
+    # summed; GRBM counters come per XCD, each counting the same active
+    # cycles, and are reduced by their maximum
     vals = collections.defaultdict(lambda: collections.defaultdict(float))
     for did, name, cname, v in c.execute(
             "select dispatch_id, name, counter_name, counter_value from pmc_events"):
-        vals[did][cname] += v
+        if cname.startswith("GRBM_"):
+            vals[did][cname] = max(vals[did][cname], v)
+        else:
+            vals[did][cname] += v
     groups = collections.defaultdict(list)
     for did, cv in vals.items():
         name, grid, dur = disp.get(did, (None, None, None))
@@ -171,7 +179,7 @@ def counters(db, out, command, kernels, simds, flops=None):
             lo, hi = cl[0], cl[-1]
             split[(name, grid if len(clusters) == 1 else f"{grid} #{i + 1}")] = [
                 r for r in rows if lo <= r[0] <= hi]
-    rec = {"command": command, "simds": simds, "kernels": []}
+    rec = {"command": command, "simds": simds, "notes": list(notes), "kernels": []}
     for (name, grid), rows in sorted(split.items(), key=lambda kv: (kv[0][0], kv[0][1])):
         n = len(rows)
         avg = collections.defaultdict(float)
@@ -186,8 +194,9 @@ def counters(db, out, command, kernels, simds, flops=None):
                 avg["GRBM_GUI_ACTIVE"] * simds)
         if "SQ_INSTS_VALU_MFMA_MOPS_F16" in avg:
             entry["mfma_f16_flop"] = avg["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512.0
-            if flops:
-                entry["mfma_f16_flop_over_algorithmic"] = entry["mfma_f16_flop"] / flops
+            if grid in flops:
+                entry["algorithmic_flop"] = flops[grid]
+                entry["mfma_f16_flop_over_algorithmic"] = entry["mfma_f16_flop"] / flops[grid]
         rec["kernels"].append(entry)
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -216,7 +225,9 @@ def main():
     a.add_argument("--command", required=True)
     a.add_argument("--kernel", action="append", required=True)
     a.add_argument("--simds", type=int, default=1024)
-    a.add_argument("--flops", type=float, default=None)
+    a.add_argument("--flops", action="append", default=[],
+                   help="GRID_LABEL=FLOPS, algorithmic flops of one dispatch of that row")
+    a.add_argument("--note", action="append", default=[])
     a = sub.add_parser("stats")
     a.add_argument("db")
     a.add_argument("out")
@@ -232,7 +243,11 @@ def main():
     if args.cmd == "stats":
         stats(args.db, args.out, args.command, args.note)
     elif args.cmd == "counters":
-        counters(args.db, args.out, args.command, args.kernel, args.simds, args.flops)
+        fl = {}
+        for item in args.flops:
+            label, _, val = item.rpartition("=")
+            fl[label] = float(val)
+        counters(args.db, args.out, args.command, args.kernel, args.simds, fl, args.note)
     else:
         traffic(args.fetch_db, args.write_db, args.out, args.copy_mib, args.command)
 

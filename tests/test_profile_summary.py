@@ -40,9 +40,13 @@ def _fake_db(path, dispatches):
     c.execute("create table pmc_events (dispatch_id, name, counter_name, counter_value)")
     for did, name, grid, dur, cnt in dispatches:
         c.execute("insert into kernels values (?, ?, ?, 1, 1, ?)", (did, name, grid, dur))
-        for k, v in cnt.items():  # two rows per counter (per-instance values are summed)
-            c.execute("insert into pmc_events values (?, ?, ?, ?)", (did, name, k, v / 2))
-            c.execute("insert into pmc_events values (?, ?, ?, ?)", (did, name, k, v / 2))
+        for k, v in cnt.items():  # two instances per counter
+            if k.startswith("GRBM_"):  # each instance counts the same active cycles
+                rows = (v, 0.9 * v)
+            else:                      # per-instance shares of the total
+                rows = (v / 2, v / 2)
+            for x in rows:
+                c.execute("insert into pmc_events values (?, ?, ?, ?)", (did, name, k, x))
     c.commit()
 
 
@@ -56,7 +60,7 @@ def test_counters_derive_mfma_busy_and_flops(tmp_path):
                   (3, "chunk_mfma_kernel", 512, 1_700_000.0, long_cnt),  # same grid, 10x longer
                   (4, "other_kernel", 64, 5_000.0, cnt)])
     rec = rs.counters(db, str(tmp_path / "out.json"), "cmd", ["chunk_mfma"], simds=1024,
-                      flops=1.0e9)
+                      flops={"512x1x1 #1": 1.0e9})
     ks = rec["kernels"]
     assert [k["grid"] for k in ks] == ["512x1x1 #1", "512x1x1 #2"]
     short = ks[0]
@@ -64,4 +68,4 @@ def test_counters_derive_mfma_busy_and_flops(tmp_path):
     assert short["mfma_busy_pct"] == 50.0          # 512e3 / (1000 * 1024)
     assert short["mfma_f16_flop"] == 2.0e6 * 512
     assert short["mfma_f16_flop_over_algorithmic"] == 2.0e6 * 512 / 1.0e9
-    assert ks[1]["mfma_busy_pct"] == 12.5
+    assert ks[1]["mfma_busy_pct"] == 12.5 and "mfma_f16_flop_over_algorithmic" not in ks[1]
