@@ -40,9 +40,11 @@ namespace pkv {
 namespace {
 
 constexpr int kOrderBuckets = 4096;  // costs at or above the last bucket share it
+constexpr int kRankSortMax = 256;    // item counts ranked directly instead
 
 // Schedule of the attention kernel: the (sequence, row tile) items sorted by
-// decreasing work (counting sort on the tile count; equal costs in any order),
+// decreasing work (counting sort on the tile count, or for at most
+// kRankSortMax items a direct ranking; equal costs in any order),
 // so the longest items are dispatched first and the short ones fill the gaps
 // at the end.  One workgroup of 1024 threads.
 __global__ __launch_bounds__(1024) void chunk_order_kernel(
@@ -53,6 +55,24 @@ __global__ __launch_bounds__(1024) void chunk_order_kernel(
   __shared__ int part[1024];
   const int tid = threadIdx.x;
   const int n = num_seqs * n_rtiles;
+  if (n <= kRankSortMax) {
+    // few items: each thread ranks its own item against all of them (rank =
+    // items of higher cost, ties broken by index), one LDS pass
+    const int c = tid < n ? chunk_item_cost(cu_q_lens, chunk_start, tid / n_rtiles,
+                                            tid - tid / n_rtiles * n_rtiles, max_blocks, num_tokens)
+                          : 0;
+    part[tid] = c;
+    __syncthreads();
+    if (tid < n) {
+      int rank = 0;
+      for (int j = 0; j < n; ++j) {
+        const int cj = part[j];
+        rank += cj > c || (cj == c && j < tid);
+      }
+      order[rank] = tid;
+    }
+    return;
+  }
   for (int c = tid; c < kOrderBuckets; c += 1024) hist[c] = 0;
   __syncthreads();
   for (int k = tid; k < n; k += 1024) {
