@@ -185,6 +185,10 @@ SMALL = {
     # with an odd number of 16-dim pieces
     "generic_i4_d96": lambda: i4(generic_shape("generic_i4_d96", "f16", 8, 2, 96)),
     "generic_i8_d48": lambda: i8(generic_shape("generic_i8_d48", "f16", 8, 2, 48)),
+    # the largest head dim the library accepts
+    "generic_f16_d256": lambda: generic_shape("generic_f16_d256", "f16", 8, 2, 256),
+    "generic_f32_d256": lambda: generic_shape("generic_f32_d256", "f32", 4, 2, 256),
+    "generic_i4_d256": lambda: i4(generic_shape("generic_i4_d256", "f16", 8, 2, 256)),
 }
 
 
