@@ -226,11 +226,23 @@ pkv_status paged_attention_decode_shared(
  *              P_b + C_b, <= max_blocks_per_seq * 16.
  * workspace    device memory of paged_attention_chunk_workspace_bytes()
  *              bytes (the schedule of the tuned kernel: one int32 per
- *              (sequence, 64-row tile)); PKV_ERR_WORKSPACE if missing or short.
+ *              (sequence, 64-row tile); for a split call also the parts'
+ *              partials, fp32 [parts][num_tokens][Hq][D + 2]);
+ *              PKV_ERR_WORKSPACE if missing or short.
+ * A call with fewer than 512 (64-row tile, KV head) work units (its rows
+ * packed in whole tiles) splits every tile's keys into `parts` even ranges
+ * (up to 8, each at least 512 keys of the longest context) and merges them by
+ * log-sum-exp, so that small batches with long prefixes fill the chip.  Rows
+ * of a split call then round differently (same tolerance) from an unsplit
+ * one; paged_attention_chunk_parts() reports the number of parts the tuned
+ * path uses for a call's sizes (1: not split; always 1 off the tuned path).
  * ------------------------------------------------------------------------- */
 pkv_status paged_attention_chunk_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
                                                  int32_t num_tokens, int32_t max_context_len,
                                                  size_t* bytes);
+pkv_status paged_attention_chunk_parts(const pkv_geom* geom, int32_t num_seqs,
+                                      int32_t num_tokens, int32_t max_context_len,
+                                      int32_t* parts);
 pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dtype,
                                  const void* q, const void* k_arena, const void* v_arena,
                                  const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -246,8 +258,10 @@ pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dt
  * paged_attention_chunk; a sequence with C_b = 1 is a decode (its row sees
  * keys 0 .. P_b, computed in 384-token splits exactly as
  * paged_attention_decode computes a row of context P_b + 1), a sequence with
- * C_b >= 2 a prefill chunk (computed exactly as paged_attention_chunk does).
- * Results are bit for bit those of the two stand-alone calls.
+ * C_b >= 2 a prefill chunk (computed exactly as paged_attention_chunk does
+ * without splitting keys).  Results are bit for bit those of the two
+ * stand-alone calls whenever paged_attention_chunk_parts() is 1 for the
+ * chunk call.
  * workspace    device memory of paged_attention_mixed_workspace_bytes()
  *              bytes: the schedule and the decode partials.  Sized from
  *              num_seqs, num_tokens and max_context_len; PKV_ERR_WORKSPACE if

@@ -64,6 +64,8 @@ _SIGS = {
                                                      _I32, _I32, _P, ctypes.c_size_t, _P]),
     "paged_attention_chunk_workspace_bytes": (ctypes.c_int, [_PG, _I32, _I32, _I32,
                                                              ctypes.POINTER(ctypes.c_size_t)]),
+    "paged_attention_chunk_parts": (ctypes.c_int, [_PG, _I32, _I32, _I32,
+                                                   ctypes.POINTER(ctypes.c_int32)]),
     "paged_attention_chunk": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32,
                                              _I32, _I32, _I32, ctypes.c_float, _P,
                                              ctypes.c_size_t, _P]),
@@ -226,12 +228,22 @@ def paged_attention_chunk_workspace_bytes(g: Geom, num_seqs: int, num_tokens: in
     return n.value
 
 
+def paged_attention_chunk_parts(g: Geom, num_seqs: int, num_tokens: int,
+                                max_context_len: int) -> int:
+    n = ctypes.c_int32()
+    _check(lib().paged_attention_chunk_parts(ctypes.byref(g), num_seqs, num_tokens,
+                                             max_context_len, ctypes.byref(n)),
+           "paged_attention_chunk_parts")
+    return n.value
+
+
 def paged_attention_chunk(g: Geom, out, q, k_arena, v_arena, block_table, cu_q_lens,
                           chunk_start, max_q_len: int, max_context_len: int, scale: float,
                           workspace=None, stream=None) -> None:
     """``workspace``: a device tensor of at least
     paged_attention_chunk_workspace_bytes(...) bytes (the schedule of the
-    attention kernel); None makes a fresh one from torch's allocator."""
+    attention kernel, and the key-range partials when the call is split);
+    None makes a fresh one from torch's allocator."""
     if workspace is None:
         need = paged_attention_chunk_workspace_bytes(g, chunk_start.shape[0], q.shape[0],
                                                      max_context_len)

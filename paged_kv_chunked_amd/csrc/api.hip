@@ -111,7 +111,18 @@ pkv_status paged_attention_chunk_workspace_bytes(const pkv_geom* geom, int32_t n
   if (st != PKV_OK) return st;
   if (!bytes) return PKV_ERR_NULL;
   if (num_seqs < 0 || num_tokens < 0 || max_context_len < 0) return PKV_ERR_RANGE;
-  *bytes = pkv::chunk_workspace_bytes(*geom, num_seqs, num_tokens);
+  *bytes = pkv::chunk_workspace_bytes(*geom, num_seqs, num_tokens, max_context_len);
+  return PKV_OK;
+}
+
+pkv_status paged_attention_chunk_parts(const pkv_geom* geom, int32_t num_seqs,
+                                      int32_t num_tokens, int32_t max_context_len,
+                                      int32_t* parts) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (!parts) return PKV_ERR_NULL;
+  if (num_seqs < 0 || num_tokens < 0 || max_context_len < 0) return PKV_ERR_RANGE;
+  *parts = pkv::chunk_parts(*geom, num_tokens, max_context_len);
   return PKV_OK;
 }
 
@@ -132,7 +143,7 @@ pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dt
   if (max_blocks_per_seq < 1 || max_q_len < 1 || max_context_len < max_q_len ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
     return PKV_ERR_RANGE;
-  const size_t need = pkv::chunk_workspace_bytes(*geom, num_seqs, num_tokens);
+  const size_t need = pkv::chunk_workspace_bytes(*geom, num_seqs, num_tokens, max_context_len);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   return hip_status(pkv::launch_chunk(*geom, (float*)out, q, k_arena, v_arena, block_table,
                                       max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs,

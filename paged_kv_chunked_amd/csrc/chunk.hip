@@ -32,6 +32,7 @@
 //     the last tile (p = 0 there, but 0 * NaN would not be 0).
 // Work items are dispatched longest first (chunk_order_kernel).  Other shapes
 // run the generic kernel.
+#include <algorithm>
 #include <cmath>
 
 #include "chunk_core.h"
@@ -41,6 +42,13 @@ namespace {
 
 constexpr int kOrderBuckets = 4096;  // costs at or above the last bucket share it
 constexpr int kRankSortMax = 256;    // item counts ranked directly instead
+// Key-range parts: a call with fewer than kChunkTargetUnits (row tile, KV
+// head) units (two per compute unit of the chip) splits each item's keys into
+// up to kChunkMaxParts parts of at least kChunkMinPartTiles key tiles, merged
+// by chunk_combine_kernel.
+constexpr long kChunkTargetUnits = 512;
+constexpr int kChunkMaxParts = 8;
+constexpr int kChunkMinPartTiles = 8;
 
 // Schedule of the attention kernel: the (sequence, row tile) items sorted by
 // decreasing work (counting sort on the tile count, or for at most
@@ -119,19 +127,61 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
     const int32_t* __restrict__ order, float scale_log2, int Hkv, int num_seqs, int n_rtiles,
-    int num_blocks, int num_tokens) {
-  // Workgroup i takes item order[i / Hkv] for KV head i % Hkv.  Linear
-  // workgroup ids are dealt to the 8 XCDs round-robin, so with Hkv a multiple
-  // of 8 every row tile of a (sequence, KV head) pair runs on one XCD and the
-  // pair's K/V tiles are fetched into that XCD's L2 once; the longest items
-  // are issued first.
+    int num_blocks, int num_tokens, int parts, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  // Workgroup i takes part (i / Hkv) % parts of item order[i / (Hkv * parts)]
+  // for KV head i % Hkv.  Linear workgroup ids are dealt to the 8 XCDs
+  // round-robin, so with Hkv a multiple of 8 every row tile (and part) of a
+  // (sequence, KV head) pair runs on one XCD and the pair's K/V tiles are
+  // fetched into that XCD's L2 once; the longest items are issued first.
   const int i = blockIdx.x;
-  const int k = i / Hkv, g = i - k * Hkv;
+  const int k = i / (Hkv * parts), rem = i - k * (Hkv * parts);
+  const int part = rem / Hkv, g = rem - part * Hkv;
   if (k >= num_seqs * n_rtiles) return;
   const int item = order[k];
   const int b = item / n_rtiles, rt = item - b * n_rtiles;
   chunk_tile_unit(out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
-                  scale_log2, Hkv, num_blocks, num_tokens, b, rt, g);
+                  scale_log2, Hkv, num_blocks, num_tokens, b, rt, g, part, parts, part_o,
+                  part_ml);
+}
+
+// Merge of the key-range parts of every chunk row (only when the call is split):
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.  One wave
+// per (row, query head), each lane 2 head dims.  Rows the attention kernel
+// skips (a sequence with no keys) are skipped here too.
+__global__ __launch_bounds__(256) void chunk_combine_kernel(
+    float* __restrict__ out, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
+    int num_seqs, int num_tokens, int max_blocks, int Hq, int parts) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int b = find_seq(cu_q_lens, num_seqs, t);
+  const int C = min(cu_q_lens[b + 1], num_tokens) - cu_q_lens[b];
+  const int Lc = min(chunk_start[b] + C, max_blocks * kBlock);
+  if (h >= Hq || Lc <= 0) return;
+  float2 ml[kChunkMaxParts], o[kChunkMaxParts];
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kChunkMaxParts; ++p) {
+    if (p < parts) {
+      const size_t pr = ((size_t)p * num_tokens + t) * Hq + h;
+      ml[p] = *(const float2*)(part_ml + 2 * pr);
+      o[p] = *(const float2*)(part_o + pr * kD + 2 * lane);
+      M = fmaxf(M, ml[p].x);
+    }
+  }
+  float den = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int p = 0; p < kChunkMaxParts; ++p) {
+    if (p < parts && ml[p].x != -INFINITY) {  // a part that saw no key of this row
+      const float w = exp2f(ml[p].x - M);
+      den += w * ml[p].y;
+      a0 += w * o[p].x;
+      a1 += w * o[p].y;
+    }
+  }
+  const float inv = 1.f / den;
+  *(float2*)(out + ((size_t)t * Hq + h) * kD + 2 * lane) = make_float2(a0 * inv, a1 * inv);
 }
 
 }  // namespace
@@ -140,10 +190,30 @@ bool chunk_fast_path(const pkv_geom& g) {
   return g.dtype == PKV_F16 && g.head_dim == kD && g.num_q_heads == kG * g.num_kv_heads;
 }
 
-size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens) {
+int chunk_parts(const pkv_geom& g, int num_tokens, int max_context_len) {
+  if (!chunk_fast_path(g) || num_tokens <= 0) return 1;
+  // fewest (row tile, KV head) units the call can have: its rows packed in
+  // whole 64-row tiles
+  const long units = (long)((num_tokens + kRows - 1) / kRows) * g.num_kv_heads;
+  if (units >= kChunkTargetUnits) return 1;
+  long parts = (kChunkTargetUnits + units - 1) / units;
+  parts = std::min(parts, (long)kChunkMaxParts);
+  parts = std::min(parts, (long)(max_context_len / (kChunkMinPartTiles * kBN)));
+  return (int)std::max(parts, 1L);
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens,
+                             int max_context_len) {
   if (!chunk_fast_path(g) || num_seqs <= 0 || num_tokens <= 0) return 0;
   // the schedule: one int32 per (sequence, row tile)
-  return (size_t)num_seqs * (size_t)((num_tokens + kRows - 1) / kRows) * sizeof(int32_t);
+  const size_t sched = (size_t)num_seqs * (size_t)((num_tokens + kRows - 1) / kRows) * sizeof(int32_t);
+  const int parts = chunk_parts(g, num_tokens, max_context_len);
+  if (parts == 1) return sched;
+  // the parts' partials: o [parts][num_tokens][Hq][D] and (m, l) [parts][num_tokens][Hq][2]
+  const size_t rows = (size_t)parts * num_tokens * g.num_q_heads;
+  return align256(sched) + align256(rows * kD * sizeof(float)) + rows * 2 * sizeof(float);
 }
 
 hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
@@ -165,11 +235,28 @@ hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void
   hipLaunchKernelGGL(chunk_order_kernel, dim3(1), dim3(1024), 0, stream, order, cu_q_lens,
                      chunk_start, num_seqs, n_rtiles, max_blocks, num_tokens);
   const float scale_log2 = scale * 1.4426950408889634f;
-  const long nwg = n_items * g.num_kv_heads;
+  const int parts = chunk_parts(g, num_tokens, max_context_len);
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (parts > 1) {
+    const size_t rows = (size_t)parts * num_tokens * g.num_q_heads;
+    const size_t sched = align256((size_t)n_items * sizeof(int32_t));
+    if (workspace_bytes < sched + align256(rows * kD * sizeof(float)) + rows * 2 * sizeof(float))
+      return hipErrorInvalidValue;
+    part_o = (float*)((char*)workspace + sched);
+    part_ml = part_o + align256(rows * kD * sizeof(float)) / sizeof(float);
+  }
+  const long nwg = n_items * g.num_kv_heads * parts;
+  if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(chunk_mfma_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, out,
                      (const _Float16*)q, (const _Float16*)k_arena, (const _Float16*)v_arena,
                      block_table, max_blocks, cu_q_lens, chunk_start, order, scale_log2,
-                     g.num_kv_heads, num_seqs, n_rtiles, g.num_blocks, num_tokens);
+                     g.num_kv_heads, num_seqs, n_rtiles, g.num_blocks, num_tokens, parts, part_o,
+                     part_ml);
+  if (parts == 1) return hipGetLastError();
+  hipLaunchKernelGGL(chunk_combine_kernel, dim3((unsigned)num_tokens, (g.num_q_heads + 3) / 4),
+                     dim3(256), 0, stream, out, part_o, part_ml, cu_q_lens, chunk_start,
+                     num_seqs, num_tokens, max_blocks, g.num_q_heads, parts);
   return hipGetLastError();
 }
 

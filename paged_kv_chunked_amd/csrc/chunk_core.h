@@ -100,13 +100,19 @@ __device__ inline u32x4 mask_unit(u32x4 x, int key0, int limit) {
   return x;
 }
 
-// Row tile rt of sequence b for KV head g.
+// Row tile rt of sequence b for KV head g.  With parts > 1 the unit covers
+// part `part` of the tile's key tiles (an even share, possibly empty) and
+// writes the unnormalised O, the running maximum (log2 units) and the
+// denominator of every row to part_o / part_ml, [part][row][head], for
+// chunk_combine_kernel to merge.
 __device__ __forceinline__ void chunk_tile_unit(
     float* __restrict__ out, const _Float16* __restrict__ q,
     const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
-    float scale_log2, int Hkv, int num_blocks, int num_tokens, int b, int rt, int g) {
+    float scale_log2, int Hkv, int num_blocks, int num_tokens, int b, int rt, int g,
+    int part = 0, int parts = 1, float* __restrict__ part_o = nullptr,
+    float* __restrict__ part_ml = nullptr) {
   const int row0 = cu_q_lens[b];
   const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
   if (rt * kRows >= C) return;
@@ -127,6 +133,7 @@ __device__ __forceinline__ void chunk_tile_unit(
   const int row_hi = min(C, rt * kRows + kRows);
   const int kend = min(Lc, P + row_hi);  // keys [0, kend) are visible to some row
   const int ntiles = (kend + kBN - 1) / kBN;
+  const int tb = (int)((long)part * ntiles / parts), te = (int)((long)(part + 1) * ntiles / parts);
   const int nblk_seq = (Lc + kBlock - 1) / kBlock;
   const int32_t* bt = block_table + (size_t)b * max_blocks;
 
@@ -165,7 +172,7 @@ __device__ __forceinline__ void chunk_tile_unit(
   // overlap; then every query load (and the first tile) is complete before
   // the next tile loads are issued, so the tile waits below count tile loads
   // only.
-  issue_tile(0);
+  if (tb < te) issue_tile(tb);
   // Q^T as the B operand: qf[rb][kd] = Q[row wrow0 + 16rb + lr][dims 32kd + 8lq .. +8]
   half8_t qf[kRB][4];
 #pragma unroll
@@ -182,8 +189,8 @@ __device__ __forceinline__ void chunk_tile_unit(
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (ntiles > 1) issue_tile(1);
-  if (ntiles > 2) issue_tile(2);
+  if (tb + 1 < te) issue_tile(tb + 1);
+  if (tb + 2 < te) issue_tile(tb + 2);
 
   // absolute positions of this lane's two rows (rows past the chunk borrow the
   // last valid position so they stay finite; they are never stored)
@@ -219,15 +226,15 @@ __device__ __forceinline__ void chunk_tile_unit(
   // (2 (16db + lr) + (lq & 1) + 16 (lq >> 1)) mod 256 of block 2u + (lq >> 1)
   const int vunit = 2 * lr + (lq & 1) + 16 * (lq >> 1);
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = tb; t < te; ++t) {
     // tile t's loads (this wave's) are done; then every wave's, and every
     // wave has finished tile t - 1, whose stage the next load reuses
-    if (t + 2 < ntiles) wait_vm<2 * kLoadsPerTile>();
-    else if (t + 1 < ntiles) wait_vm<kLoadsPerTile>();
+    if (t + 2 < te) wait_vm<2 * kLoadsPerTile>();
+    else if (t + 1 < te) wait_vm<kLoadsPerTile>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + 3 < ntiles) issue_tile(t + 3);
+    if (t + 3 < te) issue_tile(t + 3);
     const u32x4* kl = ring + (t % kStages) * kStageUnits;
     const u32x4* vl = kl + 4 * kUnitsPerBlock;
     if (t * kBN + kBN > Lc) {
@@ -330,7 +337,9 @@ __device__ __forceinline__ void chunk_tile_unit(
             mx > m_lim[rb] ? __builtin_amdgcn_exp2f((m_raw[rb] - m_new) * scale_log2) : 1.f;
         m_raw[rb] = m_new;
         m_lim[rb] = m_new + slack_raw;
-        m_off[rb] = -m_new * scale_log2;
+        // a row that has seen no key yet (only in a later part of its keys)
+        // keeps m_off = 0: its scores are all -inf, so P = 0
+        m_off[rb] = m_new == -INFINITY ? 0.f : -m_new * scale_log2;
         l_run[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; ++db) oacc[db][rb] *= alpha;
@@ -376,14 +385,24 @@ __device__ __forceinline__ void chunk_tile_unit(
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const float l = sum_xor16(sum_xor32(l_run[rb]));
-    const float inv = 1.f / l;
     const int r = wrow0 + 16 * rb + lr;
-    if (r < C) {
+    if (r >= C) continue;
+    if (parts == 1) {
+      const float inv = 1.f / l;
       float* dst = out + ((size_t)(row0 + r) * Hq + h) * kD + 4 * lq;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const f32x4 v = oacc[db][rb] * inv;
         *(f32x4*)(dst + 16 * db) = v;
+      }
+    } else {
+      const size_t pr = ((size_t)part * num_tokens + row0 + r) * Hq + h;
+      float* dst = part_o + pr * kD + 4 * lq;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = oacc[db][rb];
+      if (lq == 0) {
+        part_ml[2 * pr] = m_raw[rb] == -INFINITY ? -INFINITY : m_raw[rb] * scale_log2;
+        part_ml[2 * pr + 1] = l;
       }
     }
   }

@@ -167,7 +167,10 @@ hipError_t launch_decode_combine(const pkv_geom& g, float* out, const float* ws_
                                  int num_seqs, int nsplit_max, hipStream_t stream);
 
 bool chunk_fast_path(const pkv_geom& g);
-size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens);
+size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens,
+                             int max_context_len);
+// key-range parts paged_attention_chunk splits a call's items into (1: none)
+int chunk_parts(const pkv_geom& g, int num_tokens, int max_context_len);
 hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
                         const void* v_arena, const int32_t* block_table, int max_blocks,
                         const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,

@@ -142,6 +142,20 @@ def small_chunk():
                            max_blocks_per_seq=80)
 
 
+def split_prefix_one():
+    """One 128-row chunk after a 6000-token prefix: 16 work units, so the call
+    splits every tile's keys into 8 parts."""
+    return workloads.build("split_prefix_one", 14, "f16", 32, 8, 128, 5.0e5, [(6000, 128)],
+                           max_blocks_per_seq=384)
+
+
+def split_prefix_three():
+    """Three short chunks with prefixes of 2000, 40 and 3500 tokens: 7 key parts,
+    some of them holding no key of a row (or of a whole short item)."""
+    return workloads.build("split_prefix_three", 15, "f16", 32, 8, 128, 5.0e5,
+                           [(2000, 64), (40, 20), (3500, 100)], max_blocks_per_seq=226)
+
+
 def small_mixed():
     return workloads.mixed_step(num_chunks=2, chunk=96, num_decodes=40, lo=1, hi=1200,
                                 num_sharers=5, shared_prefix=256, parent_tokens=264)
@@ -167,6 +181,8 @@ SMALL = {
     "small_decode": small_decode,
     "small_chunk": small_chunk,
     "small_mixed": small_mixed,
+    "split_prefix_one": split_prefix_one,
+    "split_prefix_three": split_prefix_three,
     "generic_f16_d64": lambda: generic_shape("generic_f16_d64", "f16", 8, 2, 64),
     "generic_f16_g2": lambda: generic_shape("generic_f16_g2", "f16", 8, 4, 128),
     "generic_f16_g8": lambda: generic_shape("generic_f16_g8", "f16", 16, 2, 128),
