@@ -62,10 +62,11 @@ def kernel_rows(db):
     return c.execute("select name, grid_x, grid_y, grid_z, duration from kernels").fetchall()
 
 
-def split_clusters(durs, ratio=3.0):
+def split_clusters(durs, ratio=1.5):
     """Durations of one (kernel, grid) cut at every gap where the next-longer
     launch takes more than ``ratio`` times as long: two workloads that happen
-    to launch the same grid (a short and a long one) get separate lines."""
+    to launch the same grid (a short and a long one) get separate lines.  The
+    launches of one workload spread less than that (under 1.3x here)."""
     durs = sorted(durs)
     groups, cur = [], [durs[0]]
     for a, b in zip(durs, durs[1:]):
@@ -79,7 +80,7 @@ def split_clusters(durs, ratio=3.0):
 def stats(db, out, command, notes=()):
     """One line per (kernel, grid): launches of one kernel on different
     workloads have different grids and are kept apart.  A (kernel, grid) whose
-    launch durations fall into clusters more than 3x apart is listed once per
+    launch durations fall into clusters more than 1.5x apart is listed once per
     cluster (grid marked #1, #2, ... from the shortest)."""
     raw = collections.defaultdict(list)
     for name, gx, gy, gz, dur in kernel_rows(db):
@@ -140,7 +141,7 @@ def traffic(fetch_db, write_db, out, copy_mib, command):
 def counters(db, out, command, kernels, simds, flops=None, notes=()):
     """Per-dispatch averages of every counter of a --pmc run for each kernel
     whose name contains one of ``kernels`` (dispatches on different grids, or
-    in duration clusters more than 3x apart, listed apart), with the
+    in duration clusters more than 1.5x apart, listed apart), with the
     kernel-trace duration of the same dispatches, and where the counters are
     present:
       mfma_busy_pct = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES

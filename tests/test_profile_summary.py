@@ -7,7 +7,7 @@ from paged_kv_chunked_amd import rocprof_summary as rs
 
 
 def test_split_clusters_keeps_one_workload_together():
-    durs = [150.0, 139.5, 181.3, 160.2]  # one workload: spread well under 3x
+    durs = [150.0, 139.5, 181.3, 160.2]  # one workload: spread under 1.5x
     assert rs.split_clusters(durs) == [sorted(durs)]
 
 
@@ -15,8 +15,9 @@ def test_split_clusters_separates_workloads_sharing_a_grid():
     short, long_ = [139.5, 150.4, 181.3], [1632.4, 1682.3, 1850.1]
     groups = rs.split_clusters(long_ + short)
     assert groups == [sorted(short), sorted(long_)]
-    # three clusters, cut at each gap of more than 3x
-    assert rs.split_clusters([1, 2, 10, 11, 100]) == [[1, 2], [10, 11], [100]]
+    # three clusters, cut at each gap of more than 1.5x
+    assert rs.split_clusters([1, 1.2, 10, 11, 100]) == [[1, 1.2], [10, 11], [100]]
+    assert rs.split_clusters([56.0, 80.0, 137.0, 178.0]) == [[56.0, 80.0], [137.0, 178.0]]
 
 
 def test_traffic_record_needs_matching_sources(tmp_path):
