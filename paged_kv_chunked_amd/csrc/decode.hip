@@ -200,9 +200,11 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
 //     16% faster than the unpadded slot-order layout).
 //   * codes become fp16 exactly (byte b: fp16 bits 0x6400 | (b ^ 0x80) =
 //     1024 + b + 128, minus 1152), the K scale multiplies the score, and the V
-//     scale is folded into the probability: P^T holds fp16(p * s_v * 2^6), the
-//     2^6 keeping small weights out of fp16 subnormals (undone at the end).
-constexpr float kPvBoost = 64.f;
+//     scale is folded into the probability: P^T holds fp16(p * s_v * boost),
+//     the boost keeping small weights out of fp16 subnormals (undone at the
+//     end).  With p <= 1 and s_v <= 65504 / qmax the product stays below
+//     fp16's largest finite value: boost 2^6 for INT8 (s_v <= 516), 2^2 for
+//     INT4 (s_v <= 9358).
 #ifndef PKV_DECODE_I8_AHEAD
 #define PKV_DECODE_I8_AHEAD 1
 #endif
@@ -313,6 +315,7 @@ __device__ inline PairI4 load_pair_i4(const uint8_t* __restrict__ k_arena,
 // of dims block db).
 struct CodesI8 {
   using Pair = PairI8;
+  static constexpr float kPvBoost = 64.f;
   __device__ static Pair load(const uint8_t* k, const uint8_t* v, int a, int b, int Hkv, int g,
                               int ln, int lq) {
     return load_pair_i8(k, v, a, b, Hkv, g, ln, lq);
@@ -326,6 +329,7 @@ struct CodesI8 {
   }
 };
 struct CodesI4 {
+  static constexpr float kPvBoost = 4.f;
   using Pair = PairI4;
   __device__ static Pair load(const uint8_t* k, const uint8_t* v, int a, int b, int Hkv, int g,
                               int ln, int lq) {
@@ -442,7 +446,7 @@ __device__ __forceinline__ void decode_split_q(
       const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);  // 0 for keys past the end
       lsum += pe;
       // past the end the V scale may be NaN (unwritten slot): select, not multiply
-      pb[e] = e < nvalid ? (_Float16)(pe * ((float)vsc[e] * kPvBoost)) : (_Float16)0.f;
+      pb[e] = e < nvalid ? (_Float16)(pe * ((float)vsc[e] * Codes::kPvBoost)) : (_Float16)0.f;
     }
     l_run += lsum;
 #pragma unroll
@@ -476,7 +480,7 @@ __device__ __forceinline__ void decode_split_q(
   l_row += __shfl_xor(l_row, 16);
   l_row += __shfl_xor(l_row, 32);
   const int hq = g * kG + ln;
-  const float unboost = 1.f / kPvBoost;
+  const float unboost = 1.f / Codes::kPvBoost;
   if (nsplit == 1) {
     if (ln < kG) {
       const float inv = unboost / l_row;

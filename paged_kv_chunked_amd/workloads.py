@@ -70,6 +70,7 @@ class Workload:
     boost: float = 8.0
     block_size: int = BLOCK_SIZE
     kv_bits: int = 0          # 0: K/V cached in the storage dtype; 8 / 4: INT8 / INT4 codes + fp16 scales
+    v_scale: float = 1.0      # V draws multiplied by this power of two (exact unless it overflows)
 
     # ---- derived sizes -------------------------------------------------
     @property
@@ -126,7 +127,7 @@ class Workload:
         rng = self._rng(1, fill_index)
         shape = (n, self.num_kv_heads, self.head_dim)
         k = self._normal(rng, shape)
-        v = self._normal(rng, shape)
+        v = self._normal(rng, shape) * self.np_dtype(self.v_scale)
         return self._boost_keys(rng, k), v
 
     def draw_step(self, row: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
@@ -135,7 +136,7 @@ class Workload:
         rng = self._rng(2, row)
         q = self._normal(rng, (n, self.num_q_heads, self.head_dim))
         k = self._normal(rng, (n, self.num_kv_heads, self.head_dim))
-        v = self._normal(rng, (n, self.num_kv_heads, self.head_dim))
+        v = self._normal(rng, (n, self.num_kv_heads, self.head_dim)) * self.np_dtype(self.v_scale)
         return q, self._boost_keys(rng, k), v
 
     def draw_step_packed(self, rows: Sequence[int] = None, threads: int = None):

@@ -50,13 +50,17 @@ def bits(a):
 
 
 class Errors:
-    def __init__(self):
+    """Output errors, in units of the workload's V scale (the outputs are linear
+    in V, so their rounding errors scale with it)."""
+
+    def __init__(self, scale=1.0):
         self.max = 0.0
         self.sum = 0.0
         self.n = 0
+        self.scale = scale
 
     def add(self, got, exp):
-        d = np.abs(np.asarray(got, np.float64) - exp)
+        d = np.abs(np.asarray(got, np.float64) - exp) / self.scale
         assert np.isfinite(d).all(), "non-finite output"
         self.max = max(self.max, float(d.max()))
         self.sum += float(d.sum())
@@ -93,7 +97,7 @@ def run_case(w, full_arena=True, dec_sample=None, chunk_sample=None):
     elif full_arena:
         assert np.array_equal(bits(dw.k_arena.cpu().numpy()), bits(st.arena.k)), "K arena differs"
         assert np.array_equal(bits(dw.v_arena.cpu().numpy()), bits(st.arena.v)), "V arena differs"
-    errs = Errors()
+    errs = Errors(w.v_scale)
     cu = dw.cu_host
     dec_rows = dw.dec_rows if dec_sample is None else dec_sample
     for r in dec_rows:
@@ -201,6 +205,14 @@ SMALL = {
     # with an odd number of 16-dim pieces
     "generic_i4_d96": lambda: i4(generic_shape("generic_i4_d96", "f16", 8, 2, 96)),
     "generic_i8_d48": lambda: i8(generic_shape("generic_i8_d48", "f16", 8, 2, 48)),
+    # V values up to ~4e4 (N(0, 1) x 2^13): the fp16 products of probability and
+    # V scale must not overflow (INT4 scales reach 65504 / 7)
+    "large_v_decode_i4": lambda: dataclasses.replace(i4(small_decode()), name="large_v_decode_i4",
+                                                     v_scale=8192.0),
+    "large_v_decode_i8": lambda: dataclasses.replace(i8(small_decode()), name="large_v_decode_i8",
+                                                     v_scale=8192.0),
+    "large_v_chunk": lambda: dataclasses.replace(small_chunk(), name="large_v_chunk",
+                                                 v_scale=8192.0),
     # the largest head dim the library accepts
     "generic_f16_d256": lambda: generic_shape("generic_f16_d256", "f16", 8, 2, 256),
     "generic_f32_d256": lambda: generic_shape("generic_f32_d256", "f32", 4, 2, 256),
