@@ -10,8 +10,10 @@ Default run (N = 1):
   * chunk prefill (reported under "chunk_prefill"): 8 sequences with cached
     prefixes 16*U{0..224} and a 512-token chunk each; a step = restore q +
     kv_append_rope + paged_attention_chunk; TFLOP/s over visible pairs.
-  * decode over INT8 arenas (reported under "decode_int8"): the same batch with
-    K/V cached as INT8 codes plus one fp16 scale per (token, KV head) vector.
+  * decode over INT8 / INT4 arenas ("decode_int8", "decode_int4"): the same
+    batch with K/V cached as codes plus one fp16 scale per (token, KV head)
+    vector; the chunk workload over the same arenas ("chunk_prefill_int8",
+    "chunk_prefill_int4").
   * swap (reported under "swap"): 1024 blocks (64 MiB) of the decode batch out
     to pinned host memory and back (pkv_swap_out / pkv_swap_in), beside a
     plain contiguous copy of the same size in each direction.
@@ -134,9 +136,12 @@ def bench_decode(torch, args, kv_bits=0):
     return w, dw, ms_step, ms_kernel, ms_call, nbytes
 
 
-def bench_chunk(torch, args):
+def bench_chunk(torch, args, kv_bits=0):
+    import dataclasses
     from paged_kv_chunked_amd import harness, workloads
     w = workloads.chunk_batch()
+    if kv_bits:
+        w = dataclasses.replace(w, kv_bits=kv_bits)
     log(f"chunk set-up: {w.num_blocks} blocks")
     dw = harness.DeviceWorkload(w)
     layers = make_layers(torch, dw, args.layers)
@@ -493,6 +498,29 @@ def main():
             },
         }
         del dwc
+        for bits in (() if args.no_int8 else (8, 4)):
+            _, dwq, ms_cstepq, ms_chunkq, ms_ccallq, flopsq = bench_chunk(torch, args, kv_bits=bits)
+            tfq = flopsq / (ms_chunkq * 1e-3) / 1e12
+            log(f"chunk int{bits}: kernel {ms_chunkq:.4f} ms -> {tfq:.1f} TFLOP/s")
+            out[f"chunk_prefill_int{bits}"] = {
+                "workload": f"the chunk workload over INT{bits} arenas, dequantized to fp16 "
+                            "tiles in LDS",
+                "ms_per_step": round(ms_cstepq, 5),
+                "speedup_vs_fp16_arena": round(ms_chunk / ms_chunkq, 3),
+                "roofline": {
+                    "kernel": f"paged_attention_chunk (chunk_mfma_kernel<{1 if bits == 8 else 2}>)",
+                    "bound": "mfma",
+                    "achieved": round(tfq, 2),
+                    "peak": PEAK_F16_TFLOPS,
+                    "unit": "TFLOP/s",
+                    "frac": round(tfq / PEAK_F16_TFLOPS, 4),
+                    "traffic": load_traffic(TRAFFIC, f"paged_attention_chunk_i{bits}"),
+                    "algorithmic_flops_per_launch": flopsq,
+                    "avg_launch_ms": round(ms_chunkq, 5),
+                    "avg_launch_ms_isolated": round(ms_ccallq, 5),
+                },
+            }
+            del dwq
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         secs, passes, threads = cpu_baseline(w, args.cpu_seconds)

@@ -121,9 +121,10 @@ __global__ __launch_bounds__(1024) void chunk_order_kernel(
   }
 }
 
+template <int kQ>
 __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
     float* __restrict__ out, const _Float16* __restrict__ q,
-    const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
+    const void* __restrict__ k_arena, const void* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
     const int32_t* __restrict__ order, float scale_log2, int Hkv, int num_seqs, int n_rtiles,
@@ -140,9 +141,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
   if (k >= num_seqs * n_rtiles) return;
   const int item = order[k];
   const int b = item / n_rtiles, rt = item - b * n_rtiles;
-  chunk_tile_unit(out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
-                  scale_log2, Hkv, num_blocks, num_tokens, b, rt, g, part, parts, part_o,
-                  part_ml);
+  chunk_tile_unit<kQ>(out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
+                      scale_log2, Hkv, num_blocks, num_tokens, b, rt, g, part, parts, part_o,
+                      part_ml);
 }
 
 // Merge of the key-range parts of every chunk row (only when the call is split):
@@ -187,7 +188,8 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(
 }  // namespace
 
 bool chunk_fast_path(const pkv_geom& g) {
-  return g.dtype == PKV_F16 && g.head_dim == kD && g.num_q_heads == kG * g.num_kv_heads;
+  return (g.dtype == PKV_F16 || g.dtype == PKV_I8KV || g.dtype == PKV_I4KV) &&
+         g.head_dim == kD && g.num_q_heads == kG * g.num_kv_heads;
 }
 
 int chunk_parts(const pkv_geom& g, int num_tokens, int max_context_len) {
@@ -248,11 +250,12 @@ hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void
   }
   const long nwg = n_items * g.num_kv_heads * parts;
   if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(chunk_mfma_kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, out,
-                     (const _Float16*)q, (const _Float16*)k_arena, (const _Float16*)v_arena,
-                     block_table, max_blocks, cu_q_lens, chunk_start, order, scale_log2,
-                     g.num_kv_heads, num_seqs, n_rtiles, g.num_blocks, num_tokens, parts, part_o,
-                     part_ml);
+  auto kernel = g.dtype == PKV_I8KV ? chunk_mfma_kernel<1>
+                : g.dtype == PKV_I4KV ? chunk_mfma_kernel<2> : chunk_mfma_kernel<0>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(kThreads), 0, stream, out,
+                     (const _Float16*)q, k_arena, v_arena, block_table, max_blocks, cu_q_lens,
+                     chunk_start, order, scale_log2, g.num_kv_heads, num_seqs, n_rtiles,
+                     g.num_blocks, num_tokens, parts, part_o, part_ml);
   if (parts == 1) return hipGetLastError();
   hipLaunchKernelGGL(chunk_combine_kernel, dim3((unsigned)num_tokens, (g.num_q_heads + 3) / 4),
                      dim3(256), 0, stream, out, part_o, part_ml, cu_q_lens, chunk_start,

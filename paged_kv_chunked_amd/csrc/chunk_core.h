@@ -5,6 +5,7 @@
 #pragma once
 
 #include "fp16_shape.h"
+#include "quant_codes.h"
 
 namespace pkv {
 namespace {
@@ -100,14 +101,44 @@ __device__ inline u32x4 mask_unit(u32x4 x, int key0, int limit) {
   return x;
 }
 
+// Quantized arenas (head dim 128): each (block, KV head) tile holds the codes,
+// then 16 fp16 scales at byte kCodeBlk.  The codes of 3 key tiles are staged in
+// LDS ([K codes of 4 blocks][V codes of 4 blocks][K scales][V scales]); every
+// thread then dequantizes its share of one tile into a 2-stage fp16 ring laid
+// out as the fp16 unit's, so the matrix-core loop is the same.
+constexpr int kCodeStages = 3;
+template <int kQ>
+struct QGeom;
+template <>
+struct QGeom<0> {  // fp16 arena: tiles land in the fp16 ring directly
+  static constexpr int kRingUnits = kStages * kStageUnits;
+};
+template <>
+struct QGeom<1> {  // INT8: 3 loads per wave per tile (K codes, V codes, scales)
+  static constexpr int kCodeBlk = kBlock * kD;
+  static constexpr int kTile = (int)i8_tile_bytes(kD);
+  static constexpr int kLoads = 3;
+  static constexpr int kStageBytes = 8 * kCodeBlk + 256;
+  static constexpr int kRingUnits = 2 * kStageUnits + kCodeStages * kStageBytes / 16;
+};
+template <>
+struct QGeom<2> {  // INT4: 2 loads per wave per tile (K or V codes, scales)
+  static constexpr int kCodeBlk = kBlock * kD / 2;
+  static constexpr int kTile = (int)i4_tile_bytes(kD);
+  static constexpr int kLoads = 2;
+  static constexpr int kStageBytes = 8 * kCodeBlk + 256;
+  static constexpr int kRingUnits = 2 * kStageUnits + kCodeStages * kStageBytes / 16;
+};
+
 // Row tile rt of sequence b for KV head g.  With parts > 1 the unit covers
 // part `part` of the tile's key tiles (an even share, possibly empty) and
 // writes the unnormalised O, the running maximum (log2 units) and the
 // denominator of every row to part_o / part_ml, [part][row][head], for
-// chunk_combine_kernel to merge.
+// chunk_combine_kernel to merge.  kQ: arena storage, 0 fp16, 1 INT8, 2 INT4.
+template <int kQ = 0>
 __device__ __forceinline__ void chunk_tile_unit(
     float* __restrict__ out, const _Float16* __restrict__ q,
-    const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
+    const void* __restrict__ k_arena, const void* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
     float scale_log2, int Hkv, int num_blocks, int num_tokens, int b, int rt, int g,
@@ -127,8 +158,9 @@ __device__ __forceinline__ void chunk_tile_unit(
   const int h = g * kG + (wave & 3);
   const int wrow0 = rt * kRows + kBM * (wave >> 2);  // (kRowGroups waves per head)  // first chunk row of this wave
 
-  // 4 stages x (K: 4 blocks x 256 units, then V: 4 blocks x 256 units)
-  __shared__ u32x4 ring[kStages * kStageUnits];  // 128 KiB
+  // fp16 stages of (K: 4 blocks x 256 units, then V: 4 blocks x 256 units):
+  // 4 for fp16 arenas (128 KiB), else 2, then the code stages
+  __shared__ u32x4 ring[QGeom<kQ>::kRingUnits];
 
   const int row_hi = min(C, rt * kRows + kRows);
   const int kend = min(Lc, P + row_hi);  // keys [0, kend) are visible to some row
@@ -168,11 +200,113 @@ __device__ __forceinline__ void chunk_tile_unit(
     }
   };
 
+  // Quantized arenas: code tile t goes to code stage t % kCodeStages.  INT8:
+  // wave w moves half w & 1 of block w >> 1's K and V codes; INT4: waves 0-3
+  // move the K codes of block w, waves 4-7 the V codes of block w - 4; and
+  // lanes 0-1 of wave w the K (w < 4) or V scales of block w & 3.
+  const uint32_t code_lds = ring_lds + 2u * kStageUnits * 16u;
+  auto issue_codes = [&](int t) {
+    if constexpr (kQ != 0) {
+      using QG = QGeom<kQ>;
+      const uint8_t* ka8 = (const uint8_t*)k_arena;
+      const uint8_t* va8 = (const uint8_t*)v_arena;
+      const uint32_t st = code_lds + (uint32_t)((t % kCodeStages) * QG::kStageBytes);
+      int sblk = bt[min(t * 4 + (wave & 3), nblk_seq - 1)];
+      sblk = (sblk < 0 || sblk >= num_blocks) ? 0 : sblk;
+      const size_t stile = ((size_t)sblk * Hkv + g) * QG::kTile;
+      const uint8_t* sarena = wave < 4 ? ka8 : va8;
+      if constexpr (kQ == 1) {
+        int blk = bt[min(t * 4 + (wave >> 1), nblk_seq - 1)];
+        blk = (blk < 0 || blk >= num_blocks) ? 0 : blk;
+        const size_t src = ((size_t)blk * Hkv + g) * QG::kTile + 16 * (64 * (wave & 1) + lane);
+        dma16(ka8 + src, __builtin_amdgcn_readfirstlane(st + 1024u * wave));
+        dma16(va8 + src, __builtin_amdgcn_readfirstlane(st + 4u * QG::kCodeBlk + 1024u * wave));
+      } else {
+        dma16(sarena + stile + 16 * lane, __builtin_amdgcn_readfirstlane(st + 1024u * wave));
+      }
+      if (lane < 2)
+        dma16(sarena + stile + QG::kCodeBlk + 16 * lane,
+              __builtin_amdgcn_readfirstlane(st + 8u * QG::kCodeBlk + 32u * wave));
+    }
+  };
+  auto issue = [&](int t) {
+    if constexpr (kQ == 0) issue_tile(t);
+    else issue_codes(t);
+  };
+
+  // Dequantization of code tile t into fp16 stage t & 1: thread tid writes
+  // units tid and tid + 512 of the K half and of the V half, in the fp16
+  // unit's order (K: piece p * 16 + slot', slot' = slot ^ 4 in odd blocks; V:
+  // (2 dim + half + 16 (block & 1)) mod 256), multiplied by the key's scale.
+  // Keys past the sequence get scale 0 (their scale bytes are not data).
+  int kc_off[2], ks_off[2], k_key[2], vc_off[2], vs_off[2], v_key[2];
+  [[maybe_unused]] int k_sh[2];
+  if constexpr (kQ != 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int u = tid + 512 * j;
+      const int a = u >> 8, pos = u & 255, p8 = pos >> 4;
+      const int sl = (pos & 15) ^ (4 * (a & 1));
+      if constexpr (kQ == 1)
+        kc_off[j] = a * QGeom<kQ>::kCodeBlk + (p8 >> 1) * 256 + i8_kpos(sl) * 16 + 8 * (p8 & 1);
+      else
+        kc_off[j] = a * QGeom<kQ>::kCodeBlk + (p8 >> 1) * 128 + i4_krec(sl) * 8;
+      k_sh[j] = 4 * (p8 & 1);
+      ks_off[j] = 8 * QGeom<kQ>::kCodeBlk + a * 32 + 2 * sl;
+      k_key[j] = 16 * a + sl;
+      const int unit = (pos - 16 * (a & 1)) & 255, d = unit >> 1, hs = unit & 1;
+      if constexpr (kQ == 1)
+        vc_off[j] = 4 * QGeom<kQ>::kCodeBlk + a * QGeom<kQ>::kCodeBlk + 8 * unit;
+      else
+        vc_off[j] = 4 * QGeom<kQ>::kCodeBlk + a * QGeom<kQ>::kCodeBlk + i4_vbyte(d, 8 * hs, kD);
+      vs_off[j] = 8 * QGeom<kQ>::kCodeBlk + 128 + a * 32 + 16 * hs;
+      v_key[j] = 16 * a + 8 * hs;
+    }
+  }
+  auto convert = [&](int t) {
+    if constexpr (kQ != 0) {
+      const uint8_t* cs = (const uint8_t*)(ring + 2 * kStageUnits) +
+                          (t % kCodeStages) * QGeom<kQ>::kStageBytes;
+      u32x4* fs = ring + (t & 1) * kStageUnits;
+      const int lim = Lc - t * kBN;  // keys of the tile at or past this one are not data
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        half8_t h;
+        if constexpr (kQ == 1) {
+          const uint2 c = *(const uint2*)(cs + kc_off[j]);
+          h = codes_to_half(c.x, c.y);
+        } else {
+          const uint2 c = *(const uint2*)(cs + kc_off[j]);
+          h = nibbles_to_half(c.x >> k_sh[j], c.y >> k_sh[j]);
+        }
+        _Float16 ks = *(const _Float16*)(cs + ks_off[j]);
+        if (k_key[j] >= lim) ks = (_Float16)0.f;
+        fs[tid + 512 * j] = __builtin_bit_cast(u32x4, h * (half8_t)ks);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        half8_t h;
+        if constexpr (kQ == 1) {
+          const uint2 c = *(const uint2*)(cs + vc_off[j]);
+          h = codes_to_half(c.x, c.y);
+        } else {
+          const uint32_t w = *(const uint32_t*)(cs + vc_off[j]);
+          h = nibbles_to_half(w, w >> 4);
+        }
+        half8_t vs = __builtin_bit_cast(half8_t, *(const u32x4*)(cs + vs_off[j]));
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (v_key[j] + i >= lim) vs[i] = (_Float16)0.f;
+        fs[4 * kUnitsPerBlock + tid + 512 * j] = __builtin_bit_cast(u32x4, h * vs);
+      }
+    }
+  };
+
   // The first tile's loads go out before the queries' so the two latencies
   // overlap; then every query load (and the first tile) is complete before
   // the next tile loads are issued, so the tile waits below count tile loads
   // only.
-  if (tb < te) issue_tile(tb);
+  if (tb < te) issue(tb);
   // Q^T as the B operand: qf[rb][kd] = Q[row wrow0 + 16rb + lr][dims 32kd + 8lq .. +8]
   half8_t qf[kRB][4];
 #pragma unroll
@@ -189,8 +323,15 @@ __device__ __forceinline__ void chunk_tile_unit(
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (tb + 1 < te) issue_tile(tb + 1);
-  if (tb + 2 < te) issue_tile(tb + 2);
+  if (tb + 1 < te) issue(tb + 1);
+  if (tb + 2 < te) issue(tb + 2);
+  if constexpr (kQ != 0) {
+    if (tb < te) {
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      convert(tb);
+    }
+  }
 
   // absolute positions of this lane's two rows (rows past the chunk borrow the
   // last valid position so they stay finite; they are never stored)
@@ -227,17 +368,31 @@ __device__ __forceinline__ void chunk_tile_unit(
   const int vunit = 2 * lr + (lq & 1) + 16 * (lq >> 1);
 
   for (int t = tb; t < te; ++t) {
-    // tile t's loads (this wave's) are done; then every wave's, and every
-    // wave has finished tile t - 1, whose stage the next load reuses
-    if (t + 2 < te) wait_vm<2 * kLoadsPerTile>();
-    else if (t + 1 < te) wait_vm<kLoadsPerTile>();
-    else wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (t + 3 < te) issue_tile(t + 3);
-    const u32x4* kl = ring + (t % kStages) * kStageUnits;
+    if constexpr (kQ == 0) {
+      // tile t's loads (this wave's) are done; then every wave's, and every
+      // wave has finished tile t - 1, whose stage the next load reuses
+      if (t + 2 < te) wait_vm<2 * kLoadsPerTile>();
+      else if (t + 1 < te) wait_vm<kLoadsPerTile>();
+      else wait_vm<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 3 < te) issue_tile(t + 3);
+    } else {
+      // code tile t + 1 is in LDS (this wave's loads, then every wave's);
+      // after the barrier fp16 stage t & 1 is complete, every wave is done
+      // with stage (t + 1) & 1 and with code stage t % 3, which the next
+      // load reuses
+      if (t + 2 < te) wait_vm<QGeom<kQ>::kLoads>();
+      else wait_vm<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 3 < te) issue_codes(t + 3);
+      if (t + 1 < te) convert(t + 1);
+    }
+    const u32x4* kl = ring + (kQ == 0 ? t % kStages : t & 1) * kStageUnits;
     const u32x4* vl = kl + 4 * kUnitsPerBlock;
-    if (t * kBN + kBN > Lc) {
+    if (kQ == 0 && t * kBN + kBN > Lc) {
       // last tile: zero V of keys past the sequence (2 units per thread)
       u32x4* vw = ring + (t % kStages) * kStageUnits + 4 * kUnitsPerBlock;
 #pragma unroll

@@ -37,6 +37,7 @@
 //     4x slower than the second launch.)
 // Other shapes run the generic kernel.
 #include "decode_core.h"
+#include "quant_codes.h"
 
 namespace pkv {
 namespace {
@@ -216,19 +217,6 @@ struct PairI8 {
   u32x4 ks, vs;   // fp16 scales of the lane's 8 keys (K, V)
 };
 
-__device__ inline half8_t codes_to_half(uint32_t lo, uint32_t hi) {
-  const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
-  const uint32_t c = 0x64646464u;
-  // byte selectors: result bytes [a0, 0x64, a1, 0x64] etc. (perm indexes the
-  // 8 bytes {src1 (0..3), src0 (4..7)})
-  const uint32_t w0 = __builtin_amdgcn_perm(c, a, 0x05010400u);
-  const uint32_t w1 = __builtin_amdgcn_perm(c, a, 0x05030402u);
-  const uint32_t w2 = __builtin_amdgcn_perm(c, b, 0x05010400u);
-  const uint32_t w3 = __builtin_amdgcn_perm(c, b, 0x05030402u);
-  half8_t h = __builtin_bit_cast(half8_t, u32x4{w0, w1, w2, w3});
-  return h - (half8_t)(_Float16)1152.f;
-}
-
 __device__ inline PairI8 load_pair_i8(const uint8_t* __restrict__ k_arena,
                                       const uint8_t* __restrict__ v_arena, int blk_a, int blk_b,
                                       int Hkv, int g, int ln, int lq) {
@@ -268,18 +256,6 @@ struct PairI4 {
   uint32_t v[8];  // [db]: 8 codes of dim 16db + ln, the lane's 8 keys
   u32x4 ks, vs;   // fp16 scales of the lane's 8 keys (K, V)
 };
-
-// 8 nibbles (the low nibble of each byte of lo, then of hi) as fp16 codes
-__device__ inline half8_t nibbles_to_half(uint32_t lo, uint32_t hi) {
-  const uint32_t a = (lo & 0x0F0F0F0Fu) ^ 0x08080808u, b = (hi & 0x0F0F0F0Fu) ^ 0x08080808u;
-  const uint32_t c = 0x64646464u;
-  const uint32_t w0 = __builtin_amdgcn_perm(c, a, 0x05010400u);
-  const uint32_t w1 = __builtin_amdgcn_perm(c, a, 0x05030402u);
-  const uint32_t w2 = __builtin_amdgcn_perm(c, b, 0x05010400u);
-  const uint32_t w3 = __builtin_amdgcn_perm(c, b, 0x05030402u);
-  half8_t h = __builtin_bit_cast(half8_t, u32x4{w0, w1, w2, w3});
-  return h - (half8_t)(_Float16)1032.f;
-}
 
 __device__ inline PairI4 load_pair_i4(const uint8_t* __restrict__ k_arena,
                                       const uint8_t* __restrict__ v_arena, int blk_a, int blk_b,

@@ -188,7 +188,9 @@ __global__ __launch_bounds__(kThreads, 1) void mixed_kernel(
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-bool mixed_fast_path(const pkv_geom& g) { return chunk_fast_path(g) && decode_fast_path(g); }
+bool mixed_fast_path(const pkv_geom& g) {
+  return g.dtype == PKV_F16 && chunk_fast_path(g) && decode_fast_path(g);
+}
 
 // Workspace: [schedule: header + chunk list + decode list, 256-aligned]
 // [decode partials as paged_attention_decode lays them out].

@@ -213,6 +213,13 @@ SMALL = {
                                                      v_scale=8192.0),
     "large_v_chunk": lambda: dataclasses.replace(small_chunk(), name="large_v_chunk",
                                                  v_scale=8192.0),
+    # the quantized chunk kernel (dequantized into fp16 tiles in LDS)
+    "large_v_chunk_i8": lambda: dataclasses.replace(i8(small_chunk()), name="large_v_chunk_i8",
+                                                    v_scale=8192.0),
+    "large_v_chunk_i4": lambda: dataclasses.replace(i4(small_chunk()), name="large_v_chunk_i4",
+                                                    v_scale=8192.0),
+    "split_prefix_one_i8": lambda: i8(split_prefix_one()),
+    "split_prefix_three_i4": lambda: i4(split_prefix_three()),
     # the largest head dim the library accepts
     "generic_f16_d256": lambda: generic_shape("generic_f16_d256", "f16", 8, 2, 256),
     "generic_f32_d256": lambda: generic_shape("generic_f32_d256", "f32", 4, 2, 256),
@@ -235,6 +242,16 @@ def test_decode_full():
 
 def test_chunk_full():
     run_case(workloads.chunk_batch())
+
+
+def test_chunk_full_i8():
+    w = i8(workloads.chunk_batch())
+    run_case(w, chunk_sample={r: 48 for r in w.chunk_rows()})
+
+
+def test_chunk_full_i4():
+    w = i4(workloads.chunk_batch())
+    run_case(w, chunk_sample={r: 48 for r in w.chunk_rows()})
 
 
 def test_decode_full_i8():
