@@ -266,8 +266,9 @@ pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dt
  *              bytes: the schedule and the decode partials.  Sized from
  *              num_seqs, num_tokens and max_context_len; PKV_ERR_WORKSPACE if
  *              missing or short.
- * Other shapes (not fp16 / head_dim 128 / 4 query heads per KV head) run the
- * generic kernel over every row, as paged_attention_chunk does.
+ * Other shapes (not fp16, INT8 or INT4 storage / head_dim 128 / 4 query heads
+ * per KV head) run the generic kernel over every row, as paged_attention_chunk
+ * does.
  * ------------------------------------------------------------------------- */
 pkv_status paged_attention_mixed_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
                                                  int32_t num_tokens, int32_t max_context_len,

@@ -1,0 +1,286 @@
+// Quantized (INT8 / INT4) decode split: one wave per (split, KV head), used by
+// the quantized decode kernels and by the mixed-batch kernel (the design is
+// described with the quantized decode kernels in decode.hip).
+#pragma once
+
+#include "decode_core.h"
+#include "quant_codes.h"
+
+namespace pkv {
+namespace {
+
+#ifndef PKV_DECODE_I8_AHEAD
+#define PKV_DECODE_I8_AHEAD 1
+#endif
+constexpr int kI8Ahead = PKV_DECODE_I8_AHEAD;  // pairs in flight behind the computed one
+
+struct PairI8 {
+  u32x4 k[2][2];  // [u][j]: 16 codes (dims 16(4j + lq) .. +16) of the lane's key row
+  u32x2 v[8];     // [db]: 8 codes of dim 16db + ln, the lane's 8 keys
+  u32x4 ks, vs;   // fp16 scales of the lane's 8 keys (K, V)
+};
+
+__device__ inline PairI8 load_pair_i8(const uint8_t* __restrict__ k_arena,
+                                      const uint8_t* __restrict__ v_arena, int blk_a, int blk_b,
+                                      int Hkv, int g, int ln, int lq) {
+  constexpr size_t kTile = i8_tile_bytes(kD);
+  PairI8 pr;
+  // K row of this lane (MFMA row ln) for MFMA u: block A or B by ln >> 3
+  const uint8_t* kt = k_arena + ((size_t)((ln >> 3) ? blk_b : blk_a) * Hkv + g) * kTile;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    // the lane's token 8((ln >> 2) & 1) + 4u + (ln & 3) is stored at position
+    // 8u + (ln & 7): MFMA u reads one 128-byte run per (block, piece)
+    const int slot = 8 * u + (ln & 7);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pr.k[u][j] = __builtin_nontemporal_load((const u32x4*)(kt + (4 * j + lq) * 256 + slot * 16));
+  }
+  // the lane's keys (as head ln of the scores): block lq >> 1, tokens 8(lq & 1) .. +8
+  const size_t tv = ((size_t)((lq >> 1) ? blk_b : blk_a) * Hkv + g) * kTile;
+  const uint8_t* vt = v_arena + tv;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    pr.v[db] = __builtin_nontemporal_load((const u32x2*)(vt + (16 * db + ln) * kBlock + 8 * (lq & 1)));
+  pr.ks = __builtin_nontemporal_load((const u32x4*)(k_arena + tv + kBlock * kD + 16 * (lq & 1)));
+  pr.vs = __builtin_nontemporal_load((const u32x4*)(vt + kBlock * kD + 16 * (lq & 1)));
+  return pr;
+}
+
+// INT4 arenas (PKV_I4KV): the same kernel over 4-bit codes.  A lane's 16-byte
+// K load holds its two keys' records (MFMA u = 0, 1) of one 16-dim piece: low
+// nibbles are dims 0-7, high nibbles dims 8-15 of the piece, so each MFMA
+// operand is one mask per word.  Each 4-byte word of V holds the lane's 8
+// keys of one head dim (low nibbles keys 0-3, high nibbles keys 4-7), and one
+// 16-byte V load brings the words of four dim blocks.  Nibbles become fp16
+// exactly: (n ^ 8) + 1024 - 1032.
+struct PairI4 {
+  u32x4 k[2];     // [j]: records (u = 0: x, y; u = 1: z, w) of piece 4j + lq
+  uint32_t v[8];  // [db]: 8 codes of dim 16db + ln, the lane's 8 keys
+  u32x4 ks, vs;   // fp16 scales of the lane's 8 keys (K, V)
+};
+
+__device__ inline PairI4 load_pair_i4(const uint8_t* __restrict__ k_arena,
+                                      const uint8_t* __restrict__ v_arena, int blk_a, int blk_b,
+                                      int Hkv, int g, int ln, int lq) {
+  constexpr size_t kTile = i4_tile_bytes(kD);
+  PairI4 pr;
+  // the lane's key row (MFMA row ln) lives in block A or B by ln >> 3; its
+  // records for u = 0, 1 are 16 bytes at record 2 (ln & 7)
+  const uint8_t* kt = k_arena + ((size_t)((ln >> 3) ? blk_b : blk_a) * Hkv + g) * kTile;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    pr.k[j] = __builtin_nontemporal_load((const u32x4*)(kt + (4 * j + lq) * 128 + (ln & 7) * 16));
+  const size_t tv = ((size_t)((lq >> 1) ? blk_b : blk_a) * Hkv + g) * kTile;
+  const uint8_t* vt = v_arena + tv;
+  // V: the lane's 8 keys (half lq & 1 of its block) for dims 16db + ln, four
+  // dim blocks per 16-byte load (i4_vbyte with D = 128)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const u32x4 w =
+        __builtin_nontemporal_load((const u32x4*)(vt + ((2 * j + (lq & 1)) * 16 + ln) * 16));
+    pr.v[4 * j] = w.x;
+    pr.v[4 * j + 1] = w.y;
+    pr.v[4 * j + 2] = w.z;
+    pr.v[4 * j + 3] = w.w;
+  }
+  pr.ks = __builtin_nontemporal_load((const u32x4*)(k_arena + tv + kBlock * kD / 2 + 16 * (lq & 1)));
+  pr.vs = __builtin_nontemporal_load((const u32x4*)(vt + kBlock * kD / 2 + 16 * (lq & 1)));
+  return pr;
+}
+
+// The two code widths as traits of one split kernel: the pair type, its load,
+// and the MFMA operands (K operand of MFMA u, contraction step kd; V operand
+// of dims block db).
+struct CodesI8 {
+  using Pair = PairI8;
+  static constexpr float kPvBoost = 64.f;
+  __device__ static Pair load(const uint8_t* k, const uint8_t* v, int a, int b, int Hkv, int g,
+                              int ln, int lq) {
+    return load_pair_i8(k, v, a, b, Hkv, g, ln, lq);
+  }
+  __device__ static half8_t kop(const Pair& pr, int u, int kd) {
+    const u32x4 c = pr.k[u][kd >> 1];
+    return (kd & 1) ? codes_to_half(c.z, c.w) : codes_to_half(c.x, c.y);
+  }
+  __device__ static half8_t vop(const Pair& pr, int db) {
+    return codes_to_half(pr.v[db].x, pr.v[db].y);
+  }
+};
+struct CodesI4 {
+  static constexpr float kPvBoost = 4.f;
+  using Pair = PairI4;
+  __device__ static Pair load(const uint8_t* k, const uint8_t* v, int a, int b, int Hkv, int g,
+                              int ln, int lq) {
+    return load_pair_i4(k, v, a, b, Hkv, g, ln, lq);
+  }
+  __device__ static half8_t kop(const Pair& pr, int u, int kd) {
+    const u32x4 c = pr.k[kd >> 1];
+    const uint32_t w0 = u ? c.z : c.x, w1 = u ? c.w : c.y;
+    return (kd & 1) ? nibbles_to_half(w0 >> 4, w1 >> 4) : nibbles_to_half(w0, w1);
+  }
+  __device__ static half8_t vop(const Pair& pr, int db) {
+    return nibbles_to_half(pr.v[db], pr.v[db] >> 4);
+  }
+};
+
+// Waves per workgroup and minimum resident waves per SIMD of the quantized
+// split kernels (their register budget differs from the fp16 kernel's).
+#ifndef PKV_DECODE_I8_WAVES_PER_WG
+#define PKV_DECODE_I8_WAVES_PER_WG 8
+#endif
+#ifndef PKV_DECODE_I8_WAVES_PER_SIMD
+#define PKV_DECODE_I8_WAVES_PER_SIMD 2
+#endif
+constexpr int kI8WavesPerWG = PKV_DECODE_I8_WAVES_PER_WG;
+
+// Split `split` of sequence b (its block-table row and its partials in the
+// workspace) for KV head g, one wave; the query and output live at packed row
+// `row` and the context length is lens[b] + len_add.
+template <class Codes>
+__device__ __forceinline__ void decode_split_q_unit(
+    float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const _Float16* __restrict__ q,
+    const uint8_t* __restrict__ k_arena, const uint8_t* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks, int b, int row,
+    const int32_t* __restrict__ lens, int len_add, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks, int split, int g) {
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 15, lq = lane >> 4;
+  const int Hq = Hkv * kG;
+  const int blk0 = split * kSB;
+  int my_blk = 0;
+  if (lane < kSB && blk0 + lane < max_blocks)
+    my_blk = block_table[(size_t)b * max_blocks + blk0 + lane];
+  // Q^T (B operand) in the permuted dim order: MFMA kd, lane group lq holds
+  // dims 16(4(kd >> 1) + lq) + 8(kd & 1) .. +8 of head g*4+ln
+  half8_t qb[4];
+#pragma unroll
+  for (int kd = 0; kd < 4; ++kd)
+    qb[kd] = ln < kG ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + ln) * kD +
+                                         16 * (4 * (kd >> 1) + lq) + 8 * (kd & 1))
+                     : (half8_t)(_Float16)0.f;
+  const int L = min(min(lens[b] + len_add, max_blocks * kBlock), nsplit_max * kDecodeSplit);
+  if (L <= 0) {
+    if (split == 0 && ln < kG) {
+      float* o = out + ((size_t)row * Hq + g * kG + ln) * kD + 4 * lq;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f32x4*)(o + 16 * db) = (f32x4)0.f;
+    }
+    return;
+  }
+  const int nb_seq = (L + kBlock - 1) / kBlock;
+  if (blk0 >= nb_seq) return;
+  const int nb = min(kSB, nb_seq - blk0);
+  const int nsplit = (nb_seq + kSB - 1) / kSB;
+  const int npairs = (nb + 1) >> 1;
+  if (lane >= nb || my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
+
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = (f32x4)0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto pair_ids = [&](int p, int& a, int& c) {
+    a = __builtin_amdgcn_readlane(my_blk, 2 * p);
+    c = 2 * p + 1 < nb ? __builtin_amdgcn_readlane(my_blk, 2 * p + 1) : a;
+  };
+  using Pair = typename Codes::Pair;
+  auto compute = [&](const Pair& pr, int p) {
+    f32x4 s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = (f32x4)0.f;
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd)
+        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Codes::kop(pr, u, kd), qb[kd], s[u], 0, 0, 0);
+    }
+    // element e = 4u + i of this lane: token 8(lq & 1) + e of block lq >> 1
+    const half8_t ksc = __builtin_bit_cast(half8_t, pr.ks);
+    const half8_t vsc = __builtin_bit_cast(half8_t, pr.vs);
+    const int tok0 = (blk0 + 2 * p + (lq >> 1)) * kBlock + 8 * (lq & 1);
+    const int nvalid = L - tok0;  // keys e < nvalid exist
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = e < nvalid ? s[e >> 2][e & 3] * ((float)ksc[e] * scale_log2) : -INFINITY;
+      sv[e] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: the first key of a split is real
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    }
+    m_run = m_new;
+    half8_t pb;
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);  // 0 for keys past the end
+      lsum += pe;
+      // past the end the V scale may be NaN (unwritten slot): select, not multiply
+      pb[e] = e < nvalid ? (_Float16)(pe * ((float)vsc[e] * Codes::kPvBoost)) : (_Float16)0.f;
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Codes::vop(pr, db), pb, o[db], 0, 0, 0);
+  };
+
+  // kI8Ahead pairs are kept in flight behind the one being computed (same
+  // unconditional-prefetch scheme as the fp16 kernel).  One measured best:
+  // two or three cost registers (occupancy 3 -> 2) and ran 4-6% slower.
+  constexpr int kAhead = kI8Ahead;
+  Pair buf[kAhead + 1];
+#pragma unroll
+  for (int p = 0; p < kAhead; ++p) {
+    int ba, bb;
+    pair_ids(min(p, npairs - 1), ba, bb);
+    buf[p] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+  }
+#pragma unroll
+  for (int p = 0; p < kSB / 2; ++p) {
+    if (p + kAhead < kSB / 2) {
+      int ba, bb;
+      pair_ids(min(p + kAhead, npairs - 1), ba, bb);
+      buf[(p + kAhead) % (kAhead + 1)] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (p < npairs) compute(buf[p % (kAhead + 1)], p);
+  }
+
+  float l_row = l_run;
+  l_row += __shfl_xor(l_row, 16);
+  l_row += __shfl_xor(l_row, 32);
+  const int hq = g * kG + ln;
+  const float unboost = 1.f / Codes::kPvBoost;
+  if (nsplit == 1) {
+    if (ln < kG) {
+      const float inv = unboost / l_row;
+      float* dst = out + ((size_t)row * Hq + hq) * kD + 4 * lq;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * inv;
+    }
+    return;
+  }
+  if (ln < kG) {
+    const size_t part = ((size_t)b * nsplit_max + split) * Hq + hq;
+    float* dst = ws_o + part * kD + 4 * lq;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * unboost;
+    if (lq == 0) {
+      ws_ml[2 * part] = m_run;
+      ws_ml[2 * part + 1] = l_row;
+    }
+  }
+}
+
+
+}  // namespace
+}  // namespace pkv

@@ -20,8 +20,11 @@
 //     A unit runs exactly the code of the stand-alone kernels (chunk_core.h,
 //     decode_core.h), so its results are bit for bit theirs;
 //   * decode_combine_kernel then merges the splits of the decode rows.
+#include <type_traits>
+
 #include "chunk_core.h"
 #include "decode_core.h"
+#include "decode_q_core.h"
 
 namespace pkv {
 namespace {
@@ -129,10 +132,12 @@ __global__ __launch_bounds__(1024) void mixed_order_kernel(
 // Persistent: each workgroup takes the next unit until the list is exhausted.
 // Units [0, n_chunk * Hkv) are chunk tiles (item k / Hkv for KV head k % Hkv);
 // the rest are decode units (list entry j / zg for KV heads 8 (j % zg) ..).
+// kQ: arena storage, 0 fp16, 1 INT8, 2 INT4.
+template <int kQ>
 __global__ __launch_bounds__(kThreads, 1) void mixed_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
-    const _Float16* __restrict__ v_arena, const int32_t* __restrict__ block_table,
+    const _Float16* __restrict__ q, const void* __restrict__ k_arena,
+    const void* __restrict__ v_arena, const int32_t* __restrict__ block_table,
     int max_blocks, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ sched,
     int32_t* __restrict__ counter, float scale_log2, int Hkv, int zg, int num_seqs,
@@ -165,18 +170,25 @@ __global__ __launch_bounds__(kThreads, 1) void mixed_kernel(
       const int k = u / Hkv, g = u - k * Hkv;
       const int item = chunk_list[k];
       const int b = item / n_rtiles, rt = item - b * n_rtiles;
-      chunk_tile_unit(out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
-                      scale_log2, Hkv, num_blocks, num_tokens, b, rt, g);
+      chunk_tile_unit<kQ>(out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens,
+                          chunk_start, scale_log2, Hkv, num_blocks, num_tokens, b, rt, g);
     } else {
       const int j = u - n_chunk_units;
       const int e = j / zg, z = j - e * zg;
       const int unit = dec_list[e];
       const int b = unit / nsplit_max, split = unit - b * nsplit_max;
       const int g = z * kDecodeWavesPerWG + wave;
-      if (g < Hkv)
-        decode_split_unit(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, b,
-                          cu_q_lens[b], chunk_start, 1, scale_log2, Hkv, nsplit_max, num_blocks,
-                          split, g);
+      if (g < Hkv) {
+        if constexpr (kQ == 0)
+          decode_split_unit(out, ws_o, ws_ml, q, (const _Float16*)k_arena,
+                            (const _Float16*)v_arena, block_table, max_blocks, b, cu_q_lens[b],
+                            chunk_start, 1, scale_log2, Hkv, nsplit_max, num_blocks, split, g);
+        else
+          decode_split_q_unit<std::conditional_t<kQ == 1, CodesI8, CodesI4>>(
+              out, ws_o, ws_ml, q, (const uint8_t*)k_arena, (const uint8_t*)v_arena,
+              block_table, max_blocks, b, cu_q_lens[b], chunk_start, 1, scale_log2, Hkv,
+              nsplit_max, num_blocks, split, g);
+      }
     }
     if (threadIdx.x == 0) unit_slot[it & 1] = early ? next : atomicAdd(counter, 1);
     __syncthreads();  // every wave has left the unit (and its LDS) and may read the slot
@@ -188,9 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void mixed_kernel(
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-bool mixed_fast_path(const pkv_geom& g) {
-  return g.dtype == PKV_F16 && chunk_fast_path(g) && decode_fast_path(g);
-}
+bool mixed_fast_path(const pkv_geom& g) { return chunk_fast_path(g) && decode_fast_path(g); }
 
 // Workspace: [schedule: header + chunk list + decode list, 256-aligned]
 // [decode partials as paged_attention_decode lays them out].
@@ -237,12 +247,13 @@ hipError_t launch_mixed(const pkv_geom& g, float* out, const void* q, const void
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mixed_kernel, dim3((unsigned)max(num_cus, 1)), dim3(kThreads), 0, stream,
-                     out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
-                     (const _Float16*)v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
-                     sched, sched + kHdrNext, scale_log2, g.num_kv_heads, zg, num_seqs, n_rtiles,
-                     nsplit_max,
-                     g.num_blocks, num_tokens);
+  auto kernel = g.dtype == PKV_I8KV ? mixed_kernel<1>
+                : g.dtype == PKV_I4KV ? mixed_kernel<2> : mixed_kernel<0>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)max(num_cus, 1)), dim3(kThreads), 0, stream,
+                     out, ws_o, ws_ml, (const _Float16*)q, k_arena, v_arena, block_table,
+                     max_blocks, cu_q_lens, chunk_start, sched, sched + kHdrNext, scale_log2,
+                     g.num_kv_heads, zg, num_seqs, n_rtiles, nsplit_max, g.num_blocks,
+                     num_tokens);
   e = hipGetLastError();
   if (e != hipSuccess || nsplit_max <= 1) return e;
   return launch_decode_combine(g, out, ws_o, ws_ml, chunk_start, cu_q_lens, num_tokens,

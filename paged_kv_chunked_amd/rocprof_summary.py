@@ -34,15 +34,22 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 # kernel call -> (kernel symbol substrings, source files whose change invalidates it)
-_DECODE_SRC = ("decode.hip", "decode_core.h", "fp16_shape.h", "pkv_internal.h")
-_CHUNK_SRC = ("chunk.hip", "chunk_core.h", "fp16_shape.h", "pkv_internal.h")
+_DECODE_SRC = ("decode.hip", "decode_core.h", "fp16_shape.h", "pkv_internal.h", "quant_codes.h")
+_CHUNK_SRC = ("chunk.hip", "chunk_core.h", "fp16_shape.h", "pkv_internal.h", "quant_codes.h")
 CALLS = {
     "paged_attention_decode": (("decode_split_kernel", "decode_combine_kernel"), _DECODE_SRC),
     "paged_attention_decode_i8": (("decode_split_i8_kernel", "decode_combine_kernel"),
                                   _DECODE_SRC),
     "paged_attention_decode_i4": (("decode_split_i4_kernel", "decode_combine_kernel"),
                                   _DECODE_SRC),
-    "paged_attention_chunk": (("chunk_mfma_kernel",), _CHUNK_SRC),
+    # chunk_mfma_kernel<kQ>: fp16 (0), INT8 (1), INT4 (2) arenas (the trace
+    # holds the mangled or the demangled name; one of the two matches)
+    "paged_attention_chunk": (("chunk_mfma_kernelILi0E", "chunk_mfma_kernel<0>"),
+                                  _CHUNK_SRC),
+    "paged_attention_chunk_i8": (("chunk_mfma_kernelILi1E", "chunk_mfma_kernel<1>"),
+                                  _CHUNK_SRC),
+    "paged_attention_chunk_i4": (("chunk_mfma_kernelILi2E", "chunk_mfma_kernel<2>"),
+                                  _CHUNK_SRC),
     "paged_attention_mixed": (("mixed_kernel", "mixed_order_kernel"),
                               ("mixed.hip",) + _CHUNK_SRC[1:] + _DECODE_SRC[:2]),
     "kv_append_rope": (("append_rope_kernel",), ("append.hip", "pkv_internal.h")),

@@ -9,6 +9,7 @@ rows are also checked against the oracle here, and batches whose kinds
 interleave (which the separate calls cannot take as one batch) against the
 oracle alone.
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -205,3 +206,26 @@ def test_empty_sequences_change_nothing():
                               dw.mix_max_q, dw.mix_max_ctx, dw.scale)
     torch.cuda.synchronize()
     assert np.array_equal(bits(out_c.cpu().numpy()), bits(ref_c.cpu().numpy()))
+
+
+def _quant(w, bits):
+    return dataclasses.replace(w, name=f"{w.name}_i{bits}", kv_bits=bits)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_small_mixed_quant(bits):
+    """INT8 / INT4 arenas: the mixed kernel's quantized chunk and decode units
+    against the quantized stand-alone calls, bit for bit."""
+    check_against_split_calls(_quant(workloads.mixed_step(num_chunks=2, chunk=96,
+                                                          num_decodes=40, lo=1, hi=1200,
+                                                          num_sharers=5, shared_prefix=256,
+                                                          parent_tokens=264), bits))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_mixed_full_quant(bits):
+    w = _quant(workloads.mixed_step(), bits)
+    rng = np.random.default_rng(4)
+    sample = sorted(set(w.chunk_rows()[:1] +
+                        rng.choice(w.decode_rows(), size=6, replace=False).tolist()))
+    check_against_split_calls(w, sample_rows=sample)
