@@ -4,6 +4,8 @@
 // the unit owns the workgroup's 128 KiB of LDS.
 #pragma once
 
+#include <type_traits>
+
 #include "fp16_shape.h"
 #include "quant_codes.h"
 
@@ -263,7 +265,8 @@ __device__ __forceinline__ void chunk_tile_unit(
       v_key[j] = 16 * a + 8 * hs;
     }
   }
-  auto convert = [&](int t) {
+  // (masked: the tile reaches past the sequence; keys >= lim get scale 0)
+  auto convert_tile = [&](int t, auto masked) {
     if constexpr (kQ != 0) {
       const uint8_t* cs = (const uint8_t*)(ring + 2 * kStageUnits) +
                           (t % kCodeStages) * QGeom<kQ>::kStageBytes;
@@ -280,7 +283,7 @@ __device__ __forceinline__ void chunk_tile_unit(
           h = nibbles_to_half(c.x >> k_sh[j], c.y >> k_sh[j]);
         }
         _Float16 ks = *(const _Float16*)(cs + ks_off[j]);
-        if (k_key[j] >= lim) ks = (_Float16)0.f;
+        if (masked && k_key[j] >= lim) ks = (_Float16)0.f;
         fs[tid + 512 * j] = __builtin_bit_cast(u32x4, h * (half8_t)ks);
       }
 #pragma unroll
@@ -294,12 +297,18 @@ __device__ __forceinline__ void chunk_tile_unit(
           h = nibbles_to_half(w, w >> 4);
         }
         half8_t vs = __builtin_bit_cast(half8_t, *(const u32x4*)(cs + vs_off[j]));
+        if (masked) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (v_key[j] + i >= lim) vs[i] = (_Float16)0.f;
+          for (int i = 0; i < 8; ++i)
+            if (v_key[j] + i >= lim) vs[i] = (_Float16)0.f;
+        }
         fs[4 * kUnitsPerBlock + tid + 512 * j] = __builtin_bit_cast(u32x4, h * vs);
       }
     }
+  };
+  auto convert = [&](int t) {
+    if (t * kBN + kBN > Lc) convert_tile(t, std::true_type{});
+    else convert_tile(t, std::false_type{});
   };
 
   // The first tile's loads go out before the queries' so the two latencies

@@ -34,7 +34,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 # kernel call -> (kernel symbol substrings, source files whose change invalidates it)
-_DECODE_SRC = ("decode.hip", "decode_core.h", "fp16_shape.h", "pkv_internal.h", "quant_codes.h")
+_DECODE_SRC = ("decode.hip", "decode_core.h", "decode_q_core.h", "fp16_shape.h", "pkv_internal.h",
+               "quant_codes.h")
 _CHUNK_SRC = ("chunk.hip", "chunk_core.h", "fp16_shape.h", "pkv_internal.h", "quant_codes.h")
 CALLS = {
     "paged_attention_decode": (("decode_split_kernel", "decode_combine_kernel"), _DECODE_SRC),
@@ -51,7 +52,8 @@ CALLS = {
     "paged_attention_chunk_i4": (("chunk_mfma_kernelILi2E", "chunk_mfma_kernel<2>"),
                                   _CHUNK_SRC),
     "paged_attention_mixed": (("mixed_kernel", "mixed_order_kernel"),
-                              ("mixed.hip",) + _CHUNK_SRC[1:] + _DECODE_SRC[:2]),
+                              ("mixed.hip", "chunk_core.h", "decode_core.h", "decode_q_core.h",
+                               "fp16_shape.h", "pkv_internal.h", "quant_codes.h")),
     "kv_append_rope": (("append_rope_kernel",), ("append.hip", "pkv_internal.h")),
 }
 
