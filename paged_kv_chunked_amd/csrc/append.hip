@@ -97,6 +97,16 @@ struct QRotation {
   }
 };
 
+// Token of workgroup column x of n.  Workgroups are dealt to the 8 XCDs
+// round-robin by linear id; this permutation gives XCD c the tokens
+// [c q + min(c, r), ...) in order (n = 8 q + r), so the 16 tokens of an arena
+// block, whose V elements interleave within each 32-byte row of the tile, are
+// written through one L2 and merge there into whole lines.
+__device__ inline int xcd_token(int x, int n) {
+  const int q = n >> 3, r = n & 7, c = x & 7;
+  return c * q + min(c, r) + (x >> 3);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void append_rope_kernel(
     const T* q, T* q_out, const T* __restrict__ k,
@@ -105,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_kernel(
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
     int num_seqs, const double2* __restrict__ cs, int rope_max_pos, int num_blocks, int Hq,
     int Hkv, int D) {
-  const int t = blockIdx.x;
+  const int t = xcd_token(blockIdx.x, gridDim.x);
   const int half = D >> 1;
   // workgroup blockIdx.y of gridDim.y takes an even share of the token's q
   // pairs, k pairs and v elements
@@ -187,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_vec_kernel(
     int rope_max_pos, int num_blocks, int Hq, int Hkv, int D) {
   constexpr int x = 16 / sizeof(T);
   typedef T vecT __attribute__((ext_vector_type(x)));
-  const int t = blockIdx.x, sl = blockIdx.y, S = gridDim.y;
+  const int t = xcd_token(blockIdx.x, gridDim.x), sl = blockIdx.y, S = gridDim.y;
   const int half = D >> 1, cph = half / x;  // pieces per half head
   auto share = [&](int n, int& lo, int& hi) {
     lo = (int)((long)n * sl / S);
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
     int num_seqs, const double2* __restrict__ cs, int rope_max_pos, int num_blocks, int Hq,
     int Hkv, int D) {
-  const int t = blockIdx.x;
+  const int t = xcd_token(blockIdx.x, gridDim.x);
   // workgroup blockIdx.y of gridDim.y takes an even share of the q pairs and
   // the KV heads blockIdx.y * kWaves + wave, + gridDim.y * kWaves, ...
   const int sl = blockIdx.y, S = gridDim.y;
@@ -400,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
     int num_seqs, int num_tokens, const double2* __restrict__ cs, int rope_max_pos,
     int num_blocks, int Hq, int Hkv, int D) {
-  const int t = blockIdx.x;
+  const int t = xcd_token(blockIdx.x, gridDim.x);
   // workgroup blockIdx.y of gridDim.y takes an even share of the q pairs and
   // the KV heads blockIdx.y * kWaves + wave, + gridDim.y * kWaves, ...
   const int sl = blockIdx.y, S = gridDim.y;
