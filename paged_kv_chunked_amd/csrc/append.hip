@@ -97,6 +97,49 @@ struct QRotation {
   }
 };
 
+// The same rotation in 16-byte pieces of 8 pairs (head dims that are a
+// multiple of 16): thread i takes pieces n0 + i, n0 + i + kThreads, ... of the
+// workgroup's share, each read whole and written whole (in place allowed: a
+// piece is read before it is written, by the same thread).
+struct QRotationVec {
+  half8_t lo, hi;   // the thread's first piece, loaded before the position lookup
+  int n0, n, cph, iq;
+  size_t tok;
+  __device__ void load(const _Float16* q, const _Float16* k_tok, int t, int Hq, int D, int slice,
+                       int slices) {
+    cph = (D >> 1) / 8;  // pieces per half head
+    const int total = q != nullptr ? Hq * cph : 0;
+    n0 = (int)((long)total * slice / slices);
+    n = (int)((long)total * (slice + 1) / slices);
+    tok = (size_t)t * Hq * D;
+    const _Float16* src = q != nullptr ? q + tok : k_tok;
+    iq = min(n0 + (int)threadIdx.x, max(n - 1, 0));
+    const _Float16* at = src + (size_t)(iq / cph) * D + (iq % cph) * 8;
+    lo = *(const half8_t*)at;
+    hi = *(const half8_t*)(at + (D >> 1));
+  }
+  __device__ void finish(const _Float16* q, _Float16* q_out, const double2* __restrict__ row,
+                         int D) {
+    const int half = D >> 1;
+    for (int idx = n0 + (int)threadIdx.x; idx < n; idx += kThreads) {
+      const size_t off = tok + (size_t)(idx / cph) * D + (idx % cph) * 8;
+      const half8_t a = idx == iq ? lo : *(const half8_t*)(q + off);
+      const half8_t c = idx == iq ? hi : *(const half8_t*)(q + off + half);
+      half8_t oa, oc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double2 r = row[(idx % cph) * 8 + e];
+        double o0, o1;
+        rope_pair((double)a[e], (double)c[e], r.x, r.y, o0, o1);
+        oa[e] = store_f64<_Float16>(o0);
+        oc[e] = store_f64<_Float16>(o1);
+      }
+      *(half8_t*)(q_out + off) = oa;
+      *(half8_t*)(q_out + off + half) = oc;
+    }
+  }
+};
+
 // Token of workgroup column x of n.  Workgroups are dealt to the 8 XCDs
 // round-robin by linear id; this permutation gives XCD c the tokens
 // [c q + min(c, r), ...) in order (n = 8 q + r), so the 16 tokens of an arena
@@ -311,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
   // workgroup blockIdx.y of gridDim.y takes an even share of the q pairs and
   // the KV heads blockIdx.y * kWaves + wave, + gridDim.y * kWaves, ...
   const int sl = blockIdx.y, S = gridDim.y;
-  QRotation<_Float16> qr;
+  QRotationVec qr;
   qr.load(q, k + (size_t)t * Hkv * D, t, Hq, D, sl, S);  // before the position lookup
   int row0, P;
   const int b = find_seq_start(cu_q_lens, chunk_start, num_seqs, t, row0, P);
@@ -414,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
   // workgroup blockIdx.y of gridDim.y takes an even share of the q pairs and
   // the KV heads blockIdx.y * kWaves + wave, + gridDim.y * kWaves, ...
   const int sl = blockIdx.y, S = gridDim.y;
-  QRotation<_Float16> qr;
+  QRotationVec qr;
   qr.load(q, k + (size_t)t * Hkv * D, t, Hq, D, sl, S);  // before the position lookup
   int row0, P;
   const int b = find_seq_start(cu_q_lens, chunk_start, num_seqs, t, row0, P);
