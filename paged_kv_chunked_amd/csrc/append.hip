@@ -9,6 +9,7 @@
 // rounded once to the storage dtype (fp16: round-to-odd to fp32, then to
 // nearest-even; fp32: the hardware's round-to-nearest-even convert), so the
 // stored values are exactly determined by the inputs.
+#include "fp16_shape.h"
 #include "pkv_internal.h"
 
 namespace pkv {

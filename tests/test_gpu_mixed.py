@@ -158,13 +158,16 @@ def test_mixed_full():
     check_against_split_calls(w, sample_rows=sample)
 
 
-def test_empty_sequences_change_nothing():
+@pytest.mark.parametrize("kv_bits", [0, 8, 4])
+def test_empty_sequences_change_nothing(kv_bits):
     """Sequences with no new rows (a repeated cu_q_lens entry) anywhere in the
     batch leave every output bit of paged_attention_chunk and
-    paged_attention_mixed unchanged."""
+    paged_attention_mixed unchanged (fp16, INT8 and INT4 arenas)."""
     seqs = [(300, 1), (0, 70), (1000, 1), (48, 16)]
     w = workloads.build("mixed_empty", 26, "f16", 32, 8, 128, 5.0e5, seqs,
                         max_blocks_per_seq=70)
+    if kv_bits:
+        w = _quant(w, kv_bits)
     say(f"{w.name}: set-up")
     dw = harness.DeviceWorkload(w)
     dw.append()
