@@ -3,9 +3,10 @@
 // RoPE already applied at absolute positions P onward, a causal mask over the
 // chunk so that row i sees the cached prefix and the chunk up to itself).
 //
-// Tuned path (fp16 storage, head_dim 128, 4 query heads per KV head): a dense
-// contraction, so both products run on gfx950 fp16 matrix cores
-// (v_mfma_f32_16x16x32_f16, fp32 accumulation).
+// Tuned path (fp16, INT8 or INT4 storage, head_dim 128, 4 query heads per KV
+// head): a dense contraction, so both products run on gfx950 fp16 matrix cores
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation).  Quantized tiles are staged
+// as codes and dequantized to fp16 in LDS once per workgroup (chunk_core.h).
 //   * one workgroup = (sequence, KV head, tile of 64 chunk rows), 8 waves: wave
 //     w serves query head 4g + (w & 3) for rows 32 (w >> 2) .. +31 of the tile,
 //     so every K/V tile is fetched once for 4 heads x 64 rows;
