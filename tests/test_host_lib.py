@@ -282,6 +282,26 @@ def test_chunk_key_range_parts(lib):
     assert lib.paged_attention_chunk_parts(gp, 4, 1024, 8192, ctypes.byref(n)) == 0 and n.value == 4
 
 
+@pytest.mark.parametrize("dtype", [2, 3])
+def test_quantized_arenas_take_the_tuned_chunk_and_mixed_paths(lib, dtype):
+    """INT8 / INT4 arenas at head_dim 128 and 4 query heads per KV head run the
+    tuned chunk and mixed kernels: the same key-range parts, schedule and
+    partials as fp16 (the partials are fp32 either way); other shapes of the
+    same storage keep the generic path (no workspace, never split)."""
+    g16, gq = _geom(), _geom(dtype=dtype)
+    for T, ctx in ((4096, 4096), (1024, 8192), (64, 32768), (64, 1500), (100, 500)):
+        assert pkv.paged_attention_chunk_parts(gq, 4, T, ctx) == \
+            pkv.paged_attention_chunk_parts(g16, 4, T, ctx)
+        assert pkv.paged_attention_chunk_workspace_bytes(gq, 4, T, ctx) == \
+            pkv.paged_attention_chunk_workspace_bytes(g16, 4, T, ctx)
+        assert pkv.paged_attention_mixed_workspace_bytes(gq, 4, T, ctx) == \
+            pkv.paged_attention_mixed_workspace_bytes(g16, 4, T, ctx) > 0
+    gen = _geom(dtype=dtype, num_q_heads=16)   # group 2: generic kernel
+    assert pkv.paged_attention_chunk_parts(gen, 4, 64, 32768) == 1
+    assert pkv.paged_attention_chunk_workspace_bytes(gen, 4, 64, 32768) == 0
+    assert pkv.paged_attention_mixed_workspace_bytes(gen, 4, 64, 32768) == 0
+
+
 def test_pool_admission_matches_oracle(lib):
     from oracle import pool as opool
     rng = np.random.default_rng(11)
