@@ -236,6 +236,9 @@ pkv_status paged_attention_decode_shared(
  * of a split call then round differently (same tolerance) from an unsplit
  * one; paged_attention_chunk_parts() reports the number of parts the tuned
  * path uses for a call's sizes (1: not split; always 1 off the tuned path).
+ * The tuned path takes fp16, INT8 and INT4 arenas at head_dim 128 with 4 query
+ * heads per KV head, and scale > 0; other calls run the generic kernel
+ * (fp32 arithmetic, one workgroup per row and query head, no workspace use).
  * ------------------------------------------------------------------------- */
 pkv_status paged_attention_chunk_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,
                                                  int32_t num_tokens, int32_t max_context_len,
