@@ -4,12 +4,13 @@
 Default run (N = 1):
   * decode: 64 decode tokens, contexts U[512, 4096], one Llama-3-8B-shaped layer
     (Hq 32 / Hkv 8, head dim 128, fp16, 16-token blocks, shuffled arena).  A
-    step = restore the un-rotated queries + kv_append_rope for the 64 new
-    tokens + paged_attention_decode (split kernel + log-sum-exp combine).
+    step = kv_append_rope for the 64 new tokens (drawn queries in, rotated
+    queries to a buffer of their own, so every step sees the same input) +
+    paged_attention_decode (split kernel + log-sum-exp combine).
     `value` is the algorithmic decode bytes of one step / step time.
   * chunk prefill (reported under "chunk_prefill"): 8 sequences with cached
-    prefixes 16*U{0..224} and a 512-token chunk each; a step = restore q +
-    kv_append_rope + paged_attention_chunk; TFLOP/s over visible pairs.
+    prefixes 16*U{0..224} and a 512-token chunk each; a step = kv_append_rope
+    + paged_attention_chunk; TFLOP/s over visible pairs.
   * decode over INT8 / INT4 arenas ("decode_int8", "decode_int4"): the same
     batch with K/V cached as codes plus one fp16 scale per (token, KV head)
     vector; the chunk workload over the same arenas ("chunk_prefill_int8",
