@@ -276,6 +276,18 @@ def test_long_full_sampled():
     run_case(w, full_arena=False, dec_sample=[1, 17, 32], chunk_sample={0: 40})
 
 
+@pytest.mark.xfail(strict=True, reason=(
+    "known precision limit of the quantized chunk kernel: it rounds each dequantized "
+    "K value to fp16, and on this workload's x8 key vectors that moves dominant scores "
+    "enough for a max error of 8.0e-3 (mean 3.4e-4) on the chunk rows; its decode rows "
+    "are within 8.9e-5"))
+def test_long_full_sampled_i8():
+    """The long workload over an INT8 arena: 32768-token decodes and the
+    4096-row chunk after 28,672 cached tokens, 1% of key vectors x8."""
+    w = i8(workloads.long_context())
+    run_case(w, full_arena=False, dec_sample=[1, 17, 32], chunk_sample={0: 40})
+
+
 # ---------------------------------------------------------------------------
 # invariants on the GPU path
 # ---------------------------------------------------------------------------
