@@ -114,6 +114,12 @@ typedef struct pkv_geom {
 
 const char* pkv_status_string(pkv_status s);
 int32_t pkv_abi_version(void);
+/* SHA-256 (64 lowercase hex digits, NUL-terminated, static storage) of the
+ * sources and compiler flags this library was built from: every file of the
+ * kernel source folder, this header, and the flag set.  Bindings compare it
+ * with a hash of the sources beside them and refuse a library built from
+ * other sources. */
+const char* pkv_source_hash(void);
 
 /* ---------------------------------------------------------------------------
  * RoPE table (part 3, section 4: RoPE at absolute positions).

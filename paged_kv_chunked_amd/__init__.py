@@ -50,6 +50,7 @@ _PG = ctypes.POINTER(Geom)
 _SIGS = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_abi_version": (_I32, []),
+    "pkv_source_hash": (ctypes.c_char_p, []),
     "pkv_rope_table_bytes": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_rope_table_host": (ctypes.c_int, [_P, ctypes.c_double, _I32, _I32]),
     "pkv_rope_table_init": (ctypes.c_int, [_P, ctypes.c_double, _I32, _I32, _P]),
@@ -104,7 +105,8 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libpkv.so (raises if it has not been built)."""
+    """The loaded libpkv.so.  Raises if it has not been built, or if it was built
+    from sources other than the ones beside it (its embedded source hash)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -115,8 +117,19 @@ def lib() -> ctypes.CDLL:
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        from . import build as _build
+        built, here = handle.pkv_source_hash().decode(), _build.source_hash()
+        if built != here:
+            raise RuntimeError(f"{LIB_PATH} was built from other sources (library "
+                               f"{built[:12]}, sources {here[:12]}): rebuild it with "
+                               "`python -m paged_kv_chunked_amd.build`")
         _lib = handle
     return _lib
+
+
+def pkv_source_hash() -> str:
+    """Hash of the sources and flags the loaded library was built from."""
+    return lib().pkv_source_hash().decode()
 
 
 def _check(code: int, where: str) -> None:

@@ -11,6 +11,7 @@ not know that feature, which is harmless.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -34,6 +35,35 @@ EXTRA_DEVICE_FLAGS = {"chunk.hip": ["-fno-honor-nans"], "mixed.hip": ["-fno-hono
 EXTRA_FLAGS = {"mixed.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
+HEADER = os.path.join(os.path.dirname(HERE), "include", "pkv.h")
+
+
+def source_files():
+    """Every file the library is built from: the kernel sources and the C header."""
+    names = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".h", ".cpp")))
+    return [os.path.join(CSRC, n) for n in names] + [HEADER]
+
+
+def source_hash() -> str:
+    """SHA-256 of the sources (name and bytes of each file) and of the flag set;
+    embedded in the library as pkv_source_hash() and checked when it loads."""
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    flags = {"arch": ARCH, "sources": SOURCES, "common": _flag_set(),
+             "device": EXTRA_DEVICE_FLAGS, "extra": EXTRA_FLAGS}
+    h.update(repr(sorted(flags.items())).encode())
+    return h.hexdigest()
+
+
+def _flag_set():
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -42,14 +72,13 @@ def hipcc() -> str:
 
 
 def common_flags():
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(os.path.dirname(HERE), "include")]
+    return _flag_set() + ["-I", os.path.join(os.path.dirname(HERE), "include")]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + common_flags()
+    cmd.append(f'-DPKV_SOURCE_HASH="{digest}"')
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     for f in EXTRA_DEVICE_FLAGS.get(src, []):
@@ -63,8 +92,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
+    digest = source_hash()
     with cf.ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, digest), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-o", tmp, f"--offload-arch={ARCH}"] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

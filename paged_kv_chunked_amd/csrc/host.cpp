@@ -27,6 +27,12 @@ const char* pkv_status_string(pkv_status s) {
 
 int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
 
+// The build passes the hash of the sources and flags it compiled.
+#ifndef PKV_SOURCE_HASH
+#error "PKV_SOURCE_HASH must be defined by the build"
+#endif
+const char* pkv_source_hash(void) { return PKV_SOURCE_HASH; }
+
 // ---------------------------------------------------------------------------
 // RoPE table: Kshipra part 3, section 4 (RoPE at absolute positions).  fp64,
 // (cos, sin) of pos * theta^(-2i/D) from the C library, [max_pos][D/2][2].

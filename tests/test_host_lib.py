@@ -49,6 +49,15 @@ def test_exports_every_declared_symbol(lib):
     assert pkv.pkv_abi_version() == 1
 
 
+def test_library_matches_its_sources(lib):
+    """The library embeds the hash of the sources and flags it was built from;
+    the binding refuses a library whose hash differs from the sources beside it."""
+    from paged_kv_chunked_amd import build as pkv_build
+    h = pkv.pkv_source_hash()
+    assert len(h) == 64 and all(c in "0123456789abcdef" for c in h)
+    assert h == pkv_build.source_hash()
+
+
 def test_rope_table_bitwise_equals_oracle(lib):
     for theta, D, max_pos in [(1.0e4, 64, 700), (5.0e5, 128, 9000)]:
         ours = np.empty((max_pos, D // 2, 2), np.float64)
