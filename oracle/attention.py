@@ -43,10 +43,13 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, start: int, scale: float
     heads = list(range(Hq)) if heads is None else list(heads)
     q64 = np.asarray(q).astype(np.float64)
     out = np.empty((rows.size, len(heads), D), np.float64)
+    kv64 = {}   # KV head -> its keys and values in fp64 (converted once per head group)
     for hi, h in enumerate(heads):
         g = h // G
-        Kg = np.asarray(K[:, g, :]).astype(np.float64)
-        Vg = np.asarray(V[:, g, :]).astype(np.float64)
+        if g not in kv64:
+            kv64 = {g: (np.asarray(K[:, g, :]).astype(np.float64),
+                        np.asarray(V[:, g, :]).astype(np.float64))}
+        Kg, Vg = kv64[g]
         for r0 in range(0, rows.size, ROW_BLOCK):
             r = rows[r0:r0 + ROW_BLOCK]
             pos = start + r                                   # absolute positions

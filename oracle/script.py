@@ -131,8 +131,11 @@ def rotated_q(w, row: int, cos_sin=None) -> np.ndarray:
     return _rope.rotate_store(q, s.start + np.arange(s.count), cos, sin, w.np_dtype)
 
 
-def sequence_kv(w, state: State, row: int, length: Optional[int] = None, cos_sin=None):
-    """Stored K, V [length][Hkv][D] of step row ``row``'s sequence (after append)."""
+def sequence_kv(w, state: State, row: int, length: Optional[int] = None, cos_sin=None,
+                codec: bool = True):
+    """Stored K, V [length][Hkv][D] of step row ``row``'s sequence (after append).
+    For a quantized cache these are the decoded values (fp64), or with
+    ``codec=False`` the fp16 values the codec was given."""
     s = w.step[row]
     length = s.start + s.count if length is None else length
     table = state.tables[s.seq]
@@ -157,7 +160,7 @@ def sequence_kv(w, state: State, row: int, length: Optional[int] = None, cos_sin
             start = fills[int(source)][3]
         K[sel] = _rope.rotate_store(k[t], start + t, cos, sin, w.np_dtype)
         V[sel] = v[t]
-    if getattr(w, "kv_bits", 0):   # the cache holds the codes of these values
+    if codec and getattr(w, "kv_bits", 0):   # the cache holds the codes of these values
         return _quant.roundtrip(K, w.kv_bits), _quant.roundtrip(V, w.kv_bits)
     return K, V
 

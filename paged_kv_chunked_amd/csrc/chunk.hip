@@ -142,7 +142,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
   if (k >= num_seqs * n_rtiles) return;
   const int item = order[k];
   const int b = item / n_rtiles, rt = item - b * n_rtiles;
-  chunk_tile_unit<kQ>(out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
+  __shared__ u32x4 lds[ChunkLds<kQ>::kUnits];
+  chunk_tile_unit<kQ>(lds, out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
                       scale_log2, Hkv, num_blocks, num_tokens, b, rt, g, part, parts, part_o,
                       part_ml);
 }

@@ -1,7 +1,8 @@
 // Core of the tuned chunk prefill: one (sequence, 64-row tile, KV head) unit,
 // used by paged_attention_chunk and by the mixed-batch kernel (the design is
 // described at the top of chunk.hip).  A workgroup of kThreads runs one unit;
-// the unit owns the workgroup's 128 KiB of LDS.
+// the unit owns the workgroup's LDS, one array laid out by ChunkLds<kQ> and
+// declared by the kernel.
 #pragma once
 
 #include <type_traits>
@@ -106,14 +107,25 @@ __device__ inline u32x4 mask_unit(u32x4 x, int key0, int limit) {
 // Quantized arenas (head dim 128): each (block, KV head) tile holds the codes,
 // then 16 fp16 scales at byte kCodeBlk.  The codes of 3 key tiles are staged in
 // LDS ([K codes of 4 blocks][V codes of 4 blocks][K scales][V scales]); every
-// thread then dequantizes its share of one tile into a 2-stage fp16 ring laid
-// out as the fp16 unit's, so the matrix-core loop is the same.
+// thread then turns its share of one tile's codes into fp16 (exactly: every
+// code is a small integer) in a 2-stage fp16 ring laid out as the fp16 unit's,
+// so the matrix-core loop is the same, and 128 threads put the tile's scales
+// into a 2-stage fp32 scale ring.  The scales are applied where the codec's
+// decoded value code * scale enters exactly: the K scale multiplies the fp32
+// score of its key, the V scale the key's probability before it is rounded to
+// fp16 for the second product (as the quantized decode unit does).  Rounding
+// code * scale to fp16 instead would add a second rounding the codec does not
+// have.
 constexpr int kCodeStages = 3;
 template <int kQ>
 struct QGeom;
 template <>
 struct QGeom<0> {  // fp16 arena: tiles land in the fp16 ring directly
-  static constexpr int kRingUnits = kStages * kStageUnits;
+  static constexpr int kFp16Stages = kStages;
+  static constexpr int kStageBytes = 0;
+  static constexpr int kCodeStageCount = 0;
+  static constexpr int kScaleStages = 0;
+  static constexpr float kPvScale = 1.f;
 };
 template <>
 struct QGeom<1> {  // INT8: 3 loads per wave per tile (K codes, V codes, scales)
@@ -121,7 +133,12 @@ struct QGeom<1> {  // INT8: 3 loads per wave per tile (K codes, V codes, scales)
   static constexpr int kTile = (int)i8_tile_bytes(kD);
   static constexpr int kLoads = 3;
   static constexpr int kStageBytes = 8 * kCodeBlk + 256;
-  static constexpr int kRingUnits = 2 * kStageUnits + kCodeStages * kStageBytes / 16;
+  static constexpr int kFp16Stages = 2;
+  static constexpr int kCodeStageCount = kCodeStages;
+  static constexpr int kScaleStages = 2;
+  // p * s_v * kPvScale must stay finite in fp16: p <= 2^kSlack (8) and an INT8
+  // scale is at most fp16(65504 / 127) = 515.5, so 2^8 * 515.5 * 2^-2 = 32992
+  static constexpr float kPvScale = 0.25f;
 };
 template <>
 struct QGeom<2> {  // INT4: 2 loads per wave per tile (K or V codes, scales)
@@ -129,23 +146,192 @@ struct QGeom<2> {  // INT4: 2 loads per wave per tile (K or V codes, scales)
   static constexpr int kTile = (int)i4_tile_bytes(kD);
   static constexpr int kLoads = 2;
   static constexpr int kStageBytes = 8 * kCodeBlk + 256;
-  static constexpr int kRingUnits = 2 * kStageUnits + kCodeStages * kStageBytes / 16;
+  static constexpr int kFp16Stages = 2;
+  static constexpr int kCodeStageCount = kCodeStages;
+  static constexpr int kScaleStages = 2;
+  // INT4 scales reach fp16(65504 / 7) = 9360: 2^8 * 9360 * 2^-6 = 37440
+  static constexpr float kPvScale = 1.f / 64.f;
 };
+
+// Scale ring stage: 64 K scales (fp32), then 64 V scales times kPvScale.
+constexpr int kScaleStageFloats = 2 * kBN;
+
+// The unit's LDS, one array, byte offsets of its regions:
+//   [fp16 ring: kFp16Stages x kStageUnits 16-byte units (K of 4 blocks, V of 4)]
+//   [scale ring: kScaleStages x kScaleStageFloats fp32]
+//   [code ring: kCodeStageCount x kStageBytes]
+//   [slot: 16 bytes for the persistent mixed kernel's unit index]
+template <int kQ>
+struct ChunkLds {
+  using QG = QGeom<kQ>;
+  static constexpr int kFp16 = 0;
+  static constexpr int kScale = kFp16 + QG::kFp16Stages * kStageUnits * 16;
+  static constexpr int kCode = kScale + QG::kScaleStages * kScaleStageFloats * 4;
+  static constexpr int kSlot = kCode + QG::kCodeStageCount * QG::kStageBytes;
+  static constexpr int kBytes = kSlot + 16;
+  static constexpr int kUnits = kBytes / 16;  // size of the u32x4 array
+  static_assert(kScale % 16 == 0 && kCode % 16 == 0 && kSlot % 16 == 0, "16-byte regions");
+  static_assert(kBytes <= 160 * 1024, "fits the 160 KiB of LDS of a gfx950 CU");
+};
+
+// ---- where every LDS write of a unit lands (host-checkable) ---------------
+// The same functions give the kernel its addresses and the compile-time check
+// below its cases, so the check covers the code that runs.
+
+// fp16 arenas, direct-to-LDS tile load: byte address (relative to the LDS
+// array) of lane `lane`'s 16 bytes for quarter j of wave `wave`, K (kv = 0)
+// or V (kv = 1), in fp16 stage `stage`.
+__host__ __device__ constexpr int tile_dma_byte(int stage, int wave, int j, int kv, int lane) {
+  constexpr int kQuarters = 16 / kWaves;
+  const int dma_blk = (wave * kQuarters) >> 2;
+  const int qq = (wave * kQuarters + j) & 3;
+  return stage * kStageUnits * 16 + kv * 4 * kUnitsPerBlock * 16 +
+         (dma_blk * kUnitsPerBlock + qq * 64) * 16 + 16 * lane;
+}
+
+// Quantized arenas, direct-to-LDS code loads into code stage `cstage`:
+// which = 0: the K codes (INT8) or the codes (INT4) of wave `wave`; 1: the V
+// codes (INT8 only); 2: the scale run (lanes 0-1 only).
+template <int kQ>
+__host__ __device__ constexpr int code_dma_byte(int cstage, int wave, int which, int lane) {
+  using QG = QGeom<kQ>;
+  const int st = ChunkLds<kQ>::kCode + cstage * QG::kStageBytes;
+  if (which == 2) return st + 8 * QG::kCodeBlk + 32 * wave + 16 * lane;
+  return st + (which == 1 ? 4 * QG::kCodeBlk : 0) + 1024 * wave + 16 * lane;
+}
+
+// Conversion of one code tile: thread tid writes fp16 units tid + 512 j of the
+// K half (kv = 0) and of the V half (kv = 1) of fp16 stage `stage`; threads
+// below 2 kBN write one scale each.
+template <int kQ>
+__host__ __device__ constexpr int conv_unit_byte(int stage, int kv, int tid, int j) {
+  return ChunkLds<kQ>::kFp16 + stage * kStageUnits * 16 +
+         (kv * 4 * kUnitsPerBlock + tid + 512 * j) * 16;
+}
+template <int kQ>
+__host__ __device__ constexpr int conv_scale_byte(int stage, int tid) {
+  return ChunkLds<kQ>::kScale + (stage * kScaleStageFloats + tid) * 4;
+}
+
+// Offsets (bytes, within one code stage) the conversion reads for thread tid's
+// unit tid + 512 j: K codes, K scale, V codes, V scale.
+template <int kQ>
+__host__ __device__ constexpr int conv_kcode_off(int tid, int j) {
+  using QG = QGeom<kQ>;
+  const int u = tid + 512 * j;
+  const int a = u >> 8, pos = u & 255, p8 = pos >> 4;
+  const int sl = (pos & 15) ^ (4 * (a & 1));
+  if (kQ == 1) return a * QG::kCodeBlk + (p8 >> 1) * 256 + i8_kpos(sl) * 16 + 8 * (p8 & 1);
+  return a * QG::kCodeBlk + (p8 >> 1) * 128 + i4_krec(sl) * 8;
+}
+template <int kQ>
+__host__ __device__ constexpr int conv_vcode_off(int tid, int j) {
+  using QG = QGeom<kQ>;
+  const int u = tid + 512 * j;
+  const int a = u >> 8, pos = u & 255;
+  const int unit = (pos - 16 * (a & 1)) & 255, d = unit >> 1, hs = unit & 1;
+  if (kQ == 1) return 4 * QG::kCodeBlk + a * QG::kCodeBlk + 8 * unit;
+  return 4 * QG::kCodeBlk + a * QG::kCodeBlk + i4_vbyte(d, 8 * hs, kD);
+}
+// Scale of key `key` of the tile (K: kv = 0, V: kv = 1) within a code stage.
+template <int kQ>
+__host__ __device__ constexpr int conv_scale_off(int kv, int key) {
+  return 8 * QGeom<kQ>::kCodeBlk + 128 * kv + 32 * (key >> 4) + 2 * (key & 15);
+}
+
+// Every write of the unit stays inside its own region (and so never reaches
+// another region or the slot), and every conversion read stays inside the
+// part of the code stage it means to read.
+template <int kQ>
+constexpr bool chunk_lds_writes_in_bounds() {
+  using L = ChunkLds<kQ>;
+  using QG = QGeom<kQ>;
+  auto inside = [](int lo, int n, int at, int hi) { return at >= lo && at + n <= hi; };
+  if constexpr (kQ == 0) {
+    for (int st = 0; st < QG::kFp16Stages; ++st)
+      for (int w = 0; w < kWaves; ++w)
+        for (int j = 0; j < 16 / kWaves; ++j)
+          for (int kv = 0; kv < 2; ++kv)
+            for (int ln = 0; ln < 64; ++ln) {
+              const int lo = st * kStageUnits * 16 + kv * 4 * kUnitsPerBlock * 16;
+              if (!inside(lo, 16, tile_dma_byte(st, w, j, kv, ln), lo + 4 * kUnitsPerBlock * 16))
+                return false;
+            }
+    // zeroing of V past the sequence: units tid + e kThreads of the V half
+    for (int st = 0; st < QG::kFp16Stages; ++st)
+      for (int u = 0; u < 2 * kThreads; ++u)
+        if (u >= 4 * kUnitsPerBlock) return false;
+    return L::kSlot == QG::kFp16Stages * kStageUnits * 16;
+  } else {
+    for (int cs = 0; cs < QG::kCodeStageCount; ++cs) {
+      const int lo = L::kCode + cs * QG::kStageBytes;
+      for (int w = 0; w < kWaves; ++w)
+        for (int ln = 0; ln < 64; ++ln) {
+          // codes: K (and for INT8 V) regions of the stage
+          if (!inside(lo, 16, code_dma_byte<kQ>(cs, w, 0, ln),
+                      lo + (kQ == 1 ? 4 : 8) * QG::kCodeBlk))
+            return false;
+          if (kQ == 1 && !inside(lo + 4 * QG::kCodeBlk, 16, code_dma_byte<kQ>(cs, w, 1, ln),
+                                 lo + 8 * QG::kCodeBlk))
+            return false;
+          if (ln < 2 && !inside(lo + 8 * QG::kCodeBlk, 16, code_dma_byte<kQ>(cs, w, 2, ln),
+                                lo + QG::kStageBytes))
+            return false;
+        }
+    }
+    for (int st = 0; st < QG::kFp16Stages; ++st)
+      for (int tid = 0; tid < kThreads; ++tid)
+        for (int j = 0; j < 2; ++j)
+          for (int kv = 0; kv < 2; ++kv) {
+            const int lo = st * kStageUnits * 16 + kv * 4 * kUnitsPerBlock * 16;
+            if (!inside(lo, 16, conv_unit_byte<kQ>(st, kv, tid, j), lo + 4 * kUnitsPerBlock * 16))
+              return false;
+          }
+    for (int st = 0; st < QG::kScaleStages; ++st)
+      for (int tid = 0; tid < kScaleStageFloats; ++tid) {
+        const int lo = L::kScale + st * kScaleStageFloats * 4;
+        if (!inside(lo, 4, conv_scale_byte<kQ>(st, tid), lo + kScaleStageFloats * 4))
+          return false;
+      }
+    // conversion reads: codes in the K / V code regions, scales in the scale runs
+    for (int tid = 0; tid < kThreads; ++tid)
+      for (int j = 0; j < 2; ++j) {
+        if (!inside(0, 8, conv_kcode_off<kQ>(tid, j), 4 * QG::kCodeBlk)) return false;
+        if (!inside(4 * QG::kCodeBlk, kQ == 1 ? 8 : 4, conv_vcode_off<kQ>(tid, j),
+                    8 * QG::kCodeBlk))
+          return false;
+      }
+    for (int key = 0; key < kBN; ++key)
+      for (int kv = 0; kv < 2; ++kv)
+        if (!inside(8 * QG::kCodeBlk + 128 * kv, 2, conv_scale_off<kQ>(kv, key),
+                    8 * QG::kCodeBlk + 128 * kv + 128))
+          return false;
+    return L::kSlot == L::kCode + QG::kCodeStageCount * QG::kStageBytes;
+  }
+}
+static_assert(kWaves == 8 && kThreads == 512,
+              "the quantized load and conversion maps assume 8 waves of 64 lanes");
+static_assert(chunk_lds_writes_in_bounds<0>(), "fp16 unit LDS layout");
+static_assert(chunk_lds_writes_in_bounds<1>(), "INT8 unit LDS layout");
+static_assert(chunk_lds_writes_in_bounds<2>(), "INT4 unit LDS layout");
 
 // Row tile rt of sequence b for KV head g.  With parts > 1 the unit covers
 // part `part` of the tile's key tiles (an even share, possibly empty) and
 // writes the unnormalised O, the running maximum (log2 units) and the
 // denominator of every row to part_o / part_ml, [part][row][head], for
 // chunk_combine_kernel to merge.  kQ: arena storage, 0 fp16, 1 INT8, 2 INT4.
+// lds: the workgroup's LDS array of ChunkLds<kQ>::kUnits 16-byte units.
 template <int kQ = 0>
 __device__ __forceinline__ void chunk_tile_unit(
-    float* __restrict__ out, const _Float16* __restrict__ q,
+    u32x4* __restrict__ lds, float* __restrict__ out, const _Float16* __restrict__ q,
     const void* __restrict__ k_arena, const void* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
     float scale_log2, int Hkv, int num_blocks, int num_tokens, int b, int rt, int g,
     int part = 0, int parts = 1, float* __restrict__ part_o = nullptr,
     float* __restrict__ part_ml = nullptr) {
+  using QG = QGeom<kQ>;
+  using LY = ChunkLds<kQ>;
   const int row0 = cu_q_lens[b];
   const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
   if (rt * kRows >= C) return;
@@ -158,11 +344,12 @@ __device__ __forceinline__ void chunk_tile_unit(
   const int lr = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
   const int h = g * kG + (wave & 3);
-  const int wrow0 = rt * kRows + kBM * (wave >> 2);  // (kRowGroups waves per head)  // first chunk row of this wave
+  const int wrow0 = rt * kRows + kBM * (wave >> 2);  // first chunk row of this wave
 
   // fp16 stages of (K: 4 blocks x 256 units, then V: 4 blocks x 256 units):
-  // 4 for fp16 arenas (128 KiB), else 2, then the code stages
-  __shared__ u32x4 ring[QGeom<kQ>::kRingUnits];
+  // 4 for fp16 arenas (128 KiB), else 2, then the scale and code stages
+  u32x4* const ring = lds + LY::kFp16 / 16;
+  float* const scale_ring = (float*)(lds + LY::kScale / 16);
 
   const int row_hi = min(C, rt * kRows + kRows);
   const int kend = min(Lc, P + row_hi);  // keys [0, kend) are visible to some row
@@ -183,22 +370,23 @@ __device__ __forceinline__ void chunk_tile_unit(
   // contents never reach the output: scores masked, V zeroed).
   constexpr int kQuarters = 16 / kWaves;  // 1 KiB quarters of block tiles per wave
   const int dma_blk = (wave * kQuarters) >> 2;
-  const uint32_t ring_lds =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)ring;
+  const uint32_t lds_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)lds;
   auto issue_tile = [&](int t) {
     int blk = bt[min(t * 4 + dma_blk, nblk_seq - 1)];
     blk = (blk < 0 || blk >= num_blocks) ? 0 : blk;
     const u32x4* kt = (const u32x4*)k_arena + ((size_t)blk * Hkv + g) * kUnitsPerBlock;
     const u32x4* vt = (const u32x4*)v_arena + ((size_t)blk * Hkv + g) * kUnitsPerBlock;
-    const uint32_t st = ring_lds + (uint32_t)((t % kStages) * kStageUnits * 16);
+    const int stage = t % kStages;
 #pragma unroll
     for (int j = 0; j < kQuarters; ++j) {
       const int qq = (wave * kQuarters + j) & 3;
       const int pos = qq * 64 + lane;
-      const uint32_t off = (uint32_t)((dma_blk * kUnitsPerBlock + qq * 64) * 16);
-      dma16(kt + (pos ^ (4 * (dma_blk & 1))), __builtin_amdgcn_readfirstlane(st + off));
+      // lane 0's address; lane i lands 16 i bytes further
+      dma16(kt + (pos ^ (4 * (dma_blk & 1))),
+            __builtin_amdgcn_readfirstlane(lds_base + tile_dma_byte(stage, wave, j, 0, 0)));
       dma16(vt + ((pos - 16 * (dma_blk & 1)) & (kUnitsPerBlock - 1)),
-            __builtin_amdgcn_readfirstlane(st + 4 * kUnitsPerBlock * 16 + off));
+            __builtin_amdgcn_readfirstlane(lds_base + tile_dma_byte(stage, wave, j, 1, 0)));
     }
   };
 
@@ -206,13 +394,11 @@ __device__ __forceinline__ void chunk_tile_unit(
   // wave w moves half w & 1 of block w >> 1's K and V codes; INT4: waves 0-3
   // move the K codes of block w, waves 4-7 the V codes of block w - 4; and
   // lanes 0-1 of wave w the K (w < 4) or V scales of block w & 3.
-  const uint32_t code_lds = ring_lds + 2u * kStageUnits * 16u;
   auto issue_codes = [&](int t) {
     if constexpr (kQ != 0) {
-      using QG = QGeom<kQ>;
       const uint8_t* ka8 = (const uint8_t*)k_arena;
       const uint8_t* va8 = (const uint8_t*)v_arena;
-      const uint32_t st = code_lds + (uint32_t)((t % kCodeStages) * QG::kStageBytes);
+      const int cs = t % kCodeStages;
       int sblk = bt[min(t * 4 + (wave & 3), nblk_seq - 1)];
       sblk = (sblk < 0 || sblk >= num_blocks) ? 0 : sblk;
       const size_t stile = ((size_t)sblk * Hkv + g) * QG::kTile;
@@ -221,14 +407,15 @@ __device__ __forceinline__ void chunk_tile_unit(
         int blk = bt[min(t * 4 + (wave >> 1), nblk_seq - 1)];
         blk = (blk < 0 || blk >= num_blocks) ? 0 : blk;
         const size_t src = ((size_t)blk * Hkv + g) * QG::kTile + 16 * (64 * (wave & 1) + lane);
-        dma16(ka8 + src, __builtin_amdgcn_readfirstlane(st + 1024u * wave));
-        dma16(va8 + src, __builtin_amdgcn_readfirstlane(st + 4u * QG::kCodeBlk + 1024u * wave));
+        dma16(ka8 + src, __builtin_amdgcn_readfirstlane(lds_base + code_dma_byte<kQ>(cs, wave, 0, 0)));
+        dma16(va8 + src, __builtin_amdgcn_readfirstlane(lds_base + code_dma_byte<kQ>(cs, wave, 1, 0)));
       } else {
-        dma16(sarena + stile + 16 * lane, __builtin_amdgcn_readfirstlane(st + 1024u * wave));
+        dma16(sarena + stile + 16 * lane,
+              __builtin_amdgcn_readfirstlane(lds_base + code_dma_byte<kQ>(cs, wave, 0, 0)));
       }
       if (lane < 2)
         dma16(sarena + stile + QG::kCodeBlk + 16 * lane,
-              __builtin_amdgcn_readfirstlane(st + 8u * QG::kCodeBlk + 32u * wave));
+              __builtin_amdgcn_readfirstlane(lds_base + code_dma_byte<kQ>(cs, wave, 2, 0)));
     }
   };
   auto issue = [&](int t) {
@@ -236,73 +423,57 @@ __device__ __forceinline__ void chunk_tile_unit(
     else issue_codes(t);
   };
 
-  // Dequantization of code tile t into fp16 stage t & 1: thread tid writes
-  // units tid and tid + 512 of the K half and of the V half, in the fp16
-  // unit's order (K: piece p * 16 + slot', slot' = slot ^ 4 in odd blocks; V:
-  // (2 dim + half + 16 (block & 1)) mod 256), multiplied by the key's scale.
-  // Keys past the sequence get scale 0 (their scale bytes are not data).
-  int kc_off[2], ks_off[2], k_key[2], vc_off[2], vs_off[2], v_key[2];
-  [[maybe_unused]] int k_sh[2];
+  // Conversion of code tile t into fp16 stage t & 1 and scale stage t & 1:
+  // thread tid writes units tid and tid + 512 of the K half and of the V half
+  // of the fp16 stage, in the fp16 unit's order (K: piece p * 16 + slot',
+  // slot' = slot ^ 4 in odd blocks; V: (2 dim + half + 16 (block & 1)) mod
+  // 256), holding the codes as exact fp16 integers.  Threads 0-63 write the
+  // K scale of key tid as fp32, threads 64-127 the V scale of key tid - 64
+  // times kPvScale.  Keys past the sequence get scale 0 (their scale bytes are
+  // not data; their codes are finite).
+  [[maybe_unused]] int kc_off[2], vc_off[2], k_sh[2];
+  [[maybe_unused]] int sc_off = 0, sc_key = 0;
+  [[maybe_unused]] float sc_mul = 1.f;
   if constexpr (kQ != 0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int u = tid + 512 * j;
-      const int a = u >> 8, pos = u & 255, p8 = pos >> 4;
-      const int sl = (pos & 15) ^ (4 * (a & 1));
-      if constexpr (kQ == 1)
-        kc_off[j] = a * QGeom<kQ>::kCodeBlk + (p8 >> 1) * 256 + i8_kpos(sl) * 16 + 8 * (p8 & 1);
-      else
-        kc_off[j] = a * QGeom<kQ>::kCodeBlk + (p8 >> 1) * 128 + i4_krec(sl) * 8;
-      k_sh[j] = 4 * (p8 & 1);
-      ks_off[j] = 8 * QGeom<kQ>::kCodeBlk + a * 32 + 2 * sl;
-      k_key[j] = 16 * a + sl;
-      const int unit = (pos - 16 * (a & 1)) & 255, d = unit >> 1, hs = unit & 1;
-      if constexpr (kQ == 1)
-        vc_off[j] = 4 * QGeom<kQ>::kCodeBlk + a * QGeom<kQ>::kCodeBlk + 8 * unit;
-      else
-        vc_off[j] = 4 * QGeom<kQ>::kCodeBlk + a * QGeom<kQ>::kCodeBlk + i4_vbyte(d, 8 * hs, kD);
-      vs_off[j] = 8 * QGeom<kQ>::kCodeBlk + 128 + a * 32 + 16 * hs;
-      v_key[j] = 16 * a + 8 * hs;
+      kc_off[j] = conv_kcode_off<kQ>(tid, j);
+      vc_off[j] = conv_vcode_off<kQ>(tid, j);
+      k_sh[j] = 4 * ((((tid + 512 * j) & 255) >> 4) & 1);
     }
+    sc_key = tid & (kBN - 1);
+    sc_off = conv_scale_off<kQ>(tid >> 6, sc_key);
+    sc_mul = tid >= kBN ? QG::kPvScale : 1.f;
   }
   // (masked: the tile reaches past the sequence; keys >= lim get scale 0)
   auto convert_tile = [&](int t, auto masked) {
     if constexpr (kQ != 0) {
-      const uint8_t* cs = (const uint8_t*)(ring + 2 * kStageUnits) +
-                          (t % kCodeStages) * QGeom<kQ>::kStageBytes;
+      const uint8_t* cs = (const uint8_t*)lds + LY::kCode + (t % kCodeStages) * QG::kStageBytes;
       u32x4* fs = ring + (t & 1) * kStageUnits;
-      const int lim = Lc - t * kBN;  // keys of the tile at or past this one are not data
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        half8_t h;
-        if constexpr (kQ == 1) {
-          const uint2 c = *(const uint2*)(cs + kc_off[j]);
-          h = codes_to_half(c.x, c.y);
-        } else {
-          const uint2 c = *(const uint2*)(cs + kc_off[j]);
-          h = nibbles_to_half(c.x >> k_sh[j], c.y >> k_sh[j]);
-        }
-        _Float16 ks = *(const _Float16*)(cs + ks_off[j]);
-        if (masked && k_key[j] >= lim) ks = (_Float16)0.f;
-        fs[tid + 512 * j] = __builtin_bit_cast(u32x4, h * (half8_t)ks);
+        const uint2 c = *(const uint2*)(cs + kc_off[j]);
+        half8_t hk;
+        if constexpr (kQ == 1) hk = codes_to_half(c.x, c.y);
+        else hk = nibbles_to_half(c.x >> k_sh[j], c.y >> k_sh[j]);
+        fs[tid + 512 * j] = __builtin_bit_cast(u32x4, hk);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        half8_t h;
+        half8_t hv;
         if constexpr (kQ == 1) {
           const uint2 c = *(const uint2*)(cs + vc_off[j]);
-          h = codes_to_half(c.x, c.y);
+          hv = codes_to_half(c.x, c.y);
         } else {
           const uint32_t w = *(const uint32_t*)(cs + vc_off[j]);
-          h = nibbles_to_half(w, w >> 4);
+          hv = nibbles_to_half(w, w >> 4);
         }
-        half8_t vs = __builtin_bit_cast(half8_t, *(const u32x4*)(cs + vs_off[j]));
-        if (masked) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (v_key[j] + i >= lim) vs[i] = (_Float16)0.f;
-        }
-        fs[4 * kUnitsPerBlock + tid + 512 * j] = __builtin_bit_cast(u32x4, h * vs);
+        fs[4 * kUnitsPerBlock + tid + 512 * j] = __builtin_bit_cast(u32x4, hv);
+      }
+      if (tid < kScaleStageFloats) {
+        float sc = (float)*(const _Float16*)(cs + sc_off) * sc_mul;
+        if (masked && sc_key >= Lc - t * kBN) sc = 0.f;
+        scale_ring[(t & 1) * kScaleStageFloats + tid] = sc;
       }
     }
   };
@@ -375,6 +546,9 @@ __device__ __forceinline__ void chunk_tile_unit(
   // V fragment of dims block db for the keys of MFMA u: 16-byte unit
   // (2 (16db + lr) + (lq & 1) + 16 (lq >> 1)) mod 256 of block 2u + (lq >> 1)
   const int vunit = 2 * lr + (lq & 1) + 16 * (lq >> 1);
+  // Quantized arenas: this lane's scores (kb, i) are keys key_u + 4 (kb & 1) + i
+  // of the tile, u = kb >> 1, and its probabilities pb[u][..][e] keys key_u + e.
+  [[maybe_unused]] const int key_u0 = 16 * (lq >> 1) + 8 * (lq & 1);
 
   for (int t = tb; t < te; ++t) {
     if constexpr (kQ == 0) {
@@ -388,10 +562,10 @@ __device__ __forceinline__ void chunk_tile_unit(
       if (t + 3 < te) issue_tile(t + 3);
     } else {
       // code tile t + 1 is in LDS (this wave's loads, then every wave's);
-      // after the barrier fp16 stage t & 1 is complete, every wave is done
-      // with stage (t + 1) & 1 and with code stage t % 3, which the next
-      // load reuses
-      if (t + 2 < te) wait_vm<QGeom<kQ>::kLoads>();
+      // after the barrier fp16 and scale stage t & 1 are complete, every wave
+      // is done with stage (t + 1) & 1 and with code stage t % 3, which the
+      // next load reuses
+      if (t + 2 < te) wait_vm<QG::kLoads>();
       else wait_vm<0>();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -412,6 +586,16 @@ __device__ __forceinline__ void chunk_tile_unit(
         if (key0 + 8 > Lc) vw[unit] = mask_unit(vw[unit], key0, Lc);
       }
       __syncthreads();
+    }
+    // Quantized arenas: the K scales of this lane's 16 keys (requested here,
+    // used after the first product)
+    [[maybe_unused]] f32x4 ksc[2][2];
+    if constexpr (kQ != 0) {
+      const float* sl = scale_ring + (t & 1) * kScaleStageFloats;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) ksc[u][hh] = *(const f32x4*)(sl + key_u0 + 32 * u + 4 * hh);
     }
 
     // S^T[key][row] = K . Q^T (raw scores).  The K fragments of MFMA kb + 1
@@ -457,6 +641,15 @@ __device__ __forceinline__ void chunk_tile_unit(
     for (int r = 0; r < 16; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, kRB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+
+    // Quantized arenas: the product of the codes with q times the key's scale
+    // is the score of the decoded key (code * scale, exact)
+    if constexpr (kQ != 0) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) sacc[kb][rb] *= ksc[kb >> 1][kb & 1];
     }
 
     // Causal mask (and keys past the sequence) only where the tile reaches
@@ -513,21 +706,46 @@ __device__ __forceinline__ void chunk_tile_unit(
     // pb[u][rb]: B operand of the second product, keys 8(lq & 1) .. +7 of
     // block 2u + (lq >> 1) = scores (kb = 2u, i = 0..3), (kb = 2u + 1, i = 0..3)
     half8_t pb[2][kRB];
+    if constexpr (kQ == 0) {
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      float lsum = 0.f;
+      for (int rb = 0; rb < kRB; ++rb) {
+        float lsum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const half2_t ph = {
-              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i], scale_log2, m_off[rb])),
-              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i + 1], scale_log2, m_off[rb]))};
-          lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
-          pb[kb >> 1][rb][4 * (kb & 1) + i] = ph[0];
-          pb[kb >> 1][rb][4 * (kb & 1) + i + 1] = ph[1];
-        }
-      l_run[rb] += lsum;
+          for (int i = 0; i < 4; i += 2) {
+            const half2_t ph = {
+                (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i], scale_log2, m_off[rb])),
+                (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i + 1], scale_log2, m_off[rb]))};
+            lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
+            pb[kb >> 1][rb][4 * (kb & 1) + i] = ph[0];
+            pb[kb >> 1][rb][4 * (kb & 1) + i + 1] = ph[1];
+          }
+        l_run[rb] += lsum;
+      }
+    } else {
+      // the V scale (times kPvScale) multiplies the fp32 probability, which
+      // is then rounded once to fp16; the denominator sums the probabilities
+      f32x4 vsc[2][2];
+      const float* sl = scale_ring + (t & 1) * kScaleStageFloats + kBN;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) vsc[u][hh] = *(const f32x4*)(sl + key_u0 + 32 * u + 4 * hh);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pe =
+                __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i], scale_log2, m_off[rb]));
+            lsum += pe;
+            pb[kb >> 1][rb][4 * (kb & 1) + i] = (_Float16)(pe * vsc[kb >> 1][kb & 1][i]);
+          }
+        l_run[rb] += lsum;
+      }
     }
 
     // O^T[dim][row] += V^T[dim][key] . P^T[key][row].  The V fragments of dims
@@ -546,13 +764,15 @@ __device__ __forceinline__ void chunk_tile_unit(
     }
   }
 
+  // the quantized products carry the V scales times kPvScale
+  constexpr float unscale = 1.f / QG::kPvScale;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const float l = sum_xor16(sum_xor32(l_run[rb]));
     const int r = wrow0 + 16 * rb + lr;
     if (r >= C) continue;
     if (parts == 1) {
-      const float inv = 1.f / l;
+      const float inv = kQ == 0 ? 1.f / l : unscale / l;
       float* dst = out + ((size_t)(row0 + r) * Hq + h) * kD + 4 * lq;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
@@ -563,7 +783,8 @@ __device__ __forceinline__ void chunk_tile_unit(
       const size_t pr = ((size_t)part * num_tokens + row0 + r) * Hq + h;
       float* dst = part_o + pr * kD + 4 * lq;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = oacc[db][rb];
+      for (int db = 0; db < 8; ++db)
+        *(f32x4*)(dst + 16 * db) = kQ == 0 ? oacc[db][rb] : oacc[db][rb] * unscale;
       if (lq == 0) {
         part_ml[2 * pr] = m_raw[rb] == -INFINITY ? -INFINITY : m_raw[rb] * scale_log2;
         part_ml[2 * pr + 1] = l;

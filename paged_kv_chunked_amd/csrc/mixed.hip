@@ -148,8 +148,9 @@ __global__ __launch_bounds__(kThreads, 1) void mixed_kernel(
   // is fetched while the current one runs; near the end of the list a unit is
   // only claimed once the previous one is done, so the longest-first order
   // balances the tail.  The index goes through a double-buffered LDS slot
-  // (one barrier per unit).
-  __shared__ int unit_slot[2];
+  // (one barrier per unit), at the end of the chunk unit's LDS layout.
+  __shared__ u32x4 lds[ChunkLds<kQ>::kUnits];
+  int* const unit_slot = (int*)(lds + ChunkLds<kQ>::kSlot / 16);
   const int32_t* chunk_list = sched + kHdrInts;
   const int32_t* dec_list = chunk_list + (size_t)num_seqs * n_rtiles;
   const int n_chunk_units = sched[kHdrChunk] * Hkv;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void mixed_kernel(
       const int k = u / Hkv, g = u - k * Hkv;
       const int item = chunk_list[k];
       const int b = item / n_rtiles, rt = item - b * n_rtiles;
-      chunk_tile_unit<kQ>(out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens,
+      chunk_tile_unit<kQ>(lds, out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens,
                           chunk_start, scale_log2, Hkv, num_blocks, num_tokens, b, rt, g);
     } else {
       const int j = u - n_chunk_units;

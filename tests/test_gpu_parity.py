@@ -9,8 +9,9 @@ and through the oracle, and compares:
     inputs, fp32 accumulation; fp32 workloads share the bound).
 Small workloads are compared element by element everywhere; the full-size
 decode and chunk workloads are compared in full; the mixed and long-context
-workloads on sampled sequences and rows (their K/V regenerated and rotated by
-the oracle for just those sequences).
+workloads on many sampled sequences and rows (their K/V regenerated and
+rotated by the oracle for just those sequences, in worker processes), with
+those sequences' arena blocks compared bit for bit.
 """
 import dataclasses
 import os
@@ -20,6 +21,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
+import oracle_jobs  # noqa: E402
 import paged_kv_chunked_amd as pkv  # noqa: E402
 from oracle import rope as orope  # noqa: E402
 from oracle import script as oscript  # noqa: E402
@@ -262,30 +264,124 @@ def test_decode_full_i4():
     run_case(i4(workloads.decode_batch()))
 
 
-def test_mixed_full_sampled():
-    w = workloads.mixed_step()
+# ---------------------------------------------------------------------------
+# mixed and long-context workloads: many sampled rows, oracle in worker
+# processes (symbolic oracle arena: a sequence's keys are regenerated when
+# its rows are checked)
+# ---------------------------------------------------------------------------
+
+def edge_and_random_rows(count, n_random, seed):
+    """Query rows of a chunk: the first and the last 64-row tile, plus
+    ``n_random`` random rows."""
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(min(64, count)), np.arange(max(0, count - 64), count),
+                           rng.integers(0, count, size=n_random)])
+    return np.unique(rows)
+
+
+def run_sampled(w, dec_rows, chunk_rows, block_rows, chunk_jobs=8):
+    """Runs workload w on the GPU (pool script, fills, step append, chunk and
+    decode calls) and checks against the oracle:
+      * block tables, copy-on-write copies and every rotated query, bit for bit;
+      * the arena blocks of the sequences of ``block_rows``, bit for bit
+        (digests of the GPU's tiles against the oracle's images);
+      * the outputs of decode rows ``dec_rows`` and of the query rows
+        ``chunk_rows[r]`` of chunk row r, within the tolerance."""
+    say(f"{w.name}: set-up (blocks={w.num_blocks}, step rows={len(w.step)})")
+    dw = harness.DeviceWorkload(w)
+    say(f"{w.name}: step")
+    dw.step()
+    torch.cuda.synchronize()
+    say(f"{w.name}: oracle script")
+    st = oscript.run_script(w, materialize=False)
+    assert dw.copies == st.copies
+    assert np.array_equal(dw.bt_host, oscript.block_table(w, st))
+    q_rot = oscript.append_step(w, st)
+    assert np.array_equal(bits(dw.q.cpu().numpy()), bits(q_rot)), "rotated q differs"
+    block_rows = set(block_rows)
+    jobs = [(r, None, r in block_rows) for r in dec_rows]
+    for r, rows in chunk_rows.items():
+        for i, part in enumerate(np.array_split(np.asarray(rows), chunk_jobs)):
+            if part.size:
+                jobs.append((r, part, i == 0 and r in block_rows))
+    say(f"{w.name}: oracle, {len(jobs)} jobs ({len(dec_rows)} decode rows, "
+        f"{sum(len(v) for v in chunk_rows.values())} chunk rows, {len(block_rows)} sequences' blocks)")
+    results = oracle_jobs.run(w, st, q_rot, dw.cu_host, jobs, dw.scale)
+    errs = Errors(w.v_scale)
+    cu = dw.cu_host
+    for r, rows, exp, dk, dv in results:
+        s = w.step[r]
+        if dk is not None:
+            nb = -(-(s.start + s.count) // w.block_size)
+            tab = torch.tensor(dw.tables[s.seq][:nb], device=dw.device, dtype=torch.int64)
+            gk = dw.k_arena.index_select(0, tab).cpu().numpy()
+            gv = dw.v_arena.index_select(0, tab).cpu().numpy()
+            assert oracle_jobs.digest(gk) == dk, ("K blocks differ", r)
+            assert oracle_jobs.digest(gv) == dv, ("V blocks differ", r)
+        if s.count == 1:
+            got = dw.dec_out[r - dw.dec_rows[0]].cpu().numpy()[None]
+        else:
+            t0 = cu[r] - dw.chunk_tok0
+            got = dw.chunk_out[t0:t0 + s.count].cpu().numpy()[rows]
+        errs.add(got, exp)
+    errs.check(w.name)
+    return dw
+
+
+def mixed_rows(w, total=128, seed=0):
+    """Decode rows of the mixed step to check, ``total`` of them: every row
+    sharing the prefix, the 32 longest contexts (their batch's split partials
+    exceed 64 MiB, so the combine takes its 2-split prefetch form), and random
+    others."""
+    dec = w.decode_rows()
     sharers = [op[1] for op in w.script if op[0] == "fork"]
-    rng = np.random.default_rng(0)
-    others = rng.choice(w.decode_rows(), size=6, replace=False).tolist()
-    run_case(w, full_arena=False, dec_sample=sorted(set(sharers[:4] + others)),
-             chunk_sample={r: 24 for r in w.chunk_rows()})
+    longest = sorted(dec, key=lambda r: -w.step[r].start)[:32]
+    chosen = set(sharers) | set(longest)
+    rng = np.random.default_rng(seed)
+    rest = [r for r in dec if r not in chosen]
+    extra = rng.choice(rest, size=max(total - len(chosen), 0), replace=False).tolist()
+    return sorted(chosen | set(extra))
+
+
+def test_mixed_full_sampled():
+    """The 2048-token-budget step (4 chunks of 256 + 1024 decodes, 16 sharing
+    a 1024-token prefix) through the separate chunk and decode calls: 128
+    decode rows and every chunk row against the oracle, and every checked
+    sequence's arena blocks bit for bit."""
+    w = workloads.mixed_step()
+    dec = mixed_rows(w)
+    assert len(dec) >= 128
+    chunks = {r: np.arange(w.step[r].count) for r in w.chunk_rows()}
+    run_sampled(w, dec, chunks, block_rows=dec + list(chunks), chunk_jobs=2)
+
+
+def _long_rows(w):
+    r = w.chunk_rows()[0]
+    return w.decode_rows(), {r: edge_and_random_rows(w.step[r].count, 400, seed=r)}
 
 
 def test_long_full_sampled():
+    """The long workload: 32 decodes at context 32768 and one 4096-row chunk
+    after 28,672 cached tokens, 1% of key vectors x8 (fp16 arena): every
+    decode row, the first and last 64-row tiles of the chunk plus 400 random
+    rows, and every sequence's arena blocks bit for bit."""
     w = workloads.long_context()
-    run_case(w, full_arena=False, dec_sample=[1, 17, 32], chunk_sample={0: 40})
+    dec, chunks = _long_rows(w)
+    run_sampled(w, dec, chunks, block_rows=dec + list(chunks))
 
 
-@pytest.mark.xfail(strict=True, reason=(
-    "known precision limit of the quantized chunk kernel: it rounds each dequantized "
-    "K value to fp16, and on this workload's x8 key vectors that moves dominant scores "
-    "enough for a max error of 8.0e-3 (mean 3.4e-4) on the chunk rows; its decode rows "
-    "are within 8.9e-5"))
 def test_long_full_sampled_i8():
-    """The long workload over an INT8 arena: 32768-token decodes and the
-    4096-row chunk after 28,672 cached tokens, 1% of key vectors x8."""
+    """The long workload over an INT8 arena (same rows and blocks checked)."""
     w = i8(workloads.long_context())
-    run_case(w, full_arena=False, dec_sample=[1, 17, 32], chunk_sample={0: 40})
+    dec, chunks = _long_rows(w)
+    run_sampled(w, dec, chunks, block_rows=dec[:4] + list(chunks))
+
+
+def test_long_full_sampled_i4():
+    """The long workload over an INT4 arena (same rows and blocks checked)."""
+    w = i4(workloads.long_context())
+    dec, chunks = _long_rows(w)
+    run_sampled(w, dec, chunks, block_rows=dec[:4] + list(chunks))
 
 
 # ---------------------------------------------------------------------------
