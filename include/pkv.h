@@ -195,6 +195,28 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
                                   size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * paged_attention_decode_noalloc — paged_attention_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, result and
+ * kernels as paged_attention_decode, without the workspace: the split
+ * partials live in a static device array of PKV_DECODE_SCRATCH_BYTES inside
+ * the library (one per GPU, held until the process ends; its address is
+ * looked up on the first call on each device).  The call allocates nothing.
+ * Returns PKV_ERR_WORKSPACE when paged_attention_decode_workspace_bytes() for
+ * (num_seqs, max_context_len) exceeds PKV_DECODE_SCRATCH_BYTES (32 MiB: for
+ * example 64 sequences of 32 query heads up to 11,904 tokens each).  Every
+ * call on one GPU shares that array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ * ------------------------------------------------------------------------- */
+#define PKV_DECODE_SCRATCH_BYTES (32u << 20)
+pkv_status paged_attention_decode_noalloc(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                          const void* q, const void* k_arena,
+                                          const void* v_arena, const int32_t* block_table,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t max_context_len, float scale, void* stream);
+
+/* ---------------------------------------------------------------------------
  * paged_attention_decode_shared — paged_attention_decode for a batch in which
  * groups of rows share a cached prefix (part 3 section 3: requests that share
  * a prefix reuse its blocks, kept alive by reference counts).  The shared

@@ -60,6 +60,8 @@ _SIGS = {
                                                               ctypes.POINTER(ctypes.c_size_t)]),
     "paged_attention_decode": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _I32,
                                               _I32, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "paged_attention_decode_noalloc": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P,
+                                                      _I32, _I32, ctypes.c_float, _P]),
     "paged_attention_decode_shared": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P,
                                                      _I32, _I32, ctypes.c_float, _P, _P, _I32,
                                                      _I32, _I32, _P, ctypes.c_size_t, _P]),
@@ -215,6 +217,19 @@ def paged_attention_decode(g: Geom, out, q, k_arena, v_arena, block_table, conte
                                         max_context_len, scale, _ptr(workspace), ws_bytes,
                                         _stream(stream)),
            "paged_attention_decode")
+
+
+def paged_attention_decode_noalloc(g: Geom, out, q, k_arena, v_arena, block_table, context_lens,
+                                   max_context_len: int, scale: float, stream=None) -> None:
+    """paged_attention_decode without a workspace: the split partials live in
+    the library's static per-GPU scratch array (calls on one GPU must not
+    overlap)."""
+    _check(lib().paged_attention_decode_noalloc(ctypes.byref(g), _ptr(out), F32, _ptr(q),
+                                                _ptr(k_arena), _ptr(v_arena), _ptr(block_table),
+                                                block_table.shape[1], _ptr(context_lens),
+                                                context_lens.shape[0], max_context_len, scale,
+                                                _stream(stream)),
+           "paged_attention_decode_noalloc")
 
 
 def paged_attention_decode_shared(g: Geom, out, q, k_arena, v_arena, block_table, context_lens,

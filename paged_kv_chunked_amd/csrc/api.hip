@@ -79,6 +79,36 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
                                        (hipStream_t)stream));
 }
 
+pkv_status paged_attention_decode_noalloc(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                          const void* q, const void* k_arena,
+                                          const void* v_arena, const int32_t* block_table,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t max_context_len, float scale, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  if (num_seqs < 0) return PKV_ERR_RANGE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_arena || !v_arena || !block_table || !context_lens) return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || max_context_len < 1 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return PKV_ERR_RANGE;
+  const size_t need = pkv::decode_workspace_bytes(*geom, num_seqs, max_context_len);
+  if (need > PKV_DECODE_SCRATCH_BYTES) return PKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (need > 0) {
+    const hipError_t e = pkv::decode_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess) return PKV_ERR_HIP;
+    if (ws_bytes < need) return PKV_ERR_WORKSPACE;
+  }
+  return hip_status(pkv::launch_decode(*geom, (float*)out, q, k_arena, v_arena, block_table,
+                                       max_blocks_per_seq, context_lens, num_seqs,
+                                       max_context_len, scale, ws, ws_bytes,
+                                       (hipStream_t)stream));
+}
+
 pkv_status paged_attention_decode_shared(
     const pkv_geom* geom, void* out, int32_t out_dtype, const void* q, const void* k_arena,
     const void* v_arena, const int32_t* block_table, int32_t max_blocks_per_seq,

@@ -36,6 +36,8 @@
 //     this multi-XCD part write back and invalidate the L2 per wave; measured
 //     4x slower than the second launch.)
 // Other shapes run the generic kernel.
+#include <mutex>
+
 #include "decode_core.h"
 #include "decode_q_core.h"
 
@@ -327,6 +329,37 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 }
 
 }  // namespace
+
+// ---- allocation-free decode ------------------------------------------------
+// The split partials of paged_attention_decode_noalloc live in this file-scope
+// device array (each GPU the library runs on holds its own copy until the
+// process ends).  Its device address is looked up once per device, with that
+// device current, and kept; the array's name is only a host-side stand-in.
+static __device__ __align__(256) unsigned char scratch[PKV_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
 
 bool decode_fast_path(const pkv_geom& g) {
   return (g.dtype == PKV_F16 || g.dtype == PKV_I8KV || g.dtype == PKV_I4KV) && g.head_dim == kD &&

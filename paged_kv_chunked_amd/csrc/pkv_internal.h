@@ -158,6 +158,11 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
                          float scale, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, const DecodeGroups* groups = nullptr);
 
+// The device address and size of the calling device's decode scratch array
+// (the split partials of paged_attention_decode_noalloc); looked up once per
+// device.
+hipError_t decode_scratch(void** ptr, size_t* bytes);
+
 // Merge of decode split partials (decode_combine_kernel): decode rows, or the
 // one-row sequences of a varlen batch when cu_q_lens != nullptr (lens then
 // holds chunk starts).

@@ -256,6 +256,17 @@ def test_entry_point_errors(lib):
                                       0.1, FAKE, need - 1, None) == 5
     assert lib.paged_attention_decode(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000,
                                       0.1, None, need, None) == 5
+    # the allocation-free decode: batches whose partials exceed its static
+    # scratch are refused before anything is launched (32 MiB: 64 sequences of
+    # 32 heads hold up to 31 splits, i.e. contexts of 11,904 tokens)
+    assert pkv.paged_attention_decode_workspace_bytes(g, 64, 31 * 384) <= 32 << 20
+    assert pkv.paged_attention_decode_workspace_bytes(g, 64, 32 * 384) > 32 << 20
+    assert lib.paged_attention_decode_noalloc(gp, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 800, FAKE, 64,
+                                              32 * 384, 0.1, None) == 5
+    assert lib.paged_attention_decode_noalloc(gp, None, 1, FAKE, FAKE, FAKE, FAKE, 800, FAKE, 64,
+                                              384, 0.1, None) == 1
+    assert lib.paged_attention_decode_noalloc(gp, None, 1, None, None, None, None, 4, None, 0,
+                                              64, 0.1, None) == 0
     # chunk: the schedule, one int32 per (sequence, 64-row tile)
     need = pkv.paged_attention_chunk_workspace_bytes(g, 2, 100, 500)
     assert need == 2 * 2 * 4
