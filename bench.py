@@ -259,6 +259,9 @@ def bench_mixed(torch, args):
     n = max(args.steps // 5, 5)
     ms_sep = time_back_to_back(torch, lambda i: (dw.chunk(), dw.decode()), n)
     ms_mix = time_back_to_back(torch, lambda i: dw.mixed(), n)
+    # each part of the step as its own call, against its own roofline
+    ms_dec = time_back_to_back(torch, lambda i: dw.decode(), n)
+    ms_chk = time_back_to_back(torch, lambda i: dw.chunk(), n)
     # the whole step: the 2048 new tokens appended, then the attention
     ms_sep_step = time_back_to_back(torch, lambda i: (dw.append(), dw.chunk(), dw.decode()), n)
     ms_mix_step = time_back_to_back(torch, lambda i: (dw.append(), dw.mixed()), n)
@@ -275,6 +278,21 @@ def bench_mixed(torch, args):
         "speedup": round(ms_sep / ms_mix, 3),
         "ms_step_append_separate_calls": round(ms_sep_step, 5),
         "ms_step_append_mixed_call": round(ms_mix_step, 5),
+        "decode_call": {
+            "kernel": "paged_attention_decode (decode_split_kernel + decode_combine_kernel<2>)",
+            "bound": "hbm", "ms": round(ms_dec, 5), "bytes": nbytes,
+            "achieved": round(nbytes / (ms_dec * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        },
+        "chunk_call": {
+            "kernel": "paged_attention_chunk (chunk_order_kernel + chunk_mfma_kernel<0>, "
+                      "keys split into parts + chunk_combine_kernel)",
+            "bound": "mfma", "ms": round(ms_chk, 5), "flops": flops,
+            "achieved": round(flops / (ms_chk * 1e-3) / 1e12, 2), "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / (ms_chk * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+        },
         "roofline": {
             "kernel": "paged_attention_mixed (mixed_order_kernel + mixed_kernel + "
                       "decode_combine_kernel)",
@@ -317,34 +335,104 @@ def bench_long(torch, args):
     return res
 
 
-def cpu_baseline(w, target_s):
-    """The oracle (numpy fp64) on the decode workload: append + attention for
-    every decode row, repeated until about target_s seconds have passed."""
-    from oracle import script as oscript
-    from paged_kv_chunked_amd import harness
+def blas_info():
+    """Threads the oracle's BLAS runs with and which BLAS it is."""
     try:
         import threadpoolctl
-        blas = threadpoolctl.threadpool_info()
-        threads = max((p.get("num_threads", 1) for p in blas), default=1)
+        pools = threadpoolctl.threadpool_info()
     except Exception:  # pragma: no cover - reporting only
-        threads = len(os.sched_getaffinity(0))
+        pools = []
+    blas = [p for p in pools if p.get("user_api") == "blas"]
+    threads = max((p.get("num_threads", 1) for p in blas), default=1)
+    build = ", ".join(f"{p.get('internal_api')} {p.get('version')} "
+                      f"({os.path.basename(p.get('filepath', ''))})" for p in blas) or "unknown"
+    return threads, build
+
+
+def cpu_baseline(w, target_s, reps=3):
+    """The oracle (numpy fp64) on the decode workload: append + attention for
+    every decode row, repeated until about target_s / reps seconds have passed;
+    the median rate of ``reps`` such runs."""
+    from oracle import script as oscript
+    from paged_kv_chunked_amd import harness
     st = oscript.run_script(w)
     cu = [0]
     for s in w.step:
         cu.append(cu[-1] + s.count)
     scale = harness.default_scale(w.head_dim)
-    rows_done = 0
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        q_rot = oscript.append_step(w, st)
-        for r in range(len(w.step)):
+    runs = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            q_rot = oscript.append_step(w, st)
+            for r in range(len(w.step)):
+                oscript.attend_row(w, st, r, q_rot[cu[r]:cu[r + 1]], scale)
+            passes += 1
+            if time.perf_counter() - t0 >= target_s / reps:
+                break
+        runs.append((time.perf_counter() - t0, passes))
+    runs.sort(key=lambda x: x[1] / x[0])
+    return runs[len(runs) // 2]
+
+
+def cpu_baseline_chunk(w, target_s, reps=3):
+    """The oracle on the chunk workload: the attention of whole chunk
+    sequences (512 rows, all heads, fp64 dense masked softmax) taken in step
+    order until about target_s / reps seconds have passed; the median rate of
+    ``reps`` runs, in visible-pair flops (4 D Hq per pair) per second."""
+    from oracle import script as oscript
+    from paged_kv_chunked_amd import harness
+    st = oscript.run_script(w)
+    q_rot = oscript.append_step(w, st)
+    cu = [0]
+    for s in w.step:
+        cu.append(cu[-1] + s.count)
+    scale = harness.default_scale(w.head_dim)
+    per_pair = 4 * w.head_dim * w.num_q_heads
+    runs = []
+    for k in range(reps):
+        t0 = time.perf_counter()
+        flops, seqs = 0, 0
+        while True:
+            r = (k + seqs) % len(w.step)
+            s = w.step[r]
             oscript.attend_row(w, st, r, q_rot[cu[r]:cu[r + 1]], scale)
-            rows_done += 1
-        passes += 1
-        if time.perf_counter() - t0 >= target_s:
-            break
-    return time.perf_counter() - t0, passes, threads
+            flops += per_pair * (s.count * s.start + s.count * (s.count + 1) // 2)
+            seqs += 1
+            if time.perf_counter() - t0 >= target_s / reps:
+                break
+        runs.append((time.perf_counter() - t0, flops, seqs))
+    runs.sort(key=lambda x: x[1] / x[0])
+    return runs[len(runs) // 2]
+
+
+def plain_rates_GBps(torch, nbytes, copies=4, reps=20):
+    """Plain device streams over ``nbytes`` in the same run, as the achievable
+    HBM rate beside the decode's: a read (torch's sum over fp32) and a device
+    copy (read + write bytes counted), each over ``copies`` buffers in turn so
+    repeated passes are not served by the Infinity Cache."""
+    n = nbytes // 4
+    bufs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    dst = torch.empty(n, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        for i in range(copies):
+            fn(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i)
+        e.record()
+        e.synchronize()
+        return a.elapsed_time(e) / reps
+
+    ms_read = timed(lambda i: torch.sum(bufs[i % copies]))
+    ms_copy = timed(lambda i: dst.copy_(bufs[i % copies]))
+    del bufs, dst
+    return n * 4 / (ms_read * 1e-3) / 1e9, 2 * n * 4 / (ms_copy * 1e-3) / 1e9
 
 
 def main():
@@ -435,6 +523,12 @@ def main():
             "avg_launch_ms_isolated": round(ms_dcall, 5),
         },
     }
+    read_gbs, copy_gbs = plain_rates_GBps(torch, nbytes)
+    out["roofline"]["plain_read_GBps"] = round(read_gbs, 1)
+    out["roofline"]["plain_copy_GBps"] = round(copy_gbs, 1)
+    out["roofline"]["frac_of_plain_stream"] = round(achieved / max(read_gbs, copy_gbs), 4)
+    log(f"plain device streams of {nbytes / 1e6:.1f} MB: read {read_gbs:.0f} GB/s, "
+        f"copy {copy_gbs:.0f} GB/s (read + write)")
     if not args.no_swap:
         out["swap"] = bench_swap(torch, dw)
         log(f"swap: {out['swap']}")
@@ -522,17 +616,36 @@ def main():
                 },
             }
             del dwq
+    out["library_source_hash"] = pkv.pkv_source_hash()
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        secs, passes, threads = cpu_baseline(w, args.cpu_seconds)
+        threads, build = blas_info()
+        affinity = len(os.sched_getaffinity(0))
+        log("cpu baseline (oracle), decode workload")
+        secs, passes = cpu_baseline(w, args.cpu_seconds)
         out["cpu_baseline"] = {
             "value": round(nbytes * passes / secs / 1e9, 4),
             "unit": "GB/s",
             "cores": threads,
             "kind": "oracle",
             "sample": f"the whole decode step (append + attention, {len(w.step)} sequences) "
-                      f"x {passes} passes, {secs:.1f} s, numpy fp64",
+                      f"x {passes} passes in {secs:.1f} s (median of 3 runs), numpy fp64",
+            "host_cores_available": affinity,
+            "blas": build,
         }
+        if "chunk_prefill" in out:
+            from paged_kv_chunked_amd import workloads
+            log("cpu baseline (oracle), chunk workload")
+            secs, flops, seqs = cpu_baseline_chunk(workloads.chunk_batch(), args.cpu_seconds)
+            out["chunk_prefill"]["cpu_baseline"] = {
+                "value": round(flops / secs / 1e12, 6),
+                "unit": "TFLOP/s",
+                "cores": threads,
+                "kind": "oracle",
+                "sample": f"{seqs} of the 8 chunk sequences' attention (512 rows x 32 heads "
+                          f"each) in {secs:.1f} s (median of 3 runs), numpy fp64",
+                "host_cores_available": affinity,
+                "blas": build,
+            }
     print(json.dumps(out), flush=True)
 
 
