@@ -349,6 +349,40 @@ def blas_info():
     return threads, build
 
 
+def bench_tp8(torch, args):
+    """One GPU's share of the layer split by KV head over 8 GPUs (Hq 4 / Hkv 1):
+    the decode and chunk workloads at that shape, each call against its own
+    roofline (decode rotates 4 arena copies; the chunk call splits its 64 row
+    tiles' keys into parts)."""
+    from paged_kv_chunked_amd import harness, workloads
+    res = {"workload": "decode and chunk workloads at Hq 4 / Hkv 1 (one of 8 GPUs splitting "
+                       "the Llama-3-8B layer by KV head), head_dim 128, fp16"}
+    for kind, w in (("decode", workloads.tp8_decode_batch()), ("chunk", workloads.tp8_chunk_batch())):
+        dw = harness.DeviceWorkload(w)
+        dw.step()
+        layers = make_layers(torch, dw, args.layers)
+        if kind == "decode":
+            ms = time_back_to_back(torch, lambda i: dw.decode(k_arena=layers[i % len(layers)][0],
+                                                              v_arena=layers[i % len(layers)][1]),
+                                   args.steps)
+            nb = dw.decode_bytes()
+            res["decode"] = {"kernel": "paged_attention_decode", "bound": "hbm", "ms": round(ms, 5),
+                             "bytes": nb, "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        else:
+            ms = time_back_to_back(torch, lambda i: dw.chunk(k_arena=layers[i % len(layers)][0],
+                                                             v_arena=layers[i % len(layers)][1]),
+                                   args.steps)
+            fl = dw.chunk_flops()
+            res["chunk"] = {"kernel": "paged_attention_chunk", "bound": "mfma", "ms": round(ms, 5),
+                            "flops": fl, "achieved": round(fl / (ms * 1e-3) / 1e12, 2),
+                            "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
+        del dw, layers
+    return res
+
+
 def cpu_baseline(w, target_s, reps=3):
     """The oracle (numpy fp64) on the decode workload: append + attention for
     every decode row, repeated until about target_s / reps seconds have passed;
@@ -448,6 +482,7 @@ def main():
     ap.add_argument("--no-shared", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-tp8", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -567,6 +602,9 @@ def main():
     if not args.no_long:
         out["long_context"] = bench_long(torch, args)
         log(f"long context: {out['long_context']}")
+    if not args.no_tp8:
+        out["tp8_shard"] = bench_tp8(torch, args)
+        log(f"tp8 shard: {out['tp8_shard']}")
     if not args.no_chunk:
         wc, dwc, ms_cstep, ms_chunk, ms_ccall, flops = bench_chunk(torch, args)
         tf_kernel = flops / (ms_chunk * 1e-3) / 1e12

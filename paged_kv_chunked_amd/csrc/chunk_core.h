@@ -72,7 +72,9 @@ __device__ inline void wait_vm() {
 }
 
 // How far (log2 units) a row's running maximum may lag the true maximum before
-// the accumulator is rescaled: probabilities stay <= 2^8, well inside fp16.
+// the accumulator is rescaled (fp16 arenas): probabilities stay <= 2^8, well
+// inside fp16.  Quantized arenas keep the exact running maximum (slack 0), so
+// probabilities stay <= 1 and a tile's largest one is exactly 1 (QGeom).
 constexpr float kSlack = 8.f;
 
 // Work of row tile rt of sequence b, in 64-key tiles (0 if the tile is empty).
@@ -126,6 +128,7 @@ struct QGeom<0> {  // fp16 arena: tiles land in the fp16 ring directly
   static constexpr int kCodeStageCount = 0;
   static constexpr int kScaleStages = 0;
   static constexpr float kPvScale = 1.f;
+  static constexpr float kRowSlack = kSlack;
 };
 template <>
 struct QGeom<1> {  // INT8: 3 loads per wave per tile (K codes, V codes, scales)
@@ -136,9 +139,12 @@ struct QGeom<1> {  // INT8: 3 loads per wave per tile (K codes, V codes, scales)
   static constexpr int kFp16Stages = 2;
   static constexpr int kCodeStageCount = kCodeStages;
   static constexpr int kScaleStages = 2;
-  // p * s_v * kPvScale must stay finite in fp16: p <= 2^kSlack (8) and an INT8
-  // scale is at most fp16(65504 / 127) = 515.5, so 2^8 * 515.5 * 2^-2 = 32992
-  static constexpr float kPvScale = 0.25f;
+  // p * s_v * kPvScale must stay finite in fp16: p <= 1 (exact running
+  // maximum) and an INT8 scale is at most fp16(65504 / 127) = 515.5, so
+  // 515.5 * 2^6 = 32992; the factor keeps small weights out of fp16's
+  // subnormal range, where their rounding would grow
+  static constexpr float kPvScale = 64.f;
+  static constexpr float kRowSlack = 0.f;
 };
 template <>
 struct QGeom<2> {  // INT4: 2 loads per wave per tile (K or V codes, scales)
@@ -149,12 +155,14 @@ struct QGeom<2> {  // INT4: 2 loads per wave per tile (K or V codes, scales)
   static constexpr int kFp16Stages = 2;
   static constexpr int kCodeStageCount = kCodeStages;
   static constexpr int kScaleStages = 2;
-  // INT4 scales reach fp16(65504 / 7) = 9360: 2^8 * 9360 * 2^-6 = 37440
-  static constexpr float kPvScale = 1.f / 64.f;
+  // INT4 scales reach fp16(65504 / 7) = 9360: 9360 * 2^2 = 37440
+  static constexpr float kPvScale = 4.f;
+  static constexpr float kRowSlack = 0.f;
 };
 
-// Scale ring stage: 64 K scales (fp32), then 64 V scales times kPvScale.
-constexpr int kScaleStageFloats = 2 * kBN;
+// Scale ring stage (fp32): 64 K scales, 64 V scales times kPvScale, and their
+// reciprocals.
+constexpr int kScaleStageFloats = 3 * kBN;
 
 // The unit's LDS, one array, byte offsets of its regions:
 //   [fp16 ring: kFp16Stages x kStageUnits 16-byte units (K of 4 blocks, V of 4)]
@@ -429,11 +437,13 @@ __device__ __forceinline__ void chunk_tile_unit(
   // slot' = slot ^ 4 in odd blocks; V: (2 dim + half + 16 (block & 1)) mod
   // 256), holding the codes as exact fp16 integers.  Threads 0-63 write the
   // K scale of key tid as fp32, threads 64-127 the V scale of key tid - 64
-  // times kPvScale.  Keys past the sequence get scale 0 (their scale bytes are
-  // not data; their codes are finite).
+  // times kPvScale, threads 128-191 the reciprocal of that.  Keys past the
+  // sequence get 0 for all three (their scale bytes are not data; their codes
+  // are finite).
   [[maybe_unused]] int kc_off[2], vc_off[2], k_sh[2];
   [[maybe_unused]] int sc_off = 0, sc_key = 0;
   [[maybe_unused]] float sc_mul = 1.f;
+  [[maybe_unused]] bool sc_recip = false;
   if constexpr (kQ != 0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -442,8 +452,9 @@ __device__ __forceinline__ void chunk_tile_unit(
       k_sh[j] = 4 * ((((tid + 512 * j) & 255) >> 4) & 1);
     }
     sc_key = tid & (kBN - 1);
-    sc_off = conv_scale_off<kQ>(tid >> 6, sc_key);
+    sc_off = conv_scale_off<kQ>(min(tid >> 6, 1), sc_key);
     sc_mul = tid >= kBN ? QG::kPvScale : 1.f;
+    sc_recip = tid >= 2 * kBN;
   }
   // (masked: the tile reaches past the sequence; keys >= lim get scale 0)
   auto convert_tile = [&](int t, auto masked) {
@@ -472,6 +483,7 @@ __device__ __forceinline__ void chunk_tile_unit(
       }
       if (tid < kScaleStageFloats) {
         float sc = (float)*(const _Float16*)(cs + sc_off) * sc_mul;
+        if (sc_recip) sc = 1.f / sc;  // scales are at least the smallest positive fp16
         if (masked && sc_key >= Lc - t * kBN) sc = 0.f;
         scale_ring[(t & 1) * kScaleStageFloats + tid] = sc;
       }
@@ -535,7 +547,7 @@ __device__ __forceinline__ void chunk_tile_unit(
     m_off[rb] = 0.f;
     l_run[rb] = 0.f;
   }
-  const float slack_raw = kSlack / scale_log2;
+  const float slack_raw = QG::kRowSlack / scale_log2;
   const half2_t ones = {(_Float16)1.f, (_Float16)1.f};
 
   // Operand addresses (16-byte units within a stage).  K fragment of MFMA kb,
@@ -546,47 +558,39 @@ __device__ __forceinline__ void chunk_tile_unit(
   // V fragment of dims block db for the keys of MFMA u: 16-byte unit
   // (2 (16db + lr) + (lq & 1) + 16 (lq >> 1)) mod 256 of block 2u + (lq >> 1)
   const int vunit = 2 * lr + (lq & 1) + 16 * (lq >> 1);
-  // Quantized arenas: this lane's scores (kb, i) are keys key_u + 4 (kb & 1) + i
-  // of the tile, u = kb >> 1, and its probabilities pb[u][..][e] keys key_u + e.
-  [[maybe_unused]] const int key_u0 = 16 * (lq >> 1) + 8 * (lq & 1);
+  // This lane's scores (kb, i) are keys key_u + 4 (kb & 1) + i of the tile,
+  // u = kb >> 1, key_u = 32 u + key_u0, its probabilities pb[u][..][e] and its
+  // V fragments of MFMA u keys key_u + e.
+  const int key_u0 = 16 * (lq >> 1) + 8 * (lq & 1);
 
-  for (int t = tb; t < te; ++t) {
-    if constexpr (kQ == 0) {
-      // tile t's loads (this wave's) are done; then every wave's, and every
-      // wave has finished tile t - 1, whose stage the next load reuses
-      if (t + 2 < te) wait_vm<2 * kLoadsPerTile>();
-      else if (t + 1 < te) wait_vm<kLoadsPerTile>();
-      else wait_vm<0>();
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (t + 3 < te) issue_tile(t + 3);
-    } else {
-      // code tile t + 1 is in LDS (this wave's loads, then every wave's);
-      // after the barrier fp16 and scale stage t & 1 are complete, every wave
-      // is done with stage (t + 1) & 1 and with code stage t % 3, which the
-      // next load reuses
-      if (t + 2 < te) wait_vm<QG::kLoads>();
-      else wait_vm<0>();
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (t + 3 < te) issue_codes(t + 3);
-      if (t + 1 < te) convert(t + 1);
-    }
-    const u32x4* kl = ring + (kQ == 0 ? t % kStages : t & 1) * kStageUnits;
-    const u32x4* vl = kl + 4 * kUnitsPerBlock;
-    if (kQ == 0 && t * kBN + kBN > Lc) {
-      // last tile: zero V of keys past the sequence (2 units per thread)
-      u32x4* vw = ring + (t % kStages) * kStageUnits + 4 * kUnitsPerBlock;
+  // ---- the steps of one key tile -----------------------------------------
+  // Zero V of keys past the sequence in tile t (its last tile; fp16 arenas:
+  // p = 0 there, but 0 * NaN would not be 0), 2 units per thread.
+  auto zero_v_tail = [&](int t) {
+    u32x4* vw = ring + (t % kStages) * kStageUnits + 4 * kUnitsPerBlock;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int unit = tid + e * kThreads;  // [block][dim][half']
-        const int a = unit >> 8, hs = unit & 1;  // block, half (8 keys) of the unit
-        const int key0 = t * kBN + 16 * a + 8 * hs;
-        if (key0 + 8 > Lc) vw[unit] = mask_unit(vw[unit], key0, Lc);
-      }
-      __syncthreads();
+    for (int e = 0; e < 2; ++e) {
+      const int unit = tid + e * kThreads;  // [block][dim][half']
+      const int a = unit >> 8, hs = unit & 1;  // block, half (8 keys) of the unit
+      const int key0 = t * kBN + 16 * a + 8 * hs;
+      if (key0 + 8 > Lc) vw[unit] = mask_unit(vw[unit], key0, Lc);
     }
+  };
+  auto k_stage = [&](int t) { return ring + (kQ == 0 ? t % kStages : t & 1) * kStageUnits; };
+  auto read_v = [&](int t, int db, half8_t* f) {
+    const u32x4* vl = k_stage(t) + 4 * kUnitsPerBlock;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int a = 2 * u + (lq >> 1);
+      f[u] = __builtin_bit_cast(half8_t, vl[a * kUnitsPerBlock + ((32 * db + vunit) & (kUnitsPerBlock - 1))]);
+    }
+  };
+
+  // S^T[key][row] = K . Q^T (raw scores) of tile t; the K fragments of MFMA
+  // kb + 1 are read while kb's products run, and the first two V fragment
+  // pairs of the tile are requested at the end (read during the softmax).
+  auto qk = [&](int t, f32x4 (&sacc)[4][kRB], half8_t (&vf)[3][2], bool prefetch_v = true) {
+    const u32x4* kl = k_stage(t);
     // Quantized arenas: the K scales of this lane's 16 keys (requested here,
     // used after the first product)
     [[maybe_unused]] f32x4 ksc[2][2];
@@ -597,10 +601,6 @@ __device__ __forceinline__ void chunk_tile_unit(
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) ksc[u][hh] = *(const f32x4*)(sl + key_u0 + 32 * u + 4 * hh);
     }
-
-    // S^T[key][row] = K . Q^T (raw scores).  The K fragments of MFMA kb + 1
-    // are read while kb's products run.
-    f32x4 sacc[4][kRB];
     half8_t kf[2][4];
     auto read_k = [&](int kb, half8_t* f) {
       const int a = 2 * (kb >> 1) + ka;
@@ -621,17 +621,10 @@ __device__ __forceinline__ void chunk_tile_unit(
         for (int rb = 0; rb < kRB; ++rb)
           sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb & 1][kd], qf[rb][kd], sacc[kb][rb], 0, 0, 0);
     }
-    // the first two V fragment pairs are read during the softmax
-    half8_t vf[3][2];
-    auto read_v = [&](int db, half8_t* f) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int a = 2 * u + (lq >> 1);
-        f[u] = __builtin_bit_cast(half8_t, vl[a * kUnitsPerBlock + ((32 * db + vunit) & (kUnitsPerBlock - 1))]);
-      }
-    };
-    read_v(0, vf[0]);
-    read_v(1, vf[1]);
+    if (prefetch_v) {
+      read_v(t, 0, vf[0]);
+      read_v(t, 1, vf[1]);
+    }
     // Instruction order of this block: each LDS read is issued about two
     // products ahead of the first product that needs it, so the read latency
     // hides behind matrix-core work (the scheduler would otherwise place
@@ -642,7 +635,6 @@ __device__ __forceinline__ void chunk_tile_unit(
       __builtin_amdgcn_sched_group_barrier(0x008, kRB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-
     // Quantized arenas: the product of the codes with q times the key's scale
     // is the score of the decoded key (code * scale, exact)
     if constexpr (kQ != 0) {
@@ -651,7 +643,12 @@ __device__ __forceinline__ void chunk_tile_unit(
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) sacc[kb][rb] *= ksc[kb >> 1][kb & 1];
     }
+  };
 
+  // Masks, online softmax and P^T of tile t's scores (pb[u][rb]: B operand
+  // of the second product, keys 8(lq & 1) .. +7 of block 2u + (lq >> 1) =
+  // scores (kb = 2u, i = 0..3), (kb = 2u + 1, i = 0..3)).
+  auto softmax = [&](int t, f32x4 (&sacc)[4][kRB], half8_t (&pb)[2][kRB]) {
     // Causal mask (and keys past the sequence) only where the tile reaches
     // past this wave's smallest row position.  Score (kb, i) of this lane is
     // key 16(2(kb >> 1) + (lq >> 1)) + 8(lq & 1) + 4(kb & 1) + i of the tile.
@@ -669,8 +666,9 @@ __device__ __forceinline__ void chunk_tile_unit(
 
     // online softmax per row (this lane: rows 16rb + lr, 16 keys each).  A
     // row's running maximum is only raised when one of its scores exceeds it
-    // by more than kSlack; both the numerator and the denominator use the same
-    // (possibly stale) maximum, so the quotient is unchanged.  The decision is
+    // by more than the slack (kSlack for fp16 arenas, 0 for quantized ones);
+    // both the numerator and the denominator use the same (possibly stale)
+    // maximum, so the quotient is unchanged.  The decision is
     // each row's own (rows whose maximum stays get alpha = 1 exactly), so a
     // row's arithmetic does not depend on which rows share its wave.
     float mloc[kRB];
@@ -703,9 +701,6 @@ __device__ __forceinline__ void chunk_tile_unit(
       }
     }
 
-    // pb[u][rb]: B operand of the second product, keys 8(lq & 1) .. +7 of
-    // block 2u + (lq >> 1) = scores (kb = 2u, i = 0..3), (kb = 2u + 1, i = 0..3)
-    half8_t pb[2][kRB];
     if constexpr (kQ == 0) {
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
@@ -724,14 +719,21 @@ __device__ __forceinline__ void chunk_tile_unit(
         l_run[rb] += lsum;
       }
     } else {
-      // the V scale (times kPvScale) multiplies the fp32 probability, which
-      // is then rounded once to fp16; the denominator sums the probabilities
-      f32x4 vsc[2][2];
+      // The V scale (times kPvScale) multiplies the fp32 probability, which
+      // is then rounded once to fp16: w = fp16(p * s_v * kPvScale) is the
+      // weight the second product gives the exact codes.  The denominator
+      // adds w / (s_v * kPvScale), i.e. the same rounded weight in
+      // probability units, so numerator and denominator agree key by key
+      // (a single dominant key returns its decoded value code * s_v exactly).
+      f32x4 vsc[2][2], rsc[2][2];
       const float* sl = scale_ring + (t & 1) * kScaleStageFloats + kBN;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) vsc[u][hh] = *(const f32x4*)(sl + key_u0 + 32 * u + 4 * hh);
+        for (int hh = 0; hh < 2; ++hh) {
+          vsc[u][hh] = *(const f32x4*)(sl + key_u0 + 32 * u + 4 * hh);
+          rsc[u][hh] = *(const f32x4*)(sl + kBN + key_u0 + 32 * u + 4 * hh);
+        }
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         float lsum = 0.f;
@@ -741,19 +743,22 @@ __device__ __forceinline__ void chunk_tile_unit(
           for (int i = 0; i < 4; ++i) {
             const float pe =
                 __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][rb][i], scale_log2, m_off[rb]));
-            lsum += pe;
-            pb[kb >> 1][rb][4 * (kb & 1) + i] = (_Float16)(pe * vsc[kb >> 1][kb & 1][i]);
+            const _Float16 w = (_Float16)(pe * vsc[kb >> 1][kb & 1][i]);
+            lsum = __builtin_fmaf((float)w, rsc[kb >> 1][kb & 1][i], lsum);
+            pb[kb >> 1][rb][4 * (kb & 1) + i] = w;
           }
         l_run[rb] += lsum;
       }
     }
+  };
 
-    // O^T[dim][row] += V^T[dim][key] . P^T[key][row].  The V fragments of dims
-    // block db + 2 are read before block db's four products (scheduling
-    // barriers keep that order).
+  // O^T[dim][row] += V^T[dim][key] . P^T[key][row] for tile t.  The V
+  // fragments of dims block db + 2 are read before block db's four products
+  // (scheduling barriers keep that order).
+  auto pv = [&](int t, half8_t (&pb)[2][kRB], half8_t (&vf)[3][2]) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      if (db + 2 < 8) read_v(db + 2, vf[(db + 2) % 3]);
+      if (db + 2 < 8) read_v(t, db + 2, vf[(db + 2) % 3]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -762,6 +767,41 @@ __device__ __forceinline__ void chunk_tile_unit(
           oacc[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db % 3][u], pb[u][rb], oacc[db][rb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  for (int t = tb; t < te; ++t) {
+    if constexpr (kQ == 0) {
+      // tile t's loads (this wave's) are done; then every wave's, and every
+      // wave has finished tile t - 1, whose stage the next load reuses
+      if (t + 2 < te) wait_vm<2 * kLoadsPerTile>();
+      else if (t + 1 < te) wait_vm<kLoadsPerTile>();
+      else wait_vm<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 3 < te) issue_tile(t + 3);
+    } else {
+      // code tile t + 1 is in LDS (this wave's loads, then every wave's);
+      // after the barrier fp16 and scale stage t & 1 are complete, every wave
+      // is done with stage (t + 1) & 1 and with code stage t % 3, which the
+      // next load reuses
+      if (t + 2 < te) wait_vm<QG::kLoads>();
+      else wait_vm<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 3 < te) issue_codes(t + 3);
+      if (t + 1 < te) convert(t + 1);
+    }
+    if (kQ == 0 && t * kBN + kBN > Lc) {
+      zero_v_tail(t);
+      __syncthreads();
+    }
+    f32x4 sacc[4][kRB];
+    half8_t vf[3][2];
+    half8_t pb[2][kRB];
+    qk(t, sacc, vf);
+    softmax(t, sacc, pb);
+    pv(t, pb, vf);
   }
 
   // the quantized products carry the V scales times kPvScale

@@ -231,25 +231,39 @@ def tiny() -> Workload:
 
 
 def decode_batch(num_seqs: int = 64, lo: int = 512, hi: int = 4096,
-                 seed: int = 1002) -> Workload:
+                 seed: int = 1002, heads=(32, 8), name: str = "decode_llama3_8b") -> Workload:
     """64 decode tokens, contexts uniform in [512, 4096], Hq 32 / Hkv 8, D 128,
-    fp16, theta 5e5, arena = total + 10 % through a shuffled LIFO list."""
+    fp16, theta 5e5, arena = total + 10 % through a shuffled LIFO list.
+    ``heads`` = (Hq, Hkv): (4, 1) is one GPU's share of the layer split by
+    KV head over 8 GPUs."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi, size=num_seqs, endpoint=True)
     seqs = [(int(L) - 1, 1) for L in lens]
-    return build("decode_llama3_8b", seed, "f16", 32, 8, 128, 5.0e5, seqs,
+    return build(name, seed, "f16", heads[0], heads[1], 128, 5.0e5, seqs,
                  max_blocks_per_seq=_blocks(hi), shuffle_rng=rng)
 
 
 def chunk_batch(num_seqs: int = 8, chunk: int = 512, max_prefix_blocks: int = 224,
-                seed: int = 1003) -> Workload:
-    """8 sequences, cached prefix P = 16*U{0..224}, one 512-token chunk each."""
+                seed: int = 1003, heads=(32, 8), name: str = "chunk_llama3_8b") -> Workload:
+    """8 sequences, cached prefix P = 16*U{0..224}, one 512-token chunk each
+    (``heads`` as for decode_batch)."""
     rng = np.random.default_rng(seed)
     pre = 16 * rng.integers(0, max_prefix_blocks, size=num_seqs, endpoint=True)
     seqs = [(int(p), chunk) for p in pre]
-    return build("chunk_llama3_8b", seed, "f16", 32, 8, 128, 5.0e5, seqs,
+    return build(name, seed, "f16", heads[0], heads[1], 128, 5.0e5, seqs,
                  max_blocks_per_seq=_blocks(16 * max_prefix_blocks + chunk),
                  shuffle_rng=rng)
+
+
+def tp8_decode_batch() -> Workload:
+    """The decode workload at one GPU's share of a KV-head split over 8 GPUs:
+    Hq 4 / Hkv 1, same lengths and draws' shapes."""
+    return decode_batch(heads=(4, 1), name="decode_tp8_shard")
+
+
+def tp8_chunk_batch() -> Workload:
+    """The chunk workload at one GPU's share of a KV-head split over 8 GPUs."""
+    return chunk_batch(heads=(4, 1), name="chunk_tp8_shard")
 
 
 def mixed_step(num_chunks: int = 4, chunk: int = 256, num_decodes: int = 1024,

@@ -256,6 +256,26 @@ def test_chunk_full_i4():
     run_case(w, chunk_sample={r: 48 for r in w.chunk_rows()})
 
 
+def test_tp8_shard_decode():
+    """One GPU's share of the decode workload split by KV head over 8 GPUs
+    (Hq 4 / Hkv 1): every output and the whole arena."""
+    run_case(workloads.tp8_decode_batch())
+
+
+def test_tp8_shard_chunk():
+    """One GPU's share of the chunk workload split by KV head over 8 GPUs
+    (Hq 4 / Hkv 1; 64 row tiles, so the call splits keys into parts)."""
+    run_case(workloads.tp8_chunk_batch())
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_tp8_shard_quant(bits):
+    """The same shard shape over INT8 / INT4 arenas (decode and chunk)."""
+    q = i8 if bits == 8 else i4
+    run_case(q(workloads.tp8_decode_batch()))
+    run_case(q(workloads.tp8_chunk_batch()))
+
+
 def test_decode_full_i8():
     run_case(i8(workloads.decode_batch()))
 
