@@ -50,13 +50,10 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
     const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
-    int num_blocks, const int32_t* __restrict__ row_skip) {
+    int num_blocks) {
   const int split = blockIdx.x, b = blockIdx.y;
   const int g = blockIdx.z * kDecodeWavesPerWG + (threadIdx.x >> 6);
   if (g >= Hkv) return;
-  // splits below row_skip[b] are computed by decode_shared_kernel, once for
-  // every sequence sharing them
-  if (row_skip != nullptr && split < row_skip[b]) return;
   decode_split_unit(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, b, b,
                     context_lens, 0, scale_log2, Hkv, nsplit_max, num_blocks, split, g);
 }
@@ -72,18 +69,18 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
 // the partials -- and the merged output -- are bit for bit those of
 // paged_attention_decode.  All keys of a shared split are real (a member's
 // own token comes after the shared prefix), so there is no mask.
-__global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_shared_kernel(
+__device__ __forceinline__ void decode_shared_unit(
     float* __restrict__ ws_o, float* __restrict__ ws_ml, const _Float16* __restrict__ q,
     const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ group_start, const int32_t* __restrict__ row_skip,
     float scale_log2, int Hkv, int nsplit_max, int num_blocks, int zheads, int num_seqs,
-    int nsx8, int quads) {
-  // Linear workgroup i = ((group * zheads + z) * quads + quad) * nsx8 + split,
-  // nsx8 a multiple of 8: workgroups are dealt to the 8 XCDs by i mod 8, so
-  // every quad (and group) reading split s runs on XCD s mod 8, close in time,
-  // and the split's blocks come from HBM into that XCD's L2 once.
-  int i = blockIdx.x;
+    int nsx8, int quads, int i) {
+  // Workgroup i = ((group * zheads + z) * quads + quad) * nsx8 + split, nsx8
+  // a multiple of 8: workgroups are dealt to the 8 XCDs by linear id mod 8,
+  // and the shared units come first in the grid, so every quad (and group)
+  // reading split s runs on XCD s mod 8, close in time, and the split's blocks
+  // come from HBM into that XCD's L2 once.
   const int split = i % nsx8;
   i /= nsx8;
   const int quad = i % quads;
@@ -185,6 +182,36 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
       ws_ml[2 * part + 1] = l_row;
     }
   }
+}
+
+// One launch for a batch with shared splits: workgroups [0, n_shared) run the
+// shared units (decode_shared_unit), the rest the per-row splits of
+// decode_split_kernel's grid (split fastest, then row, then KV-head group),
+// skipping each row's shared splits.  Both kinds run side by side: either
+// alone is a chain of up to 12 dependent pairs per wave with little of the
+// chip busy when groups are few.  Every unit runs the code of the separate
+// kernels, so partials and outputs are those of paged_attention_decode.
+__global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_shared_kernel(
+    float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
+    const _Float16* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
+    const int32_t* __restrict__ row_skip, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks, int zheads, int num_seqs, int nsx8, int quads, int n_shared, int gx) {
+  const int i = blockIdx.x;
+  if (i < n_shared) {
+    decode_shared_unit(ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, group_start,
+                       row_skip, scale_log2, Hkv, nsplit_max, num_blocks, zheads, num_seqs, nsx8,
+                       quads, i);
+    return;
+  }
+  const int j = i - n_shared;
+  const int split = j % gx, rest = j / gx;
+  const int b = rest % num_seqs, z = rest / num_seqs;
+  const int g = z * kDecodeWavesPerWG + (threadIdx.x >> 6);
+  if (g >= Hkv || split < row_skip[b]) return;
+  decode_split_unit(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, b, b,
+                    context_lens, 0, scale_log2, Hkv, nsplit_max, num_blocks, split, g);
 }
 
 // ---- INT8 arenas (PKV_I8KV) -------------------------------------------------
@@ -413,15 +440,18 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
   if (shared) {
     const int quads = (groups->max_group_size + 3) / 4;
     const int nsx8 = (min(groups->max_skip, nsplit) + 7) / 8 * 8;
-    const long nwg = (long)nsx8 * quads * zg * groups->num_groups;
+    const long n_shared = (long)nsx8 * quads * zg * groups->num_groups;
+    const long nwg = n_shared + (long)gx * num_seqs * zg;
     if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode_shared_kernel, dim3((unsigned)nwg), dim3(64 * wpg), 0, stream, ws_o,
-                       ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
-                       (const _Float16*)v_arena, block_table, max_blocks, groups->group_start,
-                       groups->row_skip, scale_log2, g.num_kv_heads, nsplit, g.num_blocks, zg,
-                       num_seqs, nsx8, quads);
+    hipLaunchKernelGGL(decode_shared_kernel, dim3((unsigned)nwg), dim3(64 * wpg), 0, stream, out,
+                       ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
+                       (const _Float16*)v_arena, block_table, max_blocks, context_lens,
+                       groups->group_start, groups->row_skip, scale_log2, g.num_kv_heads, nsplit,
+                       g.num_blocks, zg, num_seqs, nsx8, quads, (int)n_shared, gx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return launch_decode_combine(g, out, ws_o, ws_ml, context_lens, nullptr, 0, max_blocks,
+                                 num_seqs, nsplit, stream);
   }
   if (g.dtype == PKV_I8KV || g.dtype == PKV_I4KV) {
     const int wpg8 = g.num_kv_heads < kI8WavesPerWG ? g.num_kv_heads : kI8WavesPerWG;
@@ -435,8 +465,7 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
     hipLaunchKernelGGL(decode_split_kernel, grid, dim3(64 * wpg), 0, stream,
                        out, ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
                        (const _Float16*)v_arena, block_table, max_blocks, context_lens,
-                       scale_log2, g.num_kv_heads, nsplit, g.num_blocks,
-                       shared ? groups->row_skip : nullptr);
+                       scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit <= 1) return e;
