@@ -3,6 +3,8 @@
 // described with the quantized decode kernels in decode.hip).
 #pragma once
 
+#include <type_traits>
+
 #include "decode_core.h"
 #include "quant_codes.h"
 
@@ -13,6 +15,9 @@ namespace {
 #define PKV_DECODE_I8_AHEAD 1
 #endif
 constexpr int kI8Ahead = PKV_DECODE_I8_AHEAD;  // pairs in flight behind the computed one
+
+// v_mul_legacy_f32: x * y, except that 0 times anything (NaN, infinity) is 0.
+__device__ float pkv_fmul_legacy(float, float) __asm("llvm.amdgcn.fmul.legacy");
 
 struct PairI8 {
   u32x4 k[2][2];  // [u][j]: 16 codes (dims 16(4j + lq) .. +16) of the lane's key row
@@ -125,12 +130,13 @@ struct CodesI4 {
 };
 
 // Waves per workgroup and minimum resident waves per SIMD of the quantized
-// split kernels (their register budget differs from the fp16 kernel's).
+// split kernels (their register budget differs from the fp16 kernel's):
+// three waves per SIMD keep the INT8 unit at 168 VGPRs, no spills.
 #ifndef PKV_DECODE_I8_WAVES_PER_WG
 #define PKV_DECODE_I8_WAVES_PER_WG 8
 #endif
 #ifndef PKV_DECODE_I8_WAVES_PER_SIMD
-#define PKV_DECODE_I8_WAVES_PER_SIMD 2
+#define PKV_DECODE_I8_WAVES_PER_SIMD 3
 #endif
 constexpr int kI8WavesPerWG = PKV_DECODE_I8_WAVES_PER_WG;
 
@@ -145,6 +151,11 @@ __device__ __forceinline__ void decode_split_q_unit(
     const int32_t* __restrict__ block_table, int max_blocks, int b, int row,
     const int32_t* __restrict__ lens, int len_add, float scale_log2, int Hkv, int nsplit_max,
     int num_blocks, int split, int g) {
+  // No contraction of a multiply and an add into one fma at the compiler's
+  // choice: the decode kernel and the mixed kernel inline this unit into
+  // different code and must round every step alike (the one fma wanted is
+  // written out).
+#pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
@@ -186,7 +197,15 @@ __device__ __forceinline__ void decode_split_q_unit(
     c = 2 * p + 1 < nb ? __builtin_amdgcn_readlane(my_blk, 2 * p + 1) : a;
   };
   using Pair = typename Codes::Pair;
-  auto compute = [&](const Pair& pr, int p) {
+  // The probabilities carry the factor kPvBoost from the start: the
+  // exponent gets log2(kPvBoost) added, so p * boost comes out of the
+  // exponential and one mixed multiply by the fp16 V scale gives the weight
+  // (the denominator sums the same boosted p, so the factor cancels in o / l
+  // and in the merge of the splits).  Keys past the context exist only in a
+  // sequence's last pair, which is computed after the loop with the masks
+  // (tail); the loop's pairs need none.
+  const float pv_bias = __builtin_log2f(Codes::kPvBoost);  // exact: a power of two
+  auto compute = [&](const Pair& pr, int p, auto tail) {
     f32x4 s[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -200,17 +219,22 @@ __device__ __forceinline__ void decode_split_q_unit(
     const half8_t vsc = __builtin_bit_cast(half8_t, pr.vs);
     const int tok0 = (blk0 + 2 * p + (lq >> 1)) * kBlock + 8 * (lq & 1);
     const int nvalid = L - tok0;  // keys e < nvalid exist
+    // raw score of the decoded key: (q . codes) * scale, one rounding
     float sv[8];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = e < nvalid ? s[e >> 2][e & 3] * ((float)ksc[e] * scale_log2) : -INFINITY;
-      sv[e] = x;
-      mx = fmaxf(mx, x);
+    for (int e = 0; e < 8; ++e) sv[e] = s[e >> 2][e & 3] * (float)ksc[e];
+    if constexpr (decltype(tail)::value) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = e < nvalid ? sv[e] : -INFINITY;
     }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: the first key of a split is real
+    // running max in log2 units, the raw maximum scaled once (monotone);
+    // finite: the first key of a split is real
+    const float m_new = fmaxf(m_run, mx * scale_log2);
     if (__any(m_new > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -218,14 +242,18 @@ __device__ __forceinline__ void decode_split_q_unit(
       for (int db = 0; db < 8; ++db) o[db] *= alpha;
     }
     m_run = m_new;
+    const float bias = pv_bias - m_new;
     half8_t pb;
     float lsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(sv[e] - m_new);  // 0 for keys past the end
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, bias));  // p * boost
       lsum += pe;
-      // past the end the V scale may be NaN (unwritten slot): select, not multiply
-      pb[e] = e < nvalid ? (_Float16)(pe * ((float)vsc[e] * Codes::kPvBoost)) : (_Float16)0.f;
+      // The legacy multiply gives 0 for p = 0 whatever the V scale (past the
+      // end it may be NaN: an unwritten slot), and, unlike a plain multiply,
+      // is never fused with the fp16 conversion: the weight is the fp32
+      // product rounded to fp16 in every kernel that inlines this unit.
+      pb[e] = (_Float16)pkv_fmul_legacy(pe, (float)vsc[e]);
     }
     l_run += lsum;
 #pragma unroll
@@ -237,6 +265,9 @@ __device__ __forceinline__ void decode_split_q_unit(
   // unconditional-prefetch scheme as the fp16 kernel).  One measured best:
   // two or three cost registers (occupancy 3 -> 2) and ran 4-6% slower.
   constexpr int kAhead = kI8Ahead;
+  // pairs whose keys all exist; a partial last pair is left for after the loop
+  const bool has_tail = (blk0 + 2 * npairs) * kBlock > L;
+  const int n_full = npairs - (has_tail ? 1 : 0);
   Pair buf[kAhead + 1];
 #pragma unroll
   for (int p = 0; p < kAhead; ++p) {
@@ -252,17 +283,19 @@ __device__ __forceinline__ void decode_split_q_unit(
       buf[(p + kAhead) % (kAhead + 1)] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (p < npairs) compute(buf[p % (kAhead + 1)], p);
+    if (p < n_full) compute(buf[p % (kAhead + 1)], p, std::false_type{});
   }
+  // The last prefetch (at p = kSB / 2 - 1 - kAhead, clamped to the last
+  // pair) left pair npairs - 1 in this buffer, whatever npairs is.
+  if (has_tail) compute(buf[(kSB / 2 - 1) % (kAhead + 1)], npairs - 1, std::true_type{});
 
   float l_row = l_run;
   l_row += __shfl_xor(l_row, 16);
   l_row += __shfl_xor(l_row, 32);
   const int hq = g * kG + ln;
-  const float unboost = 1.f / Codes::kPvBoost;
   if (nsplit == 1) {
     if (ln < kG) {
-      const float inv = unboost / l_row;
+      const float inv = 1.f / l_row;
       float* dst = out + ((size_t)row * Hq + hq) * kD + 4 * lq;
 #pragma unroll
       for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * inv;
@@ -273,7 +306,7 @@ __device__ __forceinline__ void decode_split_q_unit(
     const size_t part = ((size_t)b * nsplit_max + split) * Hq + hq;
     float* dst = ws_o + part * kD + 4 * lq;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * unboost;
+    for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db];
     if (lq == 0) {
       ws_ml[2 * part] = m_run;
       ws_ml[2 * part + 1] = l_row;
