@@ -494,11 +494,13 @@ __device__ __forceinline__ void chunk_tile_unit(
     else convert_tile(t, std::false_type{});
   };
 
-  // The first tile's loads go out before the queries' so the two latencies
-  // overlap; then every query load (and the first tile) is complete before
-  // the next tile loads are issued, so the tile waits below count tile loads
-  // only.
+  // The first three tiles' loads go out before the queries', so all their
+  // latencies overlap; then everything is waited for (the compiler, which
+  // does not see the tile loads, must see the queries complete before the
+  // loop, or it waits for all loads at their first use in every tile).
   if (tb < te) issue(tb);
+  if (tb + 1 < te) issue(tb + 1);
+  if (tb + 2 < te) issue(tb + 2);
   // Q^T as the B operand: qf[rb][kd] = Q[row wrow0 + 16rb + lr][dims 32kd + 8lq .. +8]
   half8_t qf[kRB][4];
 #pragma unroll
@@ -515,8 +517,6 @@ __device__ __forceinline__ void chunk_tile_unit(
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (tb + 1 < te) issue(tb + 1);
-  if (tb + 2 < te) issue(tb + 2);
   if constexpr (kQ != 0) {
     if (tb < te) {
       __builtin_amdgcn_s_barrier();

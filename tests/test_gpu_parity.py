@@ -262,6 +262,27 @@ def test_tp8_shard_decode():
     run_case(workloads.tp8_decode_batch())
 
 
+def many_units(bits=0):
+    """300 chunks of U[2, 130] rows after prefixes of 16 * U{0..24} tokens:
+    ~3600 (row tile, KV head) units with rows among 7200 listed, so every
+    persistent chunk workgroup computes a dozen or more units back to back
+    (one-tile units included) and skips the empty ones."""
+    rng = np.random.default_rng(16)
+    rows = rng.integers(2, 130, size=300, endpoint=True)
+    pre = 16 * rng.integers(0, 24, size=300, endpoint=True)
+    w = workloads.build("many_units", 16, "f16", 32, 8, 128, 5.0e5,
+                        [(int(p), int(c)) for p, c in zip(pre, rows)], max_blocks_per_seq=33)
+    return dataclasses.replace(w, name=f"many_units_i{bits}", kv_bits=bits) if bits else w
+
+
+@pytest.mark.parametrize("bits", [0, 8, 4])
+def test_many_units(bits):
+    """Every row of every chunk against the oracle when each workgroup walks
+    many units (fp16, INT8 and INT4 arenas)."""
+    w = many_units(bits)
+    run_case(w, full_arena=False)
+
+
 def test_tp8_shard_chunk():
     """One GPU's share of the chunk workload split by KV head over 8 GPUs
     (Hq 4 / Hkv 1; 64 row tiles, so the call splits keys into parts)."""
