@@ -157,12 +157,12 @@ __device__ __forceinline__ void decode_shared_unit(
   };
 
   Pair buf[2];
-  buf[0] = load_pair(k_arena, v_arena, __builtin_amdgcn_readlane(my_blk, 0),
+  buf[0] = load_pair<false>(k_arena, v_arena, __builtin_amdgcn_readlane(my_blk, 0),
                      __builtin_amdgcn_readlane(my_blk, 1), Hkv, g, ln, lq);
 #pragma unroll
   for (int p = 0; p < npairs; ++p) {
     if (p + 1 < npairs) {
-      buf[(p + 1) & 1] = load_pair(k_arena, v_arena, __builtin_amdgcn_readlane(my_blk, 2 * p + 2),
+      buf[(p + 1) & 1] = load_pair<false>(k_arena, v_arena, __builtin_amdgcn_readlane(my_blk, 2 * p + 2),
                                    __builtin_amdgcn_readlane(my_blk, 2 * p + 3), Hkv, g, ln, lq);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -190,7 +190,10 @@ __device__ __forceinline__ void decode_shared_unit(
 // skipping each row's shared splits.  Both kinds run side by side: either
 // alone is a chain of up to 12 dependent pairs per wave with little of the
 // chip busy when groups are few.  Every unit runs the code of the separate
-// kernels, so partials and outputs are those of paged_attention_decode.
+// kernels, so partials and outputs are those of paged_attention_decode.  All
+// its K/V loads are cached (the split kernel streams): the shared units' 16
+// quads per split and the rows' own splits that still hold the end of the
+// shared prompt read the same blocks close in time.
 __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_shared_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
   const int b = rest % num_seqs, z = rest / num_seqs;
   const int g = z * kDecodeWavesPerWG + (threadIdx.x >> 6);
   if (g >= Hkv || split < row_skip[b]) return;
-  decode_split_unit(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, b, b,
+  decode_split_unit<false>(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, b, b,
                     context_lens, 0, scale_log2, Hkv, nsplit_max, num_blocks, split, g);
 }
 

@@ -22,12 +22,20 @@ static_assert(kSB % 2 == 0, "splits are walked in pairs of blocks");
 // fp16 elements per 16-byte piece of the K layout [block][head][D/8][16][8].
 constexpr int kX = 8;
 
-// Streaming loads: every K/V byte is read once per call.
+// K/V loads.  Streaming (non-temporal) where every byte is read once per
+// call; cached (kNT false) where several workgroups read the same blocks
+// close in time, as the shared-prefix units do: non-temporal lines are not
+// kept for them (measured: the shared units' 16 quads per split then each
+// fetch the split from memory).
+template <bool kNT>
 __device__ inline half8_t ld16(const _Float16* p) {
-  return __builtin_bit_cast(half8_t, __builtin_nontemporal_load((const u32x4*)p));
+  if constexpr (kNT) return __builtin_bit_cast(half8_t, __builtin_nontemporal_load((const u32x4*)p));
+  else return __builtin_bit_cast(half8_t, *(const u32x4*)p);
 }
+template <bool kNT>
 __device__ inline u32x2 ld8(const _Float16* p) {
-  return __builtin_nontemporal_load((const u32x2*)p);
+  if constexpr (kNT) return __builtin_nontemporal_load((const u32x2*)p);
+  else return *(const u32x2*)p;
 }
 
 // The K and V tiles of a pair of arena blocks A, B (32 tokens), already in the
@@ -37,6 +45,7 @@ struct Pair {
   half8_t v[8];     // [db]:        A operand of O^T += V^T . P^T
 };
 
+template <bool kNT = true>
 __device__ inline Pair load_pair(const _Float16* __restrict__ k_arena,
                                  const _Float16* __restrict__ v_arena, int blk_a, int blk_b,
                                  int Hkv, int g, int ln, int lq) {
@@ -49,8 +58,8 @@ __device__ inline Pair load_pair(const _Float16* __restrict__ k_arena,
   // pieces 4kd .. 4kd+3 of all 16 tokens: 1 KiB contiguous.
 #pragma unroll
   for (int kd = 0; kd < 4; ++kd) {
-    pr.k[0][kd] = ld16(ka + ((4 * kd + lq) * kBlock + ln) * kX);
-    pr.k[1][kd] = ld16(kb + ((4 * kd + lq) * kBlock + ln) * kX);
+    pr.k[0][kd] = ld16<kNT>(ka + ((4 * kd + lq) * kBlock + ln) * kX);
+    pr.k[1][kd] = ld16<kNT>(kb + ((4 * kd + lq) * kBlock + ln) * kX);
   }
   // V^T: MFMA row ln = head dim 16db + ln; the lane supplies keys 4lq .. 4lq+3
   // of block A then of block B (the order the probabilities come out of the
@@ -59,8 +68,8 @@ __device__ inline Pair load_pair(const _Float16* __restrict__ k_arena,
   const _Float16* vb = v_arena + ((size_t)blk_b * Hkv + g) * tile;
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    const u32x2 lo = ld8(va + (16 * db + ln) * kBlock + 4 * lq);
-    const u32x2 hi = ld8(vb + (16 * db + ln) * kBlock + 4 * lq);
+    const u32x2 lo = ld8<kNT>(va + (16 * db + ln) * kBlock + 4 * lq);
+    const u32x2 hi = ld8<kNT>(vb + (16 * db + ln) * kBlock + 4 * lq);
     pr.v[db] = __builtin_bit_cast(half8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
   }
   return pr;
@@ -87,7 +96,9 @@ constexpr int kDecodeWavesPerWG = PKV_DECODE_WAVES_PER_WG;
 // Sequence b (its block-table row and its partials in the workspace), whose
 // query and output live at packed row `row`; its context length is
 // lens[b] + len_add.  Wave (threadIdx.x >> 6) serves KV head g of split
-// `split`.
+// `split`.  kNT: streaming loads (false: cached, for blocks other
+// workgroups of the call read too).
+template <bool kNT = true>
 __device__ __forceinline__ void decode_split_unit(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
@@ -206,14 +217,14 @@ __device__ __forceinline__ void decode_split_unit(
   {
     int ba, bb;
     pair_ids(0, ba, bb);
-    buf[0] = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+    buf[0] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
   }
 #pragma unroll
   for (int p = 0; p < kSB / 2; ++p) {
     if (p + 1 < kSB / 2) {
       int ba, bb;
       pair_ids(min(p + 1, npairs - 1), ba, bb);
-      buf[(p + 1) & 1] = load_pair(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+      buf[(p + 1) & 1] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
       __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the compute
     }
     if (p < npairs) compute(buf[p & 1], p);
