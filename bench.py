@@ -7,7 +7,10 @@ Default run (N = 1):
     step = kv_append_rope for the 64 new tokens (drawn queries in, rotated
     queries to a buffer of their own, so every step sees the same input) +
     paged_attention_decode (split kernel + log-sum-exp combine).
-    `value` is the algorithmic decode bytes of one step / step time.
+    `value` is the algorithmic decode bytes of one step / step time.  The
+    same step as one paged_attention_decode_append call (the append fused
+    into the split kernel) is reported beside it ("decode_append_fused";
+    --fused-append makes it the timed step).
   * chunk prefill (reported under "chunk_prefill"): 8 sequences with cached
     prefixes 16*U{0..224} and a 512-token chunk each; a step = kv_append_rope
     + paged_attention_chunk; TFLOP/s over visible pairs.
@@ -101,6 +104,11 @@ def make_layers(torch, dw, n):
 
 
 def bench_decode(torch, args, kv_bits=0):
+    """The decode step on the decode workload, rotating the arena copies: the
+    step's append (kv_append_rope) then paged_attention_decode.  For fp16
+    arenas the other form of the same step (one paged_attention_decode_append
+    call, or the two calls with --fused-append) is timed beside it, and so is
+    the decode call alone."""
     import dataclasses
     from paged_kv_chunked_amd import harness, workloads
     w = workloads.decode_batch()
@@ -109,32 +117,59 @@ def bench_decode(torch, args, kv_bits=0):
     log(f"decode set-up: {w.num_blocks} blocks")
     dw = harness.DeviceWorkload(w)
     layers = make_layers(torch, dw, args.layers)
+    fused = kv_bits == 0 and args.fused_append
     events = []
 
-    def run(i):
+    def call(i):
         k, v = layers[i % len(layers)]
-        dw.append(k_arena=k, v_arena=v)
-        dw.decode(k_arena=k, v_arena=v)
+        if fused:
+            dw.decode_append(k_arena=k, v_arena=v)
+        else:
+            dw.decode(k_arena=k, v_arena=v)
+
+    def run(i):
+        if not fused:
+            k, v = layers[i % len(layers)]
+            dw.append(k_arena=k, v_arena=v)
+        call(i)
 
     def run_events(i):
-        k, v = layers[i % len(layers)]
-        dw.append(k_arena=k, v_arena=v)
+        if not fused:
+            k, v = layers[i % len(layers)]
+            dw.append(k_arena=k, v_arena=v)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        dw.decode(k_arena=k, v_arena=v)
+        call(i)
         b.record()
         events.append((a, b))
 
     ms_step, ms_call = time_steps(torch, run, args.steps, args.warmup, run_events, events)
-
-    def call(i):
-        k, v = layers[i % len(layers)]
-        dw.decode(k_arena=k, v_arena=v)
-
     ms_kernel = time_back_to_back(torch, call, args.steps)
-    nbytes = dw.decode_bytes()
-    return w, dw, ms_step, ms_kernel, ms_call, nbytes
+    nbytes = dw.decode_append_bytes() if fused else dw.decode_bytes()
+    extra = {"fused": fused}
+    if kv_bits == 0:
+        # the other form of the same step, and the decode call alone
+        def sep(i):
+            k, v = layers[i % len(layers)]
+            dw.append(k_arena=k, v_arena=v)
+            dw.decode(k_arena=k, v_arena=v)
+
+        def fus(i):
+            k, v = layers[i % len(layers)]
+            dw.decode_append(k_arena=k, v_arena=v)
+
+        def dec(i):
+            k, v = layers[i % len(layers)]
+            dw.decode(k_arena=k, v_arena=v)
+
+        extra["ms_per_step_other_form"] = time_back_to_back(torch, sep if fused else fus,
+                                                            args.steps)
+        extra["ms_decode_call"] = time_back_to_back(torch, dec, args.steps) if fused else ms_kernel
+        extra["decode_append_bytes"] = dw.decode_append_bytes()
+    else:
+        extra["ms_decode_call"] = ms_kernel
+    return w, dw, ms_step, ms_kernel, ms_call, nbytes, extra
 
 
 def bench_chunk(torch, args, kv_bits=0):
@@ -483,6 +518,8 @@ def main():
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-tp8", action="store_true")
+    ap.add_argument("--fused-append", action="store_true",
+                    help="time the fp16 decode step as one paged_attention_decode_append call")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -518,11 +555,16 @@ def main():
         return
 
     from paged_kv_chunked_amd.rocprof_summary import load_traffic
-    w, dw, ms_step, ms_dec, ms_dcall, nbytes = bench_decode(torch, args)
-    value = nbytes / (ms_step * 1e-3) / 1e9
+    w, dw, ms_step, ms_dec, ms_dcall, nbytes, dextra = bench_decode(torch, args)
+    dec_bytes = dw.decode_bytes()
+    value = dec_bytes / (ms_step * 1e-3) / 1e9
     achieved = nbytes / (ms_dec * 1e-3) / 1e9
-    log(f"decode: step {ms_step:.4f} ms, kernel {ms_dec:.4f} ms, {nbytes / 1e6:.1f} MB "
-        f"-> {achieved:.0f} GB/s kernel, {value:.0f} GB/s step")
+    fused = dextra["fused"]
+    call_name = "paged_attention_decode_append" if fused else "paged_attention_decode"
+    call_kernels = ("decode_split_append_kernel" if fused else "decode_split_kernel") + \
+        " + decode_combine_kernel"
+    log(f"decode: step {ms_step:.4f} ms, call {ms_dec:.4f} ms, {nbytes / 1e6:.1f} MB "
+        f"-> {achieved:.0f} GB/s call, {value:.0f} GB/s step")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -539,36 +581,73 @@ def main():
         "config": {
             "workload": "decode_llama3_8b: 64 sequences x 1 query token, contexts U[512,4096], "
                         "Hq 32 / Hkv 8, head_dim 128, fp16 K/V/Q ~ N(0,1), block 16, "
-                        "shuffled arena (total + 10%), step = kv_append_rope + decode",
+                        "shuffled arena (total + 10%), step = the new tokens' append and the "
+                        "decode" + (" in one paged_attention_decode_append call" if fused else
+                                    " as kv_append_rope + paged_attention_decode"),
             "num_seqs": len(w.step),
             "context_tokens": int(sum(dw.dec_lens_host)),
             "arena_blocks": w.num_blocks,
             "layers_rotated": args.layers,
         },
         "roofline": {
-            "kernel": "paged_attention_decode (decode_split_kernel + decode_combine_kernel)",
+            "kernel": f"{call_name} ({call_kernels})",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(TRAFFIC, "paged_attention_decode"),
+            "traffic": load_traffic(TRAFFIC, call_name),
             "algorithmic_bytes_per_launch": nbytes,
             "avg_launch_ms": round(ms_dec, 5),
             "avg_launch_ms_isolated": round(ms_dcall, 5),
         },
     }
-    read_gbs, copy_gbs = plain_rates_GBps(torch, nbytes)
+    ms_dec_call = dextra["ms_decode_call"]
+    ms_other = dextra["ms_per_step_other_form"]
+    if fused:
+        ach_call = dec_bytes / (ms_dec_call * 1e-3) / 1e9
+        out["decode_separate_calls"] = {
+            "workload": "the same step as kv_append_rope followed by paged_attention_decode",
+            "ms_per_step": round(ms_other, 5),
+            "value": round(dec_bytes / (ms_other * 1e-3) / 1e9, 2),
+            "decode_call": {
+                "kernel": "paged_attention_decode (decode_split_kernel + decode_combine_kernel)",
+                "bound": "hbm", "ms": round(ms_dec_call, 5), "bytes": dec_bytes,
+                "achieved": round(ach_call, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach_call / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic(TRAFFIC, "paged_attention_decode"),
+            },
+        }
+    else:
+        # the fused form, back to back: its step is the one call
+        fb = dextra["decode_append_bytes"]
+        ach_f = fb / (ms_other * 1e-3) / 1e9
+        out["decode_append_fused"] = {
+            "workload": "the same step as one paged_attention_decode_append call (the new "
+                        "tokens' RoPE and arena append fused into the split kernel)",
+            "ms_per_step": round(ms_other, 5),
+            "value": round(dec_bytes / (ms_other * 1e-3) / 1e9, 2),
+            "call": {
+                "kernel": "paged_attention_decode_append (decode_split_append_kernel + "
+                          "decode_combine_kernel)",
+                "bound": "hbm", "ms": round(ms_other, 5), "bytes": fb,
+                "achieved": round(ach_f, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach_f / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic(TRAFFIC, "paged_attention_decode_append"),
+            },
+        }
+    log(f"other form of the step: {ms_other:.4f} ms")
+    read_gbs, copy_gbs = plain_rates_GBps(torch, dec_bytes)
     out["roofline"]["plain_read_GBps"] = round(read_gbs, 1)
     out["roofline"]["plain_copy_GBps"] = round(copy_gbs, 1)
     out["roofline"]["frac_of_plain_stream"] = round(achieved / max(read_gbs, copy_gbs), 4)
-    log(f"plain device streams of {nbytes / 1e6:.1f} MB: read {read_gbs:.0f} GB/s, "
+    log(f"plain device streams of {dec_bytes / 1e6:.1f} MB: read {read_gbs:.0f} GB/s, "
         f"copy {copy_gbs:.0f} GB/s (read + write)")
     if not args.no_swap:
         out["swap"] = bench_swap(torch, dw)
         log(f"swap: {out['swap']}")
     for bits in (() if args.no_int8 else (8, 4)):
-        _, dwq, ms_stepq, ms_decq, ms_dcallq, nbytesq = bench_decode(torch, args, kv_bits=bits)
+        _, dwq, ms_stepq, ms_decq, ms_dcallq, nbytesq, _ = bench_decode(torch, args, kv_bits=bits)
         achq = nbytesq / (ms_decq * 1e-3) / 1e9
         tokens = int(sum(dwq.dec_lens_host))
         log(f"decode int{bits}: kernel {ms_decq:.4f} ms, {nbytesq / 1e6:.1f} MB -> {achq:.0f} GB/s")
@@ -576,7 +655,7 @@ def main():
             "workload": f"the decode workload over INT{bits} arenas (codes + one fp16 scale per "
                         "(token, KV head) vector)",
             "context_tokens_per_s": round(tokens / (ms_decq * 1e-3), 1),
-            "speedup_vs_fp16_arena": round(ms_dec / ms_decq, 3),
+            "speedup_vs_fp16_arena": round(ms_dec_call / ms_decq, 3),
             "ms_per_step": round(ms_stepq, 5),
             "roofline": {
                 "kernel": f"paged_attention_decode (decode_split_i{bits}_kernel + "

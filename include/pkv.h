@@ -195,6 +195,32 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
                                   size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * paged_attention_decode_append — one decode step's append and attention in
+ * one call (part 3 sections 1 and 4): for every sequence b, its new token at
+ * position L - 1, L = context_lens[b], is appended as kv_append_rope does
+ * (q[b] and k[b] rotated by RoPE at L - 1 in fp64 and rounded once to fp16;
+ * the rotated q to q_out[b]; the rotated k and v[b] to the arena at block
+ * bt[b][(L-1)/16], slot (L-1)%16), and out[b] is paged_attention_decode's
+ * result over positions 0 .. L-1 with the rotated q.  Outputs, q_out and the
+ * arena bytes are bit for bit those of kv_append_rope (cu_q_lens = 0..num_seqs,
+ * chunk_start = L - 1) followed by paged_attention_decode.
+ * Arguments as kv_append_rope and paged_attention_decode, with q, k, v of one
+ * token per sequence: q [num_seqs][Hq][D], k, v [num_seqs][Hkv][D], read only;
+ * q_out [num_seqs][Hq][D] must not overlap q (PKV_ERR_RANGE).  The workspace
+ * is paged_attention_decode's (paged_attention_decode_workspace_bytes()).
+ * fp16 arenas with head_dim 128 and 4 query heads per KV head only
+ * (PKV_ERR_DTYPE / PKV_ERR_SHAPE otherwise).  A position at or past
+ * rope_max_pos skips the append and leaves q unrotated for the attention.
+ * ------------------------------------------------------------------------- */
+pkv_status paged_attention_decode_append(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                         const void* q, void* q_out, const void* k, const void* v,
+                                         void* k_arena, void* v_arena, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                         int32_t num_seqs, int32_t max_context_len, float scale,
+                                         const void* rope_table, int32_t rope_max_pos,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * paged_attention_decode_noalloc — paged_attention_decode for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation).  Same arguments, result and

@@ -60,6 +60,9 @@ _SIGS = {
                                                               ctypes.POINTER(ctypes.c_size_t)]),
     "paged_attention_decode": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _I32,
                                               _I32, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "paged_attention_decode_append": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                                     _I32, _P, _I32, _I32, ctypes.c_float, _P,
+                                                     _I32, _P, ctypes.c_size_t, _P]),
     "paged_attention_decode_noalloc": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P,
                                                       _I32, _I32, ctypes.c_float, _P]),
     "paged_attention_decode_shared": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P,
@@ -217,6 +220,23 @@ def paged_attention_decode(g: Geom, out, q, k_arena, v_arena, block_table, conte
                                         max_context_len, scale, _ptr(workspace), ws_bytes,
                                         _stream(stream)),
            "paged_attention_decode")
+
+
+def paged_attention_decode_append(g: Geom, out, q, q_out, k, v, k_arena, v_arena, block_table,
+                                  context_lens, max_context_len: int, scale: float, rope,
+                                  rope_max_pos: int, workspace=None, stream=None) -> None:
+    """kv_append_rope of one new token per sequence (at position
+    context_lens[b] - 1) and paged_attention_decode in one call; q_out receives
+    the rotated queries and must not overlap q."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attention_decode_append(ctypes.byref(g), _ptr(out), F32, _ptr(q),
+                                               _ptr(q_out), _ptr(k), _ptr(v), _ptr(k_arena),
+                                               _ptr(v_arena), _ptr(block_table),
+                                               block_table.shape[1], _ptr(context_lens),
+                                               context_lens.shape[0], max_context_len, scale,
+                                               _ptr(rope), rope_max_pos, _ptr(workspace),
+                                               ws_bytes, _stream(stream)),
+           "paged_attention_decode_append")
 
 
 def paged_attention_decode_noalloc(g: Geom, out, q, k_arena, v_arena, block_table, context_lens,

@@ -79,6 +79,39 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
                                        (hipStream_t)stream));
 }
 
+pkv_status paged_attention_decode_append(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                         const void* q, void* q_out, const void* k, const void* v,
+                                         void* k_arena, void* v_arena, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                         int32_t num_seqs, int32_t max_context_len, float scale,
+                                         const void* rope_table, int32_t rope_max_pos,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  if (geom->dtype != PKV_F16) return PKV_ERR_DTYPE;
+  if (!pkv::decode_fast_path(*geom)) return PKV_ERR_SHAPE;
+  if (num_seqs < 0) return PKV_ERR_RANGE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !q_out || !k || !v || !k_arena || !v_arena || !block_table ||
+      !context_lens || !rope_table)
+    return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || max_context_len < 1 || rope_max_pos < 1 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return PKV_ERR_RANGE;
+  // every workgroup of a sequence reads q while its first split writes q_out
+  const size_t qbytes = (size_t)num_seqs * geom->num_q_heads * geom->head_dim * 2;
+  const char* q0 = (const char*)q;
+  const char* o0 = (const char*)q_out;
+  if (o0 < q0 + qbytes && q0 < o0 + qbytes) return PKV_ERR_RANGE;
+  const size_t need = pkv::decode_workspace_bytes(*geom, num_seqs, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  return hip_status(pkv::launch_decode_append(*geom, (float*)out, q, q_out, k, v, k_arena, v_arena,
+                                              block_table, max_blocks_per_seq, context_lens,
+                                              num_seqs, max_context_len, scale, rope_table,
+                                              rope_max_pos, workspace, (hipStream_t)stream));
+}
+
 pkv_status paged_attention_decode_noalloc(const pkv_geom* geom, void* out, int32_t out_dtype,
                                           const void* q, const void* k_arena,
                                           const void* v_arena, const int32_t* block_table,

@@ -58,6 +58,23 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
                     context_lens, 0, scale_log2, Hkv, nsplit_max, num_blocks, split, g);
 }
 
+// The same split units with the step's append fused in (fp16 arenas): each
+// wave rotates its query and the new key at position L - 1 itself, split 0
+// writes the rotated queries, and the last split writes the new key and value
+// to the arena and takes them from registers for its last pair.
+__global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_split_append_kernel(
+    float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks, DecodeAppend app) {
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.z * kDecodeWavesPerWG + (threadIdx.x >> 6);
+  if (g >= Hkv) return;
+  decode_split_unit<true, true>(out, ws_o, ws_ml, nullptr, app.k_arena, app.v_arena, block_table,
+                                max_blocks, b, b, context_lens, 0, scale_log2, Hkv, nsplit_max,
+                                num_blocks, split, g, app);
+}
+
 // ---- splits shared by several sequences ---------------------------------------
 // Kshipra part 3, section 3: sequences that share a cached prefix share its
 // physical blocks.  For a group of rows whose first `skip` splits are the same
@@ -470,6 +487,42 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
                        (const _Float16*)v_arena, block_table, max_blocks, context_lens,
                        scale_log2, g.num_kv_heads, nsplit, g.num_blocks);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit <= 1) return e;
+  return launch_decode_combine(g, out, ws_o, ws_ml, context_lens, nullptr, 0, max_blocks, num_seqs,
+                               nsplit, stream);
+}
+
+hipError_t launch_decode_append(const pkv_geom& g, float* out, const void* q, void* q_out,
+                                const void* k, const void* v, void* k_arena, void* v_arena,
+                                const int32_t* block_table, int max_blocks,
+                                const int32_t* context_lens, int num_seqs, int max_context_len,
+                                float scale, const void* rope_table, int rope_max_pos,
+                                void* workspace, hipStream_t stream) {
+  const int nsplit = (max_context_len + kDecodeSplit - 1) / kDecodeSplit;
+  float* ws_o = nullptr;
+  float* ws_ml = nullptr;
+  if (nsplit > 1) {
+    const size_t parts = (size_t)num_seqs * g.num_q_heads * nsplit;
+    ws_o = (float*)workspace;
+    ws_ml = (float*)((char*)workspace + align256(parts * kD * sizeof(float)));
+  }
+  DecodeAppend app;
+  app.q = (const _Float16*)q;
+  app.q_out = (_Float16*)q_out;
+  app.k = (const _Float16*)k;
+  app.v = (const _Float16*)v;
+  app.k_arena = (_Float16*)k_arena;
+  app.v_arena = (_Float16*)v_arena;
+  app.rope = (const double2*)rope_table;
+  app.rope_max_pos = rope_max_pos;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int wpg = g.num_kv_heads < kDecodeWavesPerWG ? g.num_kv_heads : kDecodeWavesPerWG;
+  const int zg = (g.num_kv_heads + kDecodeWavesPerWG - 1) / kDecodeWavesPerWG;
+  const dim3 grid(nsplit | 1, num_seqs, zg);  // odd width: see launch_decode
+  hipLaunchKernelGGL(decode_split_append_kernel, grid, dim3(64 * wpg), 0, stream, out, ws_o,
+                     ws_ml, block_table, max_blocks, context_lens, scale_log2, g.num_kv_heads,
+                     nsplit, g.num_blocks, app);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit <= 1) return e;
   return launch_decode_combine(g, out, ws_o, ws_ml, context_lens, nullptr, 0, max_blocks, num_seqs,

@@ -3,7 +3,10 @@
 // kernel (the design is described at the top of decode.hip).
 #pragma once
 
+#include <type_traits>
+
 #include "fp16_shape.h"
+#include "rope_core.h"
 
 namespace pkv {
 namespace {
@@ -93,18 +96,38 @@ __device__ inline Pair load_pair(const _Float16* __restrict__ k_arena,
 #endif
 constexpr int kDecodeWavesPerWG = PKV_DECODE_WAVES_PER_WG;
 
+// The step's append fused into the decode (paged_attention_decode_append):
+// each sequence's new token, at position context length - 1, with its query,
+// key and value as the caller passes them to kv_append_rope.
+struct DecodeAppend {
+  const _Float16* q;      // [num_seqs][Hq][D] queries, not yet rotated
+  _Float16* q_out;        // [num_seqs][Hq][D] rotated queries (written by split 0)
+  const _Float16* k;      // [num_seqs][Hkv][D] keys, not yet rotated
+  const _Float16* v;      // [num_seqs][Hkv][D] values
+  _Float16* k_arena;      // the arenas, written at the new token's slot
+  _Float16* v_arena;
+  const double2* rope;    // [rope_max_pos][D/2] (cos, sin)
+  int rope_max_pos;
+};
+
 // Sequence b (its block-table row and its partials in the workspace), whose
 // query and output live at packed row `row`; its context length is
 // lens[b] + len_add.  Wave (threadIdx.x >> 6) serves KV head g of split
 // `split`.  kNT: streaming loads (false: cached, for blocks other
-// workgroups of the call read too).
-template <bool kNT = true>
+// workgroups of the call read too).  kAppend: the query is app.q rotated
+// here, and the new token's rotated key and value enter the last pair from
+// registers (and are written to the arena by the wave of the last split),
+// with the values, roundings and order of kv_append_rope followed by the
+// plain decode, so the outputs, the rotated queries and the arena bytes are
+// bit for bit those of the two calls.
+template <bool kNT = true, bool kAppend = false>
 __device__ __forceinline__ void decode_split_unit(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
     const _Float16* __restrict__ v_arena, const int32_t* __restrict__ block_table,
     int max_blocks, int b, int row, const int32_t* __restrict__ lens, int len_add,
-    float scale_log2, int Hkv, int nsplit_max, int num_blocks, int split, int g) {
+    float scale_log2, int Hkv, int nsplit_max, int num_blocks, int split, int g,
+    DecodeAppend app = DecodeAppend{}) {
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
@@ -117,10 +140,11 @@ __device__ __forceinline__ void decode_split_unit(
   if (lane < kSB && blk0 + lane < max_blocks)
     my_blk = block_table[(size_t)b * max_blocks + blk0 + lane];
   // Q^T (B operand): column ln = head g*4+ln, dims 32kd + 8lq .. +8
+  const _Float16* qsrc = kAppend ? app.q : q;
   half8_t qb[4];
 #pragma unroll
   for (int kd = 0; kd < 4; ++kd)
-    qb[kd] = ln < kG ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + ln) * kD + 32 * kd + 8 * lq)
+    qb[kd] = ln < kG ? *(const half8_t*)(qsrc + ((size_t)row * Hq + g * kG + ln) * kD + 32 * kd + 8 * lq)
                      : (half8_t)(_Float16)0.f;
   // clamp to what the grid and workspace cover (a caller contract violation
   // then gives unspecified values, never an out-of-bounds access)
@@ -138,18 +162,104 @@ __device__ __forceinline__ void decode_split_unit(
   const int nb = min(kSB, nb_seq - blk0);
   const int nsplit = (nb_seq + kSB - 1) / kSB;
   const int npairs = (nb + 1) >> 1;
-  if (lane >= nb || my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
 
+  // (the unclamped id of this split's blocks, for the fused append's write)
+  [[maybe_unused]] const int raw_blk = my_blk;
+  if (lane >= nb || my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
+  auto pair_ids = [&](int p, int& a, int& c) {
+    a = __builtin_amdgcn_readlane(my_blk, 2 * p);
+    c = 2 * p + 1 < nb ? __builtin_amdgcn_readlane(my_blk, 2 * p + 1) : a;
+  };
+  // The first pair is requested before anything else (the fused append's
+  // work then overlaps its latency).
+  Pair buf[2];
+  {
+    int ba, bb;
+    pair_ids(0, ba, bb);
+    buf[0] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+  }
+
+  // Fused append: rotate the query (and, in the sequence's last split, the new
+  // key) at pos = L - 1, spread over the wave's 64 lanes and handed to the
+  // MFMA operand layout through the wave's LDS; positions outside the table
+  // skip the append, as kv_append_rope does.  The last split keeps the new key
+  // and value in LDS until its last pair, rather than in registers across the
+  // loop.
+  [[maybe_unused]] bool app_ok = false;
+  [[maybe_unused]] _Float16* kv_lds = nullptr;
+  if constexpr (kAppend) {
+    // per wave: rotated queries of its 4 heads, then the new key and value
+    __shared__ _Float16 app_lds[kDecodeWavesPerWG][(kG + 2) * kD];
+    _Float16* wl = app_lds[threadIdx.x >> 6];
+    kv_lds = wl + kG * kD;
+    const int pos = L - 1;
+    app_ok = pos < app.rope_max_pos;
+    if (app_ok) {
+      const double2* rrow = app.rope + (size_t)pos * (kD / 2);
+      {
+        // lane l: pairs i = 4 (l & 15) .. +3 of the wave's head l >> 4
+        const int h = lane >> 4, i0 = 4 * (lane & 15);
+        const _Float16* qs = app.q + ((size_t)row * Hq + g * kG + h) * kD;
+        const half4_t lo = *(const half4_t*)(qs + i0), hi = *(const half4_t*)(qs + i0 + kD / 2);
+        half4_t olo, ohi;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const double2 c = rrow[i0 + r];
+          double o0, o1;
+          rope_pair((double)lo[r], (double)hi[r], c.x, c.y, o0, o1);
+          olo[r] = store_f64<_Float16>(o0);
+          ohi[r] = store_f64<_Float16>(o1);
+        }
+        const u32x2 wlo = __builtin_bit_cast(u32x2, olo), whi = __builtin_bit_cast(u32x2, ohi);
+        *(u32x2*)(wl + h * kD + i0) = wlo;
+        *(u32x2*)(wl + h * kD + i0 + kD / 2) = whi;
+        if (split == 0) {
+          _Float16* qo = app.q_out + ((size_t)row * Hq + g * kG + h) * kD;
+          *(u32x2*)(qo + i0) = wlo;
+          *(u32x2*)(qo + i0 + kD / 2) = whi;
+        }
+      }
+      // one wave writes and reads its LDS, in order
+      if (ln < kG) {
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd) qb[kd] = *(const half8_t*)(wl + ln * kD + 32 * kd + 8 * lq);
+      }
+      if (split == nsplit - 1) {
+        // lane l: key pair (l, l + 64) and value dims l, l + 64
+        const int nblk = __builtin_amdgcn_readlane(raw_blk, (pos >> 4) - blk0);
+        const int slot = pos & 15;
+        const _Float16* kp = app.k + ((size_t)b * Hkv + g) * kD;
+        const _Float16* vp = app.v + ((size_t)b * Hkv + g) * kD;
+        const double2 c = rrow[lane];
+        double o0, o1;
+        rope_pair((double)kp[lane], (double)kp[lane + kD / 2], c.x, c.y, o0, o1);
+        const _Float16 k0 = store_f64<_Float16>(o0), k1 = store_f64<_Float16>(o1);
+        const _Float16 v0 = vp[lane], v1 = vp[lane + kD / 2];
+        kv_lds[lane] = k0;
+        kv_lds[lane + kD / 2] = k1;
+        kv_lds[kD + lane] = v0;
+        kv_lds[kD + lane + kD / 2] = v1;
+        if (nblk >= 0 && nblk < num_blocks) {
+          _Float16* kt = app.k_arena + ((size_t)nblk * Hkv + g) * kBlock * kD;
+          kt[((lane / kX) * kBlock + slot) * kX + lane % kX] = k0;
+          kt[(((lane + kD / 2) / kX) * kBlock + slot) * kX + lane % kX] = k1;
+          _Float16* vt = app.v_arena + ((size_t)nblk * Hkv + g) * kD * kBlock;
+          vt[lane * kBlock + slot] = v0;
+          vt[(lane + kD / 2) * kBlock + slot] = v1;
+        }
+      }
+    }
+  }
   f32x4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = (f32x4)0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto pair_ids = [&](int p, int& a, int& c) {
-    a = __builtin_amdgcn_readlane(my_blk, 2 * p);
-    c = 2 * p + 1 < nb ? __builtin_amdgcn_readlane(my_blk, 2 * p + 1) : a;
-  };
-  auto compute = [&](const Pair& pr, int p) {
+  // Keys past the context exist only in a sequence's last pair.  kMask: 0
+  // masks by the position test on every pair (the plain kernel's loop, one
+  // body for all pairs), 1 none (a full pair), 2 always (the last pair).
+  auto compute = [&](const Pair& pr, int p, auto mode) {
+    constexpr int kMask = decltype(mode)::value;
     f32x4 s[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -161,6 +271,7 @@ __device__ __forceinline__ void decode_split_unit(
     // element e of this lane: token 4lq + (e & 3) of block A (e < 4) or B
     const int tok_a = (blk0 + 2 * p) * kBlock + 4 * lq;
     const int nva = L - tok_a, nvb = nva - kBlock;  // valid elements of A / B
+    auto valid = [&](int e) { return kMask == 1 || (e < 4 ? e < nva : e - 4 < nvb); };
     // The base-2 exponent of key e is fma(score_e, scale_log2, -m): one
     // rounding, written out so that no kernel leaves it to the compiler's
     // contraction choices (decode_shared_kernel must round it identically).
@@ -168,10 +279,7 @@ __device__ __forceinline__ void decode_split_unit(
     // 0 and rounding is monotone, so this is the max of the scaled scores).
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool ok = e < 4 ? e < nva : e - 4 < nvb;
-      mx = fmaxf(mx, ok ? s[e >> 2][e & 3] : -INFINITY);
-    }
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, valid(e) ? s[e >> 2][e & 3] : -INFINITY);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx * scale_log2);  // finite: the first key of a split is real
@@ -186,23 +294,20 @@ __device__ __forceinline__ void decode_split_unit(
     float lsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const bool ok = e < 4 ? e < nva : e - 4 < nvb;
-      const float arg = ok ? __builtin_fmaf(s[e >> 2][e & 3], scale_log2, -m_new) : -INFINITY;
+      const float arg = valid(e) ? __builtin_fmaf(s[e >> 2][e & 3], scale_log2, -m_new) : -INFINITY;
       const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(arg);
       pb[e] = ph;
       lsum += (float)ph;
     }
     l_run += lsum;
-    // keys past the context (only in the sequence's last pair): zero V, since
-    // their p is 0 but 0 * NaN is not
-    const bool tail_pair = (blk0 + 2 * p + 2) * kBlock > L;  // wave-uniform
+    // keys past the context: zero V, since their p is 0 but 0 * NaN is not
+    const bool tail_pair = kMask == 2 || (kMask == 0 && (blk0 + 2 * p + 2) * kBlock > L);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       half8_t va = pr.v[db];
-      if (tail_pair) {
+      if (kMask != 1 && tail_pair) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          va[e] = (e < 4 ? e < nva : e - 4 < nvb) ? va[e] : (_Float16)0.f;
+        for (int e = 0; e < 8; ++e) va[e] = valid(e) ? va[e] : (_Float16)0.f;
       }
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o[db], 0, 0, 0);
     }
@@ -213,12 +318,6 @@ __device__ __forceinline__ void decode_split_unit(
   // pair it re-requests the last pair, a cache hit), so the loads outstanding
   // at each wait are the same on every path and the wait before a pair's MFMAs
   // covers that pair only, never the prefetch behind it.
-  Pair buf[2];
-  {
-    int ba, bb;
-    pair_ids(0, ba, bb);
-    buf[0] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
-  }
 #pragma unroll
   for (int p = 0; p < kSB / 2; ++p) {
     if (p + 1 < kSB / 2) {
@@ -227,7 +326,40 @@ __device__ __forceinline__ void decode_split_unit(
       buf[(p + 1) & 1] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
       __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the compute
     }
-    if (p < npairs) compute(buf[p & 1], p);
+    if constexpr (kAppend) {
+      if (p + 1 < npairs) compute(buf[p & 1], p, std::integral_constant<int, 1>{});
+    } else {
+      if (p < npairs) compute(buf[p & 1], p, std::integral_constant<int, 0>{});
+    }
+  }
+  if constexpr (kAppend) {
+    // The last pair, after the loop: the last prefetch (at p = kSB / 2 - 2,
+    // clamped to the last pair) left pair npairs - 1 in buffer
+    // (kSB / 2 - 1) & 1.  The new token (the context's last key) enters from
+    // registers: key row `slot` of its block, and the value element of key
+    // slot in lane group slot >> 2.
+    Pair& last = buf[(kSB / 2 - 1) & 1];
+    if (app_ok && split == nsplit - 1) {
+      const int pos = L - 1, slot = pos & 15, ab = ((pos >> 4) - blk0) & 1;
+      // (ab and slot are wave-uniform; constant indices keep the pair in registers)
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) {
+        const half8_t x = *(const half8_t*)(kv_lds + 32 * kd + 8 * lq);
+        if (ln == slot) {
+          if (ab == 0) last.k[0][kd] = x;
+          else last.k[1][kd] = x;
+        }
+      }
+      const int ev = 4 * ab + (slot & 3);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const _Float16 x = kv_lds[kD + 16 * db + ln];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (lq == (slot >> 2) && e == ev) last.v[db][e] = x;
+      }
+    }
+    compute(last, npairs - 1, std::integral_constant<int, 2>{});
   }
 
   float l_row = l_run;

@@ -158,6 +158,15 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
                          float scale, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, const DecodeGroups* groups = nullptr);
 
+// paged_attention_decode with the step's append fused in (fp16 arenas on the
+// decode fast path; the caller checks).
+hipError_t launch_decode_append(const pkv_geom& g, float* out, const void* q, void* q_out,
+                                const void* k, const void* v, void* k_arena, void* v_arena,
+                                const int32_t* block_table, int max_blocks,
+                                const int32_t* context_lens, int num_seqs, int max_context_len,
+                                float scale, const void* rope_table, int rope_max_pos,
+                                void* workspace, hipStream_t stream);
+
 // The device address and size of the calling device's decode scratch array
 // (the split partials of paged_attention_decode_noalloc); looked up once per
 // device.

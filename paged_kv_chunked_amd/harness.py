@@ -20,7 +20,8 @@ import numpy as np
 from . import (BLOCK_SIZE, DECODE_SPLIT, F16, F32, I4KV, I8KV, Pool, geom, kv_append_rope, paged_attention_chunk,
                paged_attention_chunk_workspace_bytes, paged_attention_decode_shared,
                paged_attention_mixed, paged_attention_mixed_workspace_bytes,
-               paged_attention_decode, paged_attention_decode_workspace_bytes, pkv_copy_blocks,
+               paged_attention_decode, paged_attention_decode_append,
+               paged_attention_decode_workspace_bytes, pkv_copy_blocks,
                pkv_rope_table_bytes, pkv_rope_table_init)
 from . import workloads as _wl
 
@@ -337,6 +338,23 @@ class DeviceWorkload:
                                   self.chunk_max_q, self.chunk_max_ctx, self.scale,
                                   self.chunk_ws, stream=stream)
 
+    def decode_append(self, stream=None, k_arena=None, v_arena=None):
+        """The decode rows' append and attention in one paged_attention_decode_append
+        call (fp16 arenas; every step row a decode): the same q rotation, arena
+        writes and outputs as append() followed by decode()."""
+        self._need_split()
+        if self.chunk_rows:
+            raise ValueError("decode_append covers steps of decode rows only")
+        if self.dec_rows:
+            t0, n = self.dec_tok0, len(self.dec_rows)
+            paged_attention_decode_append(self.g, self.dec_out, self.q_raw[t0:t0 + n], self.dec_q,
+                                          self.k_new[t0:t0 + n], self.v_new[t0:t0 + n],
+                                          self.k_arena if k_arena is None else k_arena,
+                                          self.v_arena if v_arena is None else v_arena,
+                                          self.dec_bt, self.dec_lens, self.dec_max_len,
+                                          self.scale, self.rope, self.rope_max_pos, self.dec_ws,
+                                          stream=stream)
+
     def step(self, stream=None, k_arena=None, v_arena=None):
         """One pass of the hot path over the step batch."""
         self.append(stream, k_arena, v_arena)
@@ -367,6 +385,20 @@ class DeviceWorkload:
         blocks = int(sum(-(-int(L) // BLOCK_SIZE) for L in self.dec_lens_host))
         qo = S * w.num_q_heads * w.head_dim * (elt + 4)
         return kv + qo + 4 * blocks + 4 * S
+
+    def decode_append_bytes(self) -> int:
+        """decode_bytes() plus the fused append's own traffic: the rotated
+        queries written, each new key and value read and written to the arena,
+        and one RoPE table row (fp64 cos, sin per pair) per sequence."""
+        if not self.dec_rows:
+            return 0
+        w = self.w
+        S = len(self.dec_rows)
+        elt = 2 if w.dtype == "f16" else 4
+        q_out = S * w.num_q_heads * w.head_dim * elt
+        kv_new = 2 * 2 * S * w.num_kv_heads * w.head_dim * elt
+        rope = S * (w.head_dim // 2) * 16
+        return self.decode_bytes() + q_out + kv_new + rope
 
     def chunk_flops(self) -> int:
         """4 * D * Hq per visible (query, key) pair."""

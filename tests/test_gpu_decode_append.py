@@ -1,0 +1,96 @@
+"""paged_attention_decode_append (the decode step's append and attention in one
+call) against kv_append_rope followed by paged_attention_decode, on the same
+seeded workloads: outputs, rotated queries and K/V arena bytes bit for bit;
+and the fused call's outputs against the oracle on the edge-length batch."""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_chunked_amd as pkv  # noqa: E402
+from oracle import script as oscript  # noqa: E402
+from paged_kv_chunked_amd import harness, workloads  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.fail("libpkv.so is not built")
+    pkv.lib()
+
+
+def say(msg):
+    print(f"[gpu-append] {msg}", flush=True)
+
+
+def bits(t):
+    a = t.cpu().numpy()
+    return a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+def edge_lengths():
+    """Contexts 1 (the new token alone), block and pair edges (15 .. 33), split
+    edges (383 .. 385, 768, 769) and longer ones; Hq 32 / Hkv 8, fp16."""
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 100, 383, 384, 385, 768, 769, 1000, 2049]
+    return workloads.build("append_edges", 21, "f16", 32, 8, 128, 5.0e5,
+                           [(L - 1, 1) for L in lens], max_blocks_per_seq=130)
+
+
+def compare(w):
+    say(f"{w.name}: separate calls")
+    a = harness.DeviceWorkload(w)
+    a.step()
+    say(f"{w.name}: fused call")
+    b = harness.DeviceWorkload(w)
+    b.decode_append()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a.dec_q), bits(b.dec_q)), "rotated queries differ"
+    assert np.array_equal(bits(a.k_arena), bits(b.k_arena)), "K arena differs"
+    assert np.array_equal(bits(a.v_arena), bits(b.v_arena)), "V arena differs"
+    assert np.array_equal(bits(a.dec_out), bits(b.dec_out)), "outputs differ"
+    say(f"{w.name}: {b.dec_out.numel()} outputs, queries and arenas bit for bit")
+    return b
+
+
+def test_fused_matches_separate_decode_batch():
+    compare(workloads.decode_batch())
+
+
+def test_fused_matches_separate_shard():
+    """One GPU's share of a KV-head split over 8 GPUs (Hq 4 / Hkv 1)."""
+    compare(workloads.tp8_decode_batch())
+
+
+def test_fused_edges_against_oracle():
+    w = edge_lengths()
+    b = compare(w)
+    st = oscript.run_script(w, materialize=True)
+    q_rot = oscript.append_step(w, st)
+    assert np.array_equal(bits(b.q), q_rot.view(np.uint16)), "rotated q differs from the oracle"
+    cu = b.cu_host
+    worst = 0.0
+    for r in b.dec_rows:
+        exp = oscript.attend_row(w, st, r, q_rot[cu[r]:cu[r + 1]], b.scale)[0]
+        got = b.dec_out[r - b.dec_rows[0]].cpu().numpy()
+        worst = max(worst, float(np.abs(got - exp).max()))
+    say(f"{w.name}: max abs error against the oracle {worst:.3e}")
+    assert worst <= 2e-3
+
+
+def test_fused_repeated_steps_match():
+    """Two fused calls in a row leave the same arena as one (the second writes
+    the same bytes), and outputs do not change."""
+    w = workloads.decode_batch(num_seqs=9, seed=77)
+    b = harness.DeviceWorkload(w)
+    b.decode_append()
+    torch.cuda.synchronize()
+    out1, k1 = bits(b.dec_out), bits(b.k_arena)
+    b.decode_append()
+    torch.cuda.synchronize()
+    assert np.array_equal(out1, bits(b.dec_out)) and np.array_equal(k1, bits(b.k_arena))

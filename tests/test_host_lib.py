@@ -267,6 +267,23 @@ def test_entry_point_errors(lib):
                                               384, 0.1, None) == 1
     assert lib.paged_attention_decode_noalloc(gp, None, 1, None, None, None, None, 4, None, 0,
                                               64, 0.1, None) == 0
+    # the fused append + decode: argument checks before any launch
+    A = ctypes.c_void_p(0x100000)
+    B = ctypes.c_void_p(0x100000 + 3 * 32 * 128 * 2)          # right after A's 3 rows of q
+    dec_app = lambda *a: lib.paged_attention_decode_append(gp, *a)
+    assert dec_app(FAKE, 1, A, None, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000, 0.1,
+                   FAKE, 4096, FAKE, need, None) == 1          # q_out missing
+    assert dec_app(FAKE, 1, A, ctypes.c_void_p(0x100000 + 64), FAKE, FAKE, FAKE, FAKE, FAKE, 64,
+                   FAKE, 3, 1000, 0.1, FAKE, 4096, FAKE, need, None) == 4   # q_out overlaps q
+    assert dec_app(FAKE, 1, A, B, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000, 0.1,
+                   FAKE, 0, FAKE, need, None) == 4             # no RoPE positions
+    assert dec_app(FAKE, 1, A, B, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000, 0.1,
+                   FAKE, 4096, FAKE, need - 1, None) == 5      # workspace too small
+    assert lib.paged_attention_decode_append(ctypes.byref(_geom(dtype=2)), FAKE, 1, A, B, FAKE,
+                                             FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000, 0.1,
+                                             FAKE, 4096, FAKE, need, None) == 3   # INT8 arena
+    assert dec_app(None, 1, None, None, None, None, None, None, None, 4, None, 0, 64, 0.1,
+                   None, 1, None, 0, None) == 0                # empty batch
     # chunk: the schedule, one int32 per (sequence, 64-row tile)
     need = pkv.paged_attention_chunk_workspace_bytes(g, 2, 100, 500)
     assert need == 2 * 2 * 4
