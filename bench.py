@@ -4,13 +4,15 @@
 Default run (N = 1):
   * decode: 64 decode tokens, contexts U[512, 4096], one Llama-3-8B-shaped layer
     (Hq 32 / Hkv 8, head dim 128, fp16, 16-token blocks, shuffled arena).  A
-    step = kv_append_rope for the 64 new tokens (drawn queries in, rotated
-    queries to a buffer of their own, so every step sees the same input) +
-    paged_attention_decode (split kernel + log-sum-exp combine).
-    `value` is the algorithmic decode bytes of one step / step time.  The
-    same step as one paged_attention_decode_append call (the append fused
-    into the split kernel) is reported beside it ("decode_append_fused";
-    --fused-append makes it the timed step).
+    step = the 64 new tokens' append (RoPE, arena write) and the decode, in
+    one paged_attention_decode_append call (split kernel with the append
+    fused + log-sum-exp combine; drawn queries in, rotated queries to a buffer
+    of their own, so every step sees the same input).  `value` is the
+    algorithmic decode bytes of one step / step time.  The same step as
+    kv_append_rope + paged_attention_decode, and the decode call alone, are
+    reported beside it ("decode_separate_calls"; --separate-append makes the
+    two calls the timed step and reports the fused form as
+    "decode_append_fused").
   * chunk prefill (reported under "chunk_prefill"): 8 sequences with cached
     prefixes 16*U{0..224} and a 512-token chunk each; a step = kv_append_rope
     + paged_attention_chunk; TFLOP/s over visible pairs.
@@ -25,7 +27,7 @@ Inputs are synthetic and resident in HBM before timing.  Each timed step
 rotates over --layers copies of the arena (a layer's worth each) so repeated
 steps cannot be served from the 256 MB Infinity Cache.
 
-`roofline` refers to the dominant kernel call (paged_attention_decode): its
+`roofline` refers to the dominant kernel call (paged_attention_decode_append): its
 average duration over --steps calls issued back to back (rotating the arena
 copies) between two HIP events on the stream it is launched on
 (`avg_launch_ms`); `avg_launch_ms_isolated` is the mean of per-call events in
@@ -104,11 +106,12 @@ def make_layers(torch, dw, n):
 
 
 def bench_decode(torch, args, kv_bits=0):
-    """The decode step on the decode workload, rotating the arena copies: the
-    step's append (kv_append_rope) then paged_attention_decode.  For fp16
-    arenas the other form of the same step (one paged_attention_decode_append
-    call, or the two calls with --fused-append) is timed beside it, and so is
-    the decode call alone."""
+    """The decode step on the decode workload, rotating the arena copies.  For
+    fp16 arenas the step is one paged_attention_decode_append call (the new
+    tokens' append fused into the decode), and the same step as two calls
+    (kv_append_rope then paged_attention_decode) and the decode call alone are
+    timed beside it (--separate-append swaps the two forms); quantized arenas
+    take the two calls."""
     import dataclasses
     from paged_kv_chunked_amd import harness, workloads
     w = workloads.decode_batch()
@@ -117,7 +120,7 @@ def bench_decode(torch, args, kv_bits=0):
     log(f"decode set-up: {w.num_blocks} blocks")
     dw = harness.DeviceWorkload(w)
     layers = make_layers(torch, dw, args.layers)
-    fused = kv_bits == 0 and args.fused_append
+    fused = kv_bits == 0 and not args.separate_append
     events = []
 
     def call(i):
@@ -405,6 +408,20 @@ def bench_tp8(torch, args):
                              "bytes": nb, "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+            # the whole decode step (the 64 new tokens' append + decode), as two
+            # calls and as one paged_attention_decode_append call
+            def sep(i):
+                k, v = layers[i % len(layers)]
+                dw.append(k_arena=k, v_arena=v)
+                dw.decode(k_arena=k, v_arena=v)
+
+            def fus(i):
+                k, v = layers[i % len(layers)]
+                dw.decode_append(k_arena=k, v_arena=v)
+
+            res["decode"]["ms_step_separate_calls"] = round(time_back_to_back(torch, sep, args.steps), 5)
+            res["decode"]["ms_step_fused_call"] = round(time_back_to_back(torch, fus, args.steps), 5)
         else:
             ms = time_back_to_back(torch, lambda i: dw.chunk(k_arena=layers[i % len(layers)][0],
                                                              v_arena=layers[i % len(layers)][1]),
@@ -518,8 +535,8 @@ def main():
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-tp8", action="store_true")
-    ap.add_argument("--fused-append", action="store_true",
-                    help="time the fp16 decode step as one paged_attention_decode_append call")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="time the fp16 decode step as kv_append_rope + paged_attention_decode")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,

@@ -139,13 +139,31 @@ __device__ __forceinline__ void decode_split_unit(
   int my_blk = 0;
   if (lane < kSB && blk0 + lane < max_blocks)
     my_blk = block_table[(size_t)b * max_blocks + blk0 + lane];
-  // Q^T (B operand): column ln = head g*4+ln, dims 32kd + 8lq .. +8
-  const _Float16* qsrc = kAppend ? app.q : q;
+  // Q^T (B operand): column ln = head g*4+ln, dims 32kd + 8lq .. +8 (the
+  // fused append fills it from its rotation below)
   half8_t qb[4];
 #pragma unroll
   for (int kd = 0; kd < 4; ++kd)
-    qb[kd] = ln < kG ? *(const half8_t*)(qsrc + ((size_t)row * Hq + g * kG + ln) * kD + 32 * kd + 8 * lq)
-                     : (half8_t)(_Float16)0.f;
+    qb[kd] = !kAppend && ln < kG
+                 ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + ln) * kD + 32 * kd + 8 * lq)
+                 : (half8_t)(_Float16)0.f;
+  // The fused append's inputs that do not depend on the length (the rotation
+  // table's row does): lane l takes pairs 4 (l & 15) .. +3 of the wave's
+  // query head l >> 4, key pair (l, l + 64) and value dims l, l + 64.
+  [[maybe_unused]] const int ah = lane >> 4, ai0 = 4 * (lane & 15);
+  [[maybe_unused]] half4_t qlo, qhi;
+  [[maybe_unused]] _Float16 kr0, kr1, vr0, vr1;
+  if constexpr (kAppend) {
+    const _Float16* qs = app.q + ((size_t)row * Hq + g * kG + ah) * kD;
+    qlo = *(const half4_t*)(qs + ai0);
+    qhi = *(const half4_t*)(qs + ai0 + kD / 2);
+    const _Float16* kp = app.k + ((size_t)b * Hkv + g) * kD;
+    const _Float16* vp = app.v + ((size_t)b * Hkv + g) * kD;
+    kr0 = kp[lane];
+    kr1 = kp[lane + kD / 2];
+    vr0 = vp[lane];
+    vr1 = vp[lane + kD / 2];
+  }
   // clamp to what the grid and workspace cover (a caller contract violation
   // then gives unspecified values, never an out-of-bounds access)
   const int L = min(min(lens[b] + len_add, max_blocks * kBlock), nsplit_max * kDecodeSplit);
@@ -163,6 +181,27 @@ __device__ __forceinline__ void decode_split_unit(
   const int nsplit = (nb_seq + kSB - 1) / kSB;
   const int npairs = (nb + 1) >> 1;
 
+  // Fused append: rotate the query (and, in the sequence's last split, the new
+  // key) at pos = L - 1, spread over the wave's 64 lanes and handed to the
+  // MFMA operand layout through the wave's LDS; positions outside the table
+  // skip the append (the query stays as given), as kv_append_rope does.  The
+  // last split keeps the new key and value in LDS until its last pair, rather
+  // than in registers across the loop.  Its inputs are requested before the
+  // first two pairs, by every wave and on every path (the same number of
+  // loads outstanding everywhere, so the waits stay exact): a wait for them
+  // then leaves both pairs in flight.
+  [[maybe_unused]] const int pos = L - 1;
+  [[maybe_unused]] bool app_ok = false, app_kv = false;
+  [[maybe_unused]] double2 qc[4], kc;
+  if constexpr (kAppend) {
+    app_ok = pos < app.rope_max_pos;
+    app_kv = app_ok && split == nsplit - 1;
+    // (a position outside the table reads the table's last row, unused)
+    const double2* rrow = app.rope + (size_t)min(pos, app.rope_max_pos - 1) * (kD / 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qc[r] = rrow[ai0 + r];
+    kc = rrow[lane];
+  }
   // (the unclamped id of this split's blocks, for the fused append's write)
   [[maybe_unused]] const int raw_blk = my_blk;
   if (lane >= nb || my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
@@ -170,90 +209,85 @@ __device__ __forceinline__ void decode_split_unit(
     a = __builtin_amdgcn_readlane(my_blk, 2 * p);
     c = 2 * p + 1 < nb ? __builtin_amdgcn_readlane(my_blk, 2 * p + 1) : a;
   };
-  // The first pair is requested before anything else (the fused append's
-  // work then overlaps its latency).
+  // The first pair (with the fused append, the first two) is requested before
+  // anything else waits.
   Pair buf[2];
   {
     int ba, bb;
     pair_ids(0, ba, bb);
     buf[0] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+    if constexpr (kAppend) {
+      pair_ids(min(1, npairs - 1), ba, bb);
+      buf[1] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+    }
   }
 
-  // Fused append: rotate the query (and, in the sequence's last split, the new
-  // key) at pos = L - 1, spread over the wave's 64 lanes and handed to the
-  // MFMA operand layout through the wave's LDS; positions outside the table
-  // skip the append, as kv_append_rope does.  The last split keeps the new key
-  // and value in LDS until its last pair, rather than in registers across the
-  // loop.
-  [[maybe_unused]] bool app_ok = false;
   [[maybe_unused]] _Float16* kv_lds = nullptr;
   if constexpr (kAppend) {
     // per wave: rotated queries of its 4 heads, then the new key and value
     __shared__ _Float16 app_lds[kDecodeWavesPerWG][(kG + 2) * kD];
     _Float16* wl = app_lds[threadIdx.x >> 6];
     kv_lds = wl + kG * kD;
-    const int pos = L - 1;
-    app_ok = pos < app.rope_max_pos;
+    half4_t olo = qlo, ohi = qhi;
     if (app_ok) {
-      const double2* rrow = app.rope + (size_t)pos * (kD / 2);
-      {
-        // lane l: pairs i = 4 (l & 15) .. +3 of the wave's head l >> 4
-        const int h = lane >> 4, i0 = 4 * (lane & 15);
-        const _Float16* qs = app.q + ((size_t)row * Hq + g * kG + h) * kD;
-        const half4_t lo = *(const half4_t*)(qs + i0), hi = *(const half4_t*)(qs + i0 + kD / 2);
-        half4_t olo, ohi;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const double2 c = rrow[i0 + r];
-          double o0, o1;
-          rope_pair((double)lo[r], (double)hi[r], c.x, c.y, o0, o1);
-          olo[r] = store_f64<_Float16>(o0);
-          ohi[r] = store_f64<_Float16>(o1);
-        }
-        const u32x2 wlo = __builtin_bit_cast(u32x2, olo), whi = __builtin_bit_cast(u32x2, ohi);
-        *(u32x2*)(wl + h * kD + i0) = wlo;
-        *(u32x2*)(wl + h * kD + i0 + kD / 2) = whi;
-        if (split == 0) {
-          _Float16* qo = app.q_out + ((size_t)row * Hq + g * kG + h) * kD;
-          *(u32x2*)(qo + i0) = wlo;
-          *(u32x2*)(qo + i0 + kD / 2) = whi;
-        }
-      }
-      // one wave writes and reads its LDS, in order
-      if (ln < kG) {
-#pragma unroll
-        for (int kd = 0; kd < 4; ++kd) qb[kd] = *(const half8_t*)(wl + ln * kD + 32 * kd + 8 * lq);
-      }
-      if (split == nsplit - 1) {
-        // lane l: key pair (l, l + 64) and value dims l, l + 64
-        const int nblk = __builtin_amdgcn_readlane(raw_blk, (pos >> 4) - blk0);
-        const int slot = pos & 15;
-        const _Float16* kp = app.k + ((size_t)b * Hkv + g) * kD;
-        const _Float16* vp = app.v + ((size_t)b * Hkv + g) * kD;
-        const double2 c = rrow[lane];
+      for (int r = 0; r < 4; ++r) {
         double o0, o1;
-        rope_pair((double)kp[lane], (double)kp[lane + kD / 2], c.x, c.y, o0, o1);
-        const _Float16 k0 = store_f64<_Float16>(o0), k1 = store_f64<_Float16>(o1);
-        const _Float16 v0 = vp[lane], v1 = vp[lane + kD / 2];
-        kv_lds[lane] = k0;
-        kv_lds[lane + kD / 2] = k1;
-        kv_lds[kD + lane] = v0;
-        kv_lds[kD + lane + kD / 2] = v1;
-        if (nblk >= 0 && nblk < num_blocks) {
-          _Float16* kt = app.k_arena + ((size_t)nblk * Hkv + g) * kBlock * kD;
-          kt[((lane / kX) * kBlock + slot) * kX + lane % kX] = k0;
-          kt[(((lane + kD / 2) / kX) * kBlock + slot) * kX + lane % kX] = k1;
-          _Float16* vt = app.v_arena + ((size_t)nblk * Hkv + g) * kD * kBlock;
-          vt[lane * kBlock + slot] = v0;
-          vt[(lane + kD / 2) * kBlock + slot] = v1;
-        }
+        rope_pair((double)qlo[r], (double)qhi[r], qc[r].x, qc[r].y, o0, o1);
+        olo[r] = store_f64<_Float16>(o0);
+        ohi[r] = store_f64<_Float16>(o1);
       }
+    }
+    const u32x2 wlo = __builtin_bit_cast(u32x2, olo), whi = __builtin_bit_cast(u32x2, ohi);
+    *(u32x2*)(wl + ah * kD + ai0) = wlo;
+    *(u32x2*)(wl + ah * kD + ai0 + kD / 2) = whi;
+    if (app_ok && split == 0) {
+      _Float16* qo = app.q_out + ((size_t)row * Hq + g * kG + ah) * kD;
+      *(u32x2*)(qo + ai0) = wlo;
+      *(u32x2*)(qo + ai0 + kD / 2) = whi;
+    }
+    // one wave writes and reads its LDS, in order
+    if (ln < kG) {
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) qb[kd] = *(const half8_t*)(wl + ln * kD + 32 * kd + 8 * lq);
+    }
+    if (app_kv) {
+      // (keeps the key's conversion, and so the wait for its load, after the
+      // pair requests above)
+      asm volatile("" : "+v"(kr0), "+v"(kr1));
+      double o0, o1;
+      rope_pair((double)kr0, (double)kr1, kc.x, kc.y, o0, o1);
+      kv_lds[lane] = store_f64<_Float16>(o0);
+      kv_lds[lane + kD / 2] = store_f64<_Float16>(o1);
+      kv_lds[kD + lane] = vr0;
+      kv_lds[kD + lane + kD / 2] = vr1;
     }
   }
   f32x4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = (f32x4)0.f;
   float m_run = -INFINITY, l_run = 0.f;
+
+  // The fused append's arena write, after everything else the wave does (a
+  // store counts in the same in-order counter as the pair loads, so one issued
+  // before the loop would hold up the later pairs' waits).  Nothing in this
+  // call reads the slot back from memory: the last pair took the new key and
+  // value from LDS.
+  auto store_new_kv = [&]() {
+    if constexpr (kAppend) {
+      if (!app_kv) return;
+      const int nblk = __builtin_amdgcn_readlane(raw_blk, (pos >> 4) - blk0);
+      const int slot = pos & 15;
+      if (nblk >= 0 && nblk < num_blocks) {
+        _Float16* kt = app.k_arena + ((size_t)nblk * Hkv + g) * kBlock * kD;
+        kt[((lane / kX) * kBlock + slot) * kX + lane % kX] = kv_lds[lane];
+        kt[(((lane + kD / 2) / kX) * kBlock + slot) * kX + lane % kX] = kv_lds[lane + kD / 2];
+        _Float16* vt = app.v_arena + ((size_t)nblk * Hkv + g) * kD * kBlock;
+        vt[lane * kBlock + slot] = kv_lds[kD + lane];
+        vt[(lane + kD / 2) * kBlock + slot] = kv_lds[kD + lane + kD / 2];
+      }
+    }
+  };
 
   // Keys past the context exist only in a sequence's last pair.  kMask: 0
   // masks by the position test on every pair (the plain kernel's loop, one
@@ -317,10 +351,11 @@ __device__ __forceinline__ void decode_split_unit(
   // kSB / 2 pairs).  The prefetch is issued unconditionally (past the last
   // pair it re-requests the last pair, a cache hit), so the loads outstanding
   // at each wait are the same on every path and the wait before a pair's MFMAs
-  // covers that pair only, never the prefetch behind it.
+  // covers that pair only, never the prefetch behind it.  (The fused append
+  // has requested the second pair already.)
 #pragma unroll
   for (int p = 0; p < kSB / 2; ++p) {
-    if (p + 1 < kSB / 2) {
+    if (p + 1 < kSB / 2 && !(kAppend && p == 0)) {
       int ba, bb;
       pair_ids(min(p + 1, npairs - 1), ba, bb);
       buf[(p + 1) & 1] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
@@ -339,8 +374,8 @@ __device__ __forceinline__ void decode_split_unit(
     // registers: key row `slot` of its block, and the value element of key
     // slot in lane group slot >> 2.
     Pair& last = buf[(kSB / 2 - 1) & 1];
-    if (app_ok && split == nsplit - 1) {
-      const int pos = L - 1, slot = pos & 15, ab = ((pos >> 4) - blk0) & 1;
+    if (app_kv) {
+      const int slot = pos & 15, ab = ((pos >> 4) - blk0) & 1;
       // (ab and slot are wave-uniform; constant indices keep the pair in registers)
 #pragma unroll
       for (int kd = 0; kd < 4; ++kd) {
@@ -373,6 +408,7 @@ __device__ __forceinline__ void decode_split_unit(
 #pragma unroll
       for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db] * inv;
     }
+    store_new_kv();
     return;
   }
   if (ln < kG) {
@@ -385,6 +421,7 @@ __device__ __forceinline__ void decode_split_unit(
       ws_ml[2 * part + 1] = l_row;
     }
   }
+  store_new_kv();
 }
 
 }  // namespace

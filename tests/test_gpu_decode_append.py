@@ -42,12 +42,18 @@ def edge_lengths():
                            [(L - 1, 1) for L in lens], max_blocks_per_seq=130)
 
 
-def compare(w):
+def compare(w, rope_rows=None):
+    """rope_rows: pass only that many rows of the rotation table to both calls
+    (positions at or past it skip the append)."""
     say(f"{w.name}: separate calls")
     a = harness.DeviceWorkload(w)
+    if rope_rows:
+        a.rope_max_pos = rope_rows
     a.step()
     say(f"{w.name}: fused call")
     b = harness.DeviceWorkload(w)
+    if rope_rows:
+        b.rope_max_pos = rope_rows
     b.decode_append()
     torch.cuda.synchronize()
     assert np.array_equal(bits(a.dec_q), bits(b.dec_q)), "rotated queries differ"
@@ -81,6 +87,20 @@ def test_fused_edges_against_oracle():
         worst = max(worst, float(np.abs(got - exp).max()))
     say(f"{w.name}: max abs error against the oracle {worst:.3e}")
     assert worst <= 2e-3
+
+
+def test_fused_matches_separate_single_splits():
+    """Every context within one split: no combine pass, the split kernel
+    writes the arena."""
+    lens = [1, 7, 16, 33, 200, 383, 384]
+    compare(workloads.build("append_short", 23, "f16", 32, 8, 128, 5.0e5,
+                            [(L - 1, 1) for L in lens], max_blocks_per_seq=24))
+
+
+def test_fused_matches_separate_past_table():
+    """Positions at or past the table's end (rows of 1000 and more, with 1000
+    table rows passed) skip the append in both forms; the rest append."""
+    compare(edge_lengths(), rope_rows=1000)
 
 
 def test_fused_repeated_steps_match():
