@@ -89,6 +89,15 @@ def test_fused_edges_against_oracle():
     assert worst <= 2e-3
 
 
+@pytest.mark.parametrize("hkv,n", [(2, 7), (4, 40)])
+def test_fused_matches_separate_few_heads(hkv, n):
+    """2 or 4 KV heads (4 query heads each): 2- and 4-wave workgroups, a
+    small and a wider batch."""
+    lens = [int(x) for x in np.random.default_rng(hkv).integers(1, 4097, n)]
+    compare(workloads.build(f"append_hkv{hkv}", 29, "f16", 4 * hkv, hkv, 128, 5.0e5,
+                            [(L - 1, 1) for L in lens]))
+
+
 def test_fused_matches_separate_single_splits():
     """Every context within one split: no combine pass, the split kernel
     writes the arena."""

@@ -172,6 +172,13 @@ def generic_shape(name, dtype, hq, hkv, d):
     return workloads.build(name, 13, dtype, hq, hkv, d, 1.0e4, seqs, max_blocks_per_seq=24)
 
 
+def few_heads(name, hkv, lens, chunks=()):
+    """The tuned shape (head dim 128, 4 query heads per KV head) with 2 or 4 KV
+    heads: decode rows of the given contexts (and chunk rows (P, C))."""
+    seqs = [(L - 1, 1) for L in lens] + list(chunks)
+    return workloads.build(name, 17, "f16", 4 * hkv, hkv, 128, 5.0e5, seqs)
+
+
 def i8(w):
     """The same workload over INT8 arenas (codes + fp16 scale per head vector)."""
     return dataclasses.replace(w, name=w.name + "_i8", kv_bits=8)
@@ -226,6 +233,12 @@ SMALL = {
     "generic_f16_d256": lambda: generic_shape("generic_f16_d256", "f16", 8, 2, 256),
     "generic_f32_d256": lambda: generic_shape("generic_f32_d256", "f32", 4, 2, 256),
     "generic_i4_d256": lambda: i4(generic_shape("generic_i4_d256", "f16", 8, 2, 256)),
+    # fast paths with 2 or 4 KV heads (2- and 4-wave decode workgroups)
+    "few_heads_hkv2": lambda: few_heads("few_heads_hkv2", 2, [1, 40, 383, 384, 385, 1000, 3001],
+                                        chunks=[(37, 45)]),
+    "few_heads_hkv4_wide": lambda: few_heads(
+        "few_heads_hkv4_wide", 4,
+        [int(x) for x in np.random.default_rng(5).integers(1, 4097, 40)]),
 }
 
 
