@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) v
                                nsplit_max, num_blocks, blockIdx.x, g);
 }
 
-__global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) void decode_split_i4_kernel(
+__global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I4_WAVES_PER_SIMD) void decode_split_i4_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q, const uint8_t* __restrict__ k_arena,
     const uint8_t* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,

@@ -14,7 +14,9 @@ namespace {
 #ifndef PKV_DECODE_I8_AHEAD
 #define PKV_DECODE_I8_AHEAD 1
 #endif
-constexpr int kI8Ahead = PKV_DECODE_I8_AHEAD;  // pairs in flight behind the computed one
+#ifndef PKV_DECODE_I4_AHEAD
+#define PKV_DECODE_I4_AHEAD 1
+#endif
 
 // v_mul_legacy_f32: x * y, except that 0 times anything (NaN, infinity) is 0.
 __device__ float pkv_fmul_legacy(float, float) __asm("llvm.amdgcn.fmul.legacy");
@@ -99,7 +101,10 @@ __device__ inline PairI4 load_pair_i4(const uint8_t* __restrict__ k_arena,
 // of dims block db).
 struct CodesI8 {
   using Pair = PairI8;
+  static constexpr int kAhead = PKV_DECODE_I8_AHEAD;  // pairs in flight behind the computed one
   static constexpr float kPvBoost = 64.f;
+  static constexpr int kDimOrder[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+  static constexpr int kKeyOrder[8] = {0, 1, 2, 3, 4, 5, 6, 7};
   __device__ static Pair load(const uint8_t* k, const uint8_t* v, int a, int b, int Hkv, int g,
                               int ln, int lq) {
     return load_pair_i8(k, v, a, b, Hkv, g, ln, lq);
@@ -112,20 +117,51 @@ struct CodesI8 {
     return codes_to_half(pr.v[db].x, pr.v[db].y);
   }
 };
+// Two nibbles of a word (bits 0-3 and 16-19, or 4-7 and 20-23) as an fp16
+// pair, two instructions: one AND-XOR puts 0x6400 | (n ^ 8) (resp.
+// 0x6400 | (n ^ 8) << 4) in each half -- 1024 + (n + 8), resp. 1024 +
+// 16 (n + 8), n the signed code -- and one packed subtract of 1032 (resp. one
+// exact packed fma: times 1/16, minus 72) leaves n.  Nibbles at bits 8-15 of
+// each half take the word shifted right by 8.
+__device__ inline uint32_t nib_lo(uint32_t w) {
+  const half2_t h = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) ^ 0x64086408u);
+  return __builtin_bit_cast(uint32_t, h - (half2_t)(_Float16)1032.f);
+}
+__device__ inline uint32_t nib_hi(uint32_t w) {
+  const half2_t h = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) ^ 0x64806480u);
+  return __builtin_bit_cast(
+      uint32_t, __builtin_elementwise_fma(h, (half2_t)(_Float16)0.0625f, (half2_t)(_Float16)-72.f));
+}
+
 struct CodesI4 {
+  static constexpr int kAhead = PKV_DECODE_I4_AHEAD;
   static constexpr float kPvBoost = 4.f;
   using Pair = PairI4;
+  // Order of the 8 elements in an MFMA operand register: K operands hold dims
+  // [0, 2, 1, 3, 4, 6, 5, 7] of their 8 (the query operand is loaded in the
+  // same order), V operands keys [0, 2, 4, 6, 1, 3, 5, 7] of the lane's 8
+  // (the weights are placed in the same order): the order in which the
+  // two-instruction conversion above produces them.
+  static constexpr int kDimOrder[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+  static constexpr int kKeyOrder[8] = {0, 2, 4, 6, 1, 3, 5, 7};
   __device__ static Pair load(const uint8_t* k, const uint8_t* v, int a, int b, int Hkv, int g,
                               int ln, int lq) {
     return load_pair_i4(k, v, a, b, Hkv, g, ln, lq);
   }
+  // word w0 (w1): low nibbles dims 0-3 (4-7) of the 16-dim piece, high
+  // nibbles dims 8-11 (12-15); kd odd takes the high nibbles
   __device__ static half8_t kop(const Pair& pr, int u, int kd) {
     const u32x4 c = pr.k[kd >> 1];
-    const uint32_t w0 = u ? c.z : c.x, w1 = u ? c.w : c.y;
-    return (kd & 1) ? nibbles_to_half(w0 >> 4, w1 >> 4) : nibbles_to_half(w0, w1);
+    const uint32_t x0 = u ? c.z : c.x, x1 = u ? c.w : c.y;
+    const uint32_t y0 = x0 >> 8, y1 = x1 >> 8;
+    const u32x4 r = (kd & 1) ? u32x4{nib_hi(x0), nib_hi(y0), nib_hi(x1), nib_hi(y1)}
+                             : u32x4{nib_lo(x0), nib_lo(y0), nib_lo(x1), nib_lo(y1)};
+    return __builtin_bit_cast(half8_t, r);
   }
+  // low nibbles keys 0-3, high nibbles keys 4-7
   __device__ static half8_t vop(const Pair& pr, int db) {
-    return nibbles_to_half(pr.v[db], pr.v[db] >> 4);
+    const uint32_t x = pr.v[db], y = x >> 8;
+    return __builtin_bit_cast(half8_t, u32x4{nib_lo(x), nib_hi(x), nib_lo(y), nib_hi(y)});
   }
 };
 
@@ -137,6 +173,9 @@ struct CodesI4 {
 #endif
 #ifndef PKV_DECODE_I8_WAVES_PER_SIMD
 #define PKV_DECODE_I8_WAVES_PER_SIMD 3
+#endif
+#ifndef PKV_DECODE_I4_WAVES_PER_SIMD
+#define PKV_DECODE_I4_WAVES_PER_SIMD 3
 #endif
 constexpr int kI8WavesPerWG = PKV_DECODE_I8_WAVES_PER_WG;
 
@@ -167,10 +206,13 @@ __device__ __forceinline__ void decode_split_q_unit(
   // dims 16(4(kd >> 1) + lq) + 8(kd & 1) .. +8 of head g*4+ln
   half8_t qb[4];
 #pragma unroll
-  for (int kd = 0; kd < 4; ++kd)
-    qb[kd] = ln < kG ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + ln) * kD +
-                                         16 * (4 * (kd >> 1) + lq) + 8 * (kd & 1))
-                     : (half8_t)(_Float16)0.f;
+  for (int kd = 0; kd < 4; ++kd) {
+    const half8_t x = ln < kG ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + ln) * kD +
+                                                  16 * (4 * (kd >> 1) + lq) + 8 * (kd & 1))
+                              : (half8_t)(_Float16)0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qb[kd][j] = x[Codes::kDimOrder[j]];
+  }
   const int L = min(min(lens[b] + len_add, max_blocks * kBlock), nsplit_max * kDecodeSplit);
   if (L <= 0) {
     if (split == 0 && ln < kG) {
@@ -243,28 +285,35 @@ __device__ __forceinline__ void decode_split_q_unit(
     }
     m_run = m_new;
     const float bias = pv_bias - m_new;
-    half8_t pb;
+    float pe[8];
     float lsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, bias));  // p * boost
-      lsum += pe;
-      // The legacy multiply gives 0 for p = 0 whatever the V scale (past the
-      // end it may be NaN: an unwritten slot), and, unlike a plain multiply,
-      // is never fused with the fp16 conversion: the weight is the fp32
-      // product rounded to fp16 in every kernel that inlines this unit.
-      pb[e] = (_Float16)pkv_fmul_legacy(pe, (float)vsc[e]);
+      pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, bias));  // p * boost
+      lsum += pe[e];
     }
     l_run += lsum;
+    // The legacy multiply gives 0 for p = 0 whatever the V scale (past the end
+    // it may be NaN: an unwritten slot), and, unlike a plain multiply, is
+    // never fused with the fp16 conversion: the weight is the fp32 product
+    // rounded to fp16 in every kernel that inlines this unit.  Element j of
+    // the operand is key kKeyOrder[j], as in the V operand.
+    half8_t pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = Codes::kKeyOrder[j];
+      pb[j] = (_Float16)pkv_fmul_legacy(pe[e], (float)vsc[e]);
+    }
 #pragma unroll
     for (int db = 0; db < 8; ++db)
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Codes::vop(pr, db), pb, o[db], 0, 0, 0);
   };
 
-  // kI8Ahead pairs are kept in flight behind the one being computed (same
+  // kAhead pairs are kept in flight behind the one being computed (same
   // unconditional-prefetch scheme as the fp16 kernel).  One measured best:
-  // two or three cost registers (occupancy 3 -> 2) and ran 4-6% slower.
-  constexpr int kAhead = kI8Ahead;
+  // two or three cost registers (INT8: occupancy 3 -> 2) and ran 4-12%
+  // slower.
+  constexpr int kAhead = Codes::kAhead;
   // pairs whose keys all exist; a partial last pair is left for after the loop
   const bool has_tail = (blk0 + 2 * npairs) * kBlock > L;
   const int n_full = npairs - (has_tail ? 1 : 0);
