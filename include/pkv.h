@@ -285,7 +285,7 @@ pkv_status paged_attention_decode_shared(
  *              PKV_ERR_WORKSPACE if missing or short.
  * A call with fewer than 512 (64-row tile, KV head) work units (its rows
  * packed in whole tiles) splits every tile's keys into `parts` even ranges
- * (up to 8, each at least 512 keys of the longest context) and merges them by
+ * (up to 8, each at least 768 keys of the longest context) and merges them by
  * log-sum-exp, so that small batches with long prefixes fill the chip.  Rows
  * of a split call then round differently (same tolerance) from an unsplit
  * one; paged_attention_chunk_parts() reports the number of parts the tuned

@@ -45,11 +45,21 @@ constexpr int kOrderBuckets = 4096;  // costs at or above the last bucket share 
 constexpr int kRankSortMax = 256;    // item counts ranked directly instead
 // Key-range parts: a call with fewer than kChunkTargetUnits (row tile, KV
 // head) units (two per compute unit of the chip) splits each item's keys into
-// up to kChunkMaxParts parts of at least kChunkMinPartTiles key tiles, merged
-// by chunk_combine_kernel.
-constexpr long kChunkTargetUnits = 512;
+// up to kChunkMaxParts parts of at least kChunkMinPartTiles key tiles (of the
+// longest context), merged by chunk_combine_kernel.  Measured on one GPU's
+// share of a head-split layer (64 units, contexts up to 3632): 7 parts
+// 58.8-59.5 us, 4 parts 52.9-53.1 us, 3 parts 56.8-57.2 us, 2 parts
+// 68.6-69.4 us; on the mixed step's chunk call (128 units) 4 parts 75-77 us
+// against 104-107 us for 2 or 8.
+#ifndef PKV_CHUNK_TARGET_UNITS
+#define PKV_CHUNK_TARGET_UNITS 512
+#endif
+constexpr long kChunkTargetUnits = PKV_CHUNK_TARGET_UNITS;
 constexpr int kChunkMaxParts = 8;
-constexpr int kChunkMinPartTiles = 8;
+#ifndef PKV_CHUNK_MIN_PART_TILES
+#define PKV_CHUNK_MIN_PART_TILES 12
+#endif
+constexpr int kChunkMinPartTiles = PKV_CHUNK_MIN_PART_TILES;
 
 // Schedule of the attention kernel: the (sequence, row tile) items sorted by
 // decreasing work (counting sort on the tile count, or for at most

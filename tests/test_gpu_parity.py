@@ -150,13 +150,13 @@ def small_chunk():
 
 def split_prefix_one():
     """One 128-row chunk after a 6000-token prefix: 16 work units, so the call
-    splits every tile's keys into 8 parts."""
+    splits every tile's keys into 7 parts (one per 768 keys)."""
     return workloads.build("split_prefix_one", 14, "f16", 32, 8, 128, 5.0e5, [(6000, 128)],
                            max_blocks_per_seq=384)
 
 
 def split_prefix_three():
-    """Three short chunks with prefixes of 2000, 40 and 3500 tokens: 7 key parts,
+    """Three short chunks with prefixes of 2000, 40 and 3500 tokens: 4 key parts,
     some of them holding no key of a row (or of a whole short item)."""
     return workloads.build("split_prefix_three", 15, "f16", 32, 8, 128, 5.0e5,
                            [(2000, 64), (40, 20), (3500, 100)], max_blocks_per_seq=226)

@@ -298,14 +298,16 @@ def test_entry_point_errors(lib):
 
 def test_chunk_key_range_parts(lib):
     """A chunk call with fewer than 512 (64-row tile, KV head) units splits each
-    tile's keys into ceil(512 / units) parts, at most 8 and at most one per 512
+    tile's keys into ceil(512 / units) parts, at most 8 and at most one per 768
     keys of the longest context; the workspace then holds the parts' partials."""
     g = _geom()   # Hq 32, Hkv 8, head_dim 128, fp16: the tuned path
     parts = lambda T, ctx, geom=g: pkv.paged_attention_chunk_parts(geom, 4, T, ctx)
     assert parts(4096, 4096) == 1           # 64 tiles x 8 heads = 512 units
     assert parts(1024, 8192) == 4           # 128 units
     assert parts(64, 32768) == 8            # 8 units: capped at 8
-    assert parts(64, 1500) == 2             # at least 512 keys per part
+    assert parts(64, 1600) == 2             # at least 768 keys per part
+    assert parts(64, 1500) == 1
+    assert parts(256, 3632) == 4            # 64 units (one KV head)
     assert parts(100, 500) == 1             # too short to split
     assert parts(1024, 8192, _geom(dtype=1)) == 1     # generic path
     # workspace of a split call: schedule, then o [parts][T][Hq][D] and (m, l)
