@@ -110,8 +110,8 @@ def bench_decode(torch, args, kv_bits=0):
     fp16 arenas the step is one paged_attention_decode_append call (the new
     tokens' append fused into the decode), and the same step as two calls
     (kv_append_rope then paged_attention_decode) and the decode call alone are
-    timed beside it (--separate-append swaps the two forms); quantized arenas
-    take the two calls."""
+    timed beside it (--separate-append swaps the two forms); for quantized
+    arenas the step is the two calls, with the fused call timed beside it."""
     import dataclasses
     from paged_kv_chunked_amd import harness, workloads
     w = workloads.decode_batch()
@@ -172,6 +172,12 @@ def bench_decode(torch, args, kv_bits=0):
         extra["decode_append_bytes"] = dw.decode_append_bytes()
     else:
         extra["ms_decode_call"] = ms_kernel
+
+        def fus(i):
+            k, v = layers[i % len(layers)]
+            dw.decode_append(k_arena=k, v_arena=v)
+
+        extra["ms_per_step_fused_call"] = time_back_to_back(torch, fus, args.steps)
     return w, dw, ms_step, ms_kernel, ms_call, nbytes, extra
 
 
@@ -664,7 +670,8 @@ def main():
         out["swap"] = bench_swap(torch, dw)
         log(f"swap: {out['swap']}")
     for bits in (() if args.no_int8 else (8, 4)):
-        _, dwq, ms_stepq, ms_decq, ms_dcallq, nbytesq, _ = bench_decode(torch, args, kv_bits=bits)
+        _, dwq, ms_stepq, ms_decq, ms_dcallq, nbytesq, qextra = bench_decode(torch, args,
+                                                                            kv_bits=bits)
         achq = nbytesq / (ms_decq * 1e-3) / 1e9
         tokens = int(sum(dwq.dec_lens_host))
         log(f"decode int{bits}: kernel {ms_decq:.4f} ms, {nbytesq / 1e6:.1f} MB -> {achq:.0f} GB/s")
@@ -674,6 +681,7 @@ def main():
             "context_tokens_per_s": round(tokens / (ms_decq * 1e-3), 1),
             "speedup_vs_fp16_arena": round(ms_dec_call / ms_decq, 3),
             "ms_per_step": round(ms_stepq, 5),
+            "ms_per_step_fused_call": round(qextra["ms_per_step_fused_call"], 5),
             "roofline": {
                 "kernel": f"paged_attention_decode (decode_split_i{bits}_kernel + "
                           "decode_combine_kernel)",

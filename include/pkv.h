@@ -200,7 +200,8 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
  * position L - 1, L = context_lens[b], is appended as kv_append_rope does
  * (q[b] and k[b] rotated by RoPE at L - 1 in fp64 and rounded once to fp16;
  * the rotated q to q_out[b]; the rotated k and v[b] to the arena at block
- * bt[b][(L-1)/16], slot (L-1)%16), and out[b] is paged_attention_decode's
+ * bt[b][(L-1)/16], slot (L-1)%16, quantized with their scales for INT8 / INT4
+ * arenas), and out[b] is paged_attention_decode's
  * result over positions 0 .. L-1 with the rotated q.  Outputs, q_out and the
  * arena bytes are bit for bit those of kv_append_rope (cu_q_lens = 0..num_seqs,
  * chunk_start = L - 1) followed by paged_attention_decode.
@@ -208,8 +209,9 @@ pkv_status paged_attention_decode(const pkv_geom* geom, void* out, int32_t out_d
  * token per sequence: q [num_seqs][Hq][D], k, v [num_seqs][Hkv][D], read only;
  * q_out [num_seqs][Hq][D] must not overlap q (PKV_ERR_RANGE).  The workspace
  * is paged_attention_decode's (paged_attention_decode_workspace_bytes()).
- * fp16 arenas with head_dim 128 and 4 query heads per KV head only
- * (PKV_ERR_DTYPE / PKV_ERR_SHAPE otherwise).  A position at or past
+ * fp16, INT8 and INT4 arenas with head_dim 128 and 4 query heads per KV
+ * head only (PKV_ERR_DTYPE for fp32 arenas, PKV_ERR_SHAPE for other shapes).
+ * A position at or past
  * rope_max_pos skips the append and leaves q unrotated for the attention.
  * ------------------------------------------------------------------------- */
 pkv_status paged_attention_decode_append(const pkv_geom* geom, void* out, int32_t out_dtype,

@@ -89,7 +89,7 @@ pkv_status paged_attention_decode_append(const pkv_geom* geom, void* out, int32_
   pkv_status st = check_geom(geom);
   if (st != PKV_OK) return st;
   if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
-  if (geom->dtype != PKV_F16) return PKV_ERR_DTYPE;
+  if (geom->dtype == PKV_F32) return PKV_ERR_DTYPE;
   if (!pkv::decode_fast_path(*geom)) return PKV_ERR_SHAPE;
   if (num_seqs < 0) return PKV_ERR_RANGE;
   if (num_seqs == 0) return PKV_OK;

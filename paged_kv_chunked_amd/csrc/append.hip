@@ -11,6 +11,7 @@
 // stored values are exactly determined by the inputs.
 #include "fp16_shape.h"
 #include "pkv_internal.h"
+#include "quant_append_core.h"
 #include "rope_core.h"
 
 namespace pkv {
@@ -297,28 +298,6 @@ __global__ __launch_bounds__(kThreads) void append_rope_vec_kernel(
     put_v(idx, v[ktok + idx]);
 }
 
-// Group quantization of one (token, KV head) vector, Kshipra part 3 section
-// 2's codec: scale s = fp16(fp32(amax) / 127) (floored at the smallest
-// positive fp16), codes round-half-even(fp32(x) / fp32(s)) -- the same fp16
-// scale used to encode and to decode.  One wave per vector; lane l holds
-// elements l, l + 64, l + 128, l + 192 (those below D).
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
-
-__device__ inline _Float16 group_scale(float amax) {
-  const _Float16 s = (_Float16)(amax / 127.f);
-  const _Float16 smin = __builtin_bit_cast(_Float16, (uint16_t)1);  // 2^-24
-  return s < smin ? smin : s;
-}
-
-__device__ inline int8_t encode8(float x, float s) {
-  const float r = __builtin_rintf(x / s);
-  return (int8_t)fminf(fmaxf(r, -127.f), 127.f);
-}
-
 // kv_append_rope for INT8 arenas (q, k, v fp16).  Tile of one (block, head):
 // K codes [D/16][16][16] then 16 fp16 scales; V codes [D][16] then 16 fp16
 // scales.  k is rotated and rounded to fp16 exactly as for an fp16 arena, then
@@ -352,72 +331,13 @@ __global__ __launch_bounds__(kThreads) void append_rope_i8_kernel(
   constexpr int kWaves = kThreads / 64;
   // K: wave w quantizes heads w, w + kWaves, ...; lane l rotates the pairs
   // (l, l + half) and (l + 64, l + 64 + half) that exist
-  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
-    const _Float16* kp = k + ((size_t)t * Hkv + h) * D;
-    float x[4];
-    float amax = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = lane + 64 * u;
-      x[2 * u] = x[2 * u + 1] = 0.f;
-      if (i < half) {
-        const double2 c = row[i];
-        double o0, o1;
-        rope_pair((double)kp[i], (double)kp[i + half], c.x, c.y, o0, o1);
-        x[2 * u] = (float)store_f64<_Float16>(o0);
-        x[2 * u + 1] = (float)store_f64<_Float16>(o1);
-        amax = fmaxf(amax, fmaxf(fabsf(x[2 * u]), fabsf(x[2 * u + 1])));
-      }
-    }
-    const _Float16 sh = group_scale(wave_max(amax));
-    const float s = (float)sh;
-    uint8_t* tile = k_arena + ((size_t)blk * Hkv + h) * tile_bytes;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = lane + 64 * u;
-      if (i < half) {
-        const int d0 = i, d1 = i + half;
-        tile[(d0 >> 4) * 256 + i8_kpos(slot) * 16 + (d0 & 15)] = (uint8_t)encode8(x[2 * u], s);
-        tile[(d1 >> 4) * 256 + i8_kpos(slot) * 16 + (d1 & 15)] = (uint8_t)encode8(x[2 * u + 1], s);
-      }
-    }
-    if (lane == 0) *(_Float16*)(tile + (size_t)kBlock * D + 2 * slot) = sh;
-  }
+  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves)
+    append_k_i8(k + ((size_t)t * Hkv + h) * D, row, k_arena + ((size_t)blk * Hkv + h) * tile_bytes,
+                slot, D, lane);
   // V: lane l holds elements l, l + 64, l + 128, l + 192
-  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
-    const _Float16* vp = v + ((size_t)t * Hkv + h) * D;
-    float x[4];
-    float amax = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = lane + 64 * u;
-      x[u] = d < D ? (float)vp[d] : 0.f;
-      amax = fmaxf(amax, fabsf(x[u]));
-    }
-    const _Float16 sh = group_scale(wave_max(amax));
-    const float s = (float)sh;
-    uint8_t* tile = v_arena + ((size_t)blk * Hkv + h) * tile_bytes;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = lane + 64 * u;
-      if (d < D) tile[d * kBlock + slot] = (uint8_t)encode8(x[u], s);
-    }
-    if (lane == 0) *(_Float16*)(tile + (size_t)kBlock * D + 2 * slot) = sh;
-  }
-}
-
-// Group quantization to 4 bits: s = fp16(fp32(amax) / 7) (floored at the
-// smallest positive fp16), codes in [-7, 7] stored as two's-complement
-// nibbles.
-__device__ inline _Float16 group_scale4(float amax) {
-  const _Float16 s = (_Float16)(amax / 7.f);
-  const _Float16 smin = __builtin_bit_cast(_Float16, (uint16_t)1);  // 2^-24
-  return s < smin ? smin : s;
-}
-
-__device__ inline int encode4(float x, float s) {
-  const float r = __builtin_rintf(x / s);
-  return (int)fminf(fmaxf(r, -7.f), 7.f);
+  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves)
+    append_v_i8(v + ((size_t)t * Hkv + h) * D, v_arena + ((size_t)blk * Hkv + h) * tile_bytes,
+                slot, D, lane);
 }
 
 // kv_append_rope for INT4 arenas.  K: byte i of a key's 8-byte record in a
@@ -451,90 +371,21 @@ __global__ __launch_bounds__(kThreads) void append_rope_i4_kernel(
   qr.finish(q, q_out, row, D);
   if (blk < 0 || blk >= num_blocks) return;
   const size_t tile_bytes = i4_tile_bytes(D);
-  const size_t codes = (size_t)kBlock * D / 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   constexpr int kWaves = kThreads / 64;
-  const int krec = i4_krec(slot);
-  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
-    const _Float16* kp = k + ((size_t)t * Hkv + h) * D;
-    float x[4];
-    float amax = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = lane + 64 * u;
-      x[2 * u] = x[2 * u + 1] = 0.f;
-      if (i < half) {
-        const double2 c = row[i];
-        double o0, o1;
-        rope_pair((double)kp[i], (double)kp[i + half], c.x, c.y, o0, o1);
-        x[2 * u] = (float)store_f64<_Float16>(o0);
-        x[2 * u + 1] = (float)store_f64<_Float16>(o1);
-        amax = fmaxf(amax, fmaxf(fabsf(x[2 * u]), fabsf(x[2 * u + 1])));
-      }
-    }
-    const _Float16 sh = group_scale4(wave_max(amax));
-    const float s = (float)sh;
-    uint8_t* tile = k_arena + ((size_t)blk * Hkv + h) * tile_bytes;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = lane + 64 * u;
-      const int c0 = i < half ? encode4(x[2 * u], s) : 0;
-      const int c1 = i < half ? encode4(x[2 * u + 1], s) : 0;
-      const int p0 = __shfl_down(c0, 8), p1 = __shfl_down(c1, 8);  // dims i + 8, i + 8 + half
-      if (i < half && (i & 8) == 0) {  // half is a multiple of 16: i + half has bit 3 clear too
-        const int d0 = i, d1 = i + half;
-        tile[(d0 >> 4) * 128 + krec * 8 + (d0 & 7)] = (uint8_t)((c0 & 15) | ((p0 & 15) << 4));
-        tile[(d1 >> 4) * 128 + krec * 8 + (d1 & 7)] = (uint8_t)((c1 & 15) | ((p1 & 15) << 4));
-      }
-    }
-    if (lane == 0) *(_Float16*)(tile + codes + 2 * slot) = sh;
-  }
+  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves)
+    append_k_i4(k + ((size_t)t * Hkv + h) * D, row, k_arena + ((size_t)blk * Hkv + h) * tile_bytes,
+                slot, D, lane);
   // V: the token sharing this token's bytes, and which of the two writes them
   const int C = min(cu_q_lens[b + 1], num_tokens) - row0;
   const int ppos = pos ^ 4;
   const bool partner_in = ppos >= P && ppos < P + C;
   const bool leader = (pos & 4) == 0 || !partner_in;
   const int tp = t + (ppos - pos);
-  const int vhigh = i4_vhigh(slot);
-  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves) {
-    const _Float16* vp = v + ((size_t)t * Hkv + h) * D;
-    float x[4];
-    float amax = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = lane + 64 * u;
-      x[u] = d < D ? (float)vp[d] : 0.f;
-      amax = fmaxf(amax, fabsf(x[u]));
-    }
-    const _Float16 sh = group_scale4(wave_max(amax));
-    const float s = (float)sh;
-    uint8_t* tile = v_arena + ((size_t)blk * Hkv + h) * tile_bytes;
-    if (lane == 0) *(_Float16*)(tile + codes + 2 * slot) = sh;
-    if (!leader) continue;  // the partner's workgroup writes the shared bytes
-    float y[4] = {0.f, 0.f, 0.f, 0.f};
-    float sp = 1.f;
-    if (partner_in) {
-      const _Float16* pp = v + ((size_t)tp * Hkv + h) * D;
-      float pmax = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int d = lane + 64 * u;
-        y[u] = d < D ? (float)pp[d] : 0.f;
-        pmax = fmaxf(pmax, fabsf(y[u]));
-      }
-      sp = (float)group_scale4(wave_max(pmax));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = lane + 64 * u;
-      if (d >= D) continue;
-      uint8_t* at = tile + i4_vbyte(d, slot, D);
-      const int own = encode4(x[u], s) & 15;
-      // the other nibble: the partner's code, or what the byte holds already
-      const int other = partner_in ? (encode4(y[u], sp) & 15) : (vhigh ? (*at & 15) : (*at >> 4));
-      *at = (uint8_t)(vhigh ? (other | (own << 4)) : (own | (other << 4)));
-    }
-  }
+  for (int h = sl * kWaves + wave; h < Hkv; h += S * kWaves)
+    append_v_i4(v + ((size_t)t * Hkv + h) * D,
+                partner_in ? v + ((size_t)tp * Hkv + h) * D : nullptr, leader,
+                v_arena + ((size_t)blk * Hkv + h) * tile_bytes, slot, D, lane);
 }
 
 }  // namespace

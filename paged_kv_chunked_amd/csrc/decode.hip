@@ -281,6 +281,34 @@ __global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I4_WAVES_PER_SIMD) v
                                nsplit_max, num_blocks, blockIdx.x, g);
 }
 
+// The fused decode step over INT8 / INT4 arenas: the same split units, each
+// wave rotating its query at L - 1 (split 0 writing it out), the last split's
+// wave quantizing the new key and value into the arena before it reads its
+// pairs (decode_split_q_unit with kAppend).
+__global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I8_WAVES_PER_SIMD) void decode_split_append_i8_kernel(
+    float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    uint8_t* k_arena, uint8_t* v_arena, const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks, DecodeAppend app) {
+  const int g = blockIdx.z * kI8WavesPerWG + (threadIdx.x >> 6);
+  if (g >= Hkv) return;
+  decode_split_q_unit<CodesI8, true>(out, ws_o, ws_ml, nullptr, k_arena, v_arena, block_table,
+                                     max_blocks, blockIdx.y, blockIdx.y, context_lens, 0,
+                                     scale_log2, Hkv, nsplit_max, num_blocks, blockIdx.x, g, app);
+}
+
+__global__ __launch_bounds__(64 * kI8WavesPerWG, PKV_DECODE_I4_WAVES_PER_SIMD) void decode_split_append_i4_kernel(
+    float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    uint8_t* k_arena, uint8_t* v_arena, const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ context_lens, float scale_log2, int Hkv, int nsplit_max,
+    int num_blocks, DecodeAppend app) {
+  const int g = blockIdx.z * kI8WavesPerWG + (threadIdx.x >> 6);
+  if (g >= Hkv) return;
+  decode_split_q_unit<CodesI4, true>(out, ws_o, ws_ml, nullptr, k_arena, v_arena, block_table,
+                                     max_blocks, blockIdx.y, blockIdx.y, context_lens, 0,
+                                     scale_log2, Hkv, nsplit_max, num_blocks, blockIdx.x, g, app);
+}
+
 // Log-sum-exp merge of the splits of one (sequence b, query head h):
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 // One wave per query head (the 4 heads of KV head g form a workgroup), each
@@ -517,6 +545,19 @@ hipError_t launch_decode_append(const pkv_geom& g, float* out, const void* q, vo
   app.rope = (const double2*)rope_table;
   app.rope_max_pos = rope_max_pos;
   const float scale_log2 = scale * 1.4426950408889634f;
+  if (g.dtype == PKV_I8KV || g.dtype == PKV_I4KV) {
+    const int wpg8 = g.num_kv_heads < kI8WavesPerWG ? g.num_kv_heads : kI8WavesPerWG;
+    const dim3 grid8(nsplit | 1, num_seqs, (g.num_kv_heads + kI8WavesPerWG - 1) / kI8WavesPerWG);
+    hipLaunchKernelGGL(g.dtype == PKV_I8KV ? decode_split_append_i8_kernel
+                                           : decode_split_append_i4_kernel,
+                       grid8, dim3(64 * wpg8), 0, stream, out, ws_o, ws_ml, (uint8_t*)k_arena,
+                       (uint8_t*)v_arena, block_table, max_blocks, context_lens, scale_log2,
+                       g.num_kv_heads, nsplit, g.num_blocks, app);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit <= 1) return e;
+    return launch_decode_combine(g, out, ws_o, ws_ml, context_lens, nullptr, 0, max_blocks,
+                                 num_seqs, nsplit, stream);
+  }
   const int wpg = g.num_kv_heads < kDecodeWavesPerWG ? g.num_kv_heads : kDecodeWavesPerWG;
   const int zg = (g.num_kv_heads + kDecodeWavesPerWG - 1) / kDecodeWavesPerWG;
   const dim3 grid(nsplit | 1, num_seqs, zg);  // odd width: see launch_decode

@@ -6,6 +6,7 @@
 #include <type_traits>
 
 #include "decode_core.h"
+#include "quant_append_core.h"
 #include "quant_codes.h"
 
 namespace pkv {
@@ -101,6 +102,13 @@ __device__ inline PairI4 load_pair_i4(const uint8_t* __restrict__ k_arena,
 // of dims block db).
 struct CodesI8 {
   using Pair = PairI8;
+  static constexpr size_t kTile = i8_tile_bytes(kD);
+  // the fused append: the new key and value of one (token, head) into the tiles
+  __device__ static void append(const _Float16* kp, const _Float16* vp, const double2* row,
+                                uint8_t* kt, uint8_t* vt, int slot, int lane) {
+    append_k_i8(kp, row, kt, slot, kD, lane);
+    append_v_i8(vp, vt, slot, kD, lane);
+  }
   static constexpr int kAhead = PKV_DECODE_I8_AHEAD;  // pairs in flight behind the computed one
   static constexpr float kPvBoost = 64.f;
   static constexpr int kDimOrder[8] = {0, 1, 2, 3, 4, 5, 6, 7};
@@ -135,6 +143,14 @@ __device__ inline uint32_t nib_hi(uint32_t w) {
 
 struct CodesI4 {
   static constexpr int kAhead = PKV_DECODE_I4_AHEAD;
+  static constexpr size_t kTile = i4_tile_bytes(kD);
+  // (one token per sequence: the byte partner slot ^ 4 is never appended by
+  // the same call, so the new nibble merges with the stored one)
+  __device__ static void append(const _Float16* kp, const _Float16* vp, const double2* row,
+                                uint8_t* kt, uint8_t* vt, int slot, int lane) {
+    append_k_i4(kp, row, kt, slot, kD, lane);
+    append_v_i4(vp, nullptr, true, vt, slot, kD, lane);
+  }
   static constexpr float kPvBoost = 4.f;
   using Pair = PairI4;
   // Order of the 8 elements in an MFMA operand register: K operands hold dims
@@ -181,15 +197,21 @@ constexpr int kI8WavesPerWG = PKV_DECODE_I8_WAVES_PER_WG;
 
 // Split `split` of sequence b (its block-table row and its partials in the
 // workspace) for KV head g, one wave; the query and output live at packed row
-// `row` and the context length is lens[b] + len_add.
-template <class Codes>
+// `row` and the context length is lens[b] + len_add.  kAppend (the fused
+// decode step): the query is app.q rotated here at pos = L - 1 (split 0
+// writes it to app.q_out), and the wave of the sequence's last split first
+// quantizes the new key and value into the arena with kv_append_rope's code
+// and waits for those stores before it requests any pair, so its loads read
+// them back; the outputs, the rotated queries and the arena bytes are those
+// of kv_append_rope followed by the plain decode.
+template <class Codes, bool kAppend = false>
 __device__ __forceinline__ void decode_split_q_unit(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q,
     const uint8_t* __restrict__ k_arena, const uint8_t* __restrict__ v_arena,
     const int32_t* __restrict__ block_table, int max_blocks, int b, int row,
     const int32_t* __restrict__ lens, int len_add, float scale_log2, int Hkv, int nsplit_max,
-    int num_blocks, int split, int g) {
+    int num_blocks, int split, int g, DecodeAppend app = DecodeAppend{}) {
   // No contraction of a multiply and an add into one fma at the compiler's
   // choice: the decode kernel and the mixed kernel inline this unit into
   // different code and must round every step alike (the one fma wanted is
@@ -207,9 +229,10 @@ __device__ __forceinline__ void decode_split_q_unit(
   half8_t qb[4];
 #pragma unroll
   for (int kd = 0; kd < 4; ++kd) {
-    const half8_t x = ln < kG ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + ln) * kD +
-                                                  16 * (4 * (kd >> 1) + lq) + 8 * (kd & 1))
-                              : (half8_t)(_Float16)0.f;
+    const half8_t x = !kAppend && ln < kG
+                          ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + ln) * kD +
+                                              16 * (4 * (kd >> 1) + lq) + 8 * (kd & 1))
+                          : (half8_t)(_Float16)0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) qb[kd][j] = x[Codes::kDimOrder[j]];
   }
@@ -227,7 +250,68 @@ __device__ __forceinline__ void decode_split_q_unit(
   const int nb = min(kSB, nb_seq - blk0);
   const int nsplit = (nb_seq + kSB - 1) / kSB;
   const int npairs = (nb + 1) >> 1;
+  [[maybe_unused]] const int raw_blk = my_blk;  // (unclamped, for the fused append's write)
   if (lane >= nb || my_blk < 0 || my_blk >= num_blocks) my_blk = 0;
+
+  if constexpr (kAppend) {
+    // The query: lane l rotates pairs 4 (l & 15) .. +3 of head l >> 4 of the
+    // wave's group (fp64, one rounding: kv_append_rope's arithmetic) into the
+    // wave's LDS, and the operand lanes read their pieces in the order above.
+    // A position outside the table leaves the query as given and skips the
+    // append, as kv_append_rope does.
+    const int pos = L - 1;
+    const bool app_ok = pos < app.rope_max_pos;
+    const double2* rrow = app.rope + (size_t)min(pos, app.rope_max_pos - 1) * (kD / 2);
+    __shared__ _Float16 qapp_lds[kI8WavesPerWG][kG * kD];
+    _Float16* wl = qapp_lds[threadIdx.x >> 6];
+    {
+      const int h = lane >> 4, i0 = 4 * (lane & 15);
+      const _Float16* qs = app.q + ((size_t)row * Hq + g * kG + h) * kD;
+      const half4_t lo = *(const half4_t*)(qs + i0), hi = *(const half4_t*)(qs + i0 + kD / 2);
+      half4_t olo = lo, ohi = hi;
+      if (app_ok) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const double2 c = rrow[i0 + r];
+          double o0, o1;
+          rope_pair((double)lo[r], (double)hi[r], c.x, c.y, o0, o1);
+          olo[r] = store_f64<_Float16>(o0);
+          ohi[r] = store_f64<_Float16>(o1);
+        }
+      }
+      const u32x2 wlo = __builtin_bit_cast(u32x2, olo), whi = __builtin_bit_cast(u32x2, ohi);
+      *(u32x2*)(wl + h * kD + i0) = wlo;
+      *(u32x2*)(wl + h * kD + i0 + kD / 2) = whi;
+      if (app_ok && split == 0) {
+        _Float16* qo = app.q_out + ((size_t)row * Hq + g * kG + h) * kD;
+        *(u32x2*)(qo + i0) = wlo;
+        *(u32x2*)(qo + i0 + kD / 2) = whi;
+      }
+    }
+    // one wave writes and reads its LDS, in order
+    if (ln < kG) {
+#pragma unroll
+      for (int kd = 0; kd < 4; ++kd) {
+        const half8_t x = *(const half8_t*)(wl + ln * kD + 16 * (4 * (kd >> 1) + lq) + 8 * (kd & 1));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qb[kd][j] = x[Codes::kDimOrder[j]];
+      }
+    }
+    // The new key and value (the last split holds their block).  The tiles
+    // are addressed from the arena pointers the pairs are read through, and
+    // every store has completed before the first pair is requested.
+    if (app_ok && split == nsplit - 1) {
+      const int nblk = __builtin_amdgcn_readlane(raw_blk, (pos >> 4) - blk0);
+      if (nblk >= 0 && nblk < num_blocks) {
+        const size_t tile = ((size_t)nblk * Hkv + g) * Codes::kTile;
+        Codes::append(app.k + ((size_t)b * Hkv + g) * kD, app.v + ((size_t)b * Hkv + g) * kD,
+                      rrow, const_cast<uint8_t*>(k_arena) + tile,
+                      const_cast<uint8_t*>(v_arena) + tile, pos & 15, lane);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+  }
 
   f32x4 o[8];
 #pragma unroll

@@ -340,8 +340,8 @@ class DeviceWorkload:
 
     def decode_append(self, stream=None, k_arena=None, v_arena=None):
         """The decode rows' append and attention in one paged_attention_decode_append
-        call (fp16 arenas; every step row a decode): the same q rotation, arena
-        writes and outputs as append() followed by decode()."""
+        call (fp16, INT8 or INT4 arenas; every step row a decode): the same q
+        rotation, arena writes and outputs as append() followed by decode()."""
         self._need_split()
         if self.chunk_rows:
             raise ValueError("decode_append covers steps of decode rows only")

@@ -35,7 +35,7 @@ CSRC = os.path.join(HERE, "csrc")
 
 # kernel call -> (kernel symbol substrings, source files whose change invalidates it)
 _DECODE_SRC = ("decode.hip", "decode_core.h", "decode_q_core.h", "fp16_shape.h", "pkv_internal.h",
-               "quant_codes.h", "rope_core.h")
+               "quant_codes.h", "quant_append_core.h", "rope_core.h")
 _CHUNK_SRC = ("chunk.hip", "chunk_core.h", "fp16_shape.h", "pkv_internal.h", "quant_codes.h")
 CALLS = {
     "paged_attention_decode": (("decode_split_kernel", "decode_combine_kernel"), _DECODE_SRC),
@@ -55,9 +55,10 @@ CALLS = {
                                   _CHUNK_SRC),
     "paged_attention_mixed": (("mixed_kernel", "mixed_order_kernel"),
                               ("mixed.hip", "chunk_core.h", "decode_core.h", "decode_q_core.h",
-                               "fp16_shape.h", "pkv_internal.h", "quant_codes.h")),
+                               "fp16_shape.h", "pkv_internal.h", "quant_codes.h",
+                               "quant_append_core.h", "rope_core.h")),
     "kv_append_rope": (("append_rope_kernel", "append_rope_vec_kernel"),
-                       ("append.hip", "rope_core.h", "pkv_internal.h")),
+                       ("append.hip", "rope_core.h", "quant_append_core.h", "pkv_internal.h")),
 }
 
 

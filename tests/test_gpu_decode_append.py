@@ -1,7 +1,9 @@
 """paged_attention_decode_append (the decode step's append and attention in one
 call) against kv_append_rope followed by paged_attention_decode, on the same
-seeded workloads: outputs, rotated queries and K/V arena bytes bit for bit;
-and the fused call's outputs against the oracle on the edge-length batch."""
+seeded workloads over fp16, INT8 and INT4 arenas: outputs, rotated queries and
+K/V arena bytes bit for bit; and the fused call's outputs against the oracle on
+the edge-length batch."""
+import dataclasses
 import os
 
 import numpy as np
@@ -31,7 +33,14 @@ def say(msg):
 
 def bits(t):
     a = t.cpu().numpy()
+    if a.dtype == np.uint8:
+        return a
     return a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+def quant(w, kv_bits):
+    """The same workload over INT8 / INT4 arenas (kv_bits 0: fp16)."""
+    return dataclasses.replace(w, name=f"{w.name}_i{kv_bits}", kv_bits=kv_bits) if kv_bits else w
 
 
 def edge_lengths():
@@ -64,8 +73,9 @@ def compare(w, rope_rows=None):
     return b
 
 
-def test_fused_matches_separate_decode_batch():
-    compare(workloads.decode_batch())
+@pytest.mark.parametrize("kv_bits", [0, 8, 4])
+def test_fused_matches_separate_decode_batch(kv_bits):
+    compare(quant(workloads.decode_batch(), kv_bits))
 
 
 def test_fused_matches_separate_shard():
@@ -73,8 +83,9 @@ def test_fused_matches_separate_shard():
     compare(workloads.tp8_decode_batch())
 
 
-def test_fused_edges_against_oracle():
-    w = edge_lengths()
+@pytest.mark.parametrize("kv_bits", [0, 8, 4])
+def test_fused_edges_against_oracle(kv_bits):
+    w = quant(edge_lengths(), kv_bits)
     b = compare(w)
     st = oscript.run_script(w, materialize=True)
     q_rot = oscript.append_step(w, st)
@@ -98,18 +109,20 @@ def test_fused_matches_separate_few_heads(hkv, n):
                             [(L - 1, 1) for L in lens]))
 
 
-def test_fused_matches_separate_single_splits():
+@pytest.mark.parametrize("kv_bits", [0, 8, 4])
+def test_fused_matches_separate_single_splits(kv_bits):
     """Every context within one split: no combine pass, the split kernel
     writes the arena."""
     lens = [1, 7, 16, 33, 200, 383, 384]
-    compare(workloads.build("append_short", 23, "f16", 32, 8, 128, 5.0e5,
-                            [(L - 1, 1) for L in lens], max_blocks_per_seq=24))
+    compare(quant(workloads.build("append_short", 23, "f16", 32, 8, 128, 5.0e5,
+                                  [(L - 1, 1) for L in lens], max_blocks_per_seq=24), kv_bits))
 
 
-def test_fused_matches_separate_past_table():
+@pytest.mark.parametrize("kv_bits", [0, 8, 4])
+def test_fused_matches_separate_past_table(kv_bits):
     """Positions at or past the table's end (rows of 1000 and more, with 1000
     table rows passed) skip the append in both forms; the rest append."""
-    compare(edge_lengths(), rope_rows=1000)
+    compare(quant(edge_lengths(), kv_bits), rope_rows=1000)
 
 
 def test_fused_repeated_steps_match():

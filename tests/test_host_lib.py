@@ -279,9 +279,13 @@ def test_entry_point_errors(lib):
                    FAKE, 0, FAKE, need, None) == 4             # no RoPE positions
     assert dec_app(FAKE, 1, A, B, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000, 0.1,
                    FAKE, 4096, FAKE, need - 1, None) == 5      # workspace too small
-    assert lib.paged_attention_decode_append(ctypes.byref(_geom(dtype=2)), FAKE, 1, A, B, FAKE,
+    assert lib.paged_attention_decode_append(ctypes.byref(_geom(dtype=1)), FAKE, 1, A, B, FAKE,
                                              FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3, 1000, 0.1,
-                                             FAKE, 4096, FAKE, need, None) == 3   # INT8 arena
+                                             FAKE, 4096, FAKE, need, None) == 3   # fp32 arena
+    assert lib.paged_attention_decode_append(ctypes.byref(_geom(dtype=2, num_q_heads=16)), FAKE,
+                                             1, A, B, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 3,
+                                             1000, 0.1, FAKE, 4096, FAKE, need,
+                                             None) == 2        # INT8, group 2: not the fast path
     assert dec_app(None, 1, None, None, None, None, None, None, None, 4, None, 0, 64, 0.1,
                    None, 1, None, 0, None) == 0                # empty batch
     # chunk: the schedule, one int32 per (sequence, 64-row tile)
