@@ -298,6 +298,132 @@ __global__ __launch_bounds__(kThreads) void append_rope_vec_kernel(
     put_v(idx, v[ktok + idx]);
 }
 
+// kv_append_rope for batches of long chunks (fp16, head dims whose halves are
+// whole 16-byte pieces, at most kBlockSeqs sequences): one workgroup per
+// (sequence, arena block) the call writes, so that a block filled whole by the
+// call is written as whole lines -- each K piece's 16 slots (256 bytes) and
+// each value row's 16 slots (32 bytes, eight rows per thread) together --
+// instead of each token writing 2-byte pieces of 48 lines per head.  Blocks
+// the call fills in part (a sequence's first and last) write the slots they
+// hold, as the per-token kernel does.  The same arithmetic as
+// append_rope_vec_kernel, so the same bytes.
+constexpr int kBlockSeqs = 64;
+#ifndef PKV_APPEND_BLOCK_SLICES
+#define PKV_APPEND_BLOCK_SLICES 4
+#endif
+constexpr int kBlockSlices = PKV_APPEND_BLOCK_SLICES;  // workgroups per block
+__global__ __launch_bounds__(kThreads) void append_rope_block_kernel(
+    const _Float16* q, _Float16* q_out, const _Float16* __restrict__ k,
+    const _Float16* __restrict__ v, _Float16* __restrict__ k_arena, _Float16* __restrict__ v_arena,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ chunk_start,
+    int num_seqs, int num_tokens, const double2* __restrict__ cs, int rope_max_pos,
+    int num_blocks, int Hq, int Hkv, int D) {
+  constexpr int x = 8;  // fp16 elements per 16-byte piece
+  typedef _Float16 vecT __attribute__((ext_vector_type(x)));
+  const int lane = threadIdx.x & 63, w = blockIdx.x;
+  // workgroup slice sl of S takes items sl * kThreads + i, + S * kThreads, ...
+  const int first = blockIdx.y * kThreads + threadIdx.x, stride = gridDim.y * kThreads;
+  // the sequences' block ranges, one sequence per lane (every wave alike)
+  int row0 = 0, C = 0, P = 0, nblk = 0;
+  if (lane < num_seqs) {
+    row0 = cu_q_lens[lane];
+    C = min(cu_q_lens[lane + 1], num_tokens) - row0;
+    P = chunk_start[lane];
+    if (C > 0) nblk = ((P + C - 1) >> 4) - (P >> 4) + 1;
+  }
+  int incl = nblk;  // inclusive prefix sum over the lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  const int excl = incl - nblk;
+  const unsigned long long m = __ballot(lane < num_seqs && nblk > 0 && excl <= w && w < incl);
+  if (m == 0) return;  // past the call's blocks
+  const int sb = __ffsll((long long)m) - 1;
+  const int b_row0 = __builtin_amdgcn_readlane(row0, sb);
+  const int b_C = __builtin_amdgcn_readlane(C, sb), b_P = __builtin_amdgcn_readlane(P, sb);
+  const int j = (b_P >> 4) + (w - __builtin_amdgcn_readlane(excl, sb));
+  // positions of this block the call holds, as the per-token kernel accepts them
+  const int pos_lo = max(max(b_P, 16 * j), 0);
+  const int pos_hi = min(min(b_P + b_C, 16 * j + 16), rope_max_pos);
+  if (j < 0 || j >= max_blocks || pos_lo >= pos_hi) return;
+  const int s_lo = pos_lo - 16 * j, s_hi = pos_hi - 16 * j, ns = s_hi - s_lo;
+  const int t_lo = b_row0 + (pos_lo - b_P);  // token of slot s_lo
+  const int half = D >> 1, cph = half / x;
+  const int blk = block_table[(size_t)__builtin_amdgcn_readfirstlane(sb) * max_blocks + j];
+  auto rotate = [&](vecT lo, vecT hi, const double2* row, int c, vecT& olo, vecT& ohi) {
+#pragma unroll
+    for (int e = 0; e < x; ++e) {
+      const double2 r = row[c * x + e];
+      double o0, o1;
+      rope_pair((double)lo[e], (double)hi[e], r.x, r.y, o0, o1);
+      olo[e] = store_f64<_Float16>(o0);
+      ohi[e] = store_f64<_Float16>(o1);
+    }
+  };
+  // q (in place allowed: each piece is read and written by one thread)
+  if (q != nullptr) {
+    const int nq = ns * Hq * cph;
+    for (int idx = first; idx < nq; idx += stride) {
+      const int st = idx / (Hq * cph), r = idx - st * (Hq * cph);
+      const int h = r / cph, c = r - h * cph;
+      const size_t off = ((size_t)(t_lo + st) * Hq + h) * D + c * x;
+      const vecT lo = *(const vecT*)(q + off), hi = *(const vecT*)(q + off + half);
+      vecT olo, ohi;
+      rotate(lo, hi, cs + (size_t)(pos_lo + st) * half, c, olo, ohi);
+      *(vecT*)(q_out + off) = olo;
+      *(vecT*)(q_out + off + half) = ohi;
+    }
+  }
+  if (blk < 0 || blk >= num_blocks) return;
+  // K: item (head h, piece c, slot s), slot fastest, so a wave writes whole
+  // 256-byte runs [c][0..16][x] of a tile
+  for (int idx = first; idx < Hkv * cph * 16; idx += stride) {
+    const int s = idx & 15, hc = idx >> 4, h = hc / cph, c = hc - h * cph;
+    if (s < s_lo || s >= s_hi) continue;
+    const size_t off = ((size_t)(t_lo + s - s_lo) * Hkv + h) * D + c * x;
+    const vecT lo = *(const vecT*)(k + off), hi = *(const vecT*)(k + off + half);
+    vecT olo, ohi;
+    rotate(lo, hi, cs + (size_t)(16 * j + s) * half, c, olo, ohi);
+    _Float16* tile = k_arena + ((size_t)blk * Hkv + h) * kBlock * D;  // [D/x][16][x]
+    *(vecT*)(tile + (c * kBlock + s) * x) = olo;
+    *(vecT*)(tile + ((c + cph) * kBlock + s) * x) = ohi;
+  }
+  // V tile [D][16]
+  if (ns == kBlock) {
+    // whole block: item (head h, 8 dims from 8 g); the thread reads the 16
+    // tokens' 8 values and writes the 8 rows of 16 slots
+    for (int idx = first; idx < Hkv * (D / x); idx += stride) {
+      const int h = idx / (D / x), g8 = idx - h * (D / x);
+      vecT col[kBlock];
+#pragma unroll
+      for (int s = 0; s < kBlock; ++s)
+        col[s] = *(const vecT*)(v + ((size_t)(t_lo + s) * Hkv + h) * D + g8 * x);
+      _Float16* vt = v_arena + (((size_t)blk * Hkv + h) * D + g8 * x) * kBlock;
+#pragma unroll
+      for (int e = 0; e < x; ++e) {
+        vecT r0, r1;
+#pragma unroll
+        for (int s = 0; s < x; ++s) {
+          r0[s] = col[s][e];
+          r1[s] = col[s + x][e];
+        }
+        *(vecT*)(vt + e * kBlock) = r0;
+        *(vecT*)(vt + e * kBlock + x) = r1;
+      }
+    }
+  } else {
+    // the slots this call holds: item (head h, dim d, slot s), slot fastest
+    for (int idx = first; idx < Hkv * D * ns; idx += stride) {
+      const int st = idx % ns, hd = idx / ns, h = hd / D, d = hd - h * D;
+      v_arena[(((size_t)blk * Hkv + h) * D + d) * kBlock + s_lo + st] =
+          v[((size_t)(t_lo + st) * Hkv + h) * D + d];
+    }
+  }
+}
+
 // kv_append_rope for INT8 arenas (q, k, v fp16).  Tile of one (block, head):
 // K codes [D/16][16][16] then 16 fp16 scales; V codes [D][16] then 16 fp16
 // scales.  k is rotated and rounded to fp16 exactly as for an fp16 arena, then
@@ -420,6 +546,18 @@ hipError_t launch_append_rope(const pkv_geom& g, const void* q, void* q_out, con
     return hipGetLastError();
   }
   const bool vec = (g.head_dim / 2) % (g.dtype == PKV_F16 ? 8 : 4) == 0;
+  // batches of long chunks: one workgroup per (sequence, arena block)
+  if (g.dtype == PKV_F16 && vec && num_seqs <= kBlockSeqs && num_tokens >= 512 &&
+      num_tokens >= 32 * num_seqs) {
+    const int nwg = num_tokens / kBlock + 2 * num_seqs;
+    hipLaunchKernelGGL(append_rope_block_kernel, dim3(nwg, kBlockSlices), block, 0, stream,
+                       (const _Float16*)q, (_Float16*)q_out, (const _Float16*)k,
+                       (const _Float16*)v, (_Float16*)k_arena, (_Float16*)v_arena, block_table,
+                       max_blocks, cu_q_lens, chunk_start, num_seqs, num_tokens,
+                       (const double2*)rope_table, rope_max_pos, g.num_blocks, g.num_q_heads,
+                       g.num_kv_heads, g.head_dim);
+    return hipGetLastError();
+  }
   if (g.dtype == PKV_F16 && vec) {
     hipLaunchKernelGGL(append_rope_vec_kernel<_Float16>, grid, block, 0, stream,
                        (const _Float16*)q, (_Float16*)q_out, (const _Float16*)k,
