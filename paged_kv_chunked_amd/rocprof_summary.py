@@ -90,19 +90,35 @@ def split_clusters(durs, ratio=1.5):
     return groups + [cur]
 
 
-def stats(db, out, command, notes=()):
-    """One line per (kernel, grid): launches of one kernel on different
-    workloads have different grids and are kept apart.  A (kernel, grid) whose
-    launch durations fall into clusters more than 1.5x apart is listed once per
-    cluster (grid marked #1, #2, ... from the shortest)."""
+def stats_rows(rows, min_calls=5):
+    """(kernel, grid) -> launch durations, from (name, gx, gy, gz, duration)
+    rows.  Launches of one kernel on different workloads have different grids
+    and are kept apart; a (kernel, grid) whose durations fall into clusters
+    more than 1.5x apart is listed once per cluster (grid marked #1, #2, ...
+    from the shortest).  Grids with fewer than min_calls launches (set-up work
+    such as cache fills of varying size) are folded into one row per kernel,
+    "other grids (n)"."""
     raw = collections.defaultdict(list)
-    for name, gx, gy, gz, dur in kernel_rows(db):
+    for name, gx, gy, gz, dur in rows:
         raw[(name, f"{gx}x{gy}x{gz}")].append(dur)
-    agg = {}
+    agg, rest = {}, collections.defaultdict(list)
+    nrest = collections.Counter()
     for (name, grid), durs in raw.items():
+        if len(durs) < min_calls:
+            rest[name] += durs
+            nrest[name] += 1
+            continue
         groups = split_clusters(durs)
         for i, grp in enumerate(groups):
             agg[(name, grid if len(groups) == 1 else f"{grid} #{i + 1}")] = grp
+    for name, durs in rest.items():
+        agg[(name, f"other grids ({nrest[name]})")] = durs
+    return agg
+
+
+def stats(db, out, command, notes=()):
+    """The kernel statistics table of a kernel trace (rows as stats_rows)."""
+    agg = stats_rows(kernel_rows(db))
     lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", ""]
     lines += [f"- {n}" for n in notes] + ([""] if notes else [])
     lines += ["| kernel | grid (threads) | calls | avg (us) | min (us) | max (us) | total (ms) |",

@@ -70,3 +70,16 @@ def test_counters_derive_mfma_busy_and_flops(tmp_path):
     assert short["mfma_f16_flop"] == 2.0e6 * 512
     assert short["mfma_f16_flop_over_algorithmic"] == 2.0e6 * 512 / 1.0e9
     assert ks[1]["mfma_busy_pct"] == 12.5 and "mfma_f16_flop_over_algorithmic" not in ks[1]
+
+
+def test_stats_rows_fold_rare_grids():
+    """Timed kernels keep one row per grid; set-up launches whose grids recur
+    fewer than five times fold into one row per kernel."""
+    rows = [("decode", 5632, 64, 1, 100_000 + i) for i in range(20)]
+    rows += [("append", 256 * n, 1, 1, 3_000) for n in range(1, 40)]    # fills: one launch each
+    rows += [("append", 1024, 4, 1, 30_000) for _ in range(10)]          # the timed append
+    agg = rs.stats_rows(rows)
+    assert sorted(agg) == [("append", "1024x4x1"), ("append", "other grids (39)"),
+                           ("decode", "5632x64x1")]
+    assert len(agg[("append", "other grids (39)")]) == 39
+    assert len(agg[("decode", "5632x64x1")]) == 20
