@@ -92,17 +92,15 @@ __device__ __forceinline__ void decode_shared_unit(
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ group_start, const int32_t* __restrict__ row_skip,
     float scale_log2, int Hkv, int nsplit_max, int num_blocks, int zheads, int num_seqs,
-    int nsx8, int quads, int i) {
-  // Workgroup i = ((group * zheads + z) * quads + quad) * nsx8 + split, nsx8
-  // a multiple of 8: workgroups are dealt to the 8 XCDs by linear id mod 8,
-  // and the shared units come first in the grid, so every quad (and group)
-  // reading split s runs on XCD s mod 8, close in time, and the split's blocks
-  // come from HBM into that XCD's L2 once.
-  const int split = i % nsx8;
-  i /= nsx8;
-  const int quad = i % quads;
-  i /= quads;
-  const int zh = i % zheads, gi = i / zheads;
+    int nshared, int quads, int u) {
+  // Unit u = ((group * zheads + z) * nshared + split) * quads + quad: the 16
+  // quads of a split are consecutive units (the kernel deals them to one or
+  // two XCDs, whose L2s then fetch the split's blocks from HBM once each).
+  const int quad = u % quads;
+  u /= quads;
+  const int split = u % nshared;
+  u /= nshared;
+  const int zh = u % zheads, gi = u / zheads;
   const int g = zh * kDecodeWavesPerWG + (threadIdx.x >> 6);
   if (g >= Hkv) return;
   // rows of the group, clamped to the batch (a bad table cannot address
@@ -201,35 +199,64 @@ __device__ __forceinline__ void decode_shared_unit(
   }
 }
 
-// One launch for a batch with shared splits: workgroups [0, n_shared) run the
-// shared units (decode_shared_unit), the rest the per-row splits of
-// decode_split_kernel's grid (split fastest, then row, then KV-head group),
-// skipping each row's shared splits.  Both kinds run side by side: either
-// alone is a chain of up to 12 dependent pairs per wave with little of the
-// chip busy when groups are few.  Every unit runs the code of the separate
-// kernels, so partials and outputs are those of paged_attention_decode.  All
-// its K/V loads are cached (the split kernel streams): the shared units' 16
-// quads per split and the rows' own splits that still hold the end of the
-// shared prompt read the same blocks close in time.
+// One launch for a batch with shared splits: the shared units
+// (decode_shared_unit) first, then every row's own splits (those from its
+// skip on), run as decode_split_kernel runs them.  Both kinds run side by
+// side: either alone is a chain of up to 12 dependent pairs per wave with
+// little of the chip busy when groups are few.  Every unit runs the code of
+// the separate kernels, so partials and outputs are those of
+// paged_attention_decode.  All its K/V loads are cached (the split kernel
+// streams): the shared units' 16 quads per split and the rows' own splits
+// that still hold the end of the shared prompt read the same blocks close in
+// time.
+//
+// Grid order.  Workgroups are handed out in linear-id order, id i to XCD
+// i mod 8, and an XCD with no free compute unit holds up the hand-out of
+// every later workgroup (measured: with the shared units' XCD set to
+// split mod 8, the two XCDs drawing two splits each were full, and every
+// own-split workgroup, ids after them, started only when their shared units
+// ended, serialising the two kinds).  So:
+//   * the first n0 = num_seqs * zheads workgroups take every row's first
+//     own split (a whole split unless the row ends in it);
+//   * the next 8 per (per = ceil(n_shared / 8)) take the shared units, the
+//     i-th of them unit (i mod 8) * per + i / 8: each XCD runs a run of
+//     consecutive units, i.e. an even share, and a split's quads fall on one
+//     or two XCDs;
+//   * the rest take own split k >= 1 of row b for KV-head group z in the
+//     order (k, z, b), b fastest; the index space's tail (k past a row's
+//     splits) only exits.
+// When the units outnumber the compute units, the ones left waiting are
+// rows' later own splits, which end a row and are mostly short, and they
+// wait for the first unit of their XCD to end, typically such a short one
+// (measured on 160 shared and ~113 own units: shared units first left 1-4
+// full-length own splits per XCD waiting a whole unit, 49 us; this order
+// lets them start within a few microseconds).
 __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_shared_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
     const _Float16* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
     const int32_t* __restrict__ row_skip, float scale_log2, int Hkv, int nsplit_max,
-    int num_blocks, int zheads, int num_seqs, int nsx8, int quads, int n_shared, int gx) {
-  const int i = blockIdx.x;
-  if (i < n_shared) {
-    decode_shared_unit(ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, group_start,
-                       row_skip, scale_log2, Hkv, nsplit_max, num_blocks, zheads, num_seqs, nsx8,
-                       quads, i);
-    return;
+    int num_blocks, int zheads, int num_seqs, int nshared, int quads, int n_shared, int per) {
+  const int n0 = num_seqs * zheads;
+  int j = blockIdx.x;
+  if (j >= n0) {
+    const int i = j - n0;
+    if (i < 8 * per) {
+      const int u = (i & 7) * per + (i >> 3);
+      if (u < n_shared)
+        decode_shared_unit(ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, group_start,
+                           row_skip, scale_log2, Hkv, nsplit_max, num_blocks, zheads, num_seqs,
+                           nshared, quads, u);
+      return;
+    }
+    j = i - 8 * per + n0;
   }
-  const int j = i - n_shared;
-  const int split = j % gx, rest = j / gx;
-  const int b = rest % num_seqs, z = rest / num_seqs;
+  const int b = j % num_seqs, rest = j / num_seqs;
+  const int z = rest % zheads, k = rest / zheads;
   const int g = z * kDecodeWavesPerWG + (threadIdx.x >> 6);
-  if (g >= Hkv || split < row_skip[b]) return;
+  const int split = min(max(row_skip[b], 0), nsplit_max) + k;
+  if (g >= Hkv || split >= nsplit_max) return;
   decode_split_unit<false>(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, b, b,
                     context_lens, 0, scale_log2, Hkv, nsplit_max, num_blocks, split, g);
 }
@@ -487,15 +514,16 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
                       groups->num_groups > 0 && groups->max_skip > 0 && groups->max_group_size > 0;
   if (shared) {
     const int quads = (groups->max_group_size + 3) / 4;
-    const int nsx8 = (min(groups->max_skip, nsplit) + 7) / 8 * 8;
-    const long n_shared = (long)nsx8 * quads * zg * groups->num_groups;
-    const long nwg = n_shared + (long)gx * num_seqs * zg;
+    const int nshared = min(groups->max_skip, nsplit);
+    const long n_shared = (long)nshared * quads * zg * groups->num_groups;
+    const long per = (n_shared + 7) / 8;
+    const long nwg = 8 * per + (long)nsplit * num_seqs * zg;
     if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(decode_shared_kernel, dim3((unsigned)nwg), dim3(64 * wpg), 0, stream, out,
                        ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
                        (const _Float16*)v_arena, block_table, max_blocks, context_lens,
                        groups->group_start, groups->row_skip, scale_log2, g.num_kv_heads, nsplit,
-                       g.num_blocks, zg, num_seqs, nsx8, quads, (int)n_shared, gx);
+                       g.num_blocks, zg, num_seqs, nshared, quads, (int)n_shared, (int)per);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_combine(g, out, ws_o, ws_ml, context_lens, nullptr, 0, max_blocks,
