@@ -8,6 +8,7 @@
 #include <type_traits>
 
 #include "fp16_shape.h"
+#include "lds_dma.h"
 #include "quant_codes.h"
 
 namespace pkv {
@@ -54,21 +55,6 @@ __device__ inline float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
-}
-
-// One 16-byte direct-to-LDS load per lane: lane i's 16 bytes from `src` land
-// at LDS byte address lds + 16 i.  Issued from asm so that the compiler does
-// not drain the vector-memory counter before every LDS read; the kernel waits
-// for these loads itself (wait_vm) before the barrier that publishes a tile.
-__device__ inline void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
-}
-template <int N>
-__device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 // How far (log2 units) a row's running maximum may lag the true maximum before

@@ -40,6 +40,7 @@
 
 #include "decode_core.h"
 #include "decode_q_core.h"
+#include "lds_dma.h"
 
 namespace pkv {
 namespace {
@@ -86,36 +87,105 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
 // the partials -- and the merged output -- are bit for bit those of
 // paged_attention_decode.  All keys of a shared split are real (a member's
 // own token comes after the shared prefix), so there is no mask.
+//
+// A shared workgroup serves kHeads KV heads x kQuads quads of one shared split
+// (kWaves = kHeads * kQuads waves; wave w: head slot w / kQuads, quad slot
+// w % kQuads).  Each pair of blocks of its heads travels once from memory into
+// a kStages-deep LDS ring (direct-to-LDS loads, kDma per wave and pair) and
+// every quad's wave reads its operands from there, into the registers and
+// layouts the per-row kernel loads them to; the quads of a head share one
+// read from L2 instead of each fetching it.  Stage layout, per head slot:
+// the K tiles of blocks A and B as in the arena, then the V tiles of A and B
+// as [16-dim group][8-key half][dim & 15] (16-byte units), so that a wave's
+// 8-byte V reads (keys 4 lq .. 4 lq + 3 of dims 16 db + ln) cover 256
+// contiguous bytes per 32 lanes.
+template <int kWaves>
+struct SharedGeom {
+  static constexpr int kQuads = kWaves < 4 ? kWaves : 4;
+  static constexpr int kHeads = kWaves / kQuads;
+  static constexpr int kTile = kBlock * kD * 2;  // one (block, KV head) K or V tile
+  static constexpr int kStage = kHeads * 4 * kTile;
+  static constexpr int kStages = kWaves >= 4 ? 4 : 3;
+  static constexpr int kLds = kStages * kStage;
+  static constexpr int kDma = kStage / 1024 / kWaves;  // 1 KiB per load instruction
+  static_assert(kDma * 1024 * kWaves == kStage, "whole loads per wave");
+  static_assert(kLds <= 160 * 1024, "fits a CU's LDS");
+};
+
+// LDS byte offset, within a stage, of the V unit (dim, half) of tile slot t
+// (4 * head slot + 2 + block); the load side places source unit
+// 2 * dim + half there.
+__host__ __device__ constexpr int shared_v_unit(int dim, int half) {
+  return ((dim >> 4) * 32 + half * 16 + (dim & 15)) * 16;
+}
+
+// Every staged load lands inside the LDS array, and every operand read of a
+// stage stays inside the tile it means to read.
+template <int kWaves>
+constexpr bool shared_lds_in_bounds() {
+  using SG = SharedGeom<kWaves>;
+  for (int st = 0; st < SG::kStages; ++st)
+    for (int w = 0; w < kWaves; ++w)
+      for (int e = 0; e < SG::kDma; ++e) {
+        const int n = w * SG::kDma + e, t = n >> 2;
+        if (t >= 4 * SG::kHeads) return false;
+        const int at = st * SG::kStage + t * SG::kTile + (n & 3) * 1024;
+        if (at < 0 || at + 64 * 16 > SG::kLds) return false;
+      }
+  for (int lq = 0; lq < 4; ++lq)
+    for (int ln = 0; ln < 16; ++ln) {
+      for (int kd = 0; kd < 4; ++kd) {
+        const int off = ((4 * kd + lq) * kBlock + ln) * 16;
+        if (off < 0 || off + 16 > SG::kTile) return false;
+      }
+      for (int db = 0; db < 8; ++db) {
+        const int off = shared_v_unit(16 * db + ln, lq >> 1) + 8 * (lq & 1);
+        if (off < 0 || off + 8 > SG::kTile) return false;
+      }
+    }
+  return true;
+}
+static_assert(shared_lds_in_bounds<1>() && shared_lds_in_bounds<2>() &&
+                  shared_lds_in_bounds<4>() && shared_lds_in_bounds<8>(),
+              "shared decode LDS layout");
+
+template <int kWaves>
 __device__ __forceinline__ void decode_shared_unit(
-    float* __restrict__ ws_o, float* __restrict__ ws_ml, const _Float16* __restrict__ q,
-    const _Float16* __restrict__ k_arena, const _Float16* __restrict__ v_arena,
-    const int32_t* __restrict__ block_table, int max_blocks,
+    u32x4* __restrict__ lds, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
+    const _Float16* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ group_start, const int32_t* __restrict__ row_skip,
-    float scale_log2, int Hkv, int nsplit_max, int num_blocks, int zheads, int num_seqs,
-    int nshared, int quads, int u) {
-  // Unit u = ((group * zheads + z) * nshared + split) * quads + quad: the 16
-  // quads of a split are consecutive units (the kernel deals them to one or
-  // two XCDs, whose L2s then fetch the split's blocks from HBM once each).
-  const int quad = u % quads;
-  u /= quads;
+    float scale_log2, int Hkv, int nsplit_max, int num_blocks, int hgroups, int num_seqs,
+    int nshared, int qgroups, int u) {
+  using SG = SharedGeom<kWaves>;
+  // Unit u = ((group * hgroups + hgroup) * nshared + split) * qgroups + qgroup:
+  // the workgroups of a split are consecutive units (the kernel deals them to
+  // one or two XCDs, whose L2s then fetch the split's blocks once each).
+  const int qg = u % qgroups;
+  u /= qgroups;
   const int split = u % nshared;
   u /= nshared;
-  const int zh = u % zheads, gi = u / zheads;
-  const int g = zh * kDecodeWavesPerWG + (threadIdx.x >> 6);
-  if (g >= Hkv) return;
+  const int hg = u % hgroups, gi = u / hgroups;
   // rows of the group, clamped to the batch (a bad table cannot address
-  // memory outside the buffers)
+  // memory outside the buffers); the group's skip is the same for all waves
   const int r0 = max(0, group_start[gi]), r1 = min(num_seqs, group_start[gi + 1]);
-  const int first = r0 + 4 * quad;
-  if (first >= r1) return;
+  if (r0 >= r1) return;
   const int skip = min(row_skip[r0], nsplit_max);
   if (split >= skip) return;
+  // From here on every wave runs the whole loop (it holds barriers); a wave
+  // whose head or rows do not exist computes on clamped inputs and stores
+  // nothing.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hs = wave / SG::kQuads, quad = qg * SG::kQuads + wave % SG::kQuads;
+  const int g = hg * SG::kHeads + hs;
+  const bool head_ok = g < Hkv;
   const int lane = threadIdx.x & 63;
   const int ln = lane & 15, lq = lane >> 4;
   const int Hq = Hkv * kG;
   const int blk0 = split * kSB;
+  const int first = r0 + 4 * quad;
   const int row = first + (ln >> 2);  // this column's sequence
-  const bool col_ok = row < r1;
+  const bool col_ok = head_ok && row < r1;
   int my_blk = 0;
   if (lane < kSB && blk0 + lane < max_blocks)
     my_blk = block_table[(size_t)r0 * max_blocks + blk0 + lane];  // the group's shared blocks
@@ -125,7 +195,36 @@ __device__ __forceinline__ void decode_shared_unit(
   for (int kd = 0; kd < 4; ++kd)
     qb[kd] = col_ok ? *(const half8_t*)(q + ((size_t)row * Hq + g * kG + (ln & 3)) * kD + 32 * kd + 8 * lq)
                     : (half8_t)(_Float16)0.f;
+  // the queries and block ids are in before the first tile load (the
+  // compiler does not see those loads; its waits would otherwise cover them)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   constexpr int npairs = kSB / 2;  // a shared split is whole
+
+  // Loads of pair p into stage p % kStages: load n of the stage (1 KiB) is
+  // quarter n & 3 of tile slot n >> 2 (head slot t >> 2; K A, K B, V A, V B);
+  // wave w issues loads w * kDma .. +kDma.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)lds;
+  auto issue = [&](int p) {
+    const int stage = p % SG::kStages;
+    const int ba = __builtin_amdgcn_readlane(my_blk, 2 * p), bb = __builtin_amdgcn_readlane(my_blk, 2 * p + 1);
+#pragma unroll
+    for (int e = 0; e < SG::kDma; ++e) {
+      const int n = wave * SG::kDma + e;
+      const int t = n >> 2, quarter = n & 3;
+      const int gl = min(hg * SG::kHeads + (t >> 2), Hkv - 1);  // clamped head of the slot
+      const int kind = t & 3;
+      const int blk = (kind & 1) ? bb : ba;
+      const _Float16* tile = (kind < 2 ? k_arena : v_arena) + ((size_t)blk * Hkv + gl) * (kBlock * kD);
+      const int pos = quarter * 64 + lane;  // 16-byte unit of the staged tile
+      int src = pos;                        // K: as in the arena
+      if (kind >= 2) {                      // V: [dim group][half][dim & 15]
+        const int dim = (pos >> 5) * 16 + (pos & 15), half = (pos >> 4) & 1;
+        src = 2 * dim + half;
+      }
+      dma16(tile + 8 * src,
+            __builtin_amdgcn_readfirstlane(lds_base + stage * SG::kStage + t * SG::kTile + quarter * 1024));
+    }
+  };
 
   f32x4 o[8];
 #pragma unroll
@@ -135,11 +234,11 @@ __device__ __forceinline__ void decode_shared_unit(
   auto compute = [&](const Pair& pr) {
     f32x4 s[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      s[u] = (f32x4)0.f;
+    for (int u2 = 0; u2 < 2; ++u2) {
+      s[u2] = (f32x4)0.f;
 #pragma unroll
       for (int kd = 0; kd < 4; ++kd)
-        s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr.k[u][kd], qb[kd], s[u], 0, 0, 0);
+        s[u2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr.k[u2][kd], qb[kd], s[u2], 0, 0, 0);
     }
     // same rounding steps as decode_split_kernel: max of raw scores scaled
     // once, exponent fma(score, scale_log2, -m)
@@ -171,17 +270,43 @@ __device__ __forceinline__ void decode_shared_unit(
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr.v[db], pb, o[db], 0, 0, 0);
   };
 
-  Pair buf[2];
-  buf[0] = load_pair<false>(k_arena, v_arena, __builtin_amdgcn_readlane(my_blk, 0),
-                     __builtin_amdgcn_readlane(my_blk, 1), Hkv, g, ln, lq);
+  // The operands of pair p from its stage, in load_pair's registers and order.
+  auto read_pair = [&](int p) {
+    const char* st = (const char*)lds + (p % SG::kStages) * SG::kStage + 4 * hs * SG::kTile;
+    Pair pr;
+#pragma unroll
+    for (int kd = 0; kd < 4; ++kd) {
+      const int off = ((4 * kd + lq) * kBlock + ln) * 16;
+      pr.k[0][kd] = *(const half8_t*)(st + off);
+      pr.k[1][kd] = *(const half8_t*)(st + SG::kTile + off);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int off = shared_v_unit(16 * db + ln, lq >> 1) + 8 * (lq & 1);
+      const u32x2 lo = *(const u32x2*)(st + 2 * SG::kTile + off);
+      const u32x2 hi = *(const u32x2*)(st + 3 * SG::kTile + off);
+      pr.v[db] = __builtin_bit_cast(half8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
+    }
+    return pr;
+  };
+
+#pragma unroll
+  for (int p = 0; p < SG::kStages - 1; ++p)
+    if (p < npairs) issue(p);
 #pragma unroll
   for (int p = 0; p < npairs; ++p) {
-    if (p + 1 < npairs) {
-      buf[(p + 1) & 1] = load_pair<false>(k_arena, v_arena, __builtin_amdgcn_readlane(my_blk, 2 * p + 2),
-                                   __builtin_amdgcn_readlane(my_blk, 2 * p + 3), Hkv, g, ln, lq);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    compute(buf[p & 1]);
+    // this wave's loads of pair p are in (pairs p + 1 .. p + kStages - 2 may
+    // be in flight); after the barrier every wave's are, and every wave is
+    // done reading pair p - 1, whose stage the next load reuses
+    constexpr int kAhead = SG::kStages - 2;
+    const int inflight = min(kAhead, npairs - 1 - p);
+    if (inflight >= 2) wait_vm<2 * SG::kDma>();
+    else if (inflight == 1) wait_vm<SG::kDma>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (p + SG::kStages - 1 < npairs) issue(p + SG::kStages - 1);
+    compute(read_pair(p));
   }
 
   float l_row = l_run;
@@ -200,15 +325,14 @@ __device__ __forceinline__ void decode_shared_unit(
 }
 
 // One launch for a batch with shared splits: the shared units
-// (decode_shared_unit) first, then every row's own splits (those from its
-// skip on), run as decode_split_kernel runs them.  Both kinds run side by
-// side: either alone is a chain of up to 12 dependent pairs per wave with
-// little of the chip busy when groups are few.  Every unit runs the code of
-// the separate kernels, so partials and outputs are those of
-// paged_attention_decode.  All its K/V loads are cached (the split kernel
-// streams): the shared units' 16 quads per split and the rows' own splits
-// that still hold the end of the shared prompt read the same blocks close in
-// time.
+// (decode_shared_unit) and every row's own splits (those from its skip on),
+// run as decode_split_kernel runs them.  Both kinds run side by side: either
+// alone is a chain of up to 12 dependent pairs per wave with little of the
+// chip busy when groups are few.  Every unit runs the code of the separate
+// kernels, so partials and outputs are those of paged_attention_decode.  All
+// its K/V loads are cached (the split kernel streams): the shared units of a
+// split and the rows' own splits that still hold the end of the shared prompt
+// read the same blocks close in time.
 //
 // Grid order.  Workgroups are handed out in linear-id order, id i to XCD
 // i mod 8, and an XCD with no free compute unit holds up the hand-out of
@@ -220,24 +344,24 @@ __device__ __forceinline__ void decode_shared_unit(
 //     own split (a whole split unless the row ends in it);
 //   * the next 8 per (per = ceil(n_shared / 8)) take the shared units, the
 //     i-th of them unit (i mod 8) * per + i / 8: each XCD runs a run of
-//     consecutive units, i.e. an even share, and a split's quads fall on one
-//     or two XCDs;
+//     consecutive units, i.e. an even share, and a split's workgroups fall
+//     on one or two XCDs;
 //   * the rest take own split k >= 1 of row b for KV-head group z in the
 //     order (k, z, b), b fastest; the index space's tail (k past a row's
 //     splits) only exits.
 // When the units outnumber the compute units, the ones left waiting are
 // rows' later own splits, which end a row and are mostly short, and they
-// wait for the first unit of their XCD to end, typically such a short one
-// (measured on 160 shared and ~113 own units: shared units first left 1-4
-// full-length own splits per XCD waiting a whole unit, 49 us; this order
-// lets them start within a few microseconds).
-__global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) void decode_shared_kernel(
+// wait for the first unit of their XCD to end.
+template <int kWaves>
+__global__ __launch_bounds__(64 * kWaves, PKV_DECODE_WAVES_PER_SIMD) void decode_shared_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     const _Float16* __restrict__ q, const _Float16* __restrict__ k_arena,
     const _Float16* __restrict__ v_arena, const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
     const int32_t* __restrict__ row_skip, float scale_log2, int Hkv, int nsplit_max,
-    int num_blocks, int zheads, int num_seqs, int nshared, int quads, int n_shared, int per) {
+    int num_blocks, int zheads, int num_seqs, int nshared, int hgroups, int qgroups,
+    int n_shared, int per) {
+  __shared__ u32x4 lds[SharedGeom<kWaves>::kLds / 16];
   const int n0 = num_seqs * zheads;
   int j = blockIdx.x;
   if (j >= n0) {
@@ -245,16 +369,16 @@ __global__ __launch_bounds__(64 * kDecodeWavesPerWG, PKV_DECODE_WAVES_PER_SIMD) 
     if (i < 8 * per) {
       const int u = (i & 7) * per + (i >> 3);
       if (u < n_shared)
-        decode_shared_unit(ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, group_start,
-                           row_skip, scale_log2, Hkv, nsplit_max, num_blocks, zheads, num_seqs,
-                           nshared, quads, u);
+        decode_shared_unit<kWaves>(lds, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks,
+                                   group_start, row_skip, scale_log2, Hkv, nsplit_max, num_blocks,
+                                   hgroups, num_seqs, nshared, qgroups, u);
       return;
     }
     j = i - 8 * per + n0;
   }
   const int b = j % num_seqs, rest = j / num_seqs;
   const int z = rest % zheads, k = rest / zheads;
-  const int g = z * kDecodeWavesPerWG + (threadIdx.x >> 6);
+  const int g = z * kWaves + (threadIdx.x >> 6);
   const int split = min(max(row_skip[b], 0), nsplit_max) + k;
   if (g >= Hkv || split >= nsplit_max) return;
   decode_split_unit<false>(out, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks, b, b,
@@ -509,21 +633,31 @@ hipError_t launch_decode(const pkv_geom& g, float* out, const void* q, const voi
   // index across all XCDs; the extra column of workgroups exits at once.
   const int gx = nsplit | 1;
   const dim3 grid(gx, num_seqs, zg);
-  // shared splits (fp16 arenas; other dtypes compute every split per row)
+  // shared splits (fp16 arenas whose workgroup holds 1, 2, 4 or 8 KV heads;
+  // other dtypes and widths compute every split per row, the same result)
   const bool shared = groups != nullptr && g.dtype == PKV_F16 && nsplit > 1 &&
-                      groups->num_groups > 0 && groups->max_skip > 0 && groups->max_group_size > 0;
+                      groups->num_groups > 0 && groups->max_skip > 0 &&
+                      groups->max_group_size > 0 && (wpg == 1 || wpg == 2 || wpg == 4 || wpg == 8);
   if (shared) {
     const int quads = (groups->max_group_size + 3) / 4;
     const int nshared = min(groups->max_skip, nsplit);
-    const long n_shared = (long)nshared * quads * zg * groups->num_groups;
+    // a shared workgroup: kHeads KV heads x kQuads quads (SharedGeom<wpg>)
+    const int wq = wpg < 4 ? wpg : 4, wh = wpg / wq;
+    const int hgroups = (g.num_kv_heads + wh - 1) / wh, qgroups = (quads + wq - 1) / wq;
+    const long n_shared = (long)nshared * qgroups * hgroups * groups->num_groups;
     const long per = (n_shared + 7) / 8;
     const long nwg = 8 * per + (long)nsplit * num_seqs * zg;
     if (nwg > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode_shared_kernel, dim3((unsigned)nwg), dim3(64 * wpg), 0, stream, out,
+    auto kernel = wpg == 8   ? decode_shared_kernel<8>
+                  : wpg == 4 ? decode_shared_kernel<4>
+                  : wpg == 2 ? decode_shared_kernel<2>
+                             : decode_shared_kernel<1>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(64 * wpg), 0, stream, out,
                        ws_o, ws_ml, (const _Float16*)q, (const _Float16*)k_arena,
                        (const _Float16*)v_arena, block_table, max_blocks, context_lens,
                        groups->group_start, groups->row_skip, scale_log2, g.num_kv_heads, nsplit,
-                       g.num_blocks, zg, num_seqs, nshared, quads, (int)n_shared, (int)per);
+                       g.num_blocks, zg, num_seqs, nshared, hgroups, qgroups, (int)n_shared,
+                       (int)per);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_combine(g, out, ws_o, ws_ml, context_lens, nullptr, 0, max_blocks,

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "fp16_shape.h"
 #include "rope_core.h"
@@ -39,6 +40,15 @@ template <bool kNT>
 __device__ inline u32x2 ld8(const _Float16* p) {
   if constexpr (kNT) return __builtin_nontemporal_load((const u32x2*)p);
   else return *(const u32x2*)p;
+}
+
+// Steps f(0), f(1), ... f(N - 1) as straight-line code, stopping after the
+// first that returns false: an unrolled loop with an early exit, which the
+// compiler does not unroll when written as a loop with a break (it then
+// indexes the pair buffers at run time, from scratch memory).
+template <typename F, int... Is>
+__device__ __forceinline__ void run_steps(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}) && ...);
 }
 
 // The K and V tiles of a pair of arena blocks A, B (32 tokens), already in the
@@ -348,32 +358,37 @@ __device__ __forceinline__ void decode_split_unit(
   };
 
   // Two pair buffers in flight, loop fully unrolled (a split is at most
-  // kSB / 2 pairs).  The prefetch is issued unconditionally (past the last
-  // pair it re-requests the last pair, a cache hit), so the loads outstanding
-  // at each wait are the same on every path and the wait before a pair's MFMAs
-  // covers that pair only, never the prefetch behind it.  (The fused append
-  // has requested the second pair already.)
-#pragma unroll
-  for (int p = 0; p < kSB / 2; ++p) {
+  // kSB / 2 pairs).  Within the split's pairs the prefetch is issued
+  // unconditionally (for the last pair it re-requests that pair, a cache
+  // hit), so the loads outstanding at each wait are the same on every path
+  // and the wait before a pair's MFMAs covers that pair only, never the
+  // prefetch behind it; the loop is left (a wave-uniform branch) as soon as
+  // the split's pairs are done (the fused append: all but the last, which is
+  // computed after the loop), so a short split issues no loads past its end.
+  // (A loop that ran all kSB / 2 iterations and re-requested the last pair in
+  // each measured ~17 us for a one-pair split under load, against ~24 us for
+  // a whole one: the re-requests occupy the compute unit's vector-memory
+  // path.)  Pair p is in buffer p & 1.  (The fused append has requested the
+  // second pair already.)
+  run_steps([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    if (kAppend ? p + 1 >= npairs : p >= npairs) return false;
     if (p + 1 < kSB / 2 && !(kAppend && p == 0)) {
       int ba, bb;
       pair_ids(min(p + 1, npairs - 1), ba, bb);
       buf[(p + 1) & 1] = load_pair<kNT>(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
       __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the compute
     }
-    if constexpr (kAppend) {
-      if (p + 1 < npairs) compute(buf[p & 1], p, std::integral_constant<int, 1>{});
-    } else {
-      if (p < npairs) compute(buf[p & 1], p, std::integral_constant<int, 0>{});
-    }
-  }
+    if constexpr (kAppend) compute(buf[p & 1], p, std::integral_constant<int, 1>{});
+    else compute(buf[p & 1], p, std::integral_constant<int, 0>{});
+    return true;
+  }, std::make_integer_sequence<int, kSB / 2>{});
   if constexpr (kAppend) {
-    // The last pair, after the loop: the last prefetch (at p = kSB / 2 - 2,
-    // clamped to the last pair) left pair npairs - 1 in buffer
-    // (kSB / 2 - 1) & 1.  The new token (the context's last key) enters from
-    // registers: key row `slot` of its block, and the value element of key
-    // slot in lane group slot >> 2.
-    Pair& last = buf[(kSB / 2 - 1) & 1];
+    // The last pair, after the loop, from buffer (npairs - 1) & 1.  The new
+    // token (the context's last key) enters from registers: key row `slot`
+    // of its block, and the value element of key slot in lane group
+    // slot >> 2.
+    Pair last = ((npairs - 1) & 1) ? buf[1] : buf[0];
     if (app_kv) {
       const int slot = pos & 15, ab = ((pos >> 4) - blk0) & 1;
       // (ab and slot are wave-uniform; constant indices keep the pair in registers)

@@ -110,6 +110,9 @@ struct CodesI8 {
     append_v_i8(vp, vt, slot, kD, lane);
   }
   static constexpr int kAhead = PKV_DECODE_I8_AHEAD;  // pairs in flight behind the computed one
+  // the pair loop runs its whole length (the early exit's extra paths spill
+  // at this unit's 168 registers, three waves per SIMD)
+  static constexpr bool kEarlyExit = false;
   static constexpr float kPvBoost = 64.f;
   static constexpr int kDimOrder[8] = {0, 1, 2, 3, 4, 5, 6, 7};
   static constexpr int kKeyOrder[8] = {0, 1, 2, 3, 4, 5, 6, 7};
@@ -143,6 +146,7 @@ __device__ inline uint32_t nib_hi(uint32_t w) {
 
 struct CodesI4 {
   static constexpr int kAhead = PKV_DECODE_I4_AHEAD;
+  static constexpr bool kEarlyExit = true;  // the pair loop stops at the split's end
   static constexpr size_t kTile = i4_tile_bytes(kD);
   // (one token per sequence: the byte partner slot ^ 4 is never appended by
   // the same call, so the new nibble merges with the stored one)
@@ -408,19 +412,51 @@ __device__ __forceinline__ void decode_split_q_unit(
     pair_ids(min(p, npairs - 1), ba, bb);
     buf[p] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
   }
-#pragma unroll
-  for (int p = 0; p < kSB / 2; ++p) {
-    if (p + kAhead < kSB / 2) {
-      int ba, bb;
-      pair_ids(min(p + kAhead, npairs - 1), ba, bb);
-      buf[(p + kAhead) % (kAhead + 1)] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
-      __builtin_amdgcn_sched_barrier(0);
+  if constexpr (Codes::kEarlyExit) {
+    // The loop is left (a wave-uniform branch) once the full pairs are done,
+    // so a short split issues no loads past its end; pair p is in buffer
+    // p % (kAhead + 1), and the tail pair, requested kAhead iterations
+    // earlier or before the loop, is taken from its buffer after it.
+    run_steps([&](auto P) {
+      constexpr int p = decltype(P)::value;
+      if (p >= n_full) return false;
+      if (p + kAhead < kSB / 2) {
+        int ba, bb;
+        pair_ids(min(p + kAhead, npairs - 1), ba, bb);
+        buf[(p + kAhead) % (kAhead + 1)] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      compute(buf[p % (kAhead + 1)], p, std::false_type{});
+      return true;
+    }, std::make_integer_sequence<int, kSB / 2>{});
+    if (has_tail) {
+      // (one branch per buffer: a copy of the selected buffer would cost a
+      // pair's registers)
+      const int tb = (npairs - 1) % (kAhead + 1);
+      run_steps([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if (tb != i) return true;
+        compute(buf[i], npairs - 1, std::true_type{});
+        return false;
+      }, std::make_integer_sequence<int, kAhead + 1>{});
     }
-    if (p < n_full) compute(buf[p % (kAhead + 1)], p, std::false_type{});
+  } else {
+    // The whole loop: past the split's pairs the prefetch re-requests the
+    // last pair (cache hits), so the last prefetch (at
+    // p = kSB / 2 - 1 - kAhead, clamped to the last pair) leaves pair
+    // npairs - 1 in buffer (kSB / 2 - 1) % (kAhead + 1), whatever npairs is.
+#pragma unroll
+    for (int p = 0; p < kSB / 2; ++p) {
+      if (p + kAhead < kSB / 2) {
+        int ba, bb;
+        pair_ids(min(p + kAhead, npairs - 1), ba, bb);
+        buf[(p + kAhead) % (kAhead + 1)] = Codes::load(k_arena, v_arena, ba, bb, Hkv, g, ln, lq);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (p < n_full) compute(buf[p % (kAhead + 1)], p, std::false_type{});
+    }
+    if (has_tail) compute(buf[(kSB / 2 - 1) % (kAhead + 1)], npairs - 1, std::true_type{});
   }
-  // The last prefetch (at p = kSB / 2 - 1 - kAhead, clamped to the last
-  // pair) left pair npairs - 1 in this buffer, whatever npairs is.
-  if (has_tail) compute(buf[(kSB / 2 - 1) % (kAhead + 1)], npairs - 1, std::true_type{});
 
   float l_row = l_run;
   l_row += __shfl_xor(l_row, 16);
