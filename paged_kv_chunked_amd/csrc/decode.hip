@@ -340,18 +340,20 @@ __device__ __forceinline__ void decode_shared_unit(
 // split mod 8, the two XCDs drawing two splits each were full, and every
 // own-split workgroup, ids after them, started only when their shared units
 // ended, serialising the two kinds).  So:
-//   * the first n0 = num_seqs * zheads workgroups take every row's first
-//     own split (a whole split unless the row ends in it);
-//   * the next 8 per (per = ceil(n_shared / 8)) take the shared units, the
+//   * the first nsplit_max * n0 workgroups (n0 = num_seqs * zheads) take the
+//     rows' own splits: own split k of row b for KV-head group z in the order
+//     (k, z, b), b fastest (all rows' first own splits, then second ones, ...;
+//     k past a row's splits only exits);
+//   * the last 8 per (per = ceil(n_shared / 8)) take the shared units, the
 //     i-th of them unit (i mod 8) * per + i / 8: each XCD runs a run of
 //     consecutive units, i.e. an even share, and a split's workgroups fall
-//     on one or two XCDs;
-//   * the rest take own split k >= 1 of row b for KV-head group z in the
-//     order (k, z, b), b fastest; the index space's tail (k past a row's
-//     splits) only exits.
+//     on one or two XCDs.
 // When the units outnumber the compute units, the ones left waiting are
-// rows' later own splits, which end a row and are mostly short, and they
-// wait for the first unit of their XCD to end.
+// shared units, all of one length, and they start as a row's short last
+// split ends (measured on the shared workload, 160 shared and ~126 own
+// units: with the shared units before the rows' later splits, long later
+// splits waited for free compute units and ended at ~40 us; 8 of the 10 us
+// of that tail go with this order).
 template <int kWaves>
 __global__ __launch_bounds__(64 * kWaves, PKV_DECODE_WAVES_PER_SIMD) void decode_shared_kernel(
     float* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
@@ -362,19 +364,16 @@ __global__ __launch_bounds__(64 * kWaves, PKV_DECODE_WAVES_PER_SIMD) void decode
     int num_blocks, int zheads, int num_seqs, int nshared, int hgroups, int qgroups,
     int n_shared, int per) {
   __shared__ u32x4 lds[SharedGeom<kWaves>::kLds / 16];
-  const int n0 = num_seqs * zheads;
-  int j = blockIdx.x;
-  if (j >= n0) {
-    const int i = j - n0;
-    if (i < 8 * per) {
-      const int u = (i & 7) * per + (i >> 3);
-      if (u < n_shared)
-        decode_shared_unit<kWaves>(lds, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks,
-                                   group_start, row_skip, scale_log2, Hkv, nsplit_max, num_blocks,
-                                   hgroups, num_seqs, nshared, qgroups, u);
-      return;
-    }
-    j = i - 8 * per + n0;
+  const int n_own = nsplit_max * num_seqs * zheads;
+  const int j = blockIdx.x;
+  if (j >= n_own) {
+    const int i = j - n_own;
+    const int u = (i & 7) * per + (i >> 3);
+    if (u < n_shared)
+      decode_shared_unit<kWaves>(lds, ws_o, ws_ml, q, k_arena, v_arena, block_table, max_blocks,
+                                 group_start, row_skip, scale_log2, Hkv, nsplit_max, num_blocks,
+                                 hgroups, num_seqs, nshared, qgroups, u);
+    return;
   }
   const int b = j % num_seqs, rest = j / num_seqs;
   const int z = rest % zheads, k = rest / zheads;
