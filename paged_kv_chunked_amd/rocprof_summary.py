@@ -34,9 +34,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 # kernel call -> (kernel symbol substrings, source files whose change invalidates it)
-_DECODE_SRC = ("decode.hip", "decode_core.h", "decode_q_core.h", "fp16_shape.h", "pkv_internal.h",
-               "quant_codes.h", "quant_append_core.h", "rope_core.h")
-_CHUNK_SRC = ("chunk.hip", "chunk_core.h", "fp16_shape.h", "pkv_internal.h", "quant_codes.h")
+_DECODE_SRC = ("decode.hip", "decode_core.h", "decode_q_core.h", "fp16_shape.h", "lds_dma.h",
+               "pkv_internal.h", "quant_codes.h", "quant_append_core.h", "rope_core.h")
+_CHUNK_SRC = ("chunk.hip", "chunk_core.h", "fp16_shape.h", "lds_dma.h", "pkv_internal.h",
+              "quant_codes.h")
 CALLS = {
     "paged_attention_decode": (("decode_split_kernel", "decode_combine_kernel"), _DECODE_SRC),
     "paged_attention_decode_append": (("decode_split_append_kernel", "decode_combine_kernel"),
@@ -55,9 +56,9 @@ CALLS = {
                                   _CHUNK_SRC),
     "paged_attention_mixed": (("mixed_kernel", "mixed_order_kernel"),
                               ("mixed.hip", "chunk_core.h", "decode_core.h", "decode_q_core.h",
-                               "fp16_shape.h", "pkv_internal.h", "quant_codes.h",
+                               "fp16_shape.h", "lds_dma.h", "pkv_internal.h", "quant_codes.h",
                                "quant_append_core.h", "rope_core.h")),
-    "kv_append_rope": (("append_rope_kernel", "append_rope_vec_kernel"),
+    "kv_append_rope": (("append_rope_kernel", "append_rope_vec_kernel", "append_rope_block_kernel"),
                        ("append.hip", "rope_core.h", "quant_append_core.h", "pkv_internal.h")),
 }
 
