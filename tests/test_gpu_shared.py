@@ -34,9 +34,10 @@ def say(msg):
     print(f"[gpu-shared] {msg}", flush=True)
 
 
-def two_prompts(seed=77):
+def two_prompts(seed=77, heads=(32, 8)):
     """Rows 0-4 continue an 800-token prompt, rows 5-6 a 416-token one, rows 7-8
-    are independent: groups of 5, 2, 1, 1 (skips 2, 1, 0, 0)."""
+    are independent: groups of 5, 2, 1, 1 (skips 2, 1, 0, 0).  ``heads`` =
+    (query heads, KV heads)."""
     rng = np.random.default_rng(seed)
     prompts = [(800, 5), (416, 2)]
     seqs, parents, pool_seqs = [], [], 0
@@ -66,7 +67,8 @@ def two_prompts(seed=77):
             script.append(("fill", fi, b, pl, p - pl))
             fi += 1
     step = tuple(StepSeq(b, p, 1) for b, (p, _) in enumerate(seqs))
-    return Workload(name="two_prompts", seed=seed, dtype="f16", num_q_heads=32, num_kv_heads=8,
+    return Workload(name=f"two_prompts_{heads[0]}q{heads[1]}kv", seed=seed, dtype="f16",
+                    num_q_heads=heads[0], num_kv_heads=heads[1],
                     head_dim=128, theta=5.0e5, num_blocks=num_blocks, max_blocks_per_seq=120,
                     num_pool_seqs=S + 2, script=script, step=step)
 
@@ -124,6 +126,15 @@ def check(w, sample_rows):
 
 def test_two_prompts_bitwise_equal_to_decode():
     check(two_prompts(), sample_rows=[0, 4, 5, 8])
+
+
+# Workgroups of 4, 2 and 1 KV heads (the shared units then hold 1 head x 4, 2
+# and 1 quads), 16 KV heads (two head groups), and 3 KV heads, whose
+# workgroup width the shared units do not take (the call computes every split
+# per row, the same result).
+@pytest.mark.parametrize("heads", [(16, 4), (8, 2), (4, 1), (64, 16), (12, 3)])
+def test_two_prompts_other_head_counts(heads):
+    check(two_prompts(heads=heads), sample_rows=[0, 5, 8])
 
 
 def test_one_shared_system_prompt():
