@@ -4,15 +4,16 @@
 Default run (N = 1):
   * decode: 64 decode tokens, contexts U[512, 4096], one Llama-3-8B-shaped layer
     (Hq 32 / Hkv 8, head dim 128, fp16, 16-token blocks, shuffled arena).  A
-    step = the 64 new tokens' append (RoPE, arena write) and the decode, in
-    one paged_attention_decode_append call (split kernel with the append
-    fused + log-sum-exp combine; drawn queries in, rotated queries to a buffer
-    of their own, so every step sees the same input).  `value` is the
-    algorithmic decode bytes of one step / step time.  The same step as
-    kv_append_rope + paged_attention_decode, and the decode call alone, are
-    reported beside it ("decode_separate_calls"; --separate-append makes the
-    two calls the timed step and reports the fused form as
-    "decode_append_fused").
+    step = the 64 new tokens' append (RoPE, arena write) and the decode, as
+    the two boundary calls kv_append_rope + paged_attention_decode (split
+    kernel + log-sum-exp combine; drawn queries in, rotated queries to a
+    buffer of their own, so every step sees the same input).  `value` is the
+    algorithmic decode bytes of one step / step time; `roofline` refers to
+    the decode call.  The same step as one paged_attention_decode_append call
+    (the append fused into the split kernel, a faster step) is reported beside
+    it ("decode_append_fused", with its own roofline); --fused-append makes
+    the fused call the timed step and the `roofline` kernel, and reports the
+    two-call form as "decode_separate_calls".
   * chunk prefill (reported under "chunk_prefill"): 8 sequences with cached
     prefixes 16*U{0..224} and a 512-token chunk each; a step = kv_append_rope
     + paged_attention_chunk; TFLOP/s over visible pairs.
@@ -27,7 +28,7 @@ Inputs are synthetic and resident in HBM before timing.  Each timed step
 rotates over --layers copies of the arena (a layer's worth each) so repeated
 steps cannot be served from the 256 MB Infinity Cache.
 
-`roofline` refers to the dominant kernel call (paged_attention_decode_append): its
+`roofline` refers to the dominant kernel call (paged_attention_decode): its
 average duration over --steps calls issued back to back (rotating the arena
 copies) between two HIP events on the stream it is launched on
 (`avg_launch_ms`); `avg_launch_ms_isolated` is the mean of per-call events in
@@ -110,7 +111,7 @@ def bench_decode(torch, args, kv_bits=0):
     fp16 arenas the step is one paged_attention_decode_append call (the new
     tokens' append fused into the decode), and the same step as two calls
     (kv_append_rope then paged_attention_decode) and the decode call alone are
-    timed beside it (--separate-append swaps the two forms); for quantized
+    timed beside it (--fused-append swaps the two forms); for quantized
     arenas the step is the two calls, with the fused call timed beside it."""
     import dataclasses
     from paged_kv_chunked_amd import harness, workloads
@@ -120,7 +121,7 @@ def bench_decode(torch, args, kv_bits=0):
     log(f"decode set-up: {w.num_blocks} blocks")
     dw = harness.DeviceWorkload(w)
     layers = make_layers(torch, dw, args.layers)
-    fused = kv_bits == 0 and not args.separate_append
+    fused = kv_bits == 0 and args.fused_append
     events = []
 
     def call(i):
@@ -501,12 +502,15 @@ def cpu_baseline_chunk(w, target_s, reps=3):
 
 def plain_rates_GBps(torch, nbytes, copies=4, reps=20):
     """Plain device streams over ``nbytes`` in the same run, as the achievable
-    HBM rate beside the decode's: a read (torch's sum over fp32) and a device
-    copy (read + write bytes counted), each over ``copies`` buffers in turn so
-    repeated passes are not served by the Infinity Cache."""
-    n = nbytes // 4
+    HBM rate beside the decode's: a read (pkv_stream_read: the 16-byte
+    non-temporal loads of the decode's K/V reads in a grid-stride loop) and a
+    device copy (torch; read + write bytes counted), each over ``copies``
+    buffers in turn so repeated passes are not served by the Infinity Cache."""
+    import paged_kv_chunked_amd as pkv
+    n = nbytes // 16 * 4
     bufs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(copies)]
     dst = torch.empty(n, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def timed(fn):
         for i in range(copies):
@@ -521,9 +525,9 @@ def plain_rates_GBps(torch, nbytes, copies=4, reps=20):
         e.synchronize()
         return a.elapsed_time(e) / reps
 
-    ms_read = timed(lambda i: torch.sum(bufs[i % copies]))
+    ms_read = timed(lambda i: pkv.pkv_stream_read(bufs[i % copies], sink))
     ms_copy = timed(lambda i: dst.copy_(bufs[i % copies]))
-    del bufs, dst
+    del bufs, dst, sink
     return n * 4 / (ms_read * 1e-3) / 1e9, 2 * n * 4 / (ms_copy * 1e-3) / 1e9
 
 
@@ -541,8 +545,8 @@ def main():
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-tp8", action="store_true")
-    ap.add_argument("--separate-append", action="store_true",
-                    help="time the fp16 decode step as kv_append_rope + paged_attention_decode")
+    ap.add_argument("--fused-append", action="store_true",
+                    help="time the fp16 decode step as one paged_attention_decode_append call")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode leg (profiling the chunk kernel alone)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,

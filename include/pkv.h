@@ -259,8 +259,9 @@ pkv_status paged_attention_decode_noalloc(const pkv_geom* geom, void* out, int32
  * max_skip     host bound of row_skip; max_group_size host bound of a group's
  *              row count.  Other arguments as for paged_attention_decode.
  * num_groups == 0 is plain paged_attention_decode.  Arenas other than fp16
- * with head_dim 128 and 4 query heads per KV head compute every split per
- * row (same result).
+ * with head_dim 128 and 4 query heads per KV head, and 3, 5, 6 or 7 KV heads
+ * (whose workgroup of one wave per KV head holds 3, 5, 6 or 7 waves), compute
+ * every split per row (same result).
  * ------------------------------------------------------------------------- */
 pkv_status paged_attention_decode_shared(
     const pkv_geom* geom, void* out, int32_t out_dtype, const void* q, const void* k_arena,
@@ -453,6 +454,17 @@ pkv_status pkv_validate_tables(const pkv_geom* geom, const int32_t* h_block_tabl
  * overflow to infinity), the same routine kv_append_rope uses on the device,
  * run on the host: n values from x to out (IEEE binary16 bit patterns). */
 pkv_status pkv_f64_to_f16_host(const double* x, uint16_t* out, int64_t n);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helper (not a step of the attention path): reads `bytes` of the
+ * device buffer `src` once with the 16-byte non-temporal loads the decode
+ * kernels use for K/V, on `stream`, so a benchmark can time the achievable
+ * HBM read rate beside their rooflines.  src: device, 16-byte aligned;
+ * bytes: a multiple of 16; sink: device, at least 4 bytes, written only for
+ * one data-dependent value (it keeps the loads live).  Returns PKV_ERR_NULL /
+ * PKV_ERR_RANGE on bad arguments, PKV_ERR_HIP on a launch failure.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -104,6 +104,7 @@ _SIGS = {
     "pkv_radix_num_nodes": (_I32, [_P]),
     "pkv_validate_tables": (ctypes.c_int, [_PG, _P, _I32, _P, _I32]),
     "pkv_f64_to_f16_host": (ctypes.c_int, [_P, _P, ctypes.c_int64]),
+    "pkv_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
 }
 
 _lib = None
@@ -341,6 +342,14 @@ def paged_attention_mixed(g: Geom, out, q, k_arena, v_arena, block_table, cu_q_l
 def pkv_copy_blocks(g: Geom, k_arena, v_arena, src_dst, stream=None) -> None:
     _check(lib().pkv_copy_blocks(ctypes.byref(g), _ptr(k_arena), _ptr(v_arena), _ptr(src_dst),
                                  src_dst.shape[0], _stream(stream)), "pkv_copy_blocks")
+
+
+def pkv_stream_read(src, sink, stream=None) -> None:
+    """Measurement helper: one streaming read of the device tensor src (its
+    bytes, a multiple of 16) on the stream; sink: a device tensor of at least 4
+    bytes."""
+    _check(lib().pkv_stream_read(_ptr(src), _nbytes(src), _ptr(sink), _stream(stream)),
+           "pkv_stream_read")
 
 
 def pkv_swap_bytes(g: Geom, n: int) -> int:

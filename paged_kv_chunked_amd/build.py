@@ -23,7 +23,7 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = "gfx950"
 SOURCES = ["host.cpp", "api.hip", "append.hip", "decode.hip", "chunk.hip", "mixed.hip",
-           "generic.hip", "copy.hip"]
+           "generic.hip", "copy.hip", "stream.hip"]
 # Per-file device flags.  The chunk kernel never lets a NaN reach a max (masked
 # scores are replaced by -inf with a select, V past the sequence is zeroed as
 # integers), so its device code may drop the quieting of max operands.  The

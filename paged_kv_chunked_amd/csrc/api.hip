@@ -24,6 +24,11 @@ pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_
 
 }  // namespace
 
+namespace pkv {
+// measurement helper (stream.hip)
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
+}  // namespace pkv
+
 extern "C" {
 
 pkv_status kv_append_rope(const pkv_geom* geom, void* q, void* q_out, const void* k,
@@ -294,6 +299,12 @@ pkv_status pkv_swap_out(const pkv_geom* geom, const void* k_arena, const void* v
 pkv_status pkv_swap_in(const pkv_geom* geom, void* k_arena, void* v_arena, const int32_t* ids,
                        int32_t n, const void* buf, size_t buf_bytes, void* stream) {
   return swap_common(geom, k_arena, v_arena, ids, n, (void*)buf, buf_bytes, true, stream);
+}
+
+pkv_status pkv_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return PKV_ERR_NULL;
+  if (bytes % 16 != 0 || ((uintptr_t)src & 15) != 0) return PKV_ERR_RANGE;
+  return hip_status(pkv::launch_stream_read(src, bytes, sink, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -373,6 +373,15 @@ def test_swap_entry_point_errors(lib):
     assert lib.pkv_swap_out(gp, FAKE, FAKE, FAKE, -1, FAKE, 0, None) == 4
 
 
+def test_stream_read_helper_errors(lib):
+    # the measurement helper rejects nulls, sizes not a multiple of 16 and a
+    # misaligned source before any launch
+    assert lib.pkv_stream_read(None, 16, FAKE, None) == 1
+    assert lib.pkv_stream_read(FAKE, 16, None, None) == 1
+    assert lib.pkv_stream_read(FAKE, 24, FAKE, None) == 4
+    assert lib.pkv_stream_read(ctypes.c_void_p(0x1008), 16, FAKE, None) == 4
+
+
 def test_mixed_entry_point_errors(lib):
     g = _geom()
     gp = ctypes.byref(g)
