@@ -701,6 +701,10 @@ def main():
             },
         }
         del dwq
+        # the achievable read rate for this call's byte count, same run
+        read_q, _ = plain_rates_GBps(torch, nbytesq)
+        out[f"decode_int{bits}"]["roofline"]["plain_read_GBps"] = round(read_q, 1)
+        out[f"decode_int{bits}"]["roofline"]["frac_of_plain_read"] = round(achq / read_q, 4)
     if not args.no_shared:
         out["decode_shared_prefix"] = bench_shared(torch, args)
         log(f"shared-prefix decode: {out['decode_shared_prefix']}")
