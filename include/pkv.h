@@ -311,6 +311,37 @@ pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dt
                                  int32_t max_context_len, float scale, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* paged_attention_chunk in two halves, for a step that runs the same batch
+ * through several layers (part 3 section 5: a step's batch is fixed before
+ * its layers run).  paged_attention_chunk_plan writes the tuned kernel's
+ * schedule (the longest-first order of the (sequence, 64-row tile) items; it
+ * orders work only and changes no result) into the workspace; it reads
+ * cu_q_lens and chunk_start and takes the same sizes and checks as
+ * paged_attention_chunk.  paged_attention_chunk_run takes
+ * paged_attention_chunk's arguments and computes exactly what it computes
+ * (bit for bit), over the schedule found in the workspace: it must follow a
+ * plan call on the same stream with the same workspace, cu_q_lens,
+ * chunk_start (contents too), num_seqs, num_tokens, max_q_len and
+ * max_blocks_per_seq; q, the arenas, the block table's entries, out and scale
+ * may change between runs.  A run over a schedule of another batch gives
+ * undefined output rows, never an access outside the arguments' ranges
+ * (entries outside the item range are skipped).  Off the tuned path the plan
+ * does nothing and the run is the generic kernel.  Errors as for
+ * paged_attention_chunk (the plan does not check q, out, the arenas or the
+ * block table). */
+pkv_status paged_attention_chunk_plan(const pkv_geom* geom, int32_t max_blocks_per_seq,
+                                      const int32_t* cu_q_lens, const int32_t* chunk_start,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                                      int32_t max_context_len, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+pkv_status paged_attention_chunk_run(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                     const void* q, const void* k_arena, const void* v_arena,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* cu_q_lens, const int32_t* chunk_start,
+                                     int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                                     int32_t max_context_len, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * paged_attention_mixed — one continuous-batching step (part 3 section 5: each
  * step mixes prefill chunks and decode tokens under a token budget) in one

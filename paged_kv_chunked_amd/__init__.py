@@ -75,6 +75,11 @@ _SIGS = {
     "paged_attention_chunk": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32,
                                              _I32, _I32, _I32, ctypes.c_float, _P,
                                              ctypes.c_size_t, _P]),
+    "paged_attention_chunk_plan": (ctypes.c_int, [_PG, _I32, _P, _P, _I32, _I32, _I32, _I32, _P,
+                                                   ctypes.c_size_t, _P]),
+    "paged_attention_chunk_run": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _P,
+                                                 _I32, _I32, _I32, _I32, ctypes.c_float, _P,
+                                                 ctypes.c_size_t, _P]),
     "paged_attention_mixed_workspace_bytes": (ctypes.c_int, [_PG, _I32, _I32, _I32,
                                                              ctypes.POINTER(ctypes.c_size_t)]),
     "paged_attention_mixed": (ctypes.c_int, [_PG, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32,
@@ -306,6 +311,36 @@ def paged_attention_chunk(g: Geom, out, q, k_arena, v_arena, block_table, cu_q_l
                                        q.shape[0], max_q_len, max_context_len, scale,
                                        _ptr(workspace), ws_bytes, _stream(stream)),
            "paged_attention_chunk")
+
+
+def paged_attention_chunk_plan(g: Geom, block_table, cu_q_lens, chunk_start, num_tokens: int,
+                               max_q_len: int, max_context_len: int, workspace,
+                               stream=None) -> None:
+    """The schedule of paged_attention_chunk for this batch description into
+    ``workspace`` (``block_table`` only gives its row length); a step plans
+    once and then calls paged_attention_chunk_run per layer."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attention_chunk_plan(ctypes.byref(g), block_table.shape[1],
+                                            _ptr(cu_q_lens), _ptr(chunk_start),
+                                            chunk_start.shape[0], num_tokens, max_q_len,
+                                            max_context_len, _ptr(workspace), ws_bytes,
+                                            _stream(stream)),
+           "paged_attention_chunk_plan")
+
+
+def paged_attention_chunk_run(g: Geom, out, q, k_arena, v_arena, block_table, cu_q_lens,
+                              chunk_start, max_q_len: int, max_context_len: int, scale: float,
+                              workspace, stream=None) -> None:
+    """paged_attention_chunk over the schedule that the last
+    paged_attention_chunk_plan call with the same batch left in ``workspace``."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attention_chunk_run(ctypes.byref(g), _ptr(out), F32, _ptr(q),
+                                           _ptr(k_arena), _ptr(v_arena), _ptr(block_table),
+                                           block_table.shape[1], _ptr(cu_q_lens),
+                                           _ptr(chunk_start), chunk_start.shape[0], q.shape[0],
+                                           max_q_len, max_context_len, scale, _ptr(workspace),
+                                           ws_bytes, _stream(stream)),
+           "paged_attention_chunk_run")
 
 
 def paged_attention_mixed_workspace_bytes(g: Geom, num_seqs: int, num_tokens: int,

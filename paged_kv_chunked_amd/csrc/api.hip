@@ -194,6 +194,49 @@ pkv_status paged_attention_chunk_parts(const pkv_geom* geom, int32_t num_seqs,
   return PKV_OK;
 }
 
+// Checks shared by paged_attention_chunk and its two halves (plan, run).
+static pkv_status check_chunk_batch(const pkv_geom* geom, int32_t max_blocks_per_seq,
+                                    const int32_t* cu_q_lens,
+                                    const int32_t* chunk_start, int32_t num_seqs,
+                                    int32_t num_tokens, int32_t max_q_len,
+                                    int32_t max_context_len, void* workspace,
+                                    size_t workspace_bytes) {
+  if (!cu_q_lens || !chunk_start) return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || max_q_len < 1 || max_context_len < max_q_len ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return PKV_ERR_RANGE;
+  const size_t need = pkv::chunk_workspace_bytes(*geom, num_seqs, num_tokens, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  return PKV_OK;
+}
+
+static pkv_status chunk_call(bool plan, bool run, const pkv_geom* geom, void* out,
+                             int32_t out_dtype, const void* q, const void* k_arena,
+                             const void* v_arena, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                             const int32_t* chunk_start, int32_t num_seqs, int32_t num_tokens,
+                             int32_t max_q_len, int32_t max_context_len, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = check_geom(geom);
+  if (st != PKV_OK) return st;
+  if (run && out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0) return PKV_ERR_RANGE;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (run && (!out || !q || !k_arena || !v_arena || !block_table)) return PKV_ERR_NULL;
+  st = check_chunk_batch(geom, max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs,
+                         num_tokens, max_q_len, max_context_len, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  if (!run)
+    return hip_status(pkv::launch_chunk_plan(*geom, cu_q_lens, chunk_start, max_blocks_per_seq,
+                                             num_seqs, num_tokens, max_q_len, workspace,
+                                             workspace_bytes, (hipStream_t)stream));
+  auto launch = plan ? pkv::launch_chunk : pkv::launch_chunk_run;
+  return hip_status(launch(*geom, (float*)out, q, k_arena, v_arena, block_table,
+                           max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs, num_tokens,
+                           max_q_len, max_context_len, scale, workspace, workspace_bytes,
+                           (hipStream_t)stream));
+}
+
 pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dtype,
                                  const void* q, const void* k_arena, const void* v_arena,
                                  const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -201,22 +244,31 @@ pkv_status paged_attention_chunk(const pkv_geom* geom, void* out, int32_t out_dt
                                  int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
                                  int32_t max_context_len, float scale, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  pkv_status st = check_geom(geom);
-  if (st != PKV_OK) return st;
-  if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
-  if (num_seqs < 0 || num_tokens < 0) return PKV_ERR_RANGE;
-  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
-  if (!out || !q || !k_arena || !v_arena || !block_table || !cu_q_lens || !chunk_start)
-    return PKV_ERR_NULL;
-  if (max_blocks_per_seq < 1 || max_q_len < 1 || max_context_len < max_q_len ||
-      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
-    return PKV_ERR_RANGE;
-  const size_t need = pkv::chunk_workspace_bytes(*geom, num_seqs, num_tokens, max_context_len);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
-  return hip_status(pkv::launch_chunk(*geom, (float*)out, q, k_arena, v_arena, block_table,
-                                      max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs,
-                                      num_tokens, max_q_len, max_context_len, scale, workspace,
-                                      workspace_bytes, (hipStream_t)stream));
+  return chunk_call(true, true, geom, out, out_dtype, q, k_arena, v_arena, block_table,
+                    max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs, num_tokens, max_q_len,
+                    max_context_len, scale, workspace, workspace_bytes, stream);
+}
+
+pkv_status paged_attention_chunk_plan(const pkv_geom* geom, int32_t max_blocks_per_seq,
+                                      const int32_t* cu_q_lens, const int32_t* chunk_start,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                                      int32_t max_context_len, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return chunk_call(true, false, geom, nullptr, PKV_F32, nullptr, nullptr, nullptr, nullptr,
+                    max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs, num_tokens, max_q_len,
+                    max_context_len, 1.f, workspace, workspace_bytes, stream);
+}
+
+pkv_status paged_attention_chunk_run(const pkv_geom* geom, void* out, int32_t out_dtype,
+                                     const void* q, const void* k_arena, const void* v_arena,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* cu_q_lens, const int32_t* chunk_start,
+                                     int32_t num_seqs, int32_t num_tokens, int32_t max_q_len,
+                                     int32_t max_context_len, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return chunk_call(false, true, geom, out, out_dtype, q, k_arena, v_arena, block_table,
+                    max_blocks_per_seq, cu_q_lens, chunk_start, num_seqs, num_tokens, max_q_len,
+                    max_context_len, scale, workspace, workspace_bytes, stream);
 }
 
 pkv_status paged_attention_mixed_workspace_bytes(const pkv_geom* geom, int32_t num_seqs,

@@ -150,7 +150,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_mfma_kernel(
   const int k = i / (Hkv * parts), rem = i - k * (Hkv * parts);
   const int part = rem / Hkv, g = rem - part * Hkv;
   if (k >= num_seqs * n_rtiles) return;
+  // (a schedule left by another batch description may hold any value: an
+  // entry outside the item range is skipped, never followed)
   const int item = order[k];
+  if ((unsigned)item >= (unsigned)(num_seqs * n_rtiles)) return;
   const int b = item / n_rtiles, rt = item - b * n_rtiles;
   __shared__ u32x4 lds[ChunkLds<kQ>::kUnits];
   chunk_tile_unit<kQ>(lds, out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens, chunk_start,
@@ -230,24 +233,45 @@ size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens,
   return align256(sched) + align256(rows * kD * sizeof(float)) + rows * 2 * sizeof(float);
 }
 
-hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
-                        const void* v_arena, const int32_t* block_table, int max_blocks,
-                        const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
-                        int num_tokens, int max_q_len, int max_context_len, float scale,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)max_context_len;
-  // the fast path tracks maxima of raw scores, which needs scale > 0
-  if (!chunk_fast_path(g) || !(scale > 0.f) || !std::isfinite(scale))
-    return launch_attend_generic(g, out, q, k_arena, v_arena, block_table, max_blocks, nullptr,
-                                 cu_q_lens, chunk_start, num_seqs, num_tokens, scale, stream);
+// The tuned kernel's schedule for one batch description: the longest-first
+// order of the (sequence, 64-row tile) items, one int32 each at the head of the
+// workspace.  It depends only on cu_q_lens, chunk_start, num_seqs, num_tokens,
+// max_q_len and max_blocks, so a step computes it once for all its layers.
+hipError_t launch_chunk_plan(const pkv_geom& g, const int32_t* cu_q_lens,
+                             const int32_t* chunk_start, int max_blocks, int num_seqs,
+                             int num_tokens, int max_q_len, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!chunk_fast_path(g)) return hipSuccess;  // the generic kernel needs no schedule
   // no sequence has more rows than the batch
   const int n_rtiles = (min(max_q_len, num_tokens) + kRows - 1) / kRows;
   const long n_items = (long)num_seqs * n_rtiles;
   if (!workspace || workspace_bytes < (size_t)n_items * sizeof(int32_t))
     return hipErrorInvalidValue;
-  int32_t* order = (int32_t*)workspace;
-  hipLaunchKernelGGL(chunk_order_kernel, dim3(1), dim3(1024), 0, stream, order, cu_q_lens,
-                     chunk_start, num_seqs, n_rtiles, max_blocks, num_tokens);
+  hipLaunchKernelGGL(chunk_order_kernel, dim3(1), dim3(1024), 0, stream, (int32_t*)workspace,
+                     cu_q_lens, chunk_start, num_seqs, n_rtiles, max_blocks, num_tokens);
+  return hipGetLastError();
+}
+
+static bool chunk_tuned(const pkv_geom& g, float scale) {
+  // the fast path tracks maxima of raw scores, which needs scale > 0
+  return chunk_fast_path(g) && scale > 0.f && std::isfinite(scale);
+}
+
+// The attention (and, for a split call, the merge of its parts) over the
+// schedule that launch_chunk_plan left in the workspace.
+hipError_t launch_chunk_run(const pkv_geom& g, float* out, const void* q, const void* k_arena,
+                            const void* v_arena, const int32_t* block_table, int max_blocks,
+                            const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
+                            int num_tokens, int max_q_len, int max_context_len, float scale,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!chunk_tuned(g, scale))
+    return launch_attend_generic(g, out, q, k_arena, v_arena, block_table, max_blocks, nullptr,
+                                 cu_q_lens, chunk_start, num_seqs, num_tokens, scale, stream);
+  const int n_rtiles = (min(max_q_len, num_tokens) + kRows - 1) / kRows;
+  const long n_items = (long)num_seqs * n_rtiles;
+  if (!workspace || workspace_bytes < (size_t)n_items * sizeof(int32_t))
+    return hipErrorInvalidValue;
+  const int32_t* order = (const int32_t*)workspace;
   const float scale_log2 = scale * 1.4426950408889634f;
   const int parts = chunk_parts(g, num_tokens, max_context_len);
   float* part_o = nullptr;
@@ -273,6 +297,22 @@ hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void
                      dim3(256), 0, stream, out, part_o, part_ml, cu_q_lens, chunk_start,
                      num_seqs, num_tokens, max_blocks, g.num_q_heads, parts);
   return hipGetLastError();
+}
+
+hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
+                        const void* v_arena, const int32_t* block_table, int max_blocks,
+                        const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
+                        int num_tokens, int max_q_len, int max_context_len, float scale,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (chunk_tuned(g, scale)) {
+    const hipError_t e = launch_chunk_plan(g, cu_q_lens, chunk_start, max_blocks, num_seqs,
+                                           num_tokens, max_q_len, workspace, workspace_bytes,
+                                           stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_chunk_run(g, out, q, k_arena, v_arena, block_table, max_blocks, cu_q_lens,
+                          chunk_start, num_seqs, num_tokens, max_q_len, max_context_len, scale,
+                          workspace, workspace_bytes, stream);
 }
 
 }  // namespace pkv

@@ -185,11 +185,22 @@ size_t chunk_workspace_bytes(const pkv_geom& g, int num_seqs, int num_tokens,
                              int max_context_len);
 // key-range parts paged_attention_chunk splits a call's items into (1: none)
 int chunk_parts(const pkv_geom& g, int num_tokens, int max_context_len);
+// paged_attention_chunk = launch_chunk_plan (the schedule into the workspace)
+// then launch_chunk_run (the attention over it)
 hipError_t launch_chunk(const pkv_geom& g, float* out, const void* q, const void* k_arena,
                         const void* v_arena, const int32_t* block_table, int max_blocks,
                         const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
                         int num_tokens, int max_q_len, int max_context_len, float scale,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+hipError_t launch_chunk_plan(const pkv_geom& g, const int32_t* cu_q_lens,
+                             const int32_t* chunk_start, int max_blocks, int num_seqs,
+                             int num_tokens, int max_q_len, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+hipError_t launch_chunk_run(const pkv_geom& g, float* out, const void* q, const void* k_arena,
+                            const void* v_arena, const int32_t* block_table, int max_blocks,
+                            const int32_t* cu_q_lens, const int32_t* chunk_start, int num_seqs,
+                            int num_tokens, int max_q_len, int max_context_len, float scale,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 // One attention launch for a varlen batch of prefill chunks and decodes
 // (sequences of one row), with a schedule and decode partials in the workspace.

@@ -18,6 +18,7 @@ from typing import Dict, List
 import numpy as np
 
 from . import (BLOCK_SIZE, DECODE_SPLIT, F16, F32, I4KV, I8KV, Pool, geom, kv_append_rope, paged_attention_chunk,
+               paged_attention_chunk_plan, paged_attention_chunk_run,
                paged_attention_chunk_workspace_bytes, paged_attention_decode_shared,
                paged_attention_mixed, paged_attention_mixed_workspace_bytes,
                paged_attention_decode, paged_attention_decode_append,
@@ -337,6 +338,26 @@ class DeviceWorkload:
                                   self.chunk_bt, self.chunk_cu, self.chunk_starts,
                                   self.chunk_max_q, self.chunk_max_ctx, self.scale,
                                   self.chunk_ws, stream=stream)
+
+    def chunk_plan(self, stream=None):
+        """paged_attention_chunk_plan for the chunk rows (the schedule into
+        ``chunk_ws``)."""
+        self._need_split()
+        if self.chunk_rows:
+            paged_attention_chunk_plan(self.g, self.chunk_bt, self.chunk_cu, self.chunk_starts,
+                                       self.chunk_q.shape[0], self.chunk_max_q,
+                                       self.chunk_max_ctx, self.chunk_ws, stream=stream)
+
+    def chunk_run(self, stream=None, k_arena=None, v_arena=None):
+        """paged_attention_chunk_run over the schedule of the last chunk_plan()."""
+        self._need_split()
+        if self.chunk_rows:
+            paged_attention_chunk_run(self.g, self.chunk_out, self.chunk_q,
+                                      self.k_arena if k_arena is None else k_arena,
+                                      self.v_arena if v_arena is None else v_arena,
+                                      self.chunk_bt, self.chunk_cu, self.chunk_starts,
+                                      self.chunk_max_q, self.chunk_max_ctx, self.scale,
+                                      self.chunk_ws, stream=stream)
 
     def decode_append(self, stream=None, k_arena=None, v_arena=None):
         """The decode rows' append and attention in one paged_attention_decode_append

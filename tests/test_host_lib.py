@@ -297,6 +297,27 @@ def test_entry_point_errors(lib):
                                      64, 500, 0.1, None, need, None) == 5
     g32 = _geom(dtype=1)   # fp32 storage runs the generic kernel: no schedule
     assert pkv.paged_attention_chunk_workspace_bytes(g32, 2, 100, 500) == 0
+    # the chunk call's two halves take its checks (the plan reads no q, out,
+    # arena or block table)
+    plan = lambda *a: lib.paged_attention_chunk_plan(gp, *a)
+    assert plan(64, None, FAKE, 2, 100, 64, 500, FAKE, need, None) == 1     # cu_q_lens
+    assert plan(64, FAKE, None, 2, 100, 64, 500, FAKE, need, None) == 1     # chunk_start
+    assert plan(64, FAKE, FAKE, 2, 100, 64, 4000, FAKE, need, None) == 4    # context > table
+    assert plan(64, FAKE, FAKE, 2, 100, 600, 500, FAKE, need, None) == 4    # rows > context
+    assert plan(64, FAKE, FAKE, 2, 100, 64, 500, FAKE, need - 1, None) == 5
+    assert plan(64, FAKE, FAKE, -1, 100, 64, 500, FAKE, need, None) == 4
+    assert plan(64, None, None, 0, 0, 64, 500, None, 0, None) == 0          # empty batch
+    assert lib.paged_attention_chunk_plan(None, 64, FAKE, FAKE, 2, 100, 64, 500, FAKE, need,
+                                          None) == 1
+    run = lambda *a: lib.paged_attention_chunk_run(gp, *a)
+    assert run(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 2, 100, 64, 500, 0.1, FAKE,
+               need, None) == 3                                            # output dtype
+    assert run(FAKE, 1, FAKE, FAKE, FAKE, None, 64, FAKE, FAKE, 2, 100, 64, 500, 0.1, FAKE,
+               need, None) == 1                                            # block table
+    assert run(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 2, 100, 64, 500, 0.1, None,
+               need, None) == 5
+    assert run(None, 1, None, None, None, None, 4, None, None, 0, 0, 16, 64, 0.1, None, 0,
+               None) == 0
     assert lib.pkv_status_string(5) == b"workspace missing or too small"
 
 
