@@ -32,8 +32,8 @@ steps cannot be served from the 256 MB Infinity Cache.
 
 `roofline` refers to the dominant kernel call (paged_attention_decode): its
 average duration over --steps calls issued back to back (rotating the arena
-copies) between two HIP events on the stream it is launched on
-(`avg_launch_ms`); `avg_launch_ms_isolated` is the mean of per-call events in
+copies) between two HIP events on the stream it is launched on, the median
+of three such windows (`avg_launch_ms`); `avg_launch_ms_isolated` is the mean of per-call events in
 a separate pass of the same steps (an event record adds a gap to the stream,
 so the timed steps carry no events).  `cpu_baseline` times the CPU oracle on
 the same decode workload.
@@ -85,20 +85,25 @@ def time_steps(torch, run_step, steps, warmup, run_step_events=None, kernel_even
     return (t1 - t0) * 1e3 / steps, ms_call
 
 
-def time_back_to_back(torch, call, n):
+def time_back_to_back(torch, call, n, windows=3):
     """Average duration of one call over n calls issued back to back between two
-    HIP events on the stream the kernels are launched on."""
+    HIP events on the stream the kernels are launched on; the median of
+    ``windows`` such windows (the first window after a change of workload can
+    still catch the clocks settling)."""
     stream = torch.cuda.current_stream()
     for i in range(3):
         call(i)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for i in range(n):
-        call(i)
-    b.record(stream)
-    b.synchronize()
-    return a.elapsed_time(b) / n
+    per_call = []
+    for _ in range(windows):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            call(i)
+        b.record(stream)
+        b.synchronize()
+        per_call.append(a.elapsed_time(b) / n)
+    return sorted(per_call)[len(per_call) // 2]
 
 
 def make_layers(torch, dw, n):
